@@ -1,0 +1,122 @@
+"""ctypes binding of libpi.so (the C ABI declared in include/pi.h).
+
+Argument marshalling only: every function forwards integers (device
+addresses, sizes, the hipStream_t handle) to the library and returns its
+status code.  Nothing here computes any part of the sparse FFN, and there is
+no fallback: if libpi.so is missing or fails to load, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int, c_int32, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi.so")
+
+PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_DTYPE = 0, 1, 2, 3, 4
+PI_ERR_UNSUPPORTED, PI_ERR_WORKSPACE, PI_ERR_HIP = 5, 6, 7
+PI_ACT_RELU, PI_ACT_REGLU = 0, 1
+PI_W_F16, PI_W_I4G128 = 0, 1
+PI_PER_TOKEN, PI_UNION = 0, 1
+PI_MAX_BATCH = 32
+
+EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
+           "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
+           "pi_ffn_dense_ref_gpu")
+
+
+class PredDesc(ctypes.Structure):
+    _fields_ = [("w_p1", c_void_p), ("w_p2", c_void_p), ("bias", c_void_p),
+                ("d", c_int32), ("r", c_int32), ("F", c_int32), ("threshold", c_float)]
+
+
+class FfnDesc(ctypes.Structure):
+    _fields_ = [("w_gate", c_void_p), ("w_up", c_void_p), ("w_down", c_void_p),
+                ("s_gate", c_void_p), ("s_up", c_void_p), ("s_down", c_void_p),
+                ("d", c_int32), ("F", c_int32), ("act", c_int32), ("wfmt", c_int32)]
+
+
+class PiError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"[{status}] {detail}")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpi.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.pi_status_string.argtypes, L.pi_status_string.restype = [c_int], ctypes.c_char_p
+        L.pi_last_error.argtypes, L.pi_last_error.restype = [], ctypes.c_char_p
+        L.pi_version.argtypes, L.pi_version.restype = [], c_int
+        L.pi_workspace_bytes.argtypes = [P(PredDesc), P(FfnDesc), c_int]
+        L.pi_workspace_bytes.restype = c_size_t
+        L.pi_workspace_init.argtypes, L.pi_workspace_init.restype = [c_void_p, c_size_t, c_void_p], c_int
+        L.pi_predict.argtypes = [P(PredDesc), c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_size_t, c_void_p]
+        L.pi_predict.restype = c_int
+        L.pi_compact.argtypes = [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                 c_size_t, c_void_p]
+        L.pi_compact.restype = c_int
+        L.pi_sparse_ffn.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]
+        L.pi_sparse_ffn.restype = c_int
+        L.pi_ffn_dense_ref_gpu.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p,
+                                           c_size_t, c_void_p]
+        L.pi_ffn_dense_ref_gpu.restype = c_int
+        _LIB = L
+    return _LIB
+
+
+def _p(desc):
+    return None if desc is None else ctypes.byref(desc)
+
+
+def pi_status_string(status: int) -> str:
+    return lib().pi_status_string(status).decode()
+
+
+def pi_last_error() -> str:
+    return lib().pi_last_error().decode()
+
+
+def pi_version() -> int:
+    return lib().pi_version()
+
+
+def pi_workspace_bytes(pred, ffn, B_max: int) -> int:
+    return lib().pi_workspace_bytes(_p(pred), _p(ffn), B_max)
+
+
+def pi_workspace_init(ws: int, ws_bytes: int, stream: int) -> int:
+    return lib().pi_workspace_init(ws, ws_bytes, stream)
+
+
+def pi_predict(pred, x, B, logits, mask, idx, count, ws, ws_bytes, stream) -> int:
+    return lib().pi_predict(_p(pred), x, B, logits, mask, idx, count, ws, ws_bytes, stream)
+
+
+def pi_compact(mask, B, F, mode, idx, count, ws, ws_bytes, stream) -> int:
+    return lib().pi_compact(mask, B, F, mode, idx, count, ws, ws_bytes, stream)
+
+
+def pi_sparse_ffn(ffn, x, B, idx, count, token_mask, y, ws, ws_bytes, stream) -> int:
+    return lib().pi_sparse_ffn(_p(ffn), x, B, idx, count, token_mask, y, ws, ws_bytes, stream)
+
+
+def pi_ffn_dense_ref_gpu(ffn, x, B, y, ws, ws_bytes, stream) -> int:
+    return lib().pi_ffn_dense_ref_gpu(_p(ffn), x, B, y, ws, ws_bytes, stream)
+
+
+def check(status: int) -> None:
+    """Raise PiError with the library's message for a non-zero status."""
+    if status != PI_OK:
+        raise PiError(status, f"{pi_status_string(status)}: {pi_last_error()}")

@@ -1,0 +1,67 @@
+// Internal interface between the C ABI layer (pi_abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pi.h"
+
+namespace pi {
+
+// ---- arrival-counter slots inside the workspace (unsigned ints) ------------------------------
+constexpr int CNT_PRED1 = 0;      // one per predictor column group (r / 64 <= 256)
+constexpr int CNT_PRED2 = 256;    // one for stage 2's compaction
+constexpr int CNT_DOWN = 512;     // one per down-projection column slice (<= 512)
+constexpr int CNT_UNION = 1024;   // union path (<= 1024)
+constexpr int CNT_TOTAL = 2048;
+constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- predictor launch plan ----------------------------------------------------------------------
+struct PredPlan {
+    int ncg;      // column groups of 64 predictor columns
+    int ku;       // rows per lane in stage 1 (a block covers 32 * ku rows)
+    int nchunk;   // stage-1 row chunks
+    int nb;       // tokens per pass
+    int nblk2;    // stage-2 blocks (64 neurons each)
+    size_t off_z, off_part, bytes;
+};
+PredPlan plan_pred(int d, int r, int F, int B);
+
+// ---- batch-1 FFN launch plan ----------------------------------------------------------------------
+struct FfnPlan {
+    int q;         // 16-byte chunks per lane per row in the up kernel
+    int up_blocks; // 256-thread blocks of the up kernel
+    int cols;      // columns per down slice
+    int nslices, nsplit;
+    size_t off_h, off_part, bytes;
+    // union (B > 1) path
+    int u_tiles;   // max 32-neuron tiles of the union list
+    int u_ksplit;  // neuron splits of the union down product
+    size_t off_H, off_upart;
+};
+FfnPlan plan_ffn(int d, int F, int wfmt, int B);
+
+// ---- launchers (return hipError_t of the launch) ---------------------------------------------------
+hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
+                          float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
+                          char* ws, hipStream_t s);
+
+hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
+                          int32_t* count, hipStream_t s);
+
+// B == 1 sparse (idx/count) or dense (dense_F > 0: neuron k is row k, count = dense_F)
+hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
+                         const int32_t* idx, const int32_t* count, int dense_F, float* y,
+                         char* ws, hipStream_t s);
+
+// 1 < B <= 32 union-mask path on MFMA
+hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
+                            const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
+                            int dense, float* y, char* ws, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace pi

@@ -1,0 +1,399 @@
+// Batch-1 neuron-aware FFN on gfx950 (PowerInfer, "Neuron-aware Operator":
+// work on single row vectors of up/gate and single column vectors of down, read
+// in place from the dense neuron-major matrices, no sparse-format conversion).
+//
+//   up   h[k] = act(W_up[i_k] . x [, W_gate[i_k] . x])   for k < count, i_k = idx[k]
+//        One wave per listed neuron.  Lane l owns the 16-byte chunks l, l+64, ...
+//        of every row, so its slice of x is loaded once into registers and reused
+//        for every neuron the wave handles; every weight byte is read once with a
+//        coalesced 16-byte load; the dot product is a 64-lane reduction.
+//   down y = sum_k h[k] W_down[i_k, :]
+//        2-D tiling: a block owns one column slice (512 fp16 / 2048 int4 columns,
+//        one 16-byte chunk per lane) and one neuron split.  Waves of the block
+//        take interleaved neurons, sum in registers, combine through LDS, and
+//        write one partial row per block; the last-arriving block of each slice
+//        adds the partials in split order (deterministic, no float atomics).
+//
+// int4 group-128 (LLM Runtime page, "01 LLM Runtime"): stored nibble u, value
+// (u - 8) * s.  Up: nibbles are widened to fp16 pairs exactly by OR-ing them
+// into the mantissa of 1024.0 and subtracting 1032, then dotted with x by
+// v_dot2_f32_f16; the per-chunk sum (32 weights, always inside one group) is
+// scaled once.  Down: h*s is formed once per neuron and chunk, nibbles are
+// converted byte-wise to float, and the -8 offset is applied once at the end
+// through the running sum of h*s.
+#include "device_common.h"
+#include "internal.h"
+
+namespace pi {
+namespace {
+
+// ------------------------------------------------------------------------------------------ fp16 up
+template <int Q, bool GLU>
+__global__ __launch_bounds__(256) void k_up_f16(const uint16_t* __restrict__ x,
+                                                const uint16_t* __restrict__ Wg,
+                                                const uint16_t* __restrict__ Wu, int d, int F,
+                                                const int32_t* __restrict__ idx,
+                                                const int32_t* __restrict__ count, int dense_F,
+                                                float* __restrict__ h) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nw = gridDim.x * 4;
+    const int n = dense_F > 0 ? dense_F : min(*count, F);
+    if (gw >= n) return;
+    const int nc = d >> 3;
+    uint4 xr[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int c = lane + 64 * q;
+        xr[q] = c < nc ? ld16(x + 8 * c) : zero4();
+    }
+    for (int k = gw; k < n; k += nw) {
+        const int irow = dense_F > 0 ? k : idx[k];
+        if ((unsigned)irow >= (unsigned)F) {   // not a neuron of this layer: contributes 0
+            if (lane == 0) h[k] = 0.f;
+            continue;
+        }
+        const size_t row = (size_t)irow;
+        const uint16_t* pu = Wu + row * d;
+        const uint16_t* pg = GLU ? Wg + row * d : nullptr;
+        uint4 wu[Q], wg[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = lane + 64 * q;
+            wu[q] = c < nc ? ld16(pu + 8 * c) : zero4();
+            if (GLU) wg[q] = c < nc ? ld16(pg + 8 * c) : zero4();
+        }
+        float au = 0.f, ag = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            au = dot8(wu[q], xr[q], au);
+            if (GLU) ag = dot8(wg[q], xr[q], ag);
+        }
+        au = wave_sum(au);
+        if (GLU) ag = wave_sum(ag);
+        if (lane == 0) h[k] = GLU ? fmaxf(ag, 0.f) * au : fmaxf(au, 0.f);
+    }
+}
+
+// ------------------------------------------------------------------------------------------ int4 up
+PI_DEV float dot32_i4(const uint4& w, const uint32_t* xp) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t v = ws[m];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t bits = ((v >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+            const h2_t qv = __builtin_bit_cast(h2_t, bits) - off;   // (u - 8) exactly
+            acc = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2_t, xp[4 * m + p]), acc, false);
+        }
+    }
+    return acc;
+}
+
+template <int Q, bool GLU>
+__global__ __launch_bounds__(256) void k_up_i4(const uint16_t* __restrict__ x,
+                                               const uint8_t* __restrict__ Gq,
+                                               const uint16_t* __restrict__ Gs,
+                                               const uint8_t* __restrict__ Uq,
+                                               const uint16_t* __restrict__ Us, int d, int F,
+                                               const int32_t* __restrict__ idx,
+                                               const int32_t* __restrict__ count, int dense_F,
+                                               float* __restrict__ h) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nw = gridDim.x * 4;
+    const int n = dense_F > 0 ? dense_F : min(*count, F);
+    if (gw >= n) return;
+    const int nc = d >> 5;      // 16-byte chunks (32 weights) per row
+    const int G = d >> 7;       // scale groups per row
+    const size_t rb = (size_t)(d >> 1);
+    // x slice of each chunk, regrouped so pair p of word m is (x[8m+p], x[8m+p+4]),
+    // matching the nibble pairs (bits 4p and 16+4p) that one AND/OR extracts
+    uint32_t xp[Q][16];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int c = lane + 64 * q;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint4 a = c < nc ? ld16(x + 32 * c + 8 * m) : zero4();
+            xp[q][4 * m + 0] = (a.x & 0xFFFFu) | (a.z << 16);
+            xp[q][4 * m + 1] = (a.x >> 16) | (a.z & 0xFFFF0000u);
+            xp[q][4 * m + 2] = (a.y & 0xFFFFu) | (a.w << 16);
+            xp[q][4 * m + 3] = (a.y >> 16) | (a.w & 0xFFFF0000u);
+        }
+    }
+    for (int k = gw; k < n; k += nw) {
+        const int irow = dense_F > 0 ? k : idx[k];
+        if ((unsigned)irow >= (unsigned)F) {
+            if (lane == 0) h[k] = 0.f;
+            continue;
+        }
+        const size_t row = (size_t)irow;
+        uint4 wu[Q], wg[Q];
+        float su[Q], sg[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = lane + 64 * q;
+            const bool ok = c < nc;
+            wu[q] = ok ? ld16(Uq + row * rb + 16 * c) : zero4();
+            su[q] = ok ? h2f(Us[row * G + (c >> 2)]) : 0.f;
+            if (GLU) {
+                wg[q] = ok ? ld16(Gq + row * rb + 16 * c) : zero4();
+                sg[q] = ok ? h2f(Gs[row * G + (c >> 2)]) : 0.f;
+            }
+        }
+        float au = 0.f, ag = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            au = fmaf(dot32_i4(wu[q], xp[q]), su[q], au);
+            if (GLU) ag = fmaf(dot32_i4(wg[q], xp[q]), sg[q], ag);
+        }
+        au = wave_sum(au);
+        if (GLU) ag = wave_sum(ag);
+        if (lane == 0) h[k] = GLU ? fmaxf(ag, 0.f) * au : fmaxf(au, 0.f);
+    }
+}
+
+// ------------------------------------------------------------------------------------------ fp16 down
+constexpr int DOWN_WAVES_F16 = 16;
+constexpr int DOWN_WAVES_I4 = 8;
+
+template <int U>
+__global__ __launch_bounds__(1024) void k_down_f16(const uint16_t* __restrict__ Wd, int d, int F,
+                                                   const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ count, int dense_F,
+                                                   const float* __restrict__ h,
+                                                   float* __restrict__ part, float* __restrict__ y,
+                                                   unsigned* __restrict__ counters) {
+    constexpr int NW = DOWN_WAVES_F16;
+    __shared__ float4 s_red[NW][128];   // [wave][column / 4] over the 512-column slice
+    __shared__ float s_half[512];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+    const int nc = d >> 3;
+    const int c = slice * 64 + lane;
+    const bool cok = c < nc;
+    const int n = dense_F > 0 ? dense_F : min(*count, F);
+    const int stride = nsplit * NW;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int k0 = split * NW + wave; k0 < n; k0 += stride * U) {
+        uint4 w[U];
+        float hv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * stride;
+            const int irow = kk < n ? (dense_F > 0 ? kk : idx[kk]) : -1;
+            if ((unsigned)irow < (unsigned)F) {
+                hv[u] = h[kk];
+                w[u] = cok ? ld16(Wd + (size_t)irow * d + 8 * c) : zero4();
+            } else {
+                hv[u] = 0.f;
+                w[u] = zero4();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
+            }
+        }
+    }
+    s_red[wave][2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    s_red[wave][2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    __syncthreads();
+    // 1024 threads over 512 columns: half hf sums waves [8 hf, 8 hf + 8)
+    const int col = tid & 511, hf = tid >> 9;
+    const float* sr = reinterpret_cast<const float*>(s_red);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW / 2; ++w) s += sr[(hf * (NW / 2) + w) * 512 + col];
+    if (hf == 1) s_half[col] = s;
+    __syncthreads();
+    const int gcol = slice * 512 + col;
+    if (hf == 0 && gcol < d) part[(size_t)split * d + gcol] = s + s_half[col];
+    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
+        float t = 0.f;
+        if (gcol < d)
+            for (int sp = hf; sp < nsplit; sp += 2) t += part[(size_t)sp * d + gcol];
+        __syncthreads();
+        if (hf == 1) s_half[col] = t;
+        __syncthreads();
+        if (hf == 0 && gcol < d) y[gcol] = t + s_half[col];
+    }
+}
+
+// ------------------------------------------------------------------------------------------ int4 down
+template <int U>
+__global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
+                                                 const uint16_t* __restrict__ Ds, int d, int F,
+                                                 const int32_t* __restrict__ idx,
+                                                 const int32_t* __restrict__ count, int dense_F,
+                                                 const float* __restrict__ h,
+                                                 float* __restrict__ part, float* __restrict__ y,
+                                                 unsigned* __restrict__ counters) {
+    constexpr int NW = DOWN_WAVES_I4;
+    __shared__ float4 s_red[NW][512];   // [wave][column / 4] over the 2048-column slice
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+    const int nc = d >> 5;
+    const int G = d >> 7;
+    const size_t rb = (size_t)(d >> 1);
+    const int c = slice * 64 + lane;
+    const bool cok = c < nc;
+    const int n = dense_F > 0 ? dense_F : min(*count, F);
+    const int stride = nsplit * NW;
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+    float soff = 0.f;
+    for (int k0 = split * NW + wave; k0 < n; k0 += stride * U) {
+        uint4 w[U];
+        float hs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * stride;
+            const int irow = (kk < n && cok) ? (dense_F > 0 ? kk : idx[kk]) : -1;
+            if ((unsigned)irow < (unsigned)F) {
+                const size_t row = (size_t)irow;
+                w[u] = ld16(Dq + row * rb + 16 * c);
+                hs[u] = h[kk] * h2f(Ds[row * G + (c >> 2)]);
+            } else {
+                w[u] = zero4();
+                hs[u] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            soff += hs[u];
+            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    acc[8 * m + 2 * b] = fmaf(hs[u], (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
+                    acc[8 * m + 2 * b + 1] = fmaf(hs[u], (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; j += 4)
+        s_red[wave][8 * lane + j / 4] =
+            make_float4(fmaf(-8.f, soff, acc[j]), fmaf(-8.f, soff, acc[j + 1]),
+                        fmaf(-8.f, soff, acc[j + 2]), fmaf(-8.f, soff, acc[j + 3]));
+    __syncthreads();
+    // 512 threads x 4 columns each
+    float4 s = s_red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        const float4 t = s_red[w][tid];
+        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    const int gcol = slice * 2048 + 4 * tid;
+    if (gcol < d) *reinterpret_cast<float4*>(part + (size_t)split * d + gcol) = s;
+    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
+        if (gcol < d) {
+            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const float4 v = *reinterpret_cast<const float4*>(part + (size_t)sp * d + gcol);
+                t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+            }
+            *reinterpret_cast<float4*>(y + gcol) = t;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------ dispatch
+template <bool GLU>
+hipError_t up_f16(int q, int blocks, const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int d, int F,
+                  const int32_t* idx, const int32_t* count, int dense_F, float* h, hipStream_t s) {
+#define PI_UPF16(QQ) case QQ: hipLaunchKernelGGL((k_up_f16<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Wg, Wu, d, F, idx, count, dense_F, h); break;
+    switch (q) {
+        PI_UPF16(1) PI_UPF16(2) PI_UPF16(3) PI_UPF16(4) PI_UPF16(5) PI_UPF16(6) PI_UPF16(7) PI_UPF16(8)
+        PI_UPF16(9) PI_UPF16(10) PI_UPF16(11) PI_UPF16(12) PI_UPF16(13) PI_UPF16(14) PI_UPF16(15) PI_UPF16(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef PI_UPF16
+    return hipGetLastError();
+}
+
+template <bool GLU>
+hipError_t up_i4(int q, int blocks, const uint16_t* x, const uint8_t* Gq, const uint16_t* Gs,
+                 const uint8_t* Uq, const uint16_t* Us, int d, int F, const int32_t* idx,
+                 const int32_t* count, int dense_F, float* h, hipStream_t s) {
+#define PI_UPI4(QQ) case QQ: hipLaunchKernelGGL((k_up_i4<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Gq, Gs, Uq, Us, d, F, idx, count, dense_F, h); break;
+    switch (q) {
+        PI_UPI4(1) PI_UPI4(2) PI_UPI4(3) PI_UPI4(4) PI_UPI4(5) PI_UPI4(6) PI_UPI4(7) PI_UPI4(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef PI_UPI4
+    return hipGetLastError();
+}
+
+}  // namespace
+
+FfnPlan plan_ffn(int d, int F, int wfmt, int B) {
+    FfnPlan p{};
+    const bool f16 = wfmt == PI_W_F16;
+    p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
+    p.up_blocks = (F + 3) / 4 < 1024 ? (F + 3) / 4 : 1024;
+    p.cols = f16 ? 512 : 2048;
+    p.nslices = (d + p.cols - 1) / p.cols;
+    const int wpb = f16 ? DOWN_WAVES_F16 : DOWN_WAVES_I4;
+    int ns = 2048 / (p.nslices * wpb);
+    p.nsplit = ns < 1 ? 1 : (ns > 32 ? 32 : ns);
+    size_t off = COUNTER_BYTES;
+    p.off_h = off;
+    off = align_up(off + (size_t)F * sizeof(float), 256);
+    p.off_part = off;
+    off = align_up(off + (size_t)p.nsplit * d * sizeof(float), 256);
+    p.bytes = off;
+    // union path (B > 1) storage is appended by the union planner
+    p.u_tiles = (F + 31) / 32;
+    p.u_ksplit = 0;
+    p.off_H = p.off_upart = 0;
+    (void)B;
+    return p;
+}
+
+hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
+                         const int32_t* idx, const int32_t* count, int dense_F, float* y,
+                         char* ws, hipStream_t s) {
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
+    float* h = reinterpret_cast<float*>(ws + pl.off_h);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    const bool glu = f.act == PI_ACT_REGLU;
+    hipError_t e;
+    const dim3 gd(pl.nslices, pl.nsplit);
+    if (f.wfmt == PI_W_F16) {
+        const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
+        const uint16_t* Wu = static_cast<const uint16_t*>(f.w_up);
+        e = glu ? up_f16<true>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s)
+                : up_f16<false>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_down_f16<4>), gd, dim3(64 * DOWN_WAVES_F16), 0, s,
+                           static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, dense_F, h,
+                           part, y, cnt);
+    } else {
+        const uint8_t* Gq = static_cast<const uint8_t*>(f.w_gate);
+        const uint8_t* Uq = static_cast<const uint8_t*>(f.w_up);
+        e = glu ? up_i4<true>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s)
+                : up_i4<false>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_down_i4<4>), gd, dim3(64 * DOWN_WAVES_I4), 0, s,
+                           static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, f.F, idx, count,
+                           dense_F, h, part, y, cnt);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pi

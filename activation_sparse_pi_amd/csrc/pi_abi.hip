@@ -1,0 +1,225 @@
+// C ABI of the predictor-gated sparse FFN: host-side validation, workspace
+// planning and launches.  Every check runs before the first HIP call, so an
+// invalid request enqueues nothing and leaves the outputs untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+using namespace pi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return PI_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_pred(const pi_pred_desc* p) {
+    if (!p) return fail(PI_ERR_NULL, "pred descriptor is NULL");
+    if (!p->w_p1 || !p->w_p2 || !p->bias) return fail(PI_ERR_NULL, "pred weights/bias NULL");
+    if (p->d <= 0 || p->r <= 0 || p->F <= 0)
+        return fail(PI_ERR_SHAPE, "pred sizes must be positive (d=%d r=%d F=%d)", p->d, p->r, p->F);
+    if (p->d % 8 || p->r % 8 || p->F % 8)
+        return fail(PI_ERR_SHAPE, "pred sizes need d, r, F %% 8 == 0 (d=%d r=%d F=%d)", p->d, p->r, p->F);
+    if (p->r > 16384) return fail(PI_ERR_UNSUPPORTED, "predictor rank %d > 16384", p->r);
+    if (!aligned16(p->w_p1) || !aligned16(p->w_p2))
+        return fail(PI_ERR_ALIGN, "predictor weights must be 16-byte aligned");
+    if (!(p->threshold > 0.f && p->threshold < 1.f))
+        return fail(PI_ERR_SHAPE, "threshold must be a probability in (0,1), got %g", (double)p->threshold);
+    return PI_OK;
+}
+
+int check_ffn(const pi_ffn_desc* f, int B) {
+    if (!f) return fail(PI_ERR_NULL, "ffn descriptor is NULL");
+    if (f->act != PI_ACT_RELU && f->act != PI_ACT_REGLU)
+        return fail(PI_ERR_DTYPE, "unknown activation %d", f->act);
+    if (f->wfmt != PI_W_F16 && f->wfmt != PI_W_I4G128)
+        return fail(PI_ERR_DTYPE, "unknown weight format %d", f->wfmt);
+    if (!f->w_up || !f->w_down) return fail(PI_ERR_NULL, "w_up / w_down NULL");
+    if (f->act == PI_ACT_REGLU && !f->w_gate) return fail(PI_ERR_NULL, "ReGLU needs w_gate");
+    if (f->wfmt == PI_W_I4G128) {
+        if (!f->s_up || !f->s_down) return fail(PI_ERR_NULL, "int4 needs s_up / s_down");
+        if (f->act == PI_ACT_REGLU && !f->s_gate) return fail(PI_ERR_NULL, "int4 ReGLU needs s_gate");
+    }
+    if (f->d <= 0 || f->F <= 0) return fail(PI_ERR_SHAPE, "ffn sizes must be positive (d=%d F=%d)", f->d, f->F);
+    if (f->wfmt == PI_W_F16 && f->d % 8) return fail(PI_ERR_SHAPE, "fp16 needs d %% 8 == 0 (d=%d)", f->d);
+    if (f->wfmt == PI_W_I4G128 && f->d % 128) return fail(PI_ERR_SHAPE, "int4 needs d %% 128 == 0 (d=%d)", f->d);
+    if (f->F % 8) return fail(PI_ERR_SHAPE, "ffn needs F %% 8 == 0 (F=%d)", f->F);
+    if (f->wfmt == PI_W_F16 && f->d > PI_MAX_D_F16)
+        return fail(PI_ERR_UNSUPPORTED, "fp16 d=%d > %d", f->d, PI_MAX_D_F16);
+    if (f->wfmt == PI_W_I4G128 && f->d > PI_MAX_D_I4)
+        return fail(PI_ERR_UNSUPPORTED, "int4 d=%d > %d", f->d, PI_MAX_D_I4);
+    const void* ptrs[6] = {f->w_gate, f->w_up, f->w_down, f->s_gate, f->s_up, f->s_down};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return fail(PI_ERR_ALIGN, "ffn weights must be 16-byte aligned");
+    if (B > 1) return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path not built yet");
+    if (B > 1 && f->wfmt != PI_W_F16)
+        return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path is fp16 only");
+    if (B > 1 && f->d % 64)
+        return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path needs d %% 64 == 0");
+    return PI_OK;
+}
+
+int check_batch(int B) {
+    if (B < 1 || B > PI_MAX_BATCH) return fail(PI_ERR_SHAPE, "batch %d outside 1..%d", B, PI_MAX_BATCH);
+    return PI_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+    if (!ws) return fail(PI_ERR_WORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(PI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (have < need) return fail(PI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    return PI_OK;
+}
+
+size_t ffn_bytes(const pi_ffn_desc& f, int B) {
+    FfnPlan p = plan_ffn(f.d, f.F, f.wfmt, B);
+    return p.bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pi_status_string(int status) {
+    switch (status) {
+        case PI_OK: return "ok";
+        case PI_ERR_NULL: return "null pointer";
+        case PI_ERR_SHAPE: return "bad shape";
+        case PI_ERR_ALIGN: return "misaligned pointer";
+        case PI_ERR_DTYPE: return "bad enum";
+        case PI_ERR_UNSUPPORTED: return "unsupported";
+        case PI_ERR_WORKSPACE: return "bad workspace";
+        case PI_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* pi_last_error(void) { return g_last_error.c_str(); }
+
+int pi_version(void) { return 100; }
+
+size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
+    if (B_max < 1 || B_max > PI_MAX_BATCH) return 0;
+    size_t need = COUNTER_BYTES;
+    if (pred) {
+        if (check_pred(pred) != PI_OK) return 0;
+        for (int B = 1; B <= B_max; ++B) {
+            const size_t b = plan_pred(pred->d, pred->r, pred->F, B).bytes;
+            if (b > need) need = b;
+        }
+    }
+    if (ffn) {
+        if (check_ffn(ffn, 1) != PI_OK) return 0;
+        for (int B = 1; B <= B_max; ++B) {
+            const size_t b = ffn_bytes(*ffn, B);
+            if (b > need) need = b;
+        }
+    }
+    return need;
+}
+
+int pi_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return fail(PI_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(PI_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes == 0) return ok();
+    hipError_t e = launch_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "workspace zero fill");
+    return ok();
+}
+
+int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B, float* logits, uint32_t* mask,
+               int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+    int st;
+    if ((st = check_pred(pred)) != PI_OK) return st;
+    if ((st = check_batch(B)) != PI_OK) return st;
+    if (!x || !mask) return fail(PI_ERR_NULL, "x and mask are required");
+    if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
+    if (!aligned16(x)) return fail(PI_ERR_ALIGN, "x must be 16-byte aligned");
+    const PredPlan pl = plan_pred(pred->d, pred->r, pred->F, B);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    const double tau = pred->threshold;
+    const float theta = (float)std::log(tau / (1.0 - tau));
+    hipError_t e = launch_predict(*pred, pl, x, B, theta, logits, mask, idx, count,
+                                  static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_predict launch");
+    return ok();
+}
+
+int pi_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx, int32_t* count,
+               void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int st;
+    if (!mask || !idx || !count) return fail(PI_ERR_NULL, "mask, idx and count are required");
+    if ((st = check_batch(B)) != PI_OK) return st;
+    if (F <= 0) return fail(PI_ERR_SHAPE, "F must be positive (F=%d)", F);
+    if (mode != PI_PER_TOKEN && mode != PI_UNION) return fail(PI_ERR_DTYPE, "unknown compaction mode %d", mode);
+    hipError_t e = launch_compact(mask, B, F, mode, idx, count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_compact launch");
+    return ok();
+}
+
+int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B, const int32_t* idx,
+                  const int32_t* count, const uint32_t* token_mask, float* y, void* ws,
+                  size_t ws_bytes, void* stream) {
+    int st;
+    if ((st = check_batch(B)) != PI_OK) return st;
+    if (!x || !idx || !count || !y) return fail(PI_ERR_NULL, "x, idx, count and y are required");
+    if (B == 1 && token_mask) return fail(PI_ERR_SHAPE, "token_mask must be NULL at batch 1");
+    if (B > 1 && !token_mask) return fail(PI_ERR_NULL, "token_mask is required for batch > 1");
+    if ((st = check_ffn(ffn, B)) != PI_OK) return st;
+    if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
+    const FfnPlan pl = plan_ffn(ffn->d, ffn->F, ffn->wfmt, B);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (B == 1) {
+        e = launch_ffn_b1(*ffn, pl, x, idx, count, 0, y, static_cast<char*>(ws), s);
+    } else {
+        e = launch_ffn_union(*ffn, pl, x, B, idx, count, token_mask, 0, y, static_cast<char*>(ws), s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "pi_sparse_ffn launch");
+    return ok();
+}
+
+int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float* y, void* ws,
+                         size_t ws_bytes, void* stream) {
+    int st;
+    if ((st = check_batch(B)) != PI_OK) return st;
+    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
+    if (!x || !y) return fail(PI_ERR_NULL, "x and y are required");
+    if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
+    const FfnPlan pl = plan_ffn(ffn->d, ffn->F, ffn->wfmt, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int b = 0; b < B; ++b) {
+        hipError_t e = launch_ffn_b1(*ffn, pl, x + (size_t)b * ffn->d, nullptr, nullptr, ffn->F,
+                                     y + (size_t)b * ffn->d, static_cast<char*>(ws), s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_dense_ref_gpu launch");
+    }
+    return ok();
+}
+
+}  // extern "C"

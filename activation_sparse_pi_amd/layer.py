@@ -1,0 +1,104 @@
+"""Device-side holder of one FFN layer for the C ABI: weights, descriptors, workspace.
+
+PyTorch is used only to own device memory and to name the stream; every step
+of the method runs in libpi.so.  ``replicas`` keeps R byte-identical copies of
+the weights so that a token stream can rotate through them: each copy stands
+for another layer of a real model, so weights are fetched from HBM rather
+than from the 256 MB Infinity Cache or the L2 of a previous token.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceLayer:
+    def __init__(self, inputs: dict, replicas: int = 1, B_max: int = 1, device="cuda",
+                 threshold: float = 0.5):
+        cfg = inputs["cfg"]
+        self.cfg, self.d, self.F, self.r = cfg, cfg.d, cfg.F, cfg.r
+        self.act = L.PI_ACT_REGLU if cfg.act == "reglu" else L.PI_ACT_RELU
+        self.wfmt = L.PI_W_F16 if cfg.wfmt == "f16" else L.PI_W_I4G128
+        self.device = torch.device(device)
+        names = ["w_p1", "w_p2", "bias"]
+        mats = ("gate", "up", "down") if cfg.act == "reglu" else ("up", "down")
+        for m in mats:
+            names += ["w_" + m] if cfg.wfmt == "f16" else ["q_" + m, "s_" + m]
+        base = {k: _dev(inputs[k], self.device) for k in names}
+        self.tensors = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
+        self.pred, self.ffn = [], []
+        for t in self.tensors:
+            self.pred.append(L.PredDesc(t["w_p1"].data_ptr(), t["w_p2"].data_ptr(), t["bias"].data_ptr(),
+                                        cfg.d, cfg.r, cfg.F, threshold))
+            if cfg.wfmt == "f16":
+                g = t["w_gate"].data_ptr() if "w_gate" in t else None
+                self.ffn.append(L.FfnDesc(g, t["w_up"].data_ptr(), t["w_down"].data_ptr(), None, None,
+                                          None, cfg.d, cfg.F, self.act, self.wfmt))
+            else:
+                g = t["q_gate"].data_ptr() if "q_gate" in t else None
+                sg = t["s_gate"].data_ptr() if "s_gate" in t else None
+                self.ffn.append(L.FfnDesc(g, t["q_up"].data_ptr(), t["q_down"].data_ptr(), sg,
+                                          t["s_up"].data_ptr(), t["s_down"].data_ptr(), cfg.d, cfg.F,
+                                          self.act, self.wfmt))
+        self.ws_bytes = L.pi_workspace_bytes(self.pred[0], self.ffn[0], B_max)
+        if self.ws_bytes == 0:
+            raise L.PiError(L.PI_ERR_SHAPE, "pi_workspace_bytes rejected the layer: " + L.pi_last_error())
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        L.check(L.pi_workspace_init(self.ws.data_ptr(), self.ws_bytes, self.stream()))
+
+    @property
+    def replicas(self) -> int:
+        return len(self.tensors)
+
+    def weight_bytes(self) -> int:
+        return sum(v.numel() * v.element_size() for v in self.tensors[0].values())
+
+    def stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    # ---- thin forwards to the C ABI (pointers are tensor.data_ptr() values) -------------
+    def predict(self, x, B, logits, mask, idx, count, rep: int = 0) -> None:
+        L.check(L.pi_predict(self.pred[rep], x, B, logits, mask, idx, count, self.ws.data_ptr(),
+                             self.ws_bytes, self.stream()))
+
+    def compact(self, mask, B, mode, idx, count) -> None:
+        L.check(L.pi_compact(mask, B, self.F, mode, idx, count, None, 0, self.stream()))
+
+    def sparse_ffn(self, x, B, idx, count, token_mask, y, rep: int = 0) -> None:
+        L.check(L.pi_sparse_ffn(self.ffn[rep], x, B, idx, count, token_mask, y, self.ws.data_ptr(),
+                                self.ws_bytes, self.stream()))
+
+    def dense(self, x, B, y, rep: int = 0) -> None:
+        L.check(L.pi_ffn_dense_ref_gpu(self.ffn[rep], x, B, y, self.ws.data_ptr(), self.ws_bytes,
+                                       self.stream()))
+
+    def step(self, x, bufs: dict, rep: int = 0, logits: bool = True) -> None:
+        """One batch-1 decode step: predict + compact (fused), then the sparse FFN.
+
+        x is the device address of one fp16 token; results land in ``bufs``
+        (see ``buffers``).  Nothing is synchronised and count stays on the device.
+        """
+        self.predict(x, 1, bufs["logits"].data_ptr() if logits else None, bufs["mask"].data_ptr(),
+                     bufs["idx"].data_ptr(), bufs["count"].data_ptr(), rep)
+        self.sparse_ffn(x, 1, bufs["idx"].data_ptr(), bufs["count"].data_ptr(), None,
+                        bufs["y"].data_ptr(), rep)
+
+    # ---- output buffers --------------------------------------------------------------------
+    def buffers(self, B: int) -> dict:
+        W = (self.F + 31) // 32
+        dev = self.device
+        return dict(
+            logits=torch.empty((B, self.F), dtype=torch.float32, device=dev),
+            mask=torch.empty((B, W), dtype=torch.int32, device=dev),
+            idx=torch.empty((B, self.F), dtype=torch.int32, device=dev),
+            count=torch.empty((B,), dtype=torch.int32, device=dev),
+            uidx=torch.empty((self.F,), dtype=torch.int32, device=dev),
+            ucount=torch.empty((1,), dtype=torch.int32, device=dev),
+            y=torch.empty((B, self.d), dtype=torch.float32, device=dev),
+        )

@@ -1,0 +1,161 @@
+/*
+ * pi.h -- C ABI of the predictor-gated, neuron-aware sparse FFN for MI355X (gfx950).
+ *
+ * One FFN layer of batch-1 / small-batch LLM decode, computed the way the
+ * PowerInfer article describes it:
+ *   - "Adaptive Sparsity Predictors" / online engine: a small predictor marks,
+ *     for every token, the FFN neurons that will fire; only those are computed.
+ *   - "Neuron Placement and Management": a table maps every kept neuron back to
+ *     its position in the original matrix (here: an ascending int32 list).
+ *   - "Neuron-aware Operator": the operator works on individual row vectors
+ *     (up / gate projection) and column vectors (down projection) of the one
+ *     dense matrix, reading the selected neurons in place with no conversion to
+ *     a sparse format.
+ * Weight-only int4 with one scale per group of 128 along the row follows the
+ * Intel Extension for Transformers LLM Runtime page ("01 LLM Runtime").
+ *
+ * Conventions for every call below
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after a call returns and never allocates device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream: there is no host synchronisation, and
+ *     device-side counts never travel to the host.
+ *   - Arguments are validated on the host BEFORE any HIP call.  A call that
+ *     fails validation enqueues nothing and leaves every output untouched.
+ *     Launch failures return PI_ERR_HIP.  Faults during execution surface at
+ *     the caller's next synchronisation on that stream.
+ *   - Every call returns a status code; pi_last_error() gives a readable detail
+ *     for the calling thread.  No C++ exception crosses this boundary.
+ *   - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *   - Calls on different streams may run concurrently only with distinct
+ *     workspaces; calls sharing a workspace must be ordered on one stream.
+ */
+#ifndef PI_H
+#define PI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------- */
+#define PI_OK              0
+#define PI_ERR_NULL        1  /* a required pointer is NULL                          */
+#define PI_ERR_SHAPE       2  /* a size is out of range or inconsistent              */
+#define PI_ERR_ALIGN       3  /* a pointer is not 16-byte aligned                    */
+#define PI_ERR_DTYPE       4  /* unknown activation / weight format / mode enum      */
+#define PI_ERR_UNSUPPORTED 5  /* valid request this build does not implement         */
+#define PI_ERR_WORKSPACE   6  /* workspace missing, too small or misaligned          */
+#define PI_ERR_HIP         7  /* a HIP runtime call failed                           */
+
+/* ---- enums ------------------------------------------------------------------------ */
+#define PI_ACT_RELU   0   /* h = max(W_up[i] . x, 0)                                   */
+#define PI_ACT_REGLU  1   /* h = max(W_gate[i] . x, 0) * (W_up[i] . x)                 */
+#define PI_W_F16      0   /* fp16 weights, [F, d] neuron-major                         */
+#define PI_W_I4G128   1   /* int4: u8 [F, d/2] (even column in the low nibble, value
+                             (u - 8) * scale) + fp16 scales [F, d/128], neuron-major  */
+#define PI_PER_TOKEN  0   /* pi_compact: one index list per token                     */
+#define PI_UNION      1   /* pi_compact: one list of the OR of the B token masks      */
+
+#define PI_MAX_BATCH  32
+#define PI_MAX_D_F16  8192    /* largest d of the fp16 batch-1 kernels                */
+#define PI_MAX_D_I4   16384   /* largest d of the int4 batch-1 kernels                */
+
+/* ---- descriptors -------------------------------------------------------------------- */
+
+/* Low-rank activation predictor of one layer: l = (x W_p1) W_p2 + bias.
+ * Neuron i is predicted active iff sigmoid(l_i) > threshold, evaluated as
+ * l_i > ln(threshold / (1 - threshold)) in fp32 (strict; 0 for threshold 0.5).
+ * z = x W_p1 is accumulated and kept in fp32 (never rounded to fp16).        */
+typedef struct pi_pred_desc {
+    const uint16_t* w_p1;   /* fp16 [d, r] row-major                      */
+    const uint16_t* w_p2;   /* fp16 [r, F] row-major                      */
+    const float*    bias;   /* fp32 [F]                                   */
+    int32_t d;              /* model width, d % 8 == 0                    */
+    int32_t r;              /* predictor rank, r % 8 == 0                 */
+    int32_t F;              /* ffn width (neurons), F % 8 == 0            */
+    float   threshold;      /* probability in (0, 1); 0.5 is the default  */
+} pi_pred_desc;
+
+/* FFN weights of one layer, every matrix neuron-major [F, d]: row i of
+ * w_down is neuron i's output vector, stored contiguously.              */
+typedef struct pi_ffn_desc {
+    const void*     w_gate; /* PI_ACT_REGLU only (NULL for ReLU)                       */
+    const void*     w_up;
+    const void*     w_down;
+    const uint16_t* s_gate; /* int4 only: fp16 [F, d/128] scales; NULL for fp16        */
+    const uint16_t* s_up;
+    const uint16_t* s_down;
+    int32_t d;              /* fp16: d % 8 == 0, d <= PI_MAX_D_F16; int4: d % 128 == 0 */
+    int32_t F;
+    int32_t act;            /* PI_ACT_*                                                */
+    int32_t wfmt;           /* PI_W_*                                                  */
+} pi_ffn_desc;
+
+/* ---- status / info ------------------------------------------------------------------ */
+const char* pi_status_string(int status);   /* static string, never NULL                */
+const char* pi_last_error(void);            /* thread-local detail of the last failure  */
+int         pi_version(void);               /* major * 10000 + minor * 100 + patch      */
+
+/* ---- workspace -------------------------------------------------------------------------
+ * Bytes of device workspace needed by pi_predict / pi_sparse_ffn /
+ * pi_ffn_dense_ref_gpu for any batch 1..B_max (either descriptor may be NULL).
+ * The workspace holds partial sums, the predictor's z, the activations h and
+ * self-resetting arrival counters.  It must be 256-byte aligned and zero-filled
+ * once before first use (pi_workspace_init, or any zero fill); every kernel
+ * leaves its counters at zero when it completes.  Returns 0 on invalid input.  */
+size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max);
+
+/* Zero-fills the workspace with a kernel on `stream` (no hipMemset). */
+int pi_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* ---- pi_predict --------------------------------------------------------------------------
+ * PowerInfer, "Adaptive Sparsity Predictors": evaluate the layer's predictor on
+ * the B tokens x (fp16 [B, d]) and mark the neurons predicted to fire.
+ *   logits : fp32 [B, F] or NULL       -- l for every neuron (diagnostics)
+ *   mask   : u32 [B, ceil(F/32)]       -- bit (i % 32) of word i / 32 = neuron i active;
+ *                                         bits at positions >= F are 0
+ *   idx    : int32 [B, F] or NULL      -- with count: token b's active neuron ids in
+ *   count  : int32 [B]   or NULL          ascending order in idx[b*F .. b*F+count[b])
+ *                                         (the neuron table, "Neuron Placement and
+ *                                         Management"); entries past count are not written
+ * idx and count must both be given or both be NULL.  1 <= B <= PI_MAX_BATCH.       */
+int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B,
+               float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- pi_compact ----------------------------------------------------------------------------
+ * Turns masks (u32 [B, ceil(F/32)], as written by pi_predict) into ascending
+ * neuron-id lists.  PI_PER_TOKEN: idx int32 [B, F], count int32 [B].
+ * PI_UNION: the OR of the B masks -> idx int32 [F], count int32 [1].
+ * Mask bits at positions >= F are ignored.  Needs no workspace (ws may be NULL). */
+int pi_compact(const uint32_t* mask, int B, int F, int mode,
+               int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- pi_sparse_ffn ---------------------------------------------------------------------------
+ * PowerInfer, "Neuron-aware Operator": y = sum over listed neurons i of
+ * h_i * W_down[i, :], with h_i from the rows W_up[i] (and W_gate[i]) only.
+ *   x          : fp16 [B, d]
+ *   idx, count : device neuron list (ascending, ids < F) and its length (int32 [1]);
+ *                the list is read on the device, never on the host
+ *   token_mask : B == 1: must be NULL.  B > 1: u32 [B, ceil(F/32)] per-token masks;
+ *                idx/count then hold their union (pi_compact PI_UNION) and token b
+ *                only receives the neurons set in its own mask
+ *   y          : fp32 [B, d], overwritten (an empty list gives exactly 0)
+ * Accumulation is fp32; B > 1 runs on MFMA with h rounded to fp16.                      */
+int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B,
+                  const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
+                  float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- pi_ffn_dense_ref_gpu ------------------------------------------------------------------
+ * The same FFN over all F neurons (no predictor, no skipping): the dense
+ * reference and dense-time baseline.  y fp32 [B, d], overwritten.             */
+int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float* y,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PI_H */

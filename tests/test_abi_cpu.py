@@ -1,0 +1,151 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from activation_sparse_pi_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pi.h")
+
+# fake, 256-byte aligned "device" addresses: validation never dereferences them
+A = 0x7F0000000000
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pi_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_match_exports():
+    declared = _declared()
+    assert set(declared) == set(L.EXPORTS), declared
+
+
+def test_library_exports_every_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in _declared():
+        assert name in syms, name
+        getattr(L.lib(), name)
+
+
+def pred(**kw):
+    a = dict(w_p1=A, w_p2=A + 0x100000, bias=A + 0x200000, d=1024, r=128, F=4096, threshold=0.5)
+    a.update(kw)
+    return L.PredDesc(a["w_p1"], a["w_p2"], a["bias"], a["d"], a["r"], a["F"], a["threshold"])
+
+
+def ffn(**kw):
+    a = dict(w_gate=None, w_up=A, w_down=A + 0x1000000, s_gate=None, s_up=None, s_down=None,
+             d=1024, F=4096, act=L.PI_ACT_RELU, wfmt=L.PI_W_F16)
+    a.update(kw)
+    return L.FfnDesc(a["w_gate"], a["w_up"], a["w_down"], a["s_gate"], a["s_up"], a["s_down"],
+                     a["d"], a["F"], a["act"], a["wfmt"])
+
+
+def test_status_strings_and_version():
+    assert L.pi_status_string(0) == "ok"
+    assert L.pi_status_string(L.PI_ERR_WORKSPACE) == "bad workspace"
+    assert L.pi_status_string(99) == "unknown status"
+    assert L.pi_version() >= 100
+
+
+def test_workspace_bytes():
+    n = L.pi_workspace_bytes(pred(), ffn(), 1)
+    assert n > 0 and n % 256 == 0
+    assert L.pi_workspace_bytes(pred(), ffn(), 32) >= n
+    assert L.pi_workspace_bytes(pred(), ffn(), 0) == 0
+    assert L.pi_workspace_bytes(pred(d=1001), None, 1) == 0
+    assert L.pi_workspace_bytes(None, ffn(act=7), 1) == 0
+
+
+WS = A + 0x10000000
+WSB = 1 << 30
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(desc=None), L.PI_ERR_NULL),
+    (dict(desc=pred(w_p1=None)), L.PI_ERR_NULL),
+    (dict(desc=pred(d=0)), L.PI_ERR_SHAPE),
+    (dict(desc=pred(r=12)), L.PI_ERR_SHAPE),
+    (dict(desc=pred(F=1001)), L.PI_ERR_SHAPE),
+    (dict(desc=pred(w_p2=A + 8)), L.PI_ERR_ALIGN),
+    (dict(desc=pred(threshold=1.0)), L.PI_ERR_SHAPE),
+    (dict(desc=pred(threshold=0.0)), L.PI_ERR_SHAPE),
+    (dict(B=0), L.PI_ERR_SHAPE),
+    (dict(B=33), L.PI_ERR_SHAPE),
+    (dict(x=None), L.PI_ERR_NULL),
+    (dict(mask=None), L.PI_ERR_NULL),
+    (dict(x=A + 2), L.PI_ERR_ALIGN),
+    (dict(idx=None), L.PI_ERR_NULL),
+    (dict(ws=None), L.PI_ERR_WORKSPACE),
+    (dict(ws=WS + 16), L.PI_ERR_WORKSPACE),
+    (dict(wsb=1024), L.PI_ERR_WORKSPACE),
+])
+def test_predict_validation(kw, code):
+    a = dict(desc=pred(), x=A + 0x3000000, B=1, logits=None, mask=A + 0x4000000,
+             idx=A + 0x5000000, count=A + 0x6000000, ws=WS, wsb=WSB)
+    a.update(kw)
+    st = L.pi_predict(a["desc"], a["x"], a["B"], a["logits"], a["mask"], a["idx"], a["count"],
+                      a["ws"], a["wsb"], None)
+    assert st == code, L.pi_last_error()
+    assert L.pi_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(desc=None), L.PI_ERR_NULL),
+    (dict(desc=ffn(act=3)), L.PI_ERR_DTYPE),
+    (dict(desc=ffn(wfmt=5)), L.PI_ERR_DTYPE),
+    (dict(desc=ffn(act=L.PI_ACT_REGLU)), L.PI_ERR_NULL),
+    (dict(desc=ffn(wfmt=L.PI_W_I4G128)), L.PI_ERR_NULL),
+    (dict(desc=ffn(wfmt=L.PI_W_I4G128, s_up=A, s_down=A, d=1000)), L.PI_ERR_SHAPE),
+    (dict(desc=ffn(d=1020)), L.PI_ERR_SHAPE),
+    (dict(desc=ffn(F=4095)), L.PI_ERR_SHAPE),
+    (dict(desc=ffn(d=8200)), L.PI_ERR_UNSUPPORTED),
+    (dict(desc=ffn(w_down=A + 4)), L.PI_ERR_ALIGN),
+    (dict(B=2, token_mask=None), L.PI_ERR_NULL),
+    (dict(token_mask=A), L.PI_ERR_SHAPE),
+    (dict(idx=None), L.PI_ERR_NULL),
+    (dict(count=None), L.PI_ERR_NULL),
+    (dict(y=A + 8), L.PI_ERR_ALIGN),
+    (dict(ws=None), L.PI_ERR_WORKSPACE),
+    (dict(wsb=256), L.PI_ERR_WORKSPACE),
+])
+def test_sparse_ffn_validation(kw, code):
+    a = dict(desc=ffn(), x=A + 0x3000000, B=1, idx=A + 0x5000000, count=A + 0x6000000,
+             token_mask=None, y=A + 0x7000000, ws=WS, wsb=WSB)
+    a.update(kw)
+    st = L.pi_sparse_ffn(a["desc"], a["x"], a["B"], a["idx"], a["count"], a["token_mask"], a["y"],
+                         a["ws"], a["wsb"], None)
+    assert st == code, L.pi_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), L.PI_ERR_NULL),
+    (dict(B=0), L.PI_ERR_SHAPE),
+    (dict(F=0), L.PI_ERR_SHAPE),
+    (dict(mode=9), L.PI_ERR_DTYPE),
+    (dict(count=None), L.PI_ERR_NULL),
+])
+def test_compact_validation(kw, code):
+    a = dict(mask=A, B=1, F=4096, mode=L.PI_PER_TOKEN, idx=A + 0x100000, count=A + 0x200000)
+    a.update(kw)
+    st = L.pi_compact(a["mask"], a["B"], a["F"], a["mode"], a["idx"], a["count"], None, 0, None)
+    assert st == code, L.pi_last_error()
+
+
+def test_dense_ref_validation():
+    st = L.pi_ffn_dense_ref_gpu(ffn(), A, 1, A + 0x100, None, 0, None)
+    assert st == L.PI_ERR_WORKSPACE
+    st = L.pi_ffn_dense_ref_gpu(ffn(F=0), A, 1, A + 0x100, WS, WSB, None)
+    assert st == L.PI_ERR_SHAPE
+
+
+def test_workspace_init_validation():
+    assert L.pi_workspace_init(None, 1024, None) == L.PI_ERR_NULL
+    assert L.pi_workspace_init(A + 64, 1024, None) == L.PI_ERR_WORKSPACE
