@@ -22,7 +22,7 @@ PI_MAX_BATCH = 32
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
-           "pi_ffn_dense_ref_gpu")
+           "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu")
 
 
 class PredDesc(ctypes.Structure):
@@ -69,6 +69,15 @@ def lib() -> ctypes.CDLL:
         L.pi_sparse_ffn.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_size_t, c_void_p]
         L.pi_sparse_ffn.restype = c_int
+        L.pi_ffn_up.argtypes = [P(FfnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.pi_ffn_up.restype = c_int
+        L.pi_ffn_down.argtypes = [P(FfnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_size_t, c_void_p]
+        L.pi_ffn_down.restype = c_int
+        L.pi_decode_run.argtypes = [P(PredDesc), P(FfnDesc), c_int, c_void_p, c_int,
+                                    ctypes.c_longlong, c_int, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.pi_decode_run.restype = c_int
         L.pi_ffn_dense_ref_gpu.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p,
                                            c_size_t, c_void_p]
         L.pi_ffn_dense_ref_gpu.restype = c_int
@@ -110,6 +119,22 @@ def pi_compact(mask, B, F, mode, idx, count, ws, ws_bytes, stream) -> int:
 
 def pi_sparse_ffn(ffn, x, B, idx, count, token_mask, y, ws, ws_bytes, stream) -> int:
     return lib().pi_sparse_ffn(_p(ffn), x, B, idx, count, token_mask, y, ws, ws_bytes, stream)
+
+
+def pi_ffn_up(ffn, x, idx, count, h, stream) -> int:
+    return lib().pi_ffn_up(_p(ffn), x, idx, count, h, stream)
+
+
+def pi_ffn_down(ffn, idx, count, h, y, ws, ws_bytes, stream) -> int:
+    return lib().pi_ffn_down(_p(ffn), idx, count, h, y, ws, ws_bytes, stream)
+
+
+def pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mask, idx, count, y, events,
+                  ws, ws_bytes, stream) -> int:
+    """preds / ffns: ctypes arrays of PredDesc / FfnDesc; events: ctypes array of
+    hipEvent_t handles (c_void_p) or None."""
+    return lib().pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mask, idx, count, y,
+                               events, ws, ws_bytes, stream)
 
 
 def pi_ffn_dense_ref_gpu(ffn, x, B, y, ws, ws_bytes, stream) -> int:

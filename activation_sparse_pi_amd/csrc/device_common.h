@@ -24,6 +24,29 @@ PI_DEV float dot8(const uint4& a, const uint4& b, float acc) {
     return dot2(a.w, b.w, acc);
 }
 
+__host__ __device__ constexpr int align16i(int v) { return (v + 15) & ~15; }
+
+// sum over the 32 int4 weights of one 16-byte chunk of (u - 8) * x, with x given as the 16
+// fp16 pairs (x[8m+p], x[8m+p+4]), m = word, p = nibble pair: each pair is widened exactly by
+// OR-ing the nibbles into the mantissa of fp16 1024.0 and subtracting 1032, then dotted with
+// v_dot2_f32_f16 (fp32 accumulation).
+PI_DEV float dot32_i4(const uint4& w, const uint32_t* xp) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t v = ws[m];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t bits = ((v >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+            const h2_t qv = __builtin_bit_cast(h2_t, bits) - off;   // (u - 8) exactly
+            acc = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2_t, xp[4 * m + p]), acc, false);
+        }
+    }
+    return acc;
+}
+
 // 16-byte global load
 PI_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 PI_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
@@ -35,25 +58,43 @@ PI_DEV float wave_sum(float v) {
     return v;
 }
 
-// ---- cross-block "last arrival" --------------------------------------------------------------
-// Every block calls this once after writing its partial results.  Exactly one
-// block (the last to arrive) gets true, after an agent-scope acquire, and may
-// then read every other block's writes.  The counter is reset to zero by that
-// block, so it starts at zero for the next launch on the stream.
+// ---- cross-block "last arrival" ------------------------------------------------------------
+// Blocks hand partial results to one another through memory.  An agent-scope
+// fence here would write back and invalidate the whole L2 of the XCD for every
+// block, so instead the partials are written and read with relaxed agent-scope
+// atomic stores / loads: on gfx950 these are plain stores / loads with the sc1
+// (agent coherence) bit, coherent across the XCDs' L2s by themselves.
+PI_DEV void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+PI_DEV void st_agent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+PI_DEV float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+PI_DEV uint32_t ld_agent(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every block calls this once, after all its threads issued their st_agent
+// partials.  The barrier drains the stores (vmcnt(0)) before thread 0 bumps the
+// arrival counter, so the block that sees the final count reads complete
+// partials with ld_agent.  Exactly that last block gets true; it resets the
+// counter, which therefore starts at zero for the next launch on the stream.
 PI_DEV bool last_block_arrive(unsigned* counter, unsigned nblocks) {
     __shared__ int s_last;
-    __threadfence();                 // release this thread's writes (agent scope)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned prev = atomicAdd(counter, 1u);
-        int last = (prev == nblocks - 1u);
-        if (last) atomicExch(counter, 0u);
+        const unsigned prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == nblocks - 1u);
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last;
     }
     __syncthreads();
-    const bool last = s_last != 0;
-    if (last) __threadfence();       // acquire the other blocks' writes
-    return last;
+    return s_last != 0;
 }
 
 // ---- block-wide exclusive scan of one int per thread --------------------------------------
@@ -90,33 +131,56 @@ PI_DEV int block_exclusive_scan(int v, int* s_tmp, int* total) {
 // words apart) to out[0 .. n), and n to *count.  Each thread owns a run of
 // consecutive words, so an exclusive scan of per-thread popcounts gives every
 // thread its first output slot.
+template <bool COHERENT>
 PI_DEV uint32_t mask_word(const uint32_t* mask, int nrows, int stride, int w, int W, int F) {
     uint32_t v = 0;
-    for (int b = 0; b < nrows; ++b) v |= mask[(size_t)b * stride + w];
+    for (int b = 0; b < nrows; ++b)
+        v |= COHERENT ? ld_agent(mask + (size_t)b * stride + w) : mask[(size_t)b * stride + w];
     if (w == W - 1 && (F & 31)) v &= (1u << (F & 31)) - 1u;
     return v;
 }
 
+template <bool COHERENT>
 PI_DEV void block_compact(const uint32_t* mask, int nrows, int stride, int F, int32_t* out,
                           int32_t* count, int* s_tmp) {
+    constexpr int PERMAX = 8;   // words kept in registers per thread
     const int W = (F + 31) >> 5;
     const int per = (W + (int)blockDim.x - 1) / (int)blockDim.x;
     const int w0 = threadIdx.x * per;
+    uint32_t wr[PERMAX];
     int c = 0;
-    for (int i = 0; i < per; ++i) {
-        const int w = w0 + i;
-        if (w < W) c += __popc(mask_word(mask, nrows, stride, w, W, F));
+    if (per <= PERMAX) {
+#pragma unroll
+        for (int i = 0; i < PERMAX; ++i)    // all loads issued before any is used
+            wr[i] = (i < per && w0 + i < W) ? mask_word<COHERENT>(mask, nrows, stride, w0 + i, W, F) : 0u;
+#pragma unroll
+        for (int i = 0; i < PERMAX; ++i) c += __popc(wr[i]);
+    } else {
+        for (int i = 0; i < per; ++i)
+            if (w0 + i < W) c += __popc(mask_word<COHERENT>(mask, nrows, stride, w0 + i, W, F));
     }
     int total;
     int pos = block_exclusive_scan(c, s_tmp, &total);
-    for (int i = 0; i < per; ++i) {
-        const int w = w0 + i;
-        if (w >= W) break;
-        uint32_t v = mask_word(mask, nrows, stride, w, W, F);
-        while (v) {
-            const int b = __ffs(v) - 1;
-            out[pos++] = (w << 5) + b;
-            v &= v - 1u;
+    if (per <= PERMAX) {
+#pragma unroll
+        for (int i = 0; i < PERMAX; ++i) {
+            uint32_t v = wr[i];            // zero past this thread's words
+            while (v) {
+                const int b = __ffs(v) - 1;
+                out[pos++] = ((w0 + i) << 5) + b;
+                v &= v - 1u;
+            }
+        }
+    } else {
+        for (int i = 0; i < per; ++i) {
+            const int w = w0 + i;
+            if (w >= W) break;
+            uint32_t v = mask_word<COHERENT>(mask, nrows, stride, w, W, F);
+            while (v) {
+                const int b = __ffs(v) - 1;
+                out[pos++] = (w << 5) + b;
+                v &= v - 1u;
+            }
         }
     }
     if (threadIdx.x == 0) *count = total;

@@ -13,7 +13,8 @@ namespace pi {
 constexpr int CNT_PRED1 = 0;      // one per predictor column group (r / 64 <= 256)
 constexpr int CNT_PRED2 = 256;    // one for stage 2's compaction
 constexpr int CNT_DOWN = 512;     // one per down-projection column slice (<= 512)
-constexpr int CNT_UNION = 1024;   // union path (<= 1024)
+constexpr int CNT_UNION = 1024;   // union path (<= 512)
+constexpr int CNT_DECODE = 1536;  // fused decode step, one per down slice (<= 512)
 constexpr int CNT_TOTAL = 2048;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
 
@@ -44,6 +45,20 @@ struct FfnPlan {
 };
 FfnPlan plan_ffn(int d, int F, int wfmt, int B);
 
+// ---- fused batch-1 decode step (three kernels) --------------------------------------------
+struct DecPlan {
+    int ncg, rows, rpl;        // stage-1 column groups, rows per chunk, rows per lane
+    int ntile, q;              // stage-2 tiles of 64 neurons, chunks per lane per row
+    size_t lds_b;              // dynamic LDS of the stage-2 + up kernel
+    int cols, nslices, nsplit, wps;   // down: columns per slice, slices, neuron-range splits, mask words per split
+    size_t off_zpart, off_h, off_part, bytes;
+};
+DecPlan plan_decode(int d, int r, int F, int wfmt);
+hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
+                              const uint16_t* x, float theta, float* logits, uint32_t* mask,
+                              int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1);
+
 // ---- launchers (return hipError_t of the launch) ---------------------------------------------------
 hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                           float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
@@ -56,6 +71,14 @@ hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t*
 hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
                          const int32_t* idx, const int32_t* count, int dense_F, float* y,
                          char* ws, hipStream_t s);
+
+// the two batch-1 operators on their own (one kernel each)
+hipError_t launch_up_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
+                        const int32_t* idx, const int32_t* count, int dense_F, float* h,
+                        hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t* idx,
+                          const int32_t* count, int dense_F, const float* h, float* y, char* ws,
+                          hipStream_t s);
 
 // 1 < B <= 32 union-mask path on MFMA
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,

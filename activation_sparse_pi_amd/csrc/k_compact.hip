@@ -15,10 +15,10 @@ __global__ __launch_bounds__(1024) void k_compact(const uint32_t* __restrict__ m
     __shared__ int s_tmp[17];
     const int W = (F + 31) >> 5;
     if (union_mode) {
-        block_compact(mask, B, W, F, idx, count, s_tmp);
+        block_compact<false>(mask, B, W, F, idx, count, s_tmp);
     } else {
         const int b = blockIdx.x;
-        block_compact(mask + (size_t)b * W, 1, W, F, idx + (size_t)b * F, count + b, s_tmp);
+        block_compact<false>(mask + (size_t)b * W, 1, W, F, idx + (size_t)b * F, count + b, s_tmp);
     }
 }
 

@@ -1,0 +1,580 @@
+// Fused batch-1 decode step on gfx950: three kernels per token.
+//
+// PowerInfer (online engine, "Adaptive Sparsity Predictors", "Neuron Placement
+// and Management", "Neuron-aware Operator"): predict the neurons a token will
+// fire, compute only their rows of up/gate and their output vectors of down,
+// and keep a table of their original positions.
+//
+// On this GPU a kernel boundary costs ~2-3 us of timeline and a grid-wide
+// barrier costs as much, so the step is cut where a global dependency forces a
+// cut, and nowhere else:
+//   A  stage-1 partials  zp[p, :] = x[rows of chunk p] . W_p1[rows of chunk p, :]
+//      (P row chunks, no cross-block handoff).
+//   B  one block per 64-neuron tile: z = sum_p zp[p] (in chunk order, while the
+//      tile's W_p2 loads are already in flight), l = z . W_p2[:, tile] + b,
+//      active = l > theta, a wave ballot writes the tile's two mask words, and
+//      the block then computes h for ITS OWN active neurons (gate/up rows dotted
+//      with x staged in LDS).  No global neuron list is needed for that.
+//   C  down projection straight from the mask: block (slice, split) owns a
+//      column slice and a range of neuron ids, compacts its range in LDS, and
+//      accumulates h_i * W_down[i, slice]; the last-arriving block of a slice
+//      adds the splits' partials in split order.  The slice-0 blocks also write
+//      the global ascending neuron table (idx, count) for their range.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace pi {
+namespace {
+
+constexpr int DEC_P = 8;          // stage-1 row chunks
+constexpr int DEC_IDCAP = 4096;   // neuron ids one down block can hold (128 mask words)
+
+// --------------------------------------------------------------------------------------- A
+// Block: 512 threads = 8 column lanes (64 columns) x 64 row lanes; grid (ceil(r/64), P).
+template <int RPL>
+__global__ __launch_bounds__(512) void k_dec_stage1(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ W1, int d, int r,
+                                                    int rows_per_chunk, float* __restrict__ zpart) {
+    __shared__ float s_red[8][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = tid & 7, rl = tid >> 3;
+    const int cg = blockIdx.x, chunk = blockIdx.y;
+    const int col0 = cg * 64 + sub * 8;
+    const bool colok = col0 < r;
+    const int k0 = chunk * rows_per_chunk;
+    const int k1 = min(d, k0 + rows_per_chunk);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int kb = k0 + rl; kb < k1; kb += 64 * RPL) {
+        uint4 w[RPL];
+        float xv[RPL];
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+            const int k = kb + 64 * u;
+            const bool ok = k < k1;
+            w[u] = (ok && colok) ? ld16(W1 + (size_t)k * r + col0) : zero4();
+            xv[u] = ok ? h2f(x[k]) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(xv[u], lo_f(ww[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(xv[u], hi_f(ww[e]), acc[2 * e + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = acc[e];
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[e] = v;
+    }
+    if (lane < 8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_red[wave][lane * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < 64) {
+        const int col = cg * 64 + tid;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) v += s_red[w][tid];
+        if (col < r) zpart[(size_t)chunk * r + col] = v;
+    }
+}
+
+// --------------------------------------------------------------------------------------- B
+// WF: 0 = fp16 rows, 1 = int4 group-128 rows.  Q: 16-byte chunks per lane per row.
+// Dynamic LDS: z (r floats) then x (d/8 uint4; for int4 regrouped per 8 elements as
+// (x0,x4),(x1,x5),(x2,x6),(x3,x7) to match the nibble pairs one AND/OR extracts).
+template <int WF, bool GLU, int Q>
+__global__ __launch_bounds__(1024) void k_dec_stage2_up(
+    const float* __restrict__ zpart, const uint16_t* __restrict__ W2,
+    const float* __restrict__ bias, int r, int F, float theta, float* __restrict__ logits,
+    uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
+    const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
+    const uint16_t* __restrict__ Su, int d, float* __restrict__ h) {
+    extern __shared__ __align__(16) char smem[];
+    float* s_z = reinterpret_cast<float*>(smem);
+    uint4* s_x = reinterpret_cast<uint4*>(smem + align16i(r * 4));
+    __shared__ float s_red[16][64];
+    __shared__ float s_dot[2][64];
+    __shared__ int s_list[64];
+    __shared__ int s_n;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = tid & 7, rl = tid >> 3;   // rl: 0..127
+    const int tile = blockIdx.x;
+    const int n0 = tile * 64 + sub * 8;
+    const bool nok = n0 < F;
+    const int W = (F + 31) >> 5;
+
+    // --- logits of the tile: the first batch of W_p2 loads goes out before z is ready
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    uint4 w2[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int j = rl + 128 * u;
+        w2[u] = (nok && j < r) ? ld16(W2 + (size_t)j * F + n0) : zero4();
+    }
+    for (int j = tid; j < r; j += 1024) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < DEC_P; ++p) s += zpart[(size_t)p * r + j];
+        s_z[j] = s;
+    }
+    const int nc8 = d >> 3;
+    for (int c = tid; c < nc8; c += 1024) {
+        const uint4 a = ld16(x + 8 * c);
+        if (WF == 0) {
+            s_x[c] = a;
+        } else {
+            s_x[c] = make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
+                                (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
+        }
+    }
+    __syncthreads();
+    for (int jb = 0; jb < r; jb += 1024) {
+        if (jb > 0) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = jb + rl + 128 * u;
+                w2[u] = (nok && j < r) ? ld16(W2 + (size_t)j * F + n0) : zero4();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + rl + 128 * u;
+            const float zv = j < r ? s_z[j] : 0.f;
+            const uint32_t ww[4] = {w2[u].x, w2[u].y, w2[u].z, w2[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(zv, lo_f(ww[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(zv, hi_f(ww[e]), acc[2 * e + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = acc[e];
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[e] = v;
+    }
+    if (lane < 8)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_red[wave][lane * 8 + e] = acc[e];
+    __syncthreads();
+
+    // --- threshold, mask words, the tile's active list (wave 0: lane = neuron of the tile)
+    if (wave == 0) {
+        const int n = tile * 64 + lane;
+        bool act = false;
+        if (n < F) {
+            float l = 0.f;
+#pragma unroll
+            for (int w = 0; w < 16; ++w) l += s_red[w][lane];
+            l += bias[n];
+            act = l > theta;
+            if (logits) logits[n] = l;
+        }
+        const unsigned long long bal = __ballot(act);
+        const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+        if (lane == 0) {
+            mask[2 * tile] = lo;
+            if (2 * tile + 1 < W) mask[2 * tile + 1] = hi;
+            s_n = __popcll(bal);
+        }
+        if (act) s_list[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = lane;
+    }
+    __syncthreads();
+
+    // --- rows of the active neurons: one wave per (neuron, matrix) item
+    const int na = s_n;
+    constexpr int M = GLU ? 2 : 1;
+    const int nc = WF == 0 ? (d >> 3) : (d >> 5);   // 16-byte chunks per row
+    const int G = d >> 7;
+    const size_t rb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
+    for (int it = wave; it < na * M; it += 16) {
+        const int k = GLU ? (it >> 1) : it;
+        const int mat = GLU ? (it & 1) : 1;           // 0 = gate, 1 = up
+        const size_t row = (size_t)(tile * 64 + s_list[k]);
+        const uint8_t* base = static_cast<const uint8_t*>(mat ? Wu : Wg) + row * rb;
+        uint4 wr[Q];
+        float sc[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = lane + 64 * q;
+            wr[q] = c < nc ? ld16(base + 16 * (size_t)c) : zero4();
+            if (WF == 1) sc[q] = c < nc ? h2f((mat ? Su : Sg)[row * G + (c >> 2)]) : 0.f;
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = lane + 64 * q;
+            if (c < nc) {
+                if (WF == 0) {
+                    dot = dot8(wr[q], s_x[c], dot);
+                } else {
+                    uint32_t xp[16];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint4 t = s_x[4 * c + m];
+                        xp[4 * m] = t.x; xp[4 * m + 1] = t.y; xp[4 * m + 2] = t.z; xp[4 * m + 3] = t.w;
+                    }
+                    dot = fmaf(dot32_i4(wr[q], xp), sc[q], dot);
+                }
+            }
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) s_dot[mat][k] = dot;
+    }
+    __syncthreads();
+    for (int k = tid; k < na; k += 1024) {
+        const float a = s_dot[1][k];
+        h[tile * 64 + s_list[k]] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
+    }
+}
+
+// --------------------------------------------------------------------------------------- C
+// Block-local compaction of mask words [w0, w1) into s_ids (ascending); returns the count.
+PI_DEV int range_compact(const uint32_t* __restrict__ mask, int w0, int w1, int F, int* s_ids,
+                         int* s_tmp) {
+    const int W = (F + 31) >> 5;
+    const int t = threadIdx.x;
+    uint32_t v = 0;
+    if (w0 + t < w1) {
+        v = mask[w0 + t];
+        if (w0 + t == W - 1 && (F & 31)) v &= (1u << (F & 31)) - 1u;
+    }
+    int total;
+    int pos = block_exclusive_scan(__popc(v), s_tmp, &total);
+    while (v) {
+        const int b = __ffs(v) - 1;
+        s_ids[pos++] = ((w0 + t) << 5) + b;
+        v &= v - 1u;
+    }
+    __syncthreads();
+    return total;
+}
+
+// The global table for the slice-0 blocks: prefix = popcount of all words before w0.
+PI_DEV void write_table(const uint32_t* __restrict__ mask, int w0, int n_loc, bool last_split,
+                        const int* s_ids, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                        int* s_acc) {
+    if (threadIdx.x == 0) *s_acc = 0;
+    __syncthreads();
+    int c = 0;
+    for (int w = threadIdx.x; w < w0; w += blockDim.x) c += __popc(mask[w]);
+    c += __shfl_xor(c, 1); c += __shfl_xor(c, 2); c += __shfl_xor(c, 4);
+    c += __shfl_xor(c, 8); c += __shfl_xor(c, 16); c += __shfl_xor(c, 32);
+    if ((threadIdx.x & 63) == 0 && c) atomicAdd(s_acc, c);
+    __syncthreads();
+    const int P = *s_acc;
+    for (int i = threadIdx.x; i < n_loc; i += blockDim.x) idx[P + i] = s_ids[i];
+    if (last_split && threadIdx.x == 0) *count = P + n_loc;
+}
+
+template <int U>
+__global__ __launch_bounds__(1024) void k_dec_down_f16(
+    const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
+    const uint16_t* __restrict__ Wd, int d, int wps, float* __restrict__ part,
+    float* __restrict__ y, unsigned* __restrict__ counters, int32_t* __restrict__ idx,
+    int32_t* __restrict__ count) {
+    constexpr int NW = 16;
+    __shared__ int s_ids[DEC_IDCAP];
+    __shared__ float4 s_red[NW][128];
+    __shared__ float s_half[512];
+    __shared__ int s_tmp[17];
+    __shared__ int s_acc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+    const int W = (F + 31) >> 5;
+    const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
+    const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
+    if (slice == 0 && idx != nullptr)
+        write_table(mask, w0, n_loc, split == nsplit - 1, s_ids, idx, count, &s_acc);
+
+    const int nc = d >> 3;
+    const int c = slice * 64 + lane;
+    const bool cok = c < nc;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int k0 = wave; k0 < n_loc; k0 += NW * U) {
+        uint4 w[U];
+        float hv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * NW;
+            if (kk < n_loc) {
+                const int row = s_ids[kk];
+                hv[u] = h[row];
+                w[u] = cok ? ld16(Wd + (size_t)row * d + 8 * c) : zero4();
+            } else {
+                hv[u] = 0.f;
+                w[u] = zero4();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
+            }
+        }
+    }
+    s_red[wave][2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    s_red[wave][2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    __syncthreads();
+    const int col = tid & 511, hf = tid >> 9;
+    const float* sr = reinterpret_cast<const float*>(s_red);
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW / 2; ++w) s += sr[(hf * (NW / 2) + w) * 512 + col];
+    if (hf == 1) s_half[col] = s;
+    __syncthreads();
+    const int gcol = slice * 512 + col;
+    if (hf == 0 && gcol < d) st_agent(&part[(size_t)split * d + gcol], s + s_half[col]);
+    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
+        float t = 0.f;
+        if (gcol < d) {
+            for (int base = hf; base < nsplit; base += 32) {
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int sp = base + 2 * j;
+                    v[j] = sp < nsplit ? ld_agent(&part[(size_t)sp * d + gcol]) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t += v[j];
+            }
+        }
+        __syncthreads();
+        if (hf == 1) s_half[col] = t;
+        __syncthreads();
+        if (hf == 0 && gcol < d) y[gcol] = t + s_half[col];
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(512) void k_dec_down_i4(
+    const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
+    const uint8_t* __restrict__ Dq, const uint16_t* __restrict__ Ds, int d, int wps,
+    float* __restrict__ part, float* __restrict__ y, unsigned* __restrict__ counters,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    constexpr int NW = 8;
+    __shared__ int s_ids[DEC_IDCAP];
+    __shared__ float4 s_red[NW][512];
+    __shared__ int s_tmp[9];
+    __shared__ int s_acc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+    const int W = (F + 31) >> 5;
+    const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
+    const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
+    if (slice == 0 && idx != nullptr)
+        write_table(mask, w0, n_loc, split == nsplit - 1, s_ids, idx, count, &s_acc);
+
+    const int nc = d >> 5;
+    const int G = d >> 7;
+    const size_t rb = (size_t)(d >> 1);
+    const int c = slice * 64 + lane;
+    const bool cok = c < nc;
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+    float soff = 0.f;
+    for (int k0 = wave; k0 < n_loc; k0 += NW * U) {
+        uint4 w[U];
+        float hs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * NW;
+            if (kk < n_loc && cok) {
+                const size_t row = (size_t)s_ids[kk];
+                w[u] = ld16(Dq + row * rb + 16 * c);
+                hs[u] = h[row] * h2f(Ds[row * G + (c >> 2)]);
+            } else {
+                w[u] = zero4();
+                hs[u] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            soff += hs[u];
+            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    acc[8 * m + 2 * b] = fmaf(hs[u], (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
+                    acc[8 * m + 2 * b + 1] = fmaf(hs[u], (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; j += 4)
+        s_red[wave][8 * lane + j / 4] =
+            make_float4(fmaf(-8.f, soff, acc[j]), fmaf(-8.f, soff, acc[j + 1]),
+                        fmaf(-8.f, soff, acc[j + 2]), fmaf(-8.f, soff, acc[j + 3]));
+    __syncthreads();
+    float4 s = s_red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        const float4 t = s_red[w][tid];
+        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    const int gcol = slice * 2048 + 4 * tid;
+    if (gcol < d) {
+        float* pp = part + (size_t)split * d + gcol;
+        st_agent(pp, s.x); st_agent(pp + 1, s.y); st_agent(pp + 2, s.z); st_agent(pp + 3, s.w);
+    }
+    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
+        if (gcol < d) {
+            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int base = 0; base < nsplit; base += 8) {
+                float v[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float* pp = part + (size_t)(base + j) * d + gcol;
+                    const bool ok = base + j < nsplit;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[j][e] = ok ? ld_agent(pp + e) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    t.x += v[j][0]; t.y += v[j][1]; t.z += v[j][2]; t.w += v[j][3];
+                }
+            }
+            *reinterpret_cast<float4*>(y + gcol) = t;
+        }
+    }
+}
+
+// --------------------------------------------------------------------------------------- dispatch
+hipError_t launch_stage1(int rpl, dim3 g, const uint16_t* x, const uint16_t* W1, int d, int r,
+                         int rows, float* zpart, hipStream_t s) {
+    switch (rpl) {
+        case 1: hipLaunchKernelGGL((k_dec_stage1<1>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
+        case 2: hipLaunchKernelGGL((k_dec_stage1<2>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
+        case 4: hipLaunchKernelGGL((k_dec_stage1<4>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
+        case 8: hipLaunchKernelGGL((k_dec_stage1<8>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
+        default: hipLaunchKernelGGL((k_dec_stage1<16>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
+    }
+    return hipGetLastError();
+}
+
+template <int WF, bool GLU, int Q>
+void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* zpart,
+              const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
+              const uint16_t* x, const pi_ffn_desc& f, float* h) {
+    if (e0)
+        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(1024), (uint32_t)lds, s, e0, e1, 0,
+                              zpart, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
+                              f.s_gate, f.w_up, f.s_up, f.d, h);
+    else
+        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(1024), lds, s, zpart, p.w_p2,
+                           p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
+                           f.s_up, f.d, h);
+}
+
+template <int WF, bool GLU>
+hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                      const float* zpart, const pi_pred_desc& p, float theta, float* logits,
+                      uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h) {
+#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ>(g, lds, s, e0, e1, zpart, p, theta, logits, mask, x, f, h); break;
+    if constexpr (WF == 0) {
+        switch (q) {
+            PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
+            PI_B(9) PI_B(10) PI_B(11) PI_B(12) PI_B(13) PI_B(14) PI_B(15) PI_B(16)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (q) {
+            PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef PI_B
+    return hipGetLastError();
+}
+
+}  // namespace
+
+DecPlan plan_decode(int d, int r, int F, int wfmt) {
+    DecPlan p{};
+    p.ncg = (r + 63) / 64;
+    p.rows = (d + DEC_P - 1) / DEC_P;
+    const int rpl_need = (p.rows + 63) / 64;
+    p.rpl = rpl_need <= 1 ? 1 : rpl_need <= 2 ? 2 : rpl_need <= 4 ? 4 : rpl_need <= 8 ? 8 : 16;
+    p.ntile = (F + 63) / 64;
+    const bool f16 = wfmt == PI_W_F16;
+    p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
+    p.lds_b = (size_t)align16i(r * 4) + (size_t)(d / 8) * 16;
+    p.cols = f16 ? 512 : 2048;
+    p.nslices = (d + p.cols - 1) / p.cols;
+    const int W = (F + 31) / 32;
+    const int wpb = f16 ? 16 : 8;
+    int ns = 2048 / (p.nslices * wpb);
+    const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
+    if (ns > 32) ns = 32;
+    if (ns < ns_min) ns = ns_min;
+    if (ns < 1) ns = 1;
+    p.wps = (W + ns - 1) / ns;
+    p.nsplit = (W + p.wps - 1) / p.wps;
+    size_t off = COUNTER_BYTES;
+    p.off_zpart = off;
+    off = align_up(off + (size_t)DEC_P * r * sizeof(float), 256);
+    p.off_h = off;
+    off = align_up(off + (size_t)F * sizeof(float), 256);
+    p.off_part = off;
+    off = align_up(off + (size_t)p.nsplit * d * sizeof(float), 256);
+    p.bytes = off;
+    return p;
+}
+
+hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
+                              const uint16_t* x, float theta, float* logits, uint32_t* mask,
+                              int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
+    float* zpart = reinterpret_cast<float*>(ws + pl.off_zpart);
+    float* h = reinterpret_cast<float*>(ws + pl.off_h);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DECODE;
+    hipError_t e = launch_stage1(pl.rpl, dim3(pl.ncg, DEC_P), x, p.w_p1, p.d, p.r, pl.rows, zpart, s);
+    if (e != hipSuccess) return e;
+    const bool glu = f.act == PI_ACT_REGLU;
+    const dim3 gb(pl.ntile);
+    if (f.wfmt == PI_W_F16)
+        e = glu ? dispatch_b<0, true>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h)
+                : dispatch_b<0, false>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h);
+    else
+        e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h)
+                : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h);
+    if (e != hipSuccess) return e;
+    const dim3 gc(pl.nslices, pl.nsplit);
+    if (f.wfmt == PI_W_F16)
+        hipLaunchKernelGGL((k_dec_down_f16<4>), gc, dim3(1024), 0, s, mask, f.F, h,
+                           static_cast<const uint16_t*>(f.w_down), f.d, pl.wps, part, y, cnt, idx,
+                           count);
+    else
+        hipLaunchKernelGGL((k_dec_down_i4<4>), gc, dim3(512), 0, s, mask, f.F, h,
+                           static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, pl.wps, part, y,
+                           cnt, idx, count);
+    return hipGetLastError();
+}
+
+}  // namespace pi

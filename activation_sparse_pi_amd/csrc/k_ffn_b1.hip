@@ -21,6 +21,8 @@
 // scaled once.  Down: h*s is formed once per neuron and chunk, nibbles are
 // converted byte-wise to float, and the -8 offset is applied once at the end
 // through the running sum of h*s.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -76,23 +78,6 @@ __global__ __launch_bounds__(256) void k_up_f16(const uint16_t* __restrict__ x,
 }
 
 // ------------------------------------------------------------------------------------------ int4 up
-PI_DEV float dot32_i4(const uint4& w, const uint32_t* xp) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint32_t v = ws[m];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t bits = ((v >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-            const h2_t qv = __builtin_bit_cast(h2_t, bits) - off;   // (u - 8) exactly
-            acc = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2_t, xp[4 * m + p]), acc, false);
-        }
-    }
-    return acc;
-}
-
 template <int Q, bool GLU>
 __global__ __launch_bounds__(256) void k_up_i4(const uint16_t* __restrict__ x,
                                                const uint8_t* __restrict__ Gq,
@@ -218,11 +203,21 @@ __global__ __launch_bounds__(1024) void k_down_f16(const uint16_t* __restrict__ 
     if (hf == 1) s_half[col] = s;
     __syncthreads();
     const int gcol = slice * 512 + col;
-    if (hf == 0 && gcol < d) part[(size_t)split * d + gcol] = s + s_half[col];
+    if (hf == 0 && gcol < d) st_agent(&part[(size_t)split * d + gcol], s + s_half[col]);
     if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
         float t = 0.f;
-        if (gcol < d)
-            for (int sp = hf; sp < nsplit; sp += 2) t += part[(size_t)sp * d + gcol];
+        if (gcol < d) {
+            for (int base = hf; base < nsplit; base += 32) {   // 16 partials in flight
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int sp = base + 2 * j;
+                    v[j] = sp < nsplit ? ld_agent(&part[(size_t)sp * d + gcol]) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t += v[j];
+            }
+        }
         __syncthreads();
         if (hf == 1) s_half[col] = t;
         __syncthreads();
@@ -299,13 +294,26 @@ __global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
         s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
     }
     const int gcol = slice * 2048 + 4 * tid;
-    if (gcol < d) *reinterpret_cast<float4*>(part + (size_t)split * d + gcol) = s;
+    if (gcol < d) {
+        float* pp = part + (size_t)split * d + gcol;
+        st_agent(pp, s.x); st_agent(pp + 1, s.y); st_agent(pp + 2, s.z); st_agent(pp + 3, s.w);
+    }
     if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
         if (gcol < d) {
             float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int sp = 0; sp < nsplit; ++sp) {
-                const float4 v = *reinterpret_cast<const float4*>(part + (size_t)sp * d + gcol);
-                t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+            for (int base = 0; base < nsplit; base += 8) {     // 32 partials in flight
+                float v[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float* pp = part + (size_t)(base + j) * d + gcol;
+                    const bool ok = base + j < nsplit;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[j][e] = ok ? ld_agent(pp + e) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    t.x += v[j][0]; t.y += v[j][1]; t.z += v[j][2]; t.w += v[j][3];
+                }
             }
             *reinterpret_cast<float4*>(y + gcol) = t;
         }
@@ -315,8 +323,12 @@ __global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
 // ------------------------------------------------------------------------------------------ dispatch
 template <bool GLU>
 hipError_t up_f16(int q, int blocks, const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int d, int F,
-                  const int32_t* idx, const int32_t* count, int dense_F, float* h, hipStream_t s) {
-#define PI_UPF16(QQ) case QQ: hipLaunchKernelGGL((k_up_f16<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Wg, Wu, d, F, idx, count, dense_F, h); break;
+                  const int32_t* idx, const int32_t* count, int dense_F, float* h, hipStream_t s,
+                  hipEvent_t ev0, hipEvent_t ev1) {
+#define PI_UPF16(QQ) case QQ: \
+    if (ev0) hipExtLaunchKernelGGL((k_up_f16<QQ, GLU>), dim3(blocks), dim3(256), 0, s, ev0, ev1, 0, x, Wg, Wu, d, F, idx, count, dense_F, h); \
+    else hipLaunchKernelGGL((k_up_f16<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Wg, Wu, d, F, idx, count, dense_F, h); \
+    break;
     switch (q) {
         PI_UPF16(1) PI_UPF16(2) PI_UPF16(3) PI_UPF16(4) PI_UPF16(5) PI_UPF16(6) PI_UPF16(7) PI_UPF16(8)
         PI_UPF16(9) PI_UPF16(10) PI_UPF16(11) PI_UPF16(12) PI_UPF16(13) PI_UPF16(14) PI_UPF16(15) PI_UPF16(16)
@@ -329,8 +341,12 @@ hipError_t up_f16(int q, int blocks, const uint16_t* x, const uint16_t* Wg, cons
 template <bool GLU>
 hipError_t up_i4(int q, int blocks, const uint16_t* x, const uint8_t* Gq, const uint16_t* Gs,
                  const uint8_t* Uq, const uint16_t* Us, int d, int F, const int32_t* idx,
-                 const int32_t* count, int dense_F, float* h, hipStream_t s) {
-#define PI_UPI4(QQ) case QQ: hipLaunchKernelGGL((k_up_i4<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Gq, Gs, Uq, Us, d, F, idx, count, dense_F, h); break;
+                 const int32_t* count, int dense_F, float* h, hipStream_t s, hipEvent_t ev0,
+                 hipEvent_t ev1) {
+#define PI_UPI4(QQ) case QQ: \
+    if (ev0) hipExtLaunchKernelGGL((k_up_i4<QQ, GLU>), dim3(blocks), dim3(256), 0, s, ev0, ev1, 0, x, Gq, Gs, Uq, Us, d, F, idx, count, dense_F, h); \
+    else hipLaunchKernelGGL((k_up_i4<QQ, GLU>), dim3(blocks), dim3(256), 0, s, x, Gq, Gs, Uq, Us, d, F, idx, count, dense_F, h); \
+    break;
     switch (q) {
         PI_UPI4(1) PI_UPI4(2) PI_UPI4(3) PI_UPI4(4) PI_UPI4(5) PI_UPI4(6) PI_UPI4(7) PI_UPI4(8)
         default: return hipErrorInvalidValue;
@@ -365,35 +381,47 @@ FfnPlan plan_ffn(int d, int F, int wfmt, int B) {
     return p;
 }
 
-hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
-                         const int32_t* idx, const int32_t* count, int dense_F, float* y,
-                         char* ws, hipStream_t s) {
-    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
-    float* h = reinterpret_cast<float*>(ws + pl.off_h);
-    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+hipError_t launch_up_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
+                        const int32_t* idx, const int32_t* count, int dense_F, float* h,
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const bool glu = f.act == PI_ACT_REGLU;
-    hipError_t e;
-    const dim3 gd(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16) {
         const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
         const uint16_t* Wu = static_cast<const uint16_t*>(f.w_up);
-        e = glu ? up_f16<true>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s)
-                : up_f16<false>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s);
-        if (e != hipSuccess) return e;
+        return glu ? up_f16<true>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s, ev0, ev1)
+                   : up_f16<false>(pl.q, pl.up_blocks, x, Wg, Wu, f.d, f.F, idx, count, dense_F, h, s, ev0, ev1);
+    }
+    const uint8_t* Gq = static_cast<const uint8_t*>(f.w_gate);
+    const uint8_t* Uq = static_cast<const uint8_t*>(f.w_up);
+    return glu ? up_i4<true>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s, ev0, ev1)
+               : up_i4<false>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s, ev0, ev1);
+}
+
+hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t* idx,
+                          const int32_t* count, int dense_F, const float* h, float* y, char* ws,
+                          hipStream_t s) {
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    const dim3 gd(pl.nslices, pl.nsplit);
+    if (f.wfmt == PI_W_F16) {
         hipLaunchKernelGGL((k_down_f16<4>), gd, dim3(64 * DOWN_WAVES_F16), 0, s,
                            static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, dense_F, h,
                            part, y, cnt);
     } else {
-        const uint8_t* Gq = static_cast<const uint8_t*>(f.w_gate);
-        const uint8_t* Uq = static_cast<const uint8_t*>(f.w_up);
-        e = glu ? up_i4<true>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s)
-                : up_i4<false>(pl.q, pl.up_blocks, x, Gq, f.s_gate, Uq, f.s_up, f.d, f.F, idx, count, dense_F, h, s);
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_down_i4<4>), gd, dim3(64 * DOWN_WAVES_I4), 0, s,
                            static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, f.F, idx, count,
                            dense_F, h, part, y, cnt);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
+                         const int32_t* idx, const int32_t* count, int dense_F, float* y,
+                         char* ws, hipStream_t s) {
+    float* h = reinterpret_cast<float*>(ws + pl.off_h);
+    hipError_t e = launch_up_b1(f, pl, x, idx, count, dense_F, h, s, nullptr, nullptr);
+    if (e != hipSuccess) return e;
+    return launch_down_b1(f, pl, idx, count, dense_F, h, y, ws, s);
 }
 
 }  // namespace pi

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_pred_stage1(const uint16_t* __restrict_
             const int t = i >> 6, c = i & 63, col = cg * 64 + c;
             if (b0 + t < B && col < r) {
                 const float v = ((s_red[0][t][c] + s_red[1][t][c]) + s_red[2][t][c]) + s_red[3][t][c];
-                part[((size_t)chunk * B + b0 + t) * r + col] = v;
+                st_agent(&part[((size_t)chunk * B + b0 + t) * r + col], v);
             }
         }
         __syncthreads();
@@ -99,8 +99,19 @@ __global__ __launch_bounds__(256) void k_pred_stage1(const uint16_t* __restrict_
         const int c = tid & 63, qtr = tid >> 6, col = cg * 64 + c;
         for (int b = 0; b < B; ++b) {
             float s = 0.f;
-            if (col < r)
-                for (int ch = qtr; ch < nchunk; ch += 4) s += part[((size_t)ch * B + b) * r + col];
+            if (col < r) {
+                // 16 partials in flight per thread, summed in chunk order
+                for (int base = qtr; base < nchunk; base += 64) {
+                    float v[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int ch = base + 4 * j;
+                        v[j] = ch < nchunk ? ld_agent(&part[((size_t)ch * B + b) * r + col]) : 0.f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) s += v[j];
+                }
+            }
             s_red[qtr][0][c] = s;
             __syncthreads();
             if (qtr == 0 && col < r)
@@ -189,8 +200,8 @@ __global__ __launch_bounds__(256) void k_pred_stage2(const float* __restrict__ z
             const unsigned long long bal = __ballot(act);
             if (nn == 0 && b < B) {
                 const int wd = blockIdx.x * 2;
-                mask[(size_t)b * W + wd] = (uint32_t)bal;
-                if (wd + 1 < W) mask[(size_t)b * W + wd + 1] = (uint32_t)(bal >> 32);
+                st_agent(&mask[(size_t)b * W + wd], (uint32_t)bal);
+                if (wd + 1 < W) st_agent(&mask[(size_t)b * W + wd + 1], (uint32_t)(bal >> 32));
             }
         }
         __syncthreads();
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256) void k_pred_stage2(const float* __restrict__ z
 
     if (idx != nullptr && last_block_arrive(counter, gridDim.x)) {
         for (int b = 0; b < B; ++b)
-            block_compact(mask + (size_t)b * W, 1, W, F, idx + (size_t)b * F, count + b, s_tmp);
+            block_compact<true>(mask + (size_t)b * W, 1, W, F, idx + (size_t)b * F, count + b, s_tmp);
     }
 }
 
@@ -219,9 +230,9 @@ hipError_t launch_stage1_ku(int ku, dim3 g, const uint16_t* x, int B, const uint
 PredPlan plan_pred(int d, int r, int F, int B) {
     PredPlan p{};
     p.ncg = (r + 63) / 64;
+    // at most 64 row chunks, so the last block of a column group sums 16 partials per thread
     p.ku = 1;
-    // aim for >= 1024 stage-1 blocks while keeping at least 32 rows per block
-    while (p.ku < 8 && (long)p.ncg * ((d + 32 * p.ku * 2 - 1) / (32 * p.ku * 2)) >= 1024) p.ku *= 2;
+    while (p.ku < 8 && (d + 32 * p.ku - 1) / (32 * p.ku) > 64) p.ku *= 2;
     p.nchunk = (d + 32 * p.ku - 1) / (32 * p.ku);
     p.nb = B >= 8 ? 8 : (B >= 4 ? 4 : (B >= 2 ? 2 : 1));
     p.nblk2 = (F + 63) / 64;

@@ -137,6 +137,10 @@ size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int 
             if (b > need) need = b;
         }
     }
+    if (pred && ffn && pred->d == ffn->d && pred->F == ffn->F) {
+        const size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
+        if (b > need) need = b;
+    }
     return need;
 }
 
@@ -201,6 +205,72 @@ int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B, const int32_
         e = launch_ffn_union(*ffn, pl, x, B, idx, count, token_mask, 0, y, static_cast<char*>(ws), s);
     }
     if (e != hipSuccess) return hip_fail(e, "pi_sparse_ffn launch");
+    return ok();
+}
+
+int pi_ffn_up(const pi_ffn_desc* ffn, const uint16_t* x, const int32_t* idx, const int32_t* count,
+              float* h, void* stream) {
+    int st;
+    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
+    if (!x || !idx || !count || !h) return fail(PI_ERR_NULL, "x, idx, count and h are required");
+    if (!aligned16(x)) return fail(PI_ERR_ALIGN, "x must be 16-byte aligned");
+    const FfnPlan pl = plan_ffn(ffn->d, ffn->F, ffn->wfmt, 1);
+    hipError_t e = launch_up_b1(*ffn, pl, x, idx, count, 0, h, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_up launch");
+    return ok();
+}
+
+int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count, const float* h,
+                float* y, void* ws, size_t ws_bytes, void* stream) {
+    int st;
+    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
+    if (!idx || !count || !h || !y) return fail(PI_ERR_NULL, "idx, count, h and y are required");
+    if (!aligned16(y)) return fail(PI_ERR_ALIGN, "y must be 16-byte aligned");
+    const FfnPlan pl = plan_ffn(ffn->d, ffn->F, ffn->wfmt, 1);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    hipError_t e = launch_down_b1(*ffn, pl, idx, count, 0, h, y, static_cast<char*>(ws),
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_down launch");
+    return ok();
+}
+
+int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                  int T, long long s0, int nsteps, uint32_t* mask, int32_t* idx, int32_t* count,
+                  float* y, void* const* events, void* ws, size_t ws_bytes, void* stream) {
+    int st;
+    if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
+    if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
+    if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
+    if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
+    if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
+    if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
+    for (int i = 0; i < nrep; ++i) {
+        if ((st = check_pred(&preds[i])) != PI_OK) return st;
+        if ((st = check_ffn(&ffns[i], 1)) != PI_OK) return st;
+        if (preds[i].d != ffns[i].d || preds[i].F != ffns[i].F || preds[i].d != preds[0].d ||
+            preds[i].F != preds[0].F || preds[i].r != preds[0].r || ffns[i].act != ffns[0].act ||
+            ffns[i].wfmt != ffns[0].wfmt || preds[i].threshold != preds[0].threshold)
+            return fail(PI_ERR_SHAPE, "replica %d does not match replica 0 / its ffn", i);
+    }
+    if (events)
+        for (int i = 0; i < 2 * nsteps; ++i)
+            if (!events[i]) return fail(PI_ERR_NULL, "events[%d] is NULL", i);
+    const DecPlan pl = plan_decode(preds[0].d, preds[0].r, preds[0].F, ffns[0].wfmt);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    const double tau = preds[0].threshold;
+    const float theta = (float)std::log(tau / (1.0 - tau));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    const int d = preds[0].d;
+    for (int i = 0; i < nsteps; ++i) {
+        const long long g = s0 + i;
+        const int t = (int)(g % T), rep = (int)(g % nrep);
+        hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[2 * i]) : nullptr;
+        hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[2 * i + 1]) : nullptr;
+        hipError_t e = launch_decode_step(preds[rep], ffns[rep], pl, x + (size_t)t * d, theta,
+                                          nullptr, mask, idx, count, y, w, s, e0, e1);
+        if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
+    }
     return ok();
 }
 

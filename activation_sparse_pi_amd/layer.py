@@ -74,9 +74,31 @@ class DeviceLayer:
         L.check(L.pi_sparse_ffn(self.ffn[rep], x, B, idx, count, token_mask, y, self.ws.data_ptr(),
                                 self.ws_bytes, self.stream()))
 
+    def ffn_up(self, x, idx, count, h, rep: int = 0) -> None:
+        L.check(L.pi_ffn_up(self.ffn[rep], x, idx, count, h, self.stream()))
+
+    def ffn_down(self, idx, count, h, y, rep: int = 0) -> None:
+        L.check(L.pi_ffn_down(self.ffn[rep], idx, count, h, y, self.ws.data_ptr(), self.ws_bytes,
+                              self.stream()))
+
     def dense(self, x, B, y, rep: int = 0) -> None:
         L.check(L.pi_ffn_dense_ref_gpu(self.ffn[rep], x, B, y, self.ws.data_ptr(), self.ws_bytes,
                                        self.stream()))
+
+    def decode_run(self, x, T: int, s0: int, nsteps: int, bufs: dict, events=None) -> None:
+        """Enqueue nsteps fused batch-1 steps from native code (token (s0+i) % T, replica
+        (s0+i) % R).  events: None or a list of 2*nsteps recorded torch.cuda.Event objects."""
+        import ctypes
+        if not hasattr(self, "_pred_arr"):
+            self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
+            self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
+        ev = None
+        if events is not None:
+            ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        L.check(L.pi_decode_run(self._pred_arr, self._ffn_arr, self.replicas, x, T, s0, nsteps,
+                                bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
+                                bufs["count"].data_ptr(), bufs["y"].data_ptr(),
+                                ev, self.ws.data_ptr(), self.ws_bytes, self.stream()))
 
     def step(self, x, bufs: dict, rep: int = 0, logits: bool = True) -> None:
         """One batch-1 decode step: predict + compact (fused), then the sparse FFN.
@@ -101,4 +123,5 @@ class DeviceLayer:
             uidx=torch.empty((self.F,), dtype=torch.int32, device=dev),
             ucount=torch.empty((1,), dtype=torch.int32, device=dev),
             y=torch.empty((B, self.d), dtype=torch.float32, device=dev),
+            h=torch.empty((self.F,), dtype=torch.float32, device=dev),
         )

@@ -100,8 +100,9 @@ const char* pi_last_error(void);            /* thread-local detail of the last f
 int         pi_version(void);               /* major * 10000 + minor * 100 + patch      */
 
 /* ---- workspace -------------------------------------------------------------------------
- * Bytes of device workspace needed by pi_predict / pi_sparse_ffn /
- * pi_ffn_dense_ref_gpu for any batch 1..B_max (either descriptor may be NULL).
+ * Bytes of device workspace needed by pi_predict / pi_sparse_ffn / pi_ffn_down /
+ * pi_ffn_dense_ref_gpu for any batch 1..B_max, and (when both descriptors are
+ * given) by pi_decode_run.  Either descriptor may be NULL.
  * The workspace holds partial sums, the predictor's z, the activations h and
  * self-resetting arrival counters.  It must be 256-byte aligned and zero-filled
  * once before first use (pi_workspace_init, or any zero fill); every kernel
@@ -148,6 +149,46 @@ int pi_compact(const uint32_t* mask, int B, int F, int mode,
 int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B,
                   const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
                   float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- the two batch-1 operators on their own ----------------------------------------------
+ * pi_sparse_ffn at B == 1 is exactly pi_ffn_up followed by pi_ffn_down; each
+ * enqueues one kernel, so callers can time or schedule them separately.
+ * PowerInfer, "Neuron-aware Operator": the row operator reads single row vectors
+ * of the up (and gate) projection, the column operator single output vectors of
+ * the down projection.
+ *   pi_ffn_up   : h[k] = act(W_up[idx[k]] . x [, W_gate[idx[k]] . x]) for k < count;
+ *                 h fp32 [F] (entries from count on are not written).  Needs no
+ *                 workspace.
+ *   pi_ffn_down : y = sum over k < count of h[k] * W_down[idx[k], :]; y fp32 [d],
+ *                 overwritten.  Uses the workspace for its partial sums.
+ * Ids outside [0, F) contribute nothing; count is clamped to F.                        */
+int pi_ffn_up(const pi_ffn_desc* ffn, const uint16_t* x, const int32_t* idx,
+              const int32_t* count, float* h, void* stream);
+int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count,
+                const float* h, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- pi_decode_run: native batch-1 decode-stream executor ------------------------------
+ * Enqueues nsteps consecutive decode steps on `stream` from native code.  Step
+ * i uses token x[(s0 + i) % T] (x fp16 [T, d]) and the layer of replica
+ * (s0 + i) % nrep (preds[nrep], ffns[nrep]: layers of one shape, e.g. the layers
+ * of a model or byte-identical copies).  A step is the same computation as
+ * pi_predict + pi_sparse_ffn, fused into three kernels:
+ *   1. predictor stage-1 partial sums of z = x W_p1 over 8 row chunks;
+ *   2. per 64-neuron tile: z, logits, strict threshold, mask words, and h of the
+ *      tile's own predicted-active neurons (their up/gate rows);
+ *   3. the down projection read straight from the mask, which also writes the
+ *      ascending neuron table.
+ * mask u32 [ceil(F/32)], idx int32 [F] + count int32 [1] (both NULL or both set)
+ * and y fp32 [d] hold the LAST step's results.  The summation order of z differs
+ * from pi_predict's, so logits agree to fp32 rounding, not bit for bit.
+ * events: NULL, or 2*nsteps hipEvent_t created with timing enabled; then kernel 2
+ * of step i (the one that moves the most bytes) is launched with events[2i] /
+ * events[2i+1] attached to its own start / end (hipExtLaunchKernelGGL), so their
+ * elapsed time is exactly that kernel's execution time.                                 */
+int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
+                  const uint16_t* x, int T, long long s0, int nsteps,
+                  uint32_t* mask, int32_t* idx, int32_t* count, float* y,
+                  void* const* events, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- pi_ffn_dense_ref_gpu ------------------------------------------------------------------
  * The same FFN over all F neurons (no predictor, no skipping): the dense

@@ -163,3 +163,54 @@ def test_config_end_to_end(name):
             P.check_ffn(gpu_ffn_on(layer, xd[t, 0], ref_idx, bufs), W, X[t], ref_idx,
                         ctx=f"{name} t={t} oracle idx")
     say(f"[gpu] {name}: band disagreements {band_total}, worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_decode_run_fused(name):
+    """pi_decode_run (fused three-kernel step, native loop over replicas) against the
+    oracle: index set, neuron table, mask and y of single steps; a multi-step run ends
+    with exactly the single-step result of its last token."""
+    cfg = configs.get(name)
+    say(f"[gpu] fused decode_run on {cfg.name}")
+    inp = _full(name)
+    W = O.Weights.from_inputs(inp)
+    layer = _layer(inp, replicas=3)
+    bufs, ref = layer.buffers(1), layer.buffers(1)
+    X = inp["x"][:, 0, :]
+    xd = torch.from_numpy(X.copy()).to(layer.device)
+    tokens = sorted(set(np.linspace(0, cfg.T - 1, 5).astype(int).tolist()))
+    ref_L = O.predictor_logits(X[tokens], inp["w_p1"], inp["w_p2"], inp["bias"])
+    for i, t in enumerate(tokens):
+        layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs)
+        torch.cuda.synchronize()
+        n = int(bufs["count"][0].item())
+        gidx = _to_np(bufs["idx"][0, :n]).astype(np.int64)
+        gmask = _to_np(bufs["mask"][0]).view(np.uint32)
+        P.check_index_set(gidx, gmask, ref_L[i], cfg.F, ctx=f"{name} fused t={t}")
+        P.check_ffn(_to_np(bufs["y"][0]), W, X[t], gidx, ctx=f"{name} fused t={t}")
+    # 17 steps from s0 = 40 end on token 56 of replica 56 % 3; deterministic kernels
+    layer.decode_run(xd.data_ptr(), cfg.T, 40, 17, bufs)
+    layer.decode_run(xd.data_ptr(), cfg.T, 56, 1, ref)
+    torch.cuda.synchronize()
+    c = int(ref["count"][0].item())
+    assert int(bufs["count"][0].item()) == c
+    assert torch.equal(bufs["idx"][0, :c], ref["idx"][0, :c])
+    assert torch.equal(bufs["mask"], ref["mask"])
+    assert torch.equal(bufs["y"], ref["y"])
+
+
+def test_operators_match_sparse_ffn():
+    """pi_ffn_up + pi_ffn_down give, bit for bit, what pi_sparse_ffn gives."""
+    cfg = configs.C1
+    inp = _full("c1")
+    layer = _layer(inp)
+    bufs, ref = layer.buffers(1), layer.buffers(1)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    for t in (0, 7, 33):
+        layer.step(xd[t].data_ptr(), ref, logits=False)
+        layer.ffn_up(xd[t].data_ptr(), ref["idx"].data_ptr(), ref["count"].data_ptr(),
+                     bufs["h"].data_ptr())
+        layer.ffn_down(ref["idx"].data_ptr(), ref["count"].data_ptr(), bufs["h"].data_ptr(),
+                       bufs["y"].data_ptr())
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["y"], ref["y"])
