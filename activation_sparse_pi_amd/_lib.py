@@ -26,7 +26,7 @@ EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_byte
 
 
 class PredDesc(ctypes.Structure):
-    _fields_ = [("w_p1", c_void_p), ("w_p2", c_void_p), ("bias", c_void_p),
+    _fields_ = [("w_p1t", c_void_p), ("w_p2t", c_void_p), ("bias", c_void_p),
                 ("d", c_int32), ("r", c_int32), ("F", c_int32), ("threshold", c_float)]
 
 

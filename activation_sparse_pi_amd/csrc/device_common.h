@@ -47,14 +47,57 @@ PI_DEV float dot32_i4(const uint4& w, const uint32_t* xp) {
     return acc;
 }
 
+// sum of the 8 fp16 values of w times 8 fp32 values (za, zb), fp32 FMAs
+PI_DEV float dot8_f32(const uint4& w, const float4& za, const float4& zb) {
+    float a = lo_f(w.x) * za.x;
+    a = fmaf(hi_f(w.x), za.y, a);
+    a = fmaf(lo_f(w.y), za.z, a);
+    a = fmaf(hi_f(w.y), za.w, a);
+    a = fmaf(lo_f(w.z), zb.x, a);
+    a = fmaf(hi_f(w.z), zb.y, a);
+    a = fmaf(lo_f(w.w), zb.z, a);
+    return fmaf(hi_f(w.w), zb.w, a);
+}
+
 // 16-byte global load
 PI_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 PI_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// ---- wave-level ------------------------------------------------------------------------
+// ---- wave-level (DPP: cross-lane moves inside the VALU, no LDS round trip) ----------------------
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes whose source lane is
+// outside the row, or whose row is masked off, get `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+PI_DEV int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+PI_DEV float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+PI_DEV float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over the 64 lanes, returned (wave-uniform) to every lane.  Pairs, quads, half rows and
+// rows of 16 are summed with DPP quad_perm / row_half_mirror / row_mirror; the four row sums
+// are then read from lanes 0, 16, 32, 48.  Fixed order, so the result is deterministic.
 PI_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes (integers): row_shr 1, 2, 4, 8 inside each row of
+// 16, then row_bcast 15 / 31 carry row totals into the rows above.
+PI_DEV int wave_inclusive_scan(int v) {
+    v += dpp_i<0x111>(v);          // row_shr:1
+    v += dpp_i<0x112>(v);          // row_shr:2
+    v += dpp_i<0x114>(v);          // row_shr:4
+    v += dpp_i<0x118>(v);          // row_shr:8
+    v += dpp_i<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+    v += dpp_i<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -101,12 +144,7 @@ PI_DEV bool last_block_arrive(unsigned* counter, unsigned nblocks) {
 // s_tmp needs (blockDim.x / 64 + 1) ints.  Returns the exclusive prefix; *total gets the sum.
 PI_DEV int block_exclusive_scan(int v, int* s_tmp, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-    }
+    const int inc = wave_inclusive_scan(v);
     if (lane == 63) s_tmp[wave] = inc;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -184,4 +222,74 @@ PI_DEV void block_compact(const uint32_t* mask, int nrows, int stride, int F, in
         }
     }
     if (threadIdx.x == 0) *count = total;
+}
+
+// ---- predictor stage 2 on one 64-neuron tile (blocks of NW waves) ------------------------------
+// Wave w owns rows n0 + w*RPW .. n0 + w*RPW + RPW - 1 of W2t [F, r] (row n = neuron n's
+// predictor weights, contiguous), RPW = 64 / NW.  A row is read by all 64 lanes in segments
+// of 128 16-byte chunks (1024 predictor columns), so a segment's loads are all in flight.
+template <int NW>
+struct TileRows {
+    static constexpr int RPW = 64 / NW;
+    uint4 w[RPW][2];
+};
+
+template <int NW>
+PI_DEV void tile_rows_load(TileRows<NW>& tr, const uint16_t* __restrict__ W2t, int r, int F,
+                           int tile, int c0) {
+    constexpr int RPW = TileRows<NW>::RPW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nr = r >> 3;
+#pragma unroll
+    for (int m = 0; m < RPW; ++m) {
+        const int n = tile * 64 + wave * RPW + m;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = c0 + lane + 64 * q;
+            tr.w[m][q] = (n < F && c < nr) ? ld16(W2t + (size_t)n * r + 8 * c) : zero4();
+        }
+    }
+}
+
+// acc[m] += row m . z over the segment starting at chunk c0 (z in LDS, fp32)
+template <int NW>
+PI_DEV void tile_rows_fma(const TileRows<NW>& tr, const float* s_z, int r, int c0, float* acc) {
+    constexpr int RPW = TileRows<NW>::RPW;
+    const int lane = threadIdx.x & 63;
+    const int nr = r >> 3;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = c0 + lane + 64 * q;
+        if (c < nr) {
+            const float4 za = *reinterpret_cast<const float4*>(&s_z[8 * c]);
+            const float4 zb = *reinterpret_cast<const float4*>(&s_z[8 * c + 4]);
+#pragma unroll
+            for (int m = 0; m < RPW; ++m) acc[m] += dot8_f32(tr.w[m][q], za, zb);
+        }
+    }
+}
+
+// Finish a tile: reduce each wave's RPW row sums and store them to s_l[64].  Caller syncs.
+template <int NW>
+PI_DEV void tile_rows_store(const float* acc, float* s_l) {
+    constexpr int RPW = TileRows<NW>::RPW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < RPW; ++m) {
+        const float v = wave_sum(acc[m]);
+        if (lane == 0) s_l[wave * RPW + m] = v;
+    }
+}
+
+// s_l[k] = W2t[tile*64 + k, :] . z for k < 64 (before the bias); z in LDS.  Caller syncs after.
+template <int NW>
+PI_DEV void tile_logits(const uint16_t* __restrict__ W2t, const float* s_z, int r, int F, int tile,
+                        float* s_l) {
+    float acc[TileRows<NW>::RPW] = {};
+    for (int c0 = 0; c0 < (r >> 3); c0 += 128) {
+        TileRows<NW> tr;
+        tile_rows_load<NW>(tr, W2t, r, F, tile, c0);
+        tile_rows_fma<NW>(tr, s_z, r, c0, acc);
+    }
+    tile_rows_store<NW>(acc, s_l);
 }

@@ -22,12 +22,12 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- predictor launch plan ----------------------------------------------------------------------
 struct PredPlan {
-    int ncg;      // column groups of 64 predictor columns
-    int ku;       // rows per lane in stage 1 (a block covers 32 * ku rows)
-    int nchunk;   // stage-1 row chunks
-    int nb;       // tokens per pass
+    int qs;       // stage-1 16-byte chunks per lane per row segment
+    int nblk1;    // stage-1 blocks (4 rows each)
     int nblk2;    // stage-2 blocks (64 neurons each)
-    size_t off_z, off_part, bytes;
+    int nbz;      // tokens whose z is staged in LDS at a time (stage 2)
+    size_t lds2;  // stage-2 dynamic LDS
+    size_t off_z, bytes;
 };
 PredPlan plan_pred(int d, int r, int F, int B);
 
@@ -47,11 +47,11 @@ FfnPlan plan_ffn(int d, int F, int wfmt, int B);
 
 // ---- fused batch-1 decode step (three kernels) --------------------------------------------
 struct DecPlan {
-    int ncg, rows, rpl;        // stage-1 column groups, rows per chunk, rows per lane
+    PredPlan pred;             // stage 1 is the predictor's row GEMV (batch 1)
     int ntile, q;              // stage-2 tiles of 64 neurons, chunks per lane per row
     size_t lds_b;              // dynamic LDS of the stage-2 + up kernel
     int cols, nslices, nsplit, wps;   // down: columns per slice, slices, neuron-range splits, mask words per split
-    size_t off_zpart, off_h, off_part, bytes;
+    size_t off_z, off_h, off_part, bytes;
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
@@ -63,6 +63,9 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
 hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                           float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
                           char* ws, hipStream_t s);
+
+hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
+                              float* z, hipStream_t s);
 
 hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
                           int32_t* count, hipStream_t s);

@@ -8,10 +8,10 @@
 // On this GPU a kernel boundary costs ~2-3 us of timeline and a grid-wide
 // barrier costs as much, so the step is cut where a global dependency forces a
 // cut, and nowhere else:
-//   A  stage-1 partials  zp[p, :] = x[rows of chunk p] . W_p1[rows of chunk p, :]
-//      (P row chunks, no cross-block handoff).
-//   B  one block per 64-neuron tile: z = sum_p zp[p] (in chunk order, while the
-//      tile's W_p2 loads are already in flight), l = z . W_p2[:, tile] + b,
+//   A  predictor stage 1, z_j = W1t[j, :] . x (one wave per predictor column,
+//      the same kernel pi_predict uses).
+//   B  one block per 64-neuron tile: the tile's 64 contiguous W2t rows are
+//      already in flight while z is staged in LDS; l = W2t[tile] . z + b,
 //      active = l > theta, a wave ballot writes the tile's two mask words, and
 //      the block then computes h for ITS OWN active neurons (gate/up rows dotted
 //      with x staged in LDS).  No global neuron list is needed for that.
@@ -28,110 +28,40 @@
 namespace pi {
 namespace {
 
-constexpr int DEC_P = 8;          // stage-1 row chunks
 constexpr int DEC_IDCAP = 4096;   // neuron ids one down block can hold (128 mask words)
-
-// --------------------------------------------------------------------------------------- A
-// Block: 512 threads = 8 column lanes (64 columns) x 64 row lanes; grid (ceil(r/64), P).
-template <int RPL>
-__global__ __launch_bounds__(512) void k_dec_stage1(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ W1, int d, int r,
-                                                    int rows_per_chunk, float* __restrict__ zpart) {
-    __shared__ float s_red[8][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = tid & 7, rl = tid >> 3;
-    const int cg = blockIdx.x, chunk = blockIdx.y;
-    const int col0 = cg * 64 + sub * 8;
-    const bool colok = col0 < r;
-    const int k0 = chunk * rows_per_chunk;
-    const int k1 = min(d, k0 + rows_per_chunk);
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int kb = k0 + rl; kb < k1; kb += 64 * RPL) {
-        uint4 w[RPL];
-        float xv[RPL];
-#pragma unroll
-        for (int u = 0; u < RPL; ++u) {
-            const int k = kb + 64 * u;
-            const bool ok = k < k1;
-            w[u] = (ok && colok) ? ld16(W1 + (size_t)k * r + col0) : zero4();
-            xv[u] = ok ? h2f(x[k]) : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < RPL; ++u) {
-            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(xv[u], lo_f(ww[e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(xv[u], hi_f(ww[e]), acc[2 * e + 1]);
-            }
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float v = acc[e];
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[e] = v;
-    }
-    if (lane < 8)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_red[wave][lane * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < 64) {
-        const int col = cg * 64 + tid;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) v += s_red[w][tid];
-        if (col < r) zpart[(size_t)chunk * r + col] = v;
-    }
-}
 
 // --------------------------------------------------------------------------------------- B
 // WF: 0 = fp16 rows, 1 = int4 group-128 rows.  Q: 16-byte chunks per lane per row.
 // Dynamic LDS: z (r floats) then x (d/8 uint4; for int4 regrouped per 8 elements as
 // (x0,x4),(x1,x5),(x2,x6),(x3,x7) to match the nibble pairs one AND/OR extracts).
+constexpr int B_WAVES = 8;   // waves per tile block (two blocks fit on a CU)
+
 template <int WF, bool GLU, int Q>
-__global__ __launch_bounds__(1024) void k_dec_stage2_up(
-    const float* __restrict__ zpart, const uint16_t* __restrict__ W2,
+__global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
+    const float* __restrict__ z, const uint16_t* __restrict__ W2t,
     const float* __restrict__ bias, int r, int F, float theta, float* __restrict__ logits,
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h) {
+    constexpr int NT = B_WAVES * 64;
+    constexpr int IPW = Q <= 8 ? 2 : 1;        // row items per wave in flight
     extern __shared__ __align__(16) char smem[];
     float* s_z = reinterpret_cast<float*>(smem);
     uint4* s_x = reinterpret_cast<uint4*>(smem + align16i(r * 4));
-    __shared__ float s_red[16][64];
+    __shared__ float s_red[64];
     __shared__ float s_dot[2][64];
     __shared__ int s_list[64];
     __shared__ int s_n;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = tid & 7, rl = tid >> 3;   // rl: 0..127
     const int tile = blockIdx.x;
-    const int n0 = tile * 64 + sub * 8;
-    const bool nok = n0 < F;
     const int W = (F + 31) >> 5;
 
-    // --- logits of the tile: the first batch of W_p2 loads goes out before z is ready
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    uint4 w2[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int j = rl + 128 * u;
-        w2[u] = (nok && j < r) ? ld16(W2 + (size_t)j * F + n0) : zero4();
-    }
-    for (int j = tid; j < r; j += 1024) {
-        float s = 0.f;
-#pragma unroll
-        for (int p = 0; p < DEC_P; ++p) s += zpart[(size_t)p * r + j];
-        s_z[j] = s;
-    }
+    // --- logits of the tile: the first segment of its W2t rows goes out before z is staged
+    TileRows<B_WAVES> tr;
+    tile_rows_load<B_WAVES>(tr, W2t, r, F, tile, 0);
+    for (int j = tid; j < r; j += NT) s_z[j] = z[j];
     const int nc8 = d >> 3;
-    for (int c = tid; c < nc8; c += 1024) {
+    for (int c = tid; c < nc8; c += NT) {
         const uint4 a = ld16(x + 8 * c);
         if (WF == 0) {
             s_x[c] = a;
@@ -141,37 +71,13 @@ __global__ __launch_bounds__(1024) void k_dec_stage2_up(
         }
     }
     __syncthreads();
-    for (int jb = 0; jb < r; jb += 1024) {
-        if (jb > 0) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = jb + rl + 128 * u;
-                w2[u] = (nok && j < r) ? ld16(W2 + (size_t)j * F + n0) : zero4();
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = jb + rl + 128 * u;
-            const float zv = j < r ? s_z[j] : 0.f;
-            const uint32_t ww[4] = {w2[u].x, w2[u].y, w2[u].z, w2[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(zv, lo_f(ww[e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(zv, hi_f(ww[e]), acc[2 * e + 1]);
-            }
-        }
+    float acc[TileRows<B_WAVES>::RPW] = {};
+    tile_rows_fma<B_WAVES>(tr, s_z, r, 0, acc);
+    for (int c0 = 128; c0 < (r >> 3); c0 += 128) {
+        tile_rows_load<B_WAVES>(tr, W2t, r, F, tile, c0);
+        tile_rows_fma<B_WAVES>(tr, s_z, r, c0, acc);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float v = acc[e];
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[e] = v;
-    }
-    if (lane < 8)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_red[wave][lane * 8 + e] = acc[e];
+    tile_rows_store<B_WAVES>(acc, s_red);
     __syncthreads();
 
     // --- threshold, mask words, the tile's active list (wave 0: lane = neuron of the tile)
@@ -179,10 +85,7 @@ __global__ __launch_bounds__(1024) void k_dec_stage2_up(
         const int n = tile * 64 + lane;
         bool act = false;
         if (n < F) {
-            float l = 0.f;
-#pragma unroll
-            for (int w = 0; w < 16; ++w) l += s_red[w][lane];
-            l += bias[n];
+            const float l = s_red[lane] + bias[n];
             act = l > theta;
             if (logits) logits[n] = l;
         }
@@ -197,48 +100,60 @@ __global__ __launch_bounds__(1024) void k_dec_stage2_up(
     }
     __syncthreads();
 
-    // --- rows of the active neurons: one wave per (neuron, matrix) item
+    // --- rows of the active neurons: (neuron, matrix) items, IPW per wave in flight
     const int na = s_n;
     constexpr int M = GLU ? 2 : 1;
+    const int items = na * M;
     const int nc = WF == 0 ? (d >> 3) : (d >> 5);   // 16-byte chunks per row
     const int G = d >> 7;
     const size_t rb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
-    for (int it = wave; it < na * M; it += 16) {
-        const int k = GLU ? (it >> 1) : it;
-        const int mat = GLU ? (it & 1) : 1;           // 0 = gate, 1 = up
-        const size_t row = (size_t)(tile * 64 + s_list[k]);
-        const uint8_t* base = static_cast<const uint8_t*>(mat ? Wu : Wg) + row * rb;
-        uint4 wr[Q];
-        float sc[Q];
+    for (int it0 = wave * IPW; it0 < items; it0 += B_WAVES * IPW) {
+        uint4 wr[IPW][Q];
+        float sc[IPW][Q];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int c = lane + 64 * q;
-            wr[q] = c < nc ? ld16(base + 16 * (size_t)c) : zero4();
-            if (WF == 1) sc[q] = c < nc ? h2f((mat ? Su : Sg)[row * G + (c >> 2)]) : 0.f;
-        }
-        float dot = 0.f;
+        for (int i = 0; i < IPW; ++i) {
+            const int it = it0 + i;
+            const bool valid = it < items;
+            const int k = GLU ? (it >> 1) : it;
+            const int mat = GLU ? (it & 1) : 1;        // 0 = gate, 1 = up
+            const size_t row = valid ? (size_t)(tile * 64 + s_list[k]) : 0;
+            const uint8_t* base = static_cast<const uint8_t*>(mat ? Wu : Wg) + row * rb;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int c = lane + 64 * q;
-            if (c < nc) {
-                if (WF == 0) {
-                    dot = dot8(wr[q], s_x[c], dot);
-                } else {
-                    uint32_t xp[16];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint4 t = s_x[4 * c + m];
-                        xp[4 * m] = t.x; xp[4 * m + 1] = t.y; xp[4 * m + 2] = t.z; xp[4 * m + 3] = t.w;
-                    }
-                    dot = fmaf(dot32_i4(wr[q], xp), sc[q], dot);
-                }
+            for (int q = 0; q < Q; ++q) {
+                const int c = lane + 64 * q;
+                const bool ok = valid && c < nc;
+                wr[i][q] = ok ? ld16(base + 16 * (size_t)c) : zero4();
+                if (WF == 1) sc[i][q] = ok ? h2f((mat ? Su : Sg)[row * G + (c >> 2)]) : 0.f;
             }
         }
-        dot = wave_sum(dot);
-        if (lane == 0) s_dot[mat][k] = dot;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int it = it0 + i;
+            if (it >= items) break;
+            float dot = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int c = lane + 64 * q;
+                if (c < nc) {
+                    if (WF == 0) {
+                        dot = dot8(wr[i][q], s_x[c], dot);
+                    } else {
+                        uint32_t xp[16];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const uint4 t = s_x[4 * c + m];
+                            xp[4 * m] = t.x; xp[4 * m + 1] = t.y; xp[4 * m + 2] = t.z; xp[4 * m + 3] = t.w;
+                        }
+                        dot = fmaf(dot32_i4(wr[i][q], xp), sc[i][q], dot);
+                    }
+                }
+            }
+            dot = wave_sum(dot);
+            if (lane == 0) s_dot[GLU ? (it & 1) : 1][GLU ? (it >> 1) : it] = dot;
+        }
     }
     __syncthreads();
-    for (int k = tid; k < na; k += 1024) {
+    for (int k = tid; k < na; k += NT) {
         const float a = s_dot[1][k];
         h[tile * 64 + s_list[k]] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
     }
@@ -465,37 +380,25 @@ __global__ __launch_bounds__(512) void k_dec_down_i4(
 }
 
 // --------------------------------------------------------------------------------------- dispatch
-hipError_t launch_stage1(int rpl, dim3 g, const uint16_t* x, const uint16_t* W1, int d, int r,
-                         int rows, float* zpart, hipStream_t s) {
-    switch (rpl) {
-        case 1: hipLaunchKernelGGL((k_dec_stage1<1>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
-        case 2: hipLaunchKernelGGL((k_dec_stage1<2>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
-        case 4: hipLaunchKernelGGL((k_dec_stage1<4>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
-        case 8: hipLaunchKernelGGL((k_dec_stage1<8>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
-        default: hipLaunchKernelGGL((k_dec_stage1<16>), g, dim3(512), 0, s, x, W1, d, r, rows, zpart); break;
-    }
-    return hipGetLastError();
-}
-
 template <int WF, bool GLU, int Q>
-void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* zpart,
+void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
               const uint16_t* x, const pi_ffn_desc& f, float* h) {
     if (e0)
-        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(1024), (uint32_t)lds, s, e0, e1, 0,
-                              zpart, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
+        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(B_WAVES * 64), (uint32_t)lds, s, e0, e1, 0,
+                              z, p.w_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
                               f.s_gate, f.w_up, f.s_up, f.d, h);
     else
-        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(1024), lds, s, zpart, p.w_p2,
+        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
                            p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
                            f.s_up, f.d, h);
 }
 
 template <int WF, bool GLU>
 hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
-                      const float* zpart, const pi_pred_desc& p, float theta, float* logits,
+                      const float* z, const pi_pred_desc& p, float theta, float* logits,
                       uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h) {
-#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ>(g, lds, s, e0, e1, zpart, p, theta, logits, mask, x, f, h); break;
+#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h); break;
     if constexpr (WF == 0) {
         switch (q) {
             PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
@@ -516,10 +419,7 @@ hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, h
 
 DecPlan plan_decode(int d, int r, int F, int wfmt) {
     DecPlan p{};
-    p.ncg = (r + 63) / 64;
-    p.rows = (d + DEC_P - 1) / DEC_P;
-    const int rpl_need = (p.rows + 63) / 64;
-    p.rpl = rpl_need <= 1 ? 1 : rpl_need <= 2 ? 2 : rpl_need <= 4 ? 4 : rpl_need <= 8 ? 8 : 16;
+    p.pred = plan_pred(d, r, F, 1);
     p.ntile = (F + 63) / 64;
     const bool f16 = wfmt == PI_W_F16;
     p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
@@ -527,17 +427,19 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     p.cols = f16 ? 512 : 2048;
     p.nslices = (d + p.cols - 1) / p.cols;
     const int W = (F + 31) / 32;
-    const int wpb = f16 ? 16 : 8;
-    int ns = 2048 / (p.nslices * wpb);
+    // about 128 down blocks: enough waves to keep each one's rows (U = 8) in flight, few
+    // enough partials for the last block of a slice to sum them in one batch of loads
+    int ns = (128 + p.nslices - 1) / p.nslices;
     const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
-    if (ns > 32) ns = 32;
+    if (ns > 64) ns = 64;
+    if (ns > W) ns = W;
     if (ns < ns_min) ns = ns_min;
     if (ns < 1) ns = 1;
     p.wps = (W + ns - 1) / ns;
     p.nsplit = (W + p.wps - 1) / p.wps;
     size_t off = COUNTER_BYTES;
-    p.off_zpart = off;
-    off = align_up(off + (size_t)DEC_P * r * sizeof(float), 256);
+    p.off_z = off;
+    off = align_up(off + (size_t)r * sizeof(float), 256);
     p.off_h = off;
     off = align_up(off + (size_t)F * sizeof(float), 256);
     p.off_part = off;
@@ -550,28 +452,28 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
                               int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s,
                               hipEvent_t e0, hipEvent_t e1) {
-    float* zpart = reinterpret_cast<float*>(ws + pl.off_zpart);
+    float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DECODE;
-    hipError_t e = launch_stage1(pl.rpl, dim3(pl.ncg, DEC_P), x, p.w_p1, p.d, p.r, pl.rows, zpart, s);
+    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s);
     if (e != hipSuccess) return e;
     const bool glu = f.act == PI_ACT_REGLU;
     const dim3 gb(pl.ntile);
     if (f.wfmt == PI_W_F16)
-        e = glu ? dispatch_b<0, true>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h)
-                : dispatch_b<0, false>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h);
+        e = glu ? dispatch_b<0, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
+                : dispatch_b<0, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
     else
-        e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h)
-                : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, zpart, p, theta, logits, mask, x, f, h);
+        e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
+                : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
     if (e != hipSuccess) return e;
     const dim3 gc(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16)
-        hipLaunchKernelGGL((k_dec_down_f16<4>), gc, dim3(1024), 0, s, mask, f.F, h,
+        hipLaunchKernelGGL((k_dec_down_f16<8>), gc, dim3(1024), 0, s, mask, f.F, h,
                            static_cast<const uint16_t*>(f.w_down), f.d, pl.wps, part, y, cnt, idx,
                            count);
     else
-        hipLaunchKernelGGL((k_dec_down_i4<4>), gc, dim3(512), 0, s, mask, f.F, h,
+        hipLaunchKernelGGL((k_dec_down_i4<8>), gc, dim3(512), 0, s, mask, f.F, h,
                            static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, pl.wps, part, y,
                            cnt, idx, count);
     return hipGetLastError();

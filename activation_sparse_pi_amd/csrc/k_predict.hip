@@ -1,246 +1,152 @@
 // Low-rank activation predictor + threshold + neuron-table compaction (gfx950).
 //
 // PowerInfer, "Adaptive Sparsity Predictors": each layer's predictor marks the
-// neurons a token will fire, so the FFN touches only those.  The predictor
-// here is the pair l = (x W_p1) W_p2 + b; a neuron is active when l > theta
-// (theta = logit of the probability threshold).  "Neuron Placement and
-// Management": the active neurons' original positions are written as an
-// ascending int32 list.
+// neurons a token will fire, so the FFN touches only those.  The predictor is
+// the pair l = (x W_p1) W_p2 + b; a neuron is active when l > theta (theta =
+// logit of the probability threshold).  "Neuron Placement and Management": the
+// active neurons' original positions are written as an ascending int32 list.
 //
-// Both stages are memory-bound GEMVs (B small), so they are tiled for
-// coalesced 16-byte loads with fp32 accumulation, not for MFMA:
-//   stage 1  z[b, :] = x[b, :] W_p1     W_p1 [d, r] row-major.  Block = 64
-//            columns x (32*KU) rows; the row chunks are split-K partials that
-//            the last-arriving block of each column group sums in a fixed
-//            order (deterministic).
-//   stage 2  l[b, :] = z[b, :] W_p2 + b  W_p2 [r, F] row-major.  Block = 64
-//            neurons x all r rows; one wave ballot turns 64 decisions into two
-//            mask words; the last-arriving block compacts the whole mask.
+// Both factors are stored neuron-major / row-contiguous on the device:
+//   W1t [r, d]  row j = column j of W_p1   ->  z_j = W1t[j, :] . x
+//   W2t [F, r]  row i = column i of W_p2   ->  l_i = W2t[i, :] . z + b_i
+// so both stages are row GEMVs over contiguous rows (DRAM-friendly 16-byte
+// coalesced loads, no split-K partial sums, no cross-block hand-off), fp32
+// accumulation throughout.
+//   stage 1  one wave per row j; x slice in registers; 64-lane reduction.
+//   stage 2  one block per 64-neuron tile, 8 waves x 8 rows; z staged in LDS;
+//            one wave ballot turns the tile's 64 decisions into two mask words;
+//            the last-arriving block compacts the mask into the ascending table.
 #include "device_common.h"
 #include "internal.h"
 
 namespace pi {
 namespace {
 
-template <int NB, int KU>
-__global__ __launch_bounds__(256) void k_pred_stage1(const uint16_t* __restrict__ x, int B,
-                                                     const uint16_t* __restrict__ W1, int d, int r,
-                                                     float* __restrict__ part,
-                                                     float* __restrict__ z,
-                                                     unsigned* __restrict__ counters) {
-    __shared__ float s_red[4][NB][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = tid & 7;   // which 8-column piece of the group this lane loads
-    const int rl = tid >> 3;   // row lane 0..31
-    const int cg = blockIdx.x, chunk = blockIdx.y, nchunk = gridDim.y;
-    const int col0 = cg * 64 + sub * 8;
-    const bool colok = col0 < r;
-    const int kbase = chunk * 32 * KU;
-
-    uint4 w[KU];
+// ------------------------------------------------------------------------------------ stage 1
+// z[b, j] = W1t[j, :] . x[b, :].  Block: 4 waves = 4 rows.  The row is read in segments of
+// QS 16-byte chunks per lane (all loads of a segment in flight together).
+template <int QS>
+__global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
+                                            const uint16_t* __restrict__ W1t, int d, int r,
+                                            float* __restrict__ z) {
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= r) return;
+    const int nc = d >> 3;
+    const uint16_t* row = W1t + (size_t)j * d;
+    if (B == 1 && nc <= 64 * QS) {
+        // one segment: row and x chunks all in flight together
+        uint4 w[QS], xr[QS];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-        const int k = kbase + rl + 32 * u;
-        w[u] = (colok && k < d) ? ld16(W1 + (size_t)k * r + col0) : zero4();
+        for (int q = 0; q < QS; ++q) {
+            const int c = lane + 64 * q;
+            w[q] = c < nc ? ld16(row + 8 * c) : zero4();
+            xr[q] = c < nc ? ld16(x + 8 * c) : zero4();
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < QS; ++q) acc = dot8(w[q], xr[q], acc);
+        acc = wave_sum(acc);
+        if (lane == 0) z[j] = acc;
+        return;
     }
-
-    for (int b0 = 0; b0 < B; b0 += NB) {
-        float acc[NB][8];
+    for (int b = 0; b < B; ++b) {
+        float acc = 0.f;
+        for (int c0 = 0; c0 < nc; c0 += 64 * QS) {
+            uint4 w[QS], xr[QS];
 #pragma unroll
-        for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int k = kbase + rl + 32 * u;
-            if (k < d) {
-                const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-                for (int t = 0; t < NB; ++t) {
-                    const float xv = (b0 + t < B) ? h2f(x[(size_t)(b0 + t) * d + k]) : 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[t][2 * e] = fmaf(xv, lo_f(ww[e]), acc[t][2 * e]);
-                        acc[t][2 * e + 1] = fmaf(xv, hi_f(ww[e]), acc[t][2 * e + 1]);
-                    }
-                }
+            for (int q = 0; q < QS; ++q) {
+                const int c = c0 + lane + 64 * q;
+                w[q] = c < nc ? ld16(row + 8 * c) : zero4();
+                xr[q] = c < nc ? ld16(x + (size_t)b * d + 8 * c) : zero4();
             }
+#pragma unroll
+            for (int q = 0; q < QS; ++q) acc = dot8(w[q], xr[q], acc);
         }
-        // reduce over the 8 row lanes of this wave that share the columns (lane bits 3..5)
-#pragma unroll
-        for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = acc[t][e];
-                v += __shfl_xor(v, 8);
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                acc[t][e] = v;
-            }
-        if (lane < 8) {
-#pragma unroll
-            for (int t = 0; t < NB; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s_red[wave][t][lane * 8 + e] = acc[t][e];
-        }
-        __syncthreads();
-        for (int i = tid; i < NB * 64; i += 256) {
-            const int t = i >> 6, c = i & 63, col = cg * 64 + c;
-            if (b0 + t < B && col < r) {
-                const float v = ((s_red[0][t][c] + s_red[1][t][c]) + s_red[2][t][c]) + s_red[3][t][c];
-                st_agent(&part[((size_t)chunk * B + b0 + t) * r + col], v);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (last_block_arrive(&counters[cg], (unsigned)nchunk)) {
-        // z = sum over row chunks, in chunk order split into 4 interleaved runs, then combined
-        const int c = tid & 63, qtr = tid >> 6, col = cg * 64 + c;
-        for (int b = 0; b < B; ++b) {
-            float s = 0.f;
-            if (col < r) {
-                // 16 partials in flight per thread, summed in chunk order
-                for (int base = qtr; base < nchunk; base += 64) {
-                    float v[16];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int ch = base + 4 * j;
-                        v[j] = ch < nchunk ? ld_agent(&part[((size_t)ch * B + b) * r + col]) : 0.f;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s += v[j];
-                }
-            }
-            s_red[qtr][0][c] = s;
-            __syncthreads();
-            if (qtr == 0 && col < r)
-                z[(size_t)b * r + col] =
-                    ((s_red[0][0][c] + s_red[1][0][c]) + s_red[2][0][c]) + s_red[3][0][c];
-            __syncthreads();
-        }
+        acc = wave_sum(acc);
+        if (lane == 0) z[(size_t)b * r + j] = acc;
     }
 }
 
-template <int NB, int JU>
-__global__ __launch_bounds__(256) void k_pred_stage2(const float* __restrict__ z, int B,
-                                                     const uint16_t* __restrict__ W2,
-                                                     const float* __restrict__ bias, int r, int F,
-                                                     float theta, float* __restrict__ logits,
-                                                     uint32_t* __restrict__ mask,
-                                                     int32_t* __restrict__ idx,
-                                                     int32_t* __restrict__ count,
-                                                     unsigned* __restrict__ counter) {
-    __shared__ float s_red[4][NB][64];
-    __shared__ int s_tmp[8];
+// ------------------------------------------------------------------------------------ stage 2
+// l[b, n] = W2t[n, :] . z[b, :] + bias[n] for the 64 neurons of tile blockIdx.x.
+// 512 threads: wave w owns rows n0 + 8w .. n0 + 8w + 7 (tile_logits); z of nbz tokens
+// at a time sits in dynamic LDS.
+constexpr int P2_WAVES = 8;
+
+__global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ z, int B,
+                                             const uint16_t* __restrict__ W2t,
+                                             const float* __restrict__ bias, int r, int F,
+                                             float theta, int nbz, float* __restrict__ logits,
+                                             uint32_t* __restrict__ mask,
+                                             int32_t* __restrict__ idx,
+                                             int32_t* __restrict__ count,
+                                             unsigned* __restrict__ counter) {
+    extern __shared__ __align__(16) float s_z[];   // [nbz][r]
+    __shared__ float s_l[64];
+    __shared__ int s_tmp[P2_WAVES + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = tid & 7, rl = tid >> 3;
-    const int n0 = blockIdx.x * 64 + sub * 8;
-    const bool nok = n0 < F;
+    const int tile = blockIdx.x;
     const int W = (F + 31) >> 5;
-
-    for (int b0 = 0; b0 < B; b0 += NB) {
-        float acc[NB][8];
-#pragma unroll
-        for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-        for (int j0 = 0; j0 < r; j0 += 32 * JU) {
-            uint4 w[JU];
-            float zv[JU][NB];
-#pragma unroll
-            for (int u = 0; u < JU; ++u) {
-                const int j = j0 + rl + 32 * u;
-                w[u] = (nok && j < r) ? ld16(W2 + (size_t)j * F + n0) : zero4();
-#pragma unroll
-                for (int t = 0; t < NB; ++t)
-                    zv[u][t] = (j < r && b0 + t < B) ? z[(size_t)(b0 + t) * r + j] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < JU; ++u) {
-                const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-                for (int t = 0; t < NB; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[t][2 * e] = fmaf(zv[u][t], lo_f(ww[e]), acc[t][2 * e]);
-                        acc[t][2 * e + 1] = fmaf(zv[u][t], hi_f(ww[e]), acc[t][2 * e + 1]);
-                    }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = acc[t][e];
-                v += __shfl_xor(v, 8);
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                acc[t][e] = v;
-            }
-        if (lane < 8) {
-#pragma unroll
-            for (int t = 0; t < NB; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s_red[wave][t][lane * 8 + e] = acc[t][e];
-        }
+    for (int b0 = 0; b0 < B; b0 += nbz) {
+        const int nb = min(nbz, B - b0);
+        for (int i = tid; i < nb * r; i += P2_WAVES * 64) s_z[i] = z[(size_t)b0 * r + i];
         __syncthreads();
-        // wave t handles token b0 + t: lane = neuron within the 64-neuron tile
-        for (int i = tid; i < NB * 64; i += 256) {
-            const int t = i >> 6, nn = i & 63, neuron = blockIdx.x * 64 + nn;
-            const int b = b0 + t;
-            bool act = false;
-            if (neuron < F && b < B) {
-                const float l =
-                    (((s_red[0][t][nn] + s_red[1][t][nn]) + s_red[2][t][nn]) + s_red[3][t][nn]) +
-                    bias[neuron];
-                act = l > theta;
-                if (logits) logits[(size_t)b * F + neuron] = l;
+        for (int t = 0; t < nb; ++t) {
+            tile_logits<P2_WAVES>(W2t, s_z + t * r, r, F, tile, s_l);
+            __syncthreads();
+            if (wave == 0) {
+                const int n = tile * 64 + lane;
+                const int b = b0 + t;
+                bool act = false;
+                if (n < F) {
+                    const float l = s_l[lane] + bias[n];
+                    act = l > theta;
+                    if (logits) logits[(size_t)b * F + n] = l;
+                }
+                const unsigned long long bal = __ballot(act);
+                if (lane == 0) {
+                    st_agent(&mask[(size_t)b * W + 2 * tile], (uint32_t)bal);
+                    if (2 * tile + 1 < W) st_agent(&mask[(size_t)b * W + 2 * tile + 1], (uint32_t)(bal >> 32));
+                }
             }
-            const unsigned long long bal = __ballot(act);
-            if (nn == 0 && b < B) {
-                const int wd = blockIdx.x * 2;
-                st_agent(&mask[(size_t)b * W + wd], (uint32_t)bal);
-                if (wd + 1 < W) st_agent(&mask[(size_t)b * W + wd + 1], (uint32_t)(bal >> 32));
-            }
+            __syncthreads();
         }
-        __syncthreads();
     }
-
     if (idx != nullptr && last_block_arrive(counter, gridDim.x)) {
         for (int b = 0; b < B; ++b)
             block_compact<true>(mask + (size_t)b * W, 1, W, F, idx + (size_t)b * F, count + b, s_tmp);
     }
 }
 
-template <int NB>
-hipError_t launch_stage1_ku(int ku, dim3 g, const uint16_t* x, int B, const uint16_t* W1, int d,
-                            int r, float* part, float* z, unsigned* cnt, hipStream_t s) {
-    switch (ku) {
-        case 1: hipLaunchKernelGGL((k_pred_stage1<NB, 1>), g, dim3(256), 0, s, x, B, W1, d, r, part, z, cnt); break;
-        case 2: hipLaunchKernelGGL((k_pred_stage1<NB, 2>), g, dim3(256), 0, s, x, B, W1, d, r, part, z, cnt); break;
-        case 4: hipLaunchKernelGGL((k_pred_stage1<NB, 4>), g, dim3(256), 0, s, x, B, W1, d, r, part, z, cnt); break;
-        default: hipLaunchKernelGGL((k_pred_stage1<NB, 8>), g, dim3(256), 0, s, x, B, W1, d, r, part, z, cnt); break;
+}  // namespace
+
+hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
+                              float* z, hipStream_t s) {
+#define PI_P1(QQ) case QQ: hipLaunchKernelGGL((k_p1<QQ>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z); break;
+    switch (pl.qs) {
+        PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)
+        PI_P1(9) PI_P1(10) PI_P1(11) PI_P1(12) PI_P1(13) PI_P1(14) PI_P1(15) PI_P1(16)
+        default: return hipErrorInvalidValue;
     }
+#undef PI_P1
     return hipGetLastError();
 }
 
-}  // namespace
-
 PredPlan plan_pred(int d, int r, int F, int B) {
     PredPlan p{};
-    p.ncg = (r + 63) / 64;
-    // at most 64 row chunks, so the last block of a column group sums 16 partials per thread
-    p.ku = 1;
-    while (p.ku < 8 && (d + 32 * p.ku - 1) / (32 * p.ku) > 64) p.ku *= 2;
-    p.nchunk = (d + 32 * p.ku - 1) / (32 * p.ku);
-    p.nb = B >= 8 ? 8 : (B >= 4 ? 4 : (B >= 2 ? 2 : 1));
+    const int q = (d / 8 + 63) / 64;
+    p.qs = q < 1 ? 1 : (q > 16 ? 16 : q);
+    p.nblk1 = (r + 3) / 4;
     p.nblk2 = (F + 63) / 64;
+    int nbz = (32 * 1024) / (r * 4);        // z of nbz tokens in at most 32 KB of LDS
+    if (nbz < 1) nbz = 1;
+    if (nbz > B) nbz = B;
+    p.nbz = nbz;
+    p.lds2 = (size_t)nbz * r * sizeof(float);
     size_t off = COUNTER_BYTES;
     p.off_z = off;
     off = align_up(off + (size_t)B * r * sizeof(float), 256);
-    p.off_part = off;
-    off = align_up(off + (size_t)p.nchunk * B * r * sizeof(float), 256);
     p.bytes = off;
     return p;
 }
@@ -250,23 +156,10 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
                           char* ws, hipStream_t s) {
     unsigned* cnt = reinterpret_cast<unsigned*>(ws);
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
-    float* part = reinterpret_cast<float*>(ws + pl.off_part);
-    const dim3 g1(pl.ncg, pl.nchunk);
-    hipError_t e;
-    switch (pl.nb) {
-        case 1: e = launch_stage1_ku<1>(pl.ku, g1, x, B, p.w_p1, p.d, p.r, part, z, cnt + CNT_PRED1, s); break;
-        case 2: e = launch_stage1_ku<2>(pl.ku, g1, x, B, p.w_p1, p.d, p.r, part, z, cnt + CNT_PRED1, s); break;
-        case 4: e = launch_stage1_ku<4>(pl.ku, g1, x, B, p.w_p1, p.d, p.r, part, z, cnt + CNT_PRED1, s); break;
-        default: e = launch_stage1_ku<8>(pl.ku, g1, x, B, p.w_p1, p.d, p.r, part, z, cnt + CNT_PRED1, s); break;
-    }
+    hipError_t e = launch_pred_stage1(p, pl, x, B, z, s);
     if (e != hipSuccess) return e;
-    const dim3 g2(pl.nblk2);
-    switch (pl.nb) {
-        case 1: hipLaunchKernelGGL((k_pred_stage2<1, 8>), g2, dim3(256), 0, s, z, B, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, idx, count, cnt + CNT_PRED2); break;
-        case 2: hipLaunchKernelGGL((k_pred_stage2<2, 8>), g2, dim3(256), 0, s, z, B, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, idx, count, cnt + CNT_PRED2); break;
-        case 4: hipLaunchKernelGGL((k_pred_stage2<4, 4>), g2, dim3(256), 0, s, z, B, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, idx, count, cnt + CNT_PRED2); break;
-        default: hipLaunchKernelGGL((k_pred_stage2<8, 4>), g2, dim3(256), 0, s, z, B, p.w_p2, p.bias, p.r, p.F, theta, logits, mask, idx, count, cnt + CNT_PRED2); break;
-    }
+    hipLaunchKernelGGL(k_p2, dim3(pl.nblk2), dim3(P2_WAVES * 64), pl.lds2, s, z, B, p.w_p2t, p.bias, p.r,
+                       p.F, theta, pl.nbz, logits, mask, idx, count, cnt + CNT_PRED2);
     return hipGetLastError();
 }
 

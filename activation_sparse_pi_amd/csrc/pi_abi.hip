@@ -37,13 +37,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_pred(const pi_pred_desc* p) {
     if (!p) return fail(PI_ERR_NULL, "pred descriptor is NULL");
-    if (!p->w_p1 || !p->w_p2 || !p->bias) return fail(PI_ERR_NULL, "pred weights/bias NULL");
+    if (!p->w_p1t || !p->w_p2t || !p->bias) return fail(PI_ERR_NULL, "pred weights/bias NULL");
     if (p->d <= 0 || p->r <= 0 || p->F <= 0)
         return fail(PI_ERR_SHAPE, "pred sizes must be positive (d=%d r=%d F=%d)", p->d, p->r, p->F);
     if (p->d % 8 || p->r % 8 || p->F % 8)
         return fail(PI_ERR_SHAPE, "pred sizes need d, r, F %% 8 == 0 (d=%d r=%d F=%d)", p->d, p->r, p->F);
     if (p->r > 16384) return fail(PI_ERR_UNSUPPORTED, "predictor rank %d > 16384", p->r);
-    if (!aligned16(p->w_p1) || !aligned16(p->w_p2))
+    if (!aligned16(p->w_p1t) || !aligned16(p->w_p2t))
         return fail(PI_ERR_ALIGN, "predictor weights must be 16-byte aligned");
     if (!(p->threshold > 0.f && p->threshold < 1.f))
         return fail(PI_ERR_SHAPE, "threshold must be a probability in (0,1), got %g", (double)p->threshold);

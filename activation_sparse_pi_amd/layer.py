@@ -30,7 +30,11 @@ class DeviceLayer:
         mats = ("gate", "up", "down") if cfg.act == "reglu" else ("up", "down")
         for m in mats:
             names += ["w_" + m] if cfg.wfmt == "f16" else ["q_" + m, "s_" + m]
-        base = {k: _dev(inputs[k], self.device) for k in names}
+        host = {k: inputs[k] for k in names}
+        # predictor factors go to the device transposed: one contiguous row per output
+        host["w_p1"] = np.ascontiguousarray(inputs["w_p1"].T)    # [r, d]
+        host["w_p2"] = np.ascontiguousarray(inputs["w_p2"].T)    # [F, r]
+        base = {k: _dev(v, self.device) for k, v in host.items()}
         self.tensors = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
         self.pred, self.ffn = [], []
         for t in self.tensors:

@@ -65,13 +65,17 @@ extern "C" {
 
 /* ---- descriptors -------------------------------------------------------------------- */
 
-/* Low-rank activation predictor of one layer: l = (x W_p1) W_p2 + bias.
- * Neuron i is predicted active iff sigmoid(l_i) > threshold, evaluated as
- * l_i > ln(threshold / (1 - threshold)) in fp32 (strict; 0 for threshold 0.5).
- * z = x W_p1 is accumulated and kept in fp32 (never rounded to fp16).        */
+/* Low-rank activation predictor of one layer: l = (x W_p1) W_p2 + bias, with
+ * W_p1 [d, r] and W_p2 [r, F].  Both factors are passed TRANSPOSED, so that every
+ * predictor output is one contiguous row: w_p1t[j, :] is column j of W_p1 and
+ * w_p2t[i, :] is column i of W_p2 -- neuron i's predictor weights, neuron-major like
+ * the FFN matrices.  Neuron i is predicted active iff sigmoid(l_i) > threshold,
+ * evaluated as l_i > ln(threshold / (1 - threshold)) in fp32 (strict; 0 for
+ * threshold 0.5).  z = x W_p1 is accumulated and kept in fp32 (never rounded to
+ * fp16).                                                                       */
 typedef struct pi_pred_desc {
-    const uint16_t* w_p1;   /* fp16 [d, r] row-major                      */
-    const uint16_t* w_p2;   /* fp16 [r, F] row-major                      */
+    const uint16_t* w_p1t;  /* fp16 [r, d] row-major (= W_p1 transposed)  */
+    const uint16_t* w_p2t;  /* fp16 [F, r] row-major (= W_p2 transposed)  */
     const float*    bias;   /* fp32 [F]                                   */
     int32_t d;              /* model width, d % 8 == 0                    */
     int32_t r;              /* predictor rank, r % 8 == 0                 */
@@ -173,7 +177,7 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  * (s0 + i) % nrep (preds[nrep], ffns[nrep]: layers of one shape, e.g. the layers
  * of a model or byte-identical copies).  A step is the same computation as
  * pi_predict + pi_sparse_ffn, fused into three kernels:
- *   1. predictor stage-1 partial sums of z = x W_p1 over 8 row chunks;
+ *   1. predictor stage 1, z = x W_p1 (one wave per predictor column);
  *   2. per 64-neuron tile: z, logits, strict threshold, mask words, and h of the
  *      tile's own predicted-active neurons (their up/gate rows);
  *   3. the down projection read straight from the mask, which also writes the
