@@ -50,7 +50,7 @@ struct DecPlan {
     PredPlan pred;             // stage 1 is the predictor's row GEMV (batch 1)
     int ntile, q;              // stage-2 tiles of 64 neurons, chunks per lane per row
     size_t lds_b;              // dynamic LDS of the stage-2 + up kernel
-    int cols, nslices, nsplit, wps;   // down: columns per slice, slices, neuron-range splits, mask words per split
+    int nslices, nsplit, wps;  // down: column slices, neuron-range splits, mask words per split
     size_t off_z, off_h, off_part, bytes;
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);

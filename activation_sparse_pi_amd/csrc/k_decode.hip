@@ -160,6 +160,23 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
 }
 
 // --------------------------------------------------------------------------------------- C
+// Down projection straight from the mask, 2-D tiled.  Block (slice, split) owns a column
+// slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte loads, or 1024 int4
+// columns with 8-byte loads) and the neuron ids of a range of mask words.  It compacts
+// its range in LDS, its 16 waves take interleaved active neurons (U rows in flight per
+// wave; each row's h and scale are wave-uniform scalar loads), the waves' sums meet in
+// LDS, and the block's partial row goes out with agent-coherent stores; the last block
+// to arrive on a slice adds the splits' partials in split order (deterministic).  The
+// slice-0 blocks also write the global ascending neuron table for their range.
+constexpr int DN_NW = 16;
+
+template <int WF>
+struct DnGeom {
+    static constexpr int LB = WF == 0 ? 16 : 8;      // bytes per lane load
+    static constexpr int V = WF == 0 ? 8 : 16;       // columns per lane
+    static constexpr int SC = 64 * V;                // columns per slice
+};
+
 // Block-local compaction of mask words [w0, w1) into s_ids (ascending); returns the count.
 PI_DEV int range_compact(const uint32_t* __restrict__ mask, int w0, int w1, int F, int* s_ids,
                          int* s_tmp) {
@@ -189,8 +206,7 @@ PI_DEV void write_table(const uint32_t* __restrict__ mask, int w0, int n_loc, bo
     __syncthreads();
     int c = 0;
     for (int w = threadIdx.x; w < w0; w += blockDim.x) c += __popc(mask[w]);
-    c += __shfl_xor(c, 1); c += __shfl_xor(c, 2); c += __shfl_xor(c, 4);
-    c += __shfl_xor(c, 8); c += __shfl_xor(c, 16); c += __shfl_xor(c, 32);
+    c = (int)wave_sum((float)c);   // exact: counts stay far below 2^24
     if ((threadIdx.x & 63) == 0 && c) atomicAdd(s_acc, c);
     __syncthreads();
     const int P = *s_acc;
@@ -198,17 +214,17 @@ PI_DEV void write_table(const uint32_t* __restrict__ mask, int w0, int n_loc, bo
     if (last_split && threadIdx.x == 0) *count = P + n_loc;
 }
 
-template <int U>
-__global__ __launch_bounds__(1024) void k_dec_down_f16(
+template <int WF, int U>
+__global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
-    const uint16_t* __restrict__ Wd, int d, int wps, float* __restrict__ part,
-    float* __restrict__ y, unsigned* __restrict__ counters, int32_t* __restrict__ idx,
-    int32_t* __restrict__ count) {
-    constexpr int NW = 16;
+    const void* __restrict__ Wd, const uint16_t* __restrict__ Sd, int d, int wps,
+    float* __restrict__ part, float* __restrict__ y, unsigned* __restrict__ counters,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    using Gm = DnGeom<WF>;
     __shared__ int s_ids[DEC_IDCAP];
-    __shared__ float4 s_red[NW][128];
+    __shared__ __align__(16) float s_red[DN_NW * Gm::SC];
     __shared__ float s_half[512];
-    __shared__ int s_tmp[17];
+    __shared__ int s_tmp[DN_NW + 1];
     __shared__ int s_acc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
@@ -218,163 +234,107 @@ __global__ __launch_bounds__(1024) void k_dec_down_f16(
     if (slice == 0 && idx != nullptr)
         write_table(mask, w0, n_loc, split == nsplit - 1, s_ids, idx, count, &s_acc);
 
-    const int nc = d >> 3;
-    const int c = slice * 64 + lane;
-    const bool cok = c < nc;
-    float acc[8];
+    const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
+    const size_t boff = ((size_t)slice * 64 + lane) * Gm::LB;
+    const bool cok = boff < rowb;
+    const int G = d >> 7;
+    const int sg = (slice * Gm::SC + lane * Gm::V) >> 7;   // int4 scale group of this lane
+    const uint8_t* Wb = static_cast<const uint8_t*>(Wd);
+    float acc[Gm::V];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int k0 = wave; k0 < n_loc; k0 += NW * U) {
-        uint4 w[U];
-        float hv[U];
+    for (int v = 0; v < Gm::V; ++v) acc[v] = 0.f;
+    float soff = 0.f;
+    for (int k0 = wave; k0 < n_loc; k0 += DN_NW * U) {
+        float hv[U], sv[U];
+        uint4 w16[U];
+        uint2 w8[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * NW;
-            if (kk < n_loc) {
-                const int row = s_ids[kk];
+            const int k = k0 + u * DN_NW;
+            hv[u] = 0.f;
+            sv[u] = 0.f;
+            if (WF == 0) w16[u] = zero4(); else w8[u] = make_uint2(0u, 0u);
+            if (k < n_loc) {
+                const size_t row = (size_t)__builtin_amdgcn_readfirstlane(s_ids[k]);
                 hv[u] = h[row];
-                w[u] = cok ? ld16(Wd + (size_t)row * d + 8 * c) : zero4();
-            } else {
-                hv[u] = 0.f;
-                w[u] = zero4();
+                if (cok) {
+                    if (WF == 0) {
+                        w16[u] = ld16(Wb + row * rowb + boff);
+                    } else {
+                        w8[u] = *reinterpret_cast<const uint2*>(Wb + row * rowb + boff);
+                        sv[u] = h2f(Sd[row * G + sg]);
+                    }
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+            if (WF == 0) {
+                const uint32_t ww[4] = {w16[u].x, w16[u].y, w16[u].z, w16[u].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
+                }
+            } else {
+                const float hs = hv[u] * sv[u];
+                soff += hs;
+                const uint32_t ws[2] = {w8[u].x, w8[u].y};
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int bb = 0; bb < 4; ++bb) {
+                        acc[8 * m + 2 * bb] = fmaf(hs, (float)((lo >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb]);
+                        acc[8 * m + 2 * bb + 1] = fmaf(hs, (float)((hi >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb + 1]);
+                    }
+                }
             }
         }
     }
-    s_red[wave][2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    s_red[wave][2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    __syncthreads();
-    const int col = tid & 511, hf = tid >> 9;
-    const float* sr = reinterpret_cast<const float*>(s_red);
-    float s = 0.f;
+    if (WF == 1) {
 #pragma unroll
-    for (int w = 0; w < NW / 2; ++w) s += sr[(hf * (NW / 2) + w) * 512 + col];
-    if (hf == 1) s_half[col] = s;
+        for (int v = 0; v < Gm::V; ++v) acc[v] = fmaf(-8.f, soff, acc[v]);   // stored u = q + 8
+    }
+    {
+        float4* dst = reinterpret_cast<float4*>(&s_red[wave * Gm::SC + lane * Gm::V]);
+#pragma unroll
+        for (int v = 0; v < Gm::V; v += 4) dst[v / 4] = make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+    }
     __syncthreads();
-    const int gcol = slice * 512 + col;
-    if (hf == 0 && gcol < d) st_agent(&part[(size_t)split * d + gcol], s + s_half[col]);
+    // waves' sums -> this block's partial row of the slice (fixed order)
+    float s = 0.f;
+    int col;
+    if (WF == 0) {                       // 512 columns: two half-sums per column
+        col = tid & 511;
+        const int hf = tid >> 9;
+#pragma unroll
+        for (int w = 0; w < DN_NW / 2; ++w) s += s_red[(hf * (DN_NW / 2) + w) * Gm::SC + col];
+        if (hf == 1) s_half[col] = s;
+        __syncthreads();
+        if (hf == 0) s += s_half[col];
+    } else {                             // 1024 columns: one per thread
+        col = tid;
+#pragma unroll
+        for (int w = 0; w < DN_NW; ++w) s += s_red[w * Gm::SC + col];
+    }
+    const int gcol = slice * Gm::SC + col;
+    const bool writer = WF == 0 ? (tid < 512) : true;
+    if (writer && gcol < d) st_agent(&part[(size_t)split * d + gcol], s);
     if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
         float t = 0.f;
-        if (gcol < d) {
-            for (int base = hf; base < nsplit; base += 32) {
+        if (writer && gcol < d) {
+            for (int base = 0; base < nsplit; base += 16) {      // 16 partials in flight
                 float v[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int sp = base + 2 * j;
+                    const int sp = base + j;
                     v[j] = sp < nsplit ? ld_agent(&part[(size_t)sp * d + gcol]) : 0.f;
                 }
 #pragma unroll
                 for (int j = 0; j < 16; ++j) t += v[j];
             }
-        }
-        __syncthreads();
-        if (hf == 1) s_half[col] = t;
-        __syncthreads();
-        if (hf == 0 && gcol < d) y[gcol] = t + s_half[col];
-    }
-}
-
-template <int U>
-__global__ __launch_bounds__(512) void k_dec_down_i4(
-    const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
-    const uint8_t* __restrict__ Dq, const uint16_t* __restrict__ Ds, int d, int wps,
-    float* __restrict__ part, float* __restrict__ y, unsigned* __restrict__ counters,
-    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-    constexpr int NW = 8;
-    __shared__ int s_ids[DEC_IDCAP];
-    __shared__ float4 s_red[NW][512];
-    __shared__ int s_tmp[9];
-    __shared__ int s_acc;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
-    const int W = (F + 31) >> 5;
-    const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
-    const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
-    if (slice == 0 && idx != nullptr)
-        write_table(mask, w0, n_loc, split == nsplit - 1, s_ids, idx, count, &s_acc);
-
-    const int nc = d >> 5;
-    const int G = d >> 7;
-    const size_t rb = (size_t)(d >> 1);
-    const int c = slice * 64 + lane;
-    const bool cok = c < nc;
-    float acc[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
-    float soff = 0.f;
-    for (int k0 = wave; k0 < n_loc; k0 += NW * U) {
-        uint4 w[U];
-        float hs[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * NW;
-            if (kk < n_loc && cok) {
-                const size_t row = (size_t)s_ids[kk];
-                w[u] = ld16(Dq + row * rb + 16 * c);
-                hs[u] = h[row] * h2f(Ds[row * G + (c >> 2)]);
-            } else {
-                w[u] = zero4();
-                hs[u] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            soff += hs[u];
-            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    acc[8 * m + 2 * b] = fmaf(hs[u], (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
-                    acc[8 * m + 2 * b + 1] = fmaf(hs[u], (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 32; j += 4)
-        s_red[wave][8 * lane + j / 4] =
-            make_float4(fmaf(-8.f, soff, acc[j]), fmaf(-8.f, soff, acc[j + 1]),
-                        fmaf(-8.f, soff, acc[j + 2]), fmaf(-8.f, soff, acc[j + 3]));
-    __syncthreads();
-    float4 s = s_red[0][tid];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        const float4 t = s_red[w][tid];
-        s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-    }
-    const int gcol = slice * 2048 + 4 * tid;
-    if (gcol < d) {
-        float* pp = part + (size_t)split * d + gcol;
-        st_agent(pp, s.x); st_agent(pp + 1, s.y); st_agent(pp + 2, s.z); st_agent(pp + 3, s.w);
-    }
-    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
-        if (gcol < d) {
-            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int base = 0; base < nsplit; base += 8) {
-                float v[8][4];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float* pp = part + (size_t)(base + j) * d + gcol;
-                    const bool ok = base + j < nsplit;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[j][e] = ok ? ld_agent(pp + e) : 0.f;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    t.x += v[j][0]; t.y += v[j][1]; t.z += v[j][2]; t.w += v[j][3];
-                }
-            }
-            *reinterpret_cast<float4*>(y + gcol) = t;
+            y[gcol] = t;
         }
     }
 }
@@ -424,14 +384,14 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     const bool f16 = wfmt == PI_W_F16;
     p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
     p.lds_b = (size_t)align16i(r * 4) + (size_t)(d / 8) * 16;
-    p.cols = f16 ? 512 : 2048;
-    p.nslices = (d + p.cols - 1) / p.cols;
+    const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
+    p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
-    // about 128 down blocks: enough waves to keep each one's rows (U = 8) in flight, few
-    // enough partials for the last block of a slice to sum them in one batch of loads
+    // about 128 down blocks: enough waves to keep each one's rows (U in flight) streaming,
+    // few enough partials for the last block of a slice to sum them in one batch of loads
     int ns = (128 + p.nslices - 1) / p.nslices;
     const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
-    if (ns > 64) ns = 64;
+    if (ns > 16) ns = 16;
     if (ns > W) ns = W;
     if (ns < ns_min) ns = ns_min;
     if (ns < 1) ns = 1;
@@ -454,8 +414,6 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
                               hipEvent_t e0, hipEvent_t e1) {
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
-    float* part = reinterpret_cast<float*>(ws + pl.off_part);
-    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DECODE;
     hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s);
     if (e != hipSuccess) return e;
     const bool glu = f.act == PI_ACT_REGLU;
@@ -467,15 +425,15 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
         e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
                 : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
     if (e != hipSuccess) return e;
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DECODE;
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
     const dim3 gc(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16)
-        hipLaunchKernelGGL((k_dec_down_f16<8>), gc, dim3(1024), 0, s, mask, f.F, h,
-                           static_cast<const uint16_t*>(f.w_down), f.d, pl.wps, part, y, cnt, idx,
-                           count);
+        hipLaunchKernelGGL((k_dec_down<0, 8>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
+                           f.s_down, f.d, pl.wps, part, y, cnt, idx, count);
     else
-        hipLaunchKernelGGL((k_dec_down_i4<8>), gc, dim3(512), 0, s, mask, f.F, h,
-                           static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, pl.wps, part, y,
-                           cnt, idx, count);
+        hipLaunchKernelGGL((k_dec_down<1, 12>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
+                           f.s_down, f.d, pl.wps, part, y, cnt, idx, count);
     return hipGetLastError();
 }
 

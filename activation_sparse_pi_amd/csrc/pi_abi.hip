@@ -252,6 +252,7 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
             ffns[i].wfmt != ffns[0].wfmt || preds[i].threshold != preds[0].threshold)
             return fail(PI_ERR_SHAPE, "replica %d does not match replica 0 / its ffn", i);
     }
+    if (preds[0].F > 131072) return fail(PI_ERR_UNSUPPORTED, "pi_decode_run supports F <= 131072");
     if (events)
         for (int i = 0; i < 2 * nsteps; ++i)
             if (!events[i]) return fail(PI_ERR_NULL, "events[%d] is NULL", i);
