@@ -38,10 +38,8 @@ struct FfnPlan {
     int cols;      // columns per down slice
     int nslices, nsplit;
     size_t off_h, off_part, bytes;
-    // union (B > 1) path
-    int u_tiles;   // max 32-neuron tiles of the union list
-    int u_ksplit;  // neuron splits of the union down product
-    size_t off_H, off_upart;
+    // union (B > 1) path: fp16 H, token-major [32, F] (0 when B == 1)
+    size_t off_H;
 };
 FfnPlan plan_ffn(int d, int F, int wfmt, int B);
 

@@ -372,12 +372,12 @@ FfnPlan plan_ffn(int d, int F, int wfmt, int B) {
     off = align_up(off + (size_t)F * sizeof(float), 256);
     p.off_part = off;
     off = align_up(off + (size_t)p.nsplit * d * sizeof(float), 256);
+    p.off_H = 0;
+    if (B > 1) {
+        p.off_H = off;
+        off = align_up(off + (size_t)32 * F * sizeof(uint16_t), 256);
+    }
     p.bytes = off;
-    // union path (B > 1) storage is appended by the union planner
-    p.u_tiles = (F + 31) / 32;
-    p.u_ksplit = 0;
-    p.off_H = p.off_upart = 0;
-    (void)B;
     return p;
 }
 

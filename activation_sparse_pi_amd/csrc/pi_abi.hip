@@ -73,11 +73,8 @@ int check_ffn(const pi_ffn_desc* f, int B) {
     const void* ptrs[6] = {f->w_gate, f->w_up, f->w_down, f->s_gate, f->s_up, f->s_down};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return fail(PI_ERR_ALIGN, "ffn weights must be 16-byte aligned");
-    if (B > 1) return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path not built yet");
     if (B > 1 && f->wfmt != PI_W_F16)
         return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path is fp16 only");
-    if (B > 1 && f->d % 64)
-        return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path needs d %% 64 == 0");
     return PI_OK;
 }
 

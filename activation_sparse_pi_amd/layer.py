@@ -115,6 +115,16 @@ class DeviceLayer:
         self.sparse_ffn(x, 1, bufs["idx"].data_ptr(), bufs["count"].data_ptr(), None,
                         bufs["y"].data_ptr(), rep)
 
+    def batch_step(self, x, B: int, bufs: dict, rep: int = 0, logits: bool = True) -> None:
+        """One small-batch step (1 < B <= 32): per-token masks and tables, their union,
+        then the union FFN where token b only receives the neurons of its own mask."""
+        self.predict(x, B, bufs["logits"].data_ptr() if logits else None, bufs["mask"].data_ptr(),
+                     bufs["idx"].data_ptr(), bufs["count"].data_ptr(), rep)
+        self.compact(bufs["mask"].data_ptr(), B, L.PI_UNION, bufs["uidx"].data_ptr(),
+                     bufs["ucount"].data_ptr())
+        self.sparse_ffn(x, B, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr(),
+                        bufs["mask"].data_ptr(), bufs["y"].data_ptr(), rep)
+
     # ---- output buffers --------------------------------------------------------------------
     def buffers(self, B: int) -> dict:
         W = (self.F + 31) // 32

@@ -58,6 +58,8 @@ def test_status_strings_and_version():
 def test_workspace_bytes():
     n = L.pi_workspace_bytes(pred(), ffn(), 1)
     assert n > 0 and n % 256 == 0
+    # batch > 1 adds the fp16 H buffer [32, F] of the union path
+    assert L.pi_workspace_bytes(None, ffn(), 32) >= L.pi_workspace_bytes(None, ffn(), 1) + 32 * 4096 * 2
     assert L.pi_workspace_bytes(pred(), ffn(), 32) >= n
     assert L.pi_workspace_bytes(pred(), ffn(), 0) == 0
     assert L.pi_workspace_bytes(pred(d=1001), None, 1) == 0
@@ -109,6 +111,8 @@ def test_predict_validation(kw, code):
     (dict(desc=ffn(d=8200)), L.PI_ERR_UNSUPPORTED),
     (dict(desc=ffn(w_down=A + 4)), L.PI_ERR_ALIGN),
     (dict(B=2, token_mask=None), L.PI_ERR_NULL),
+    (dict(B=2, token_mask=A, desc=ffn(wfmt=L.PI_W_I4G128, s_up=A, s_down=A)), L.PI_ERR_UNSUPPORTED),
+    (dict(B=32, token_mask=A, wsb=L.pi_workspace_bytes(None, ffn(), 1)), L.PI_ERR_WORKSPACE),
     (dict(token_mask=A), L.PI_ERR_SHAPE),
     (dict(idx=None), L.PI_ERR_NULL),
     (dict(count=None), L.PI_ERR_NULL),
