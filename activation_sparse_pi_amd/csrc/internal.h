@@ -38,10 +38,14 @@ struct FfnPlan {
     int cols;      // columns per down slice
     int nslices, nsplit;
     size_t off_h, off_part, bytes;
-    // union (B > 1) path: fp16 H, token-major [32, F] (0 when B == 1)
-    size_t off_H;
+    // union (B > 1) path: H fragments, down-product column groups and list shares,
+    // the shares' partial sums (all 0 when B == 1)
+    int u_ncg, u_ks;
+    size_t off_H, off_upart;
 };
 FfnPlan plan_ffn(int d, int F, int wfmt, int B);
+// appends the union path's workspace to p from offset off; returns the new end
+size_t plan_union(FfnPlan& p, int d, int F, size_t off);
 
 // ---- fused batch-1 decode step (three kernels) --------------------------------------------
 struct DecPlan {
@@ -84,7 +88,7 @@ hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t
 // 1 < B <= 32 union-mask path on MFMA
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
                             const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
-                            int dense, float* y, char* ws, hipStream_t s);
+                            float* y, char* ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

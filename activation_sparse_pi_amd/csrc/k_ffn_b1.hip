@@ -372,11 +372,9 @@ FfnPlan plan_ffn(int d, int F, int wfmt, int B) {
     off = align_up(off + (size_t)F * sizeof(float), 256);
     p.off_part = off;
     off = align_up(off + (size_t)p.nsplit * d * sizeof(float), 256);
-    p.off_H = 0;
-    if (B > 1) {
-        p.off_H = off;
-        off = align_up(off + (size_t)32 * F * sizeof(uint16_t), 256);
-    }
+    p.u_ncg = p.u_ks = 0;
+    p.off_H = p.off_upart = 0;
+    if (B > 1) off = plan_union(p, d, F, off);
     p.bytes = off;
     return p;
 }

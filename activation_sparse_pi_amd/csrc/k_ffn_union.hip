@@ -11,20 +11,27 @@
 //   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + j], j < 8
 //   B (16 x 32): lane l holds B[8 * (l / 32) + j][l % 32]
 //   D (32 x 32): lane l, register r holds D[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32]
-// The k slots of one MFMA may be any permutation shared by A and B, which lets a lane
-// read long contiguous runs of its row.
 //
-//   up    Ht[b, k] = act(W_up[u_k] . x_b)  (fp16, token-major [32, F]), zero where neuron
-//         u_k is not in token b's mask.  Block = one 32-neuron tile of the union list x
-//         all 32 token slots; its 8 waves split d; each lane streams 64-byte runs of its
-//         neuron's row and of its token's x (4 MFMAs per run); waves meet in LDS.
-//   down  y[b, :] = sum_k Ht[b, k] W_down[u_k, :].  Block = one 32-column slice of y; its
-//         8 waves split the union list; per step of 16 neurons a lane loads 16 bytes of
-//         one row and writes them transposed into its wave's own LDS tile, so the MFMA B
-//         operand (8 consecutive neurons of one column) is one 16-byte LDS read and no
-//         block barrier sits in the streaming loop; waves meet in LDS at the end and the
-//         block writes its slice of y (no partial sums leave the block).  The two slices
-//         sharing a 128-byte line run on blocks of the same XCD.
+// Global loads are always whole 128-byte lines spread over 8 lanes (16 bytes each);
+// operands reach the MFMA layout through a wave-private LDS area (XOR-swizzled so
+// that neither the staging writes nor the operand reads conflict).  No block barrier
+// sits in either streaming loop: each wave stages and consumes its own data.
+//
+//   up    one block per 32-neuron tile of the union list; its 8 waves split d in runs
+//         of 64 elements.  Per run a wave stages the tile's 32 rows x 128 bytes of
+//         W_up (and W_gate) and the 32 tokens' x, then issues 4 (8) MFMAs.  The waves
+//         meet in LDS; h = act(.) * [neuron in token b's mask] is rounded to fp16 and
+//         written in the down kernel's A-operand order ("H fragments": for each group
+//         of 16 union positions, 64 lanes x 16 bytes, lane l holding positions
+//         8 (l / 32) .. + 7 of token l % 32), so that operand is one 1 KB load.
+//   down  y[b, :] = sum_k H[b, k] W_down[u_k, :].  Block = 64 columns (one 128-byte
+//         line of every row) x one of KS interleaved shares of the union list; its 8
+//         waves take stages of 64 union positions round-robin.  Per stage a lane loads
+//         16 bytes of 8 consecutive rows, transposes the 8 x 8 fp16 block in registers
+//         into 8 column vectors of 8 positions (exactly B-operand units) and writes them
+//         to LDS; then 4 K-steps x 2 column tiles of MFMA.  The waves meet in LDS; with
+//         KS > 1 the shares meet in the workspace and the last-arriving block of the
+//         column group adds them in a fixed order (bitwise reproducible).
 #include "device_common.h"
 #include "internal.h"
 
@@ -34,207 +41,299 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int UN_NW = 8;           // waves per block
-
-PI_DEV half8_t as_h8(const uint4& v) { return __builtin_bit_cast(half8_t, v); }
+constexpr int UP_NW = 8;      // waves per up block
+constexpr int DN_NWU = 8;     // waves per down block
+constexpr int DN_COLS = 64;   // columns per down block
 
 PI_DEV f32x16_t mfma16(const uint4& a, const uint4& b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
 PI_DEV bool bit_of(const uint32_t* __restrict__ mask, int W, int b, int i) {
     return (mask[(size_t)b * W + (i >> 5)] >> (i & 31)) & 1u;
 }
 
+PI_DEV uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
 // ------------------------------------------------------------------------------------ up
 template <bool GLU>
-__global__ __launch_bounds__(UN_NW * 64) void k_union_up(
+__global__ __launch_bounds__(UP_NW * 64) void k_union_up(
     const uint16_t* __restrict__ x, int B, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, int d, int F, const int32_t* __restrict__ uidx,
     const int32_t* __restrict__ ucount, const uint32_t* __restrict__ tmask,
-    uint16_t* __restrict__ Ht) {
-    __shared__ float s_red[UN_NW][16][64];
+    uint4* __restrict__ Hf) {
+    constexpr int NP = GLU ? 3 : 2;                   // staged pieces per run: x, up [, gate]
+    __shared__ uint4 s_st[UP_NW][NP][32][8];          // per wave: piece, row, swizzled 16-B slot
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int U = min(*ucount, F);
     const int tile = blockIdx.x;
-    if (tile * 32 >= U) return;                        // whole block: past the union
-    const int mi = lane & 31, half = lane >> 5;
-    const int kpos = tile * 32 + mi;                   // this lane's union position (A row)
-    int row = kpos < U ? uidx[kpos] : -1;
-    if ((unsigned)row >= (unsigned)F) row = -1;
-    const int tok = mi;                                // this lane's token (B column)
-    const uint8_t* pu = row >= 0 ? reinterpret_cast<const uint8_t*>(Wu + (size_t)row * d) : nullptr;
-    const uint8_t* pg = (GLU && row >= 0) ? reinterpret_cast<const uint8_t*>(Wg + (size_t)row * d) : nullptr;
-    const uint8_t* px = tok < B ? reinterpret_cast<const uint8_t*>(x + (size_t)tok * d) : nullptr;
+    if (tile * 32 >= U) return;                       // whole block: past the union
 
-    // this wave's share of d, in runs of 64 elements (lane half h reads elements [32h, 32h+32))
-    const int nrun = (d + 63) / 64;
-    const int per = (nrun + UN_NW - 1) / UN_NW;
-    const int r0 = wave * per, r1 = min(nrun, r0 + per);
+    // loader role: load q (0..3) of a run brings row 8q + lrow, 16-byte chunk lch
+    const int lrow = lane >> 3, lch = lane & 7;
+    long long offw[4], offx[4];                       // element offsets, -1 = zero row
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int kp = tile * 32 + 8 * q + lrow;
+        int row = kp < U ? uidx[kp] : -1;
+        if ((unsigned)row >= (unsigned)F) row = -1;
+        offw[q] = row < 0 ? -1 : (long long)row * d;
+        const int tok = 8 * q + lrow;
+        offx[q] = tok < B ? (long long)tok * d : -1;
+    }
+    // MFMA role: A row / B column mi, k-slot half
+    const int mi = lane & 31, half = lane >> 5;
+    const int nrun = (d + 63) / 64, per = (nrun + UP_NW - 1) / UP_NW;
+    const int r0 = min(nrun, wave * per), r1 = min(nrun, r0 + per);
+    uint4(*st)[32][8] = s_st[wave];
+
     f32x16_t cu = {}, cg = {};
-    for (int rr = r0; rr < r1; ++rr) {
-        const int e0 = rr * 64 + half * 32;            // first element of this lane's run
-        uint4 wa[4], ga[4], xb[4];
+    uint4 ra[NP][4], rb[NP][4];
+    auto load = [&](int rr, uint4(&v)[NP][4]) {
+        const int e = rr * 64 + lch * 8;
+        const bool ok = e < d;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int e = e0 + 8 * s;
-            const bool ok = e < d;
-            wa[s] = (ok && pu) ? ld16(pu + 2 * (size_t)e) : zero4();
-            if (GLU) ga[s] = (ok && pg) ? ld16(pg + 2 * (size_t)e) : zero4();
-            xb[s] = (ok && px) ? ld16(px + 2 * (size_t)e) : zero4();
+        for (int q = 0; q < 4; ++q) {
+            v[0][q] = (ok && offx[q] >= 0) ? ld16(x + offx[q] + e) : zero4();
+            v[1][q] = (ok && offw[q] >= 0) ? ld16(Wu + offw[q] + e) : zero4();
+            if constexpr (GLU) v[2][q] = (ok && offw[q] >= 0) ? ld16(Wg + offw[q] + e) : zero4();
         }
+    };
+    // row r = 8q + lrow keeps chunk c in slot c ^ (r % 8)
+    auto stage = [&](const uint4(&v)[NP][4]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) st[p][8 * q + lrow][lch ^ lrow] = v[p][q];
+    };
+    // k-step s takes chunk 2s + half of row mi: k-slot 8 half + j <-> element 16 s + 8 half + j
+    auto compute = [&]() {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            cu = mfma16(wa[s], xb[s], cu);
-            if (GLU) cg = mfma16(ga[s], xb[s], cg);
+            const int slot = (2 * s + half) ^ (mi & 7);
+            const uint4 bx = st[0][mi][slot];
+            cu = mfma16(st[1][mi][slot], bx, cu);
+            if constexpr (GLU) cg = mfma16(st[2][mi][slot], bx, cg);
+        }
+    };
+    // two register sets: the run after next is in flight while one run is consumed
+    if (r0 < r1) load(r0, ra);
+    if (r0 + 1 < r1) load(r0 + 1, rb);
+    for (int rr = r0; rr < r1; rr += 2) {
+        stage(ra);
+        if (rr + 2 < r1) load(rr + 2, ra);
+        compute();
+        if (rr + 1 < r1) {
+            stage(rb);
+            if (rr + 3 < r1) load(rr + 3, rb);
+            compute();
         }
     }
-    // Reduce the 8 waves' 32 x 32 tiles.  Thread o covers outputs o and o + 512 with
-    // token b = o / 32 and tile row n = o % 32, so 32 neighbouring threads store 32
-    // consecutive entries of one H row.  D[n][b] sits in register (n/8)*4 + n%4 of
-    // lane b + 32 * ((n/4) % 2).
-    float a[2], g[2] = {0.f, 0.f};
+
+    // the waves meet in LDS (each wave's staging area holds its own accumulators)
+    float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_red[wave][r][lane] = cu[r];
+    for (int r = 0; r < 16; ++r) {
+        red[r * 64 + lane] = cu[r];
+        if constexpr (GLU) red[1024 + r * 64 + lane] = cg[r];
+    }
     __syncthreads();
+    if (tid < 128) {
+        // H-fragment lane fl of group 2 tile + gg: token b = fl % 32, positions
+        // 16 gg + 8 (fl / 32) + j.  D[n][b] sits in register (n/8)*4 + n%4 of lane
+        // b + 32 ((n/4) % 2).
+        const int fl = tid & 63, gg = tid >> 6, h = fl >> 5, b = fl & 31;
+        const int W = (F + 31) >> 5;
+        float hv[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int o = tid + q * UN_NW * 64, b = o >> 5, n = o & 31;
-        const int rg = (n >> 3) * 4 + (n & 3), ln = b + 32 * ((n >> 2) & 1);
-        float t = 0.f;
+        for (int j = 0; j < 8; ++j) {
+            const int rg = (2 * gg + h) * 4 + (j & 3), ln = b + 32 * (j >> 2);
+            float a = 0.f, g = 0.f;
 #pragma unroll
-        for (int w = 0; w < UN_NW; ++w) t += s_red[w][rg][ln];
-        a[q] = t;
-    }
-    if (GLU) {
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s_red[wave][r][lane] = cg[r];
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int o = tid + q * UN_NW * 64, b = o >> 5, n = o & 31;
-            const int rg = (n >> 3) * 4 + (n & 3), ln = b + 32 * ((n >> 2) & 1);
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < UN_NW; ++w) t += s_red[w][rg][ln];
-            g[q] = t;
+            for (int w = 0; w < UP_NW; ++w) {
+                const float* rw = reinterpret_cast<const float*>(&s_st[w][0][0][0]);
+                a += rw[rg * 64 + ln];
+                if constexpr (GLU) g += rw[1024 + rg * 64 + ln];
+            }
+            const int k = tile * 32 + gg * 16 + 8 * h + j;
+            float v = 0.f;                     // positions past U and tokens past B give 0
+            if (k < U && b < B) {
+                const int i = uidx[k];
+                if ((unsigned)i < (unsigned)F && bit_of(tmask, W, b, i))
+                    v = GLU ? fmaxf(g, 0.f) * a : fmaxf(a, 0.f);
+            }
+            hv[j] = v;
         }
-    }
-    const int W = (F + 31) >> 5;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int o = tid + q * UN_NW * 64, b = o >> 5, n = o & 31;
-        const int k = tile * 32 + n;
-        if (b >= B || k >= F) continue;
-        // positions from U to the end of the last tile are written as 0: the down
-        // product reads H in 8-neuron groups
-        float hv = 0.f;
-        if (k < U) {
-            const int i = uidx[k];
-            if ((unsigned)i < (unsigned)F && bit_of(tmask, W, b, i))
-                hv = GLU ? fmaxf(g[q], 0.f) * a[q] : fmaxf(a[q], 0.f);
-        }
-        Ht[(size_t)b * F + k] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        Hf[(size_t)(tile * 2 + gg) * 64 + fl] =
+            make_uint4(pack_h2(hv[0], hv[1]), pack_h2(hv[2], hv[3]), pack_h2(hv[4], hv[5]),
+                       pack_h2(hv[6], hv[7]));
     }
 }
 
 // ------------------------------------------------------------------------------------ down
-PI_DEV int xcd_pair_slice(int b) {
-    // slices 2m and 2m+1 (one 128-byte line of every row) on blocks b and b + 8: same XCD
-    return ((b >> 4) * 8 + (b & 7)) * 2 + ((b >> 3) & 1);
-}
+// column c of a stage keeps k-block kb in unit kb * 64 + (c ^ ((c >> 3) & 7))
+PI_DEV int dn_slot(int c) { return c ^ ((c >> 3) & 7); }
 
-constexpr int DN_PF = 8;   // steps of 16 neurons kept in flight per lane
-
-__global__ __launch_bounds__(UN_NW * 64) void k_union_down(
-    const uint16_t* __restrict__ Ht, int B, const uint16_t* __restrict__ Wd, int d, int F,
-    const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucount, int nslices,
-    float* __restrict__ y) {
-    __shared__ __align__(16) uint16_t s_t[UN_NW][32][16];      // per wave: [column][neuron]
-    __shared__ float s_red[UN_NW][16][64];
+__global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
+    const uint4* __restrict__ Hf, int B, const uint16_t* __restrict__ Wd, int d, int F,
+    const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucount, int ncg, int nks,
+    float* __restrict__ part, unsigned* __restrict__ counter, float* __restrict__ y) {
+    __shared__ uint4 s_t[DN_NWU][8][64];             // per wave: k-block, swizzled column unit
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slice = xcd_pair_slice(blockIdx.x);
-    if (slice >= nslices) return;                               // padding block
+    const int cgi = blockIdx.x % ncg, ks = blockIdx.x / ncg;
     const int U = min(*ucount, F);
-    const int c0 = slice * 32;                                  // first column of the slice
-    const size_t rowb = (size_t)d * 2;
-    // loader role: lane -> neuron r = lane / 4 of the step, 8 columns at cc = (lane % 4) * 8
-    const int lr = lane >> 2, lcc = (lane & 3) * 8;
-    const bool col_ok = c0 + lcc < d;
-    // MFMA roles: A = Ht[token = lane % 32][k .. k+8], B = s_t[column = lane % 32][8 half ..]
-    const int mtok = lane & 31, khalf = (lane >> 5) * 8;
-    const int nsteps = (U + 15) / 16;
-    f32x16_t acc = {};
-    uint4 wbuf[DN_PF];
-    // step s of this wave: global step g = s * UN_NW + wave
-    auto load_step = [&](int g, uint4& dst) {
-        const int k = g * 16 + lr;
-        int row = k < U ? uidx[k] : -1;
-        dst = (row >= 0 && row < F && col_ok) ? ld16(reinterpret_cast<const uint8_t*>(Wd) + (size_t)row * rowb + 2 * (size_t)(c0 + lcc))
-                                              : zero4();
-    };
-    const int my_steps = nsteps > wave ? (nsteps - wave + UN_NW - 1) / UN_NW : 0;
+    const int c0 = cgi * DN_COLS;
+    const int nst = (U + 63) / 64;                    // stages of 64 union positions
+    const int nw = nks * DN_NWU;                      // waves sharing the list
+    // loader role: lane -> rows 8 rbk .. 8 rbk + 7 of a stage, columns 8 ch .. 8 ch + 7
+    const int rbk = lane >> 3, ch = lane & 7;
+    const bool col_ok = c0 + ch * 8 < d;
+    // MFMA role: B column n of each 32-column tile, k half h
+    const int n = lane & 31, h = lane >> 5;
+    const int slot0 = dn_slot(n), slot1 = dn_slot(32 + n);
+    uint4(*st)[64] = s_t[wave];
+
+    f32x16_t acc0 = {}, acc1 = {};
+    int rows[8];
+    uint4 R[8], Rn[8], A[4], An[4];
+    auto load_rows = [&](int s) {
 #pragma unroll
-    for (int p = 0; p < DN_PF; ++p)
-        if (p < my_steps) load_step(p * UN_NW + wave, wbuf[p]);
-    for (int s = 0; s < my_steps; s += DN_PF) {
-#pragma unroll
-        for (int p = 0; p < DN_PF; ++p) {
-            if (s + p >= my_steps) break;
-            const int g = (s + p) * UN_NW + wave;
-            // transpose this step's 16 rows x 32 columns into the wave's LDS tile
-            const uint32_t ww[4] = {wbuf[p].x, wbuf[p].y, wbuf[p].z, wbuf[p].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s_t[wave][lcc + 2 * j][lr] = (uint16_t)(ww[j] & 0xFFFFu);
-                s_t[wave][lcc + 2 * j + 1][lr] = (uint16_t)(ww[j] >> 16);
-            }
-            // refill this slot with the step DN_PF ahead
-            if (s + p + DN_PF < my_steps) load_step((s + p + DN_PF) * UN_NW + wave, wbuf[p]);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
-            const uint4 bop = *reinterpret_cast<const uint4*>(&s_t[wave][mtok][khalf]);
-            const int k = g * 16 + khalf;
-            const uint4 aop = (k < U && mtok < B) ? ld16(Ht + (size_t)mtok * F + k) : zero4();
-            acc = mfma16(aop, bop, acc);
+        for (int j = 0; j < 8; ++j) {
+            const int k = s * 64 + rbk * 8 + j;
+            int r = (s < nst && k < U) ? uidx[k] : -1;
+            rows[j] = (unsigned)r < (unsigned)F ? r : -1;
         }
-    }
+    };
+    auto load_w = [&](uint4(&v)[8]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_red[wave][r][lane] = acc[r];
+        for (int j = 0; j < 8; ++j)
+            v[j] = (rows[j] >= 0 && col_ok) ? ld16(Wd + (size_t)rows[j] * d + c0 + ch * 8) : zero4();
+    };
+    auto load_a = [&](int s, uint4(&a)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int g = s * 4 + q;                  // group of 16 positions
+            a[q] = g * 16 < U ? Hf[(size_t)g * 64 + lane] : zero4();
+        }
+    };
+    int s = ks * DN_NWU + wave;
+    if (s < nst) {
+        load_rows(s);
+        load_w(R);
+        load_a(s, A);
+        load_rows(s + nw);
+    }
+    for (; s < nst; s += nw) {
+        const int sn = s + nw;
+        if (sn < nst) {
+            load_w(Rn);
+            load_a(sn, An);
+            load_rows(sn + nw);
+        }
+        // 8 x 8 transpose: unit e = column 8 ch + e over rows 8 rbk .. 8 rbk + 7
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t o[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo = (&R[2 * p].x)[e >> 1], hi = (&R[2 * p + 1].x)[e >> 1];
+                o[p] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+            }
+            st[rbk][8 * ch + (e ^ ch)] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kb = 2 * q + h;
+            acc0 = mfma16(A[q], st[kb][slot0], acc0);
+            acc1 = mfma16(A[q], st[kb][slot1], acc1);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) R[j] = Rn[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) A[q] = An[q];
+    }
+
+    // the waves meet in LDS
+    float* red = reinterpret_cast<float*>(&s_t[wave][0][0]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        red[r * 64 + lane] = acc0[r];
+        red[1024 + r * 64 + lane] = acc1[r];
+    }
     __syncthreads();
-    for (int o = tid; o < 1024; o += UN_NW * 64) {
-        const int r = o >> 6, l = o & 63;
+    // 32 tokens x 64 columns, four per thread; output o: tile o / 1024, register
+    // (o / 64) % 16, lane o % 64
+    float v[4];
+    int ob[4], oc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int o = tid + q * DN_NWU * 64;
+        const int nt = o >> 10, r = (o >> 6) & 15, l = o & 63;
         float t = 0.f;
 #pragma unroll
-        for (int w = 0; w < UN_NW; ++w) t += s_red[w][r][l];
-        const int b = (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);    // token (D row)
-        const int col = c0 + (l & 31);                           // column (D column)
-        if (b < B && col < d) y[(size_t)b * d + col] = t;
+        for (int w = 0; w < DN_NWU; ++w)
+            t += reinterpret_cast<const float*>(&s_t[w][0][0])[nt * 1024 + r * 64 + l];
+        v[q] = t;
+        ob[q] = (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+        oc[q] = c0 + nt * 32 + (l & 31);
+    }
+    if (nks == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (ob[q] < B && oc[q] < d) y[(size_t)ob[q] * d + oc[q]] = v[q];
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (ob[q] < B && oc[q] < d) st_agent(&part[((size_t)ks * 32 + ob[q]) * d + oc[q]], v[q]);
+    if (!last_block_arrive(&counter[cgi], nks)) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (ob[q] >= B || oc[q] >= d) continue;
+        float t = 0.f;
+        for (int k2 = 0; k2 < nks; ++k2)
+            t += k2 == ks ? v[q] : ld_agent(&part[((size_t)k2 * 32 + ob[q]) * d + oc[q]]);
+        y[(size_t)ob[q] * d + oc[q]] = t;
     }
 }
 
 }  // namespace
 
+size_t plan_union(FfnPlan& p, int d, int F, size_t off) {
+    p.off_H = off;
+    off = align_up(off + (size_t)((F + 31) / 32) * 2048, 256);   // H fragments, 2 KB per tile
+    p.u_ncg = (d + DN_COLS - 1) / DN_COLS;
+    int ks = (256 + p.u_ncg - 1) / p.u_ncg;                      // >= 256 down blocks
+    p.u_ks = ks < 1 ? 1 : (ks > 16 ? 16 : ks);
+    p.off_upart = off;
+    if (p.u_ks > 1) off = align_up(off + (size_t)p.u_ks * 32 * d * sizeof(float), 256);
+    return off;
+}
+
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
                             const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
-                            int dense, float* y, char* ws, hipStream_t s) {
-    (void)dense;
-    uint16_t* Ht = reinterpret_cast<uint16_t*>(ws + pl.off_H);
+                            float* y, char* ws, hipStream_t s) {
+    uint4* Hf = reinterpret_cast<uint4*>(ws + pl.off_H);
     const int tiles = (f.F + 31) / 32;
     const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
     const uint16_t* Wu = static_cast<const uint16_t*>(f.w_up);
     if (f.act == PI_ACT_REGLU)
-        hipLaunchKernelGGL((k_union_up<true>), dim3(tiles), dim3(UN_NW * 64), 0, s, x, B, Wg, Wu,
-                           f.d, f.F, idx, count, token_mask, Ht);
+        hipLaunchKernelGGL((k_union_up<true>), dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu,
+                           f.d, f.F, idx, count, token_mask, Hf);
     else
-        hipLaunchKernelGGL((k_union_up<false>), dim3(tiles), dim3(UN_NW * 64), 0, s, x, B, Wg, Wu,
-                           f.d, f.F, idx, count, token_mask, Ht);
+        hipLaunchKernelGGL((k_union_up<false>), dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu,
+                           f.d, f.F, idx, count, token_mask, Hf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nslices = (f.d + 31) / 32;
-    const int blocks = (nslices + 15) / 16 * 16;
-    hipLaunchKernelGGL(k_union_down, dim3(blocks), dim3(UN_NW * 64), 0, s, Ht, B,
-                       static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, nslices, y);
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_UNION;
+    float* part = reinterpret_cast<float*>(ws + pl.off_upart);
+    hipLaunchKernelGGL(k_union_down, dim3(pl.u_ncg * pl.u_ks), dim3(DN_NWU * 64), 0, s, Hf, B,
+                       static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, pl.u_ncg,
+                       pl.u_ks, part, cnt, y);
     return hipGetLastError();
 }
 

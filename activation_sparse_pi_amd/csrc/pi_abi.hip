@@ -199,7 +199,7 @@ int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B, const int32_
     if (B == 1) {
         e = launch_ffn_b1(*ffn, pl, x, idx, count, 0, y, static_cast<char*>(ws), s);
     } else {
-        e = launch_ffn_union(*ffn, pl, x, B, idx, count, token_mask, 0, y, static_cast<char*>(ws), s);
+        e = launch_ffn_union(*ffn, pl, x, B, idx, count, token_mask, y, static_cast<char*>(ws), s);
     }
     if (e != hipSuccess) return hip_fail(e, "pi_sparse_ffn launch");
     return ok();

@@ -31,6 +31,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -54,6 +56,9 @@ def parse():
     return ap.parse_args()
 
 
+parse_defaults = {"steps": 5440, "warmup": 1088}
+
+
 # ------------------------------------------------------------------------------- byte accounting
 def bytes_model(cfg, n):
     """Algorithmic bytes of one step with n active neurons.
@@ -74,6 +79,20 @@ def bytes_model(cfg, n):
     c = n * d * wb + F / 8 + 8 * n + 4 * d
     up = m_up * n * d * wb + 2 * d + 8 * n
     return dict(A=a, B=b, C=c, up=up, total=a + b + c)
+
+
+def bytes_model_batch(cfg, n_tok, U):
+    """Algorithmic bytes of one batch step (B tokens, per-token active counts n_tok,
+    union size U).  Predictor: 2dr + 2rF + 4F + B*2d (x) + B*F/8 (masks) + 4*sum(n) (tables).
+    Union compaction: B*F/8 + 4U.  Union FFN (the two MFMA kernels): the U gathered rows of
+    each matrix, m*U*d*2 (m = 3 for ReGLU, 2 for ReLU), x B*2d, the union table twice 8U,
+    the masks B*F/8, H written and read 2*B*U*2, y 4*B*d."""
+    d, F, r, B = cfg.d, cfg.F, cfg.r, cfg.B
+    m = 3 if cfg.act == "reglu" else 2
+    pred = 2 * d * r + 2 * r * F + 4 * F + B * 2 * d + B * F / 8 + 4 * float(np.sum(n_tok))
+    comp = B * F / 8 + 4 * U
+    ffn = m * U * d * 2 + B * 2 * d + 8 * U + B * F / 8 + 4 * B * U + 4 * B * d
+    return dict(pred=pred, compact=comp, ffn=ffn, total=pred + comp + ffn)
 
 
 def src_sha() -> str:
@@ -122,6 +141,122 @@ def cpu_baseline(inputs, budget_s):
                       f"numpy float64, {dt:.1f} s"}
 
 
+# ------------------------------------------------------------------------------- batch path
+def cpu_baseline_batch(inputs, budget_s):
+    import oracle.pi_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = O.Weights.from_inputs(inputs)
+    X = inputs["x"]                      # [T, B, d]
+    T, B = X.shape[0], X.shape[1]
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s and n < T * B:
+        O.token_step(inputs, W, X[(n // B) % T, n % B])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} tokens of step 0 onwards, each through its own predicted "
+                      f"neuron list (what the union path computes per token), numpy float64, "
+                      f"{dt:.1f} s"}
+
+
+def bench_batch(a, cfg):
+    """Small-batch decode: one step = pi_predict(B) -> pi_compact(UNION) -> pi_sparse_ffn(B)
+    over one batch of B independent tokens (the union FFN runs on MFMA)."""
+    import torch
+
+    from activation_sparse_pi_amd.layer import DeviceLayer
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    inputs = gen.make(cfg)
+    B, T = cfg.B, cfg.T
+    K = a.steps if a.steps != parse_defaults["steps"] else 640
+    Wm = a.warmup if a.warmup != parse_defaults["warmup"] else 64
+    xd = torch.from_numpy(inputs["x"].copy()).to(dev)                    # [T, B, d] in HBM
+    probe = bytes_model_batch(cfg, np.full(B, cfg.mean_rate * cfg.F), 0.6 * cfg.F)
+    R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
+    layer = DeviceLayer(inputs, replicas=R, B_max=B, device=dev)
+    bufs = layer.buffers(B)
+    # per-step active counts and union sizes (replicas are identical)
+    n_tok = np.zeros((T, B)); U = np.zeros(T)
+    for t in range(T):
+        layer.batch_step(xd[t].data_ptr(), B, bufs, logits=False)
+        n_tok[t] = bufs["count"][:B].cpu().numpy()
+        U[t] = int(bufs["ucount"][0].item())
+
+    def step(s, ev=None):
+        t, rep = s % T, s % R
+        xp = xd[t].data_ptr()
+        layer.predict(xp, B, None, bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
+                      bufs["count"].data_ptr(), rep)
+        layer.compact(bufs["mask"].data_ptr(), B, 1, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr())
+        if ev is not None:
+            ev[0].record()
+        layer.sparse_ffn(xp, B, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr(),
+                         bufs["mask"].data_ptr(), bufs["y"].data_ptr(), rep)
+        if ev is not None:
+            ev[1].record()
+
+    for s in range(Wm):
+        step(s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(K):
+        step(Wm + s, ev[s])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ffn_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    steps = (Wm + np.arange(K)) % T
+    ffn_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["ffn"] for t in steps]))
+    path_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["total"] for t in steps]))
+    ms_per_step = total_ms / K
+    achieved = ffn_bytes / (float(ffn_ms.mean()) * 1e-3) / 1e9
+    path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
+    kernel_key = f"k_union_up[{cfg.act}] + k_union_down {cfg.name}"
+    out = {
+        "metric": f"sparse-FFN decode tokens/sec at batch {B} (union path) + effective HBM GB/s (% of peak)",
+        "value": round(K * B / (total_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one FFN layer, d={cfg.d}, ffn={cfg.F}, {cfg.act}, fp16 weights, "
+                        f"fp32 accumulate, predictor rank {cfg.r}, batch {B} independent tokens per "
+                        f"step, {T}-step stream, union FFN on MFMA",
+            "batch": B, "d": cfg.d, "ffn": cfg.F, "rank": cfg.r, "replicas": R,
+            "mean_active_per_token": round(float(n_tok.mean()), 1),
+            "mean_union": round(float(U.mean()), 1),
+            "launch": "three ABI calls per step from Python (pi_predict, pi_compact, pi_sparse_ffn)",
+        },
+        "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": round(path_bytes)},
+        "roofline": {
+            "bound": "hbm", "kernel": kernel_key,
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(kernel_key),
+            "avg_us": round(float(ffn_ms.mean()) * 1e3, 3),
+            "bytes_per_launch": round(ffn_bytes),
+            "mfma_tflops": round((3 if cfg.act == "reglu" else 2) * 2 * B * U[steps].mean() * cfg.d
+                                 / (float(ffn_ms.mean()) * 1e-3) / 1e12, 1),
+        },
+    }
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline_batch(inputs, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------------------- main
 def main():
     a = parse()
@@ -140,7 +275,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = configs.get(a.config)
     if cfg.B != 1:
-        raise SystemExit("bench.py times the batch-1 path; batch configs are parity cases")
+        return bench_batch(a, cfg)
     dev = torch.device("cuda:0")
     inputs = gen.make(cfg)
     probe = bytes_model(cfg, cfg.mean_rate * cfg.F)

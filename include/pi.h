@@ -151,8 +151,8 @@ int pi_compact(const uint32_t* mask, int B, int F, int mode,
  *   y          : fp32 [B, d], overwritten (an empty list gives exactly 0)
  * Accumulation is fp32; B > 1 runs on MFMA with h rounded to fp16 and takes fp16
  * weights only (int4 at B > 1 returns PI_ERR_UNSUPPORTED).  The B > 1 path keeps H in
- * the workspace (32 * F fp16 past the counters; pi_workspace_bytes with B_max > 1
- * includes it).                                                                          */
+ * the workspace (2 KB per 32 neurons of F) with the down product's partial sums
+ * (up to 16 * 32 * d fp32); pi_workspace_bytes with B_max > 1 includes both.           */
 int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B,
                   const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
                   float* y, void* ws, size_t ws_bytes, void* stream);

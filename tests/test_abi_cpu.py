@@ -58,7 +58,7 @@ def test_status_strings_and_version():
 def test_workspace_bytes():
     n = L.pi_workspace_bytes(pred(), ffn(), 1)
     assert n > 0 and n % 256 == 0
-    # batch > 1 adds the fp16 H buffer [32, F] of the union path
+    # batch > 1 adds the union path's H fragments (2 KB per 32 neurons) and partial sums
     assert L.pi_workspace_bytes(None, ffn(), 32) >= L.pi_workspace_bytes(None, ffn(), 1) + 32 * 4096 * 2
     assert L.pi_workspace_bytes(pred(), ffn(), 32) >= n
     assert L.pi_workspace_bytes(pred(), ffn(), 0) == 0
