@@ -172,8 +172,17 @@ PI_DEV int block_exclusive_scan(int v, int* s_tmp, int* total) {
 template <bool COHERENT>
 PI_DEV uint32_t mask_word(const uint32_t* mask, int nrows, int stride, int w, int W, int F) {
     uint32_t v = 0;
-    for (int b = 0; b < nrows; ++b)
-        v |= COHERENT ? ld_agent(mask + (size_t)b * stride + w) : mask[(size_t)b * stride + w];
+    // the rows' words in groups of 16 independent loads (one memory round trip per group)
+    for (int b0 = 0; b0 < nrows; b0 += 16) {
+        uint32_t t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t* p = mask + (size_t)(b0 + i) * stride + w;
+            t[i] = b0 + i < nrows ? (COHERENT ? ld_agent(p) : *p) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v |= t[i];
+    }
     if (w == W - 1 && (F & 31)) v &= (1u << (F & 31)) - 1u;
     return v;
 }

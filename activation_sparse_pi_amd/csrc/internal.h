@@ -28,8 +28,13 @@ struct PredPlan {
     int nbz;      // tokens whose z is staged in LDS at a time (stage 2)
     size_t lds2;  // stage-2 dynamic LDS
     size_t off_z, bytes;
+    // 1 < B <= 32 (MFMA stages): stage-1 row tiles of 32, shares of d, share partial sums
+    int b_ntile, b_nks;
+    size_t off_zpart;
 };
 PredPlan plan_pred(int d, int r, int F, int B);
+// appends the batch predictor's workspace to p from offset off (advanced in place)
+void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off);
 
 // ---- batch-1 FFN launch plan ----------------------------------------------------------------------
 struct FfnPlan {
@@ -65,6 +70,11 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
 hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                           float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
                           char* ws, hipStream_t s);
+
+// 1 < B <= 32: stage 1 and stage 2 with threshold and mask words (no neuron tables)
+hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
+                                int B, float theta, float* logits, uint32_t* mask, char* ws,
+                                hipStream_t s);
 
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                               float* z, hipStream_t s);

@@ -7,11 +7,6 @@
 // Each token still uses its own mask: a neuron outside token b's mask contributes
 // nothing to y[b] (its h is zeroed before the down product).
 //
-// v_mfma_f32_32x32x16_f16 (gfx950) lane layout, checked on the device:
-//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + j], j < 8
-//   B (16 x 32): lane l holds B[8 * (l / 32) + j][l % 32]
-//   D (32 x 32): lane l, register r holds D[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32]
-//
 // Global loads are always whole 128-byte lines spread over 8 lanes (16 bytes each);
 // operands reach the MFMA layout through a wave-private LDS area (XOR-swizzled so
 // that neither the staging writes nor the operand reads conflict).  No block barrier
@@ -32,23 +27,15 @@
 //         to LDS; then 4 K-steps x 2 column tiles of MFMA.  The waves meet in LDS; with
 //         KS > 1 the shares meet in the workspace and the last-arriving block of the
 //         column group adds them in a fixed order (bitwise reproducible).
-#include "device_common.h"
 #include "internal.h"
+#include "mfma_tile.h"
 
 namespace pi {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int UP_NW = 8;      // waves per up block
 constexpr int DN_NWU = 8;     // waves per down block
 constexpr int DN_COLS = 64;   // columns per down block
-
-PI_DEV f32x16_t mfma16(const uint4& a, const uint4& b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-}
 
 PI_DEV bool bit_of(const uint32_t* __restrict__ mask, int W, int b, int i) {
     return (mask[(size_t)b * W + (i >> 5)] >> (i & 31)) & 1u;
@@ -66,15 +53,15 @@ __global__ __launch_bounds__(UP_NW * 64) void k_union_up(
     const uint16_t* __restrict__ Wu, int d, int F, const int32_t* __restrict__ uidx,
     const int32_t* __restrict__ ucount, const uint32_t* __restrict__ tmask,
     uint4* __restrict__ Hf) {
-    constexpr int NP = GLU ? 3 : 2;                   // staged pieces per run: x, up [, gate]
-    __shared__ uint4 s_st[UP_NW][NP][32][8];          // per wave: piece, row, swizzled 16-B slot
+    constexpr int NM = GLU ? 2 : 1;                   // weight matrices: up [, gate]
+    __shared__ uint4 s_st[UP_NW][NM + 1][32][8];      // per wave: x, up [, gate] staging
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int U = min(*ucount, F);
     const int tile = blockIdx.x;
     if (tile * 32 >= U) return;                       // whole block: past the union
 
-    // loader role: load q (0..3) of a run brings row 8q + lrow, 16-byte chunk lch
-    const int lrow = lane >> 3, lch = lane & 7;
+    // loader slot q (0..3) of a run brings row 8q + lane/8 of the tile and of x
+    const int lrow = lane >> 3;
     long long offw[4], offx[4];                       // element offsets, -1 = zero row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -85,61 +72,23 @@ __global__ __launch_bounds__(UP_NW * 64) void k_union_up(
         const int tok = 8 * q + lrow;
         offx[q] = tok < B ? (long long)tok * d : -1;
     }
-    // MFMA role: A row / B column mi, k-slot half
-    const int mi = lane & 31, half = lane >> 5;
     const int nrun = (d + 63) / 64, per = (nrun + UP_NW - 1) / UP_NW;
     const int r0 = min(nrun, wave * per), r1 = min(nrun, r0 + per);
-    uint4(*st)[32][8] = s_st[wave];
-
-    f32x16_t cu = {}, cg = {};
-    uint4 ra[NP][4], rb[NP][4];
-    auto load = [&](int rr, uint4(&v)[NP][4]) {
-        const int e = rr * 64 + lch * 8;
-        const bool ok = e < d;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v[0][q] = (ok && offx[q] >= 0) ? ld16(x + offx[q] + e) : zero4();
-            v[1][q] = (ok && offw[q] >= 0) ? ld16(Wu + offw[q] + e) : zero4();
-            if constexpr (GLU) v[2][q] = (ok && offw[q] >= 0) ? ld16(Wg + offw[q] + e) : zero4();
-        }
-    };
-    // row r = 8q + lrow keeps chunk c in slot c ^ (r % 8)
-    auto stage = [&](const uint4(&v)[NP][4]) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) st[p][8 * q + lrow][lch ^ lrow] = v[p][q];
-    };
-    // k-step s takes chunk 2s + half of row mi: k-slot 8 half + j <-> element 16 s + 8 half + j
-    auto compute = [&]() {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int slot = (2 * s + half) ^ (mi & 7);
-            const uint4 bx = st[0][mi][slot];
-            cu = mfma16(st[1][mi][slot], bx, cu);
-            if constexpr (GLU) cg = mfma16(st[2][mi][slot], bx, cg);
-        }
-    };
-    // two register sets: the run after next is in flight while one run is consumed
-    if (r0 < r1) load(r0, ra);
-    if (r0 + 1 < r1) load(r0 + 1, rb);
-    for (int rr = r0; rr < r1; rr += 2) {
-        stage(ra);
-        if (rr + 2 < r1) load(rr + 2, ra);
-        compute();
-        if (rr + 1 < r1) {
-            stage(rb);
-            if (rr + 3 < r1) load(rr + 3, rb);
-            compute();
-        }
+    f32x16_t acc[NM] = {};
+    if constexpr (GLU) {
+        const uint16_t* const Wm[2] = {Wu, Wg};
+        runs_mfma<2>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
+    } else {
+        const uint16_t* const Wm[1] = {Wu};
+        runs_mfma<1>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
     }
 
     // the waves meet in LDS (each wave's staging area holds its own accumulators)
     float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        red[r * 64 + lane] = cu[r];
-        if constexpr (GLU) red[1024 + r * 64 + lane] = cg[r];
+        red[r * 64 + lane] = acc[0][r];
+        if constexpr (GLU) red[1024 + r * 64 + lane] = acc[1][r];
     }
     __syncthreads();
     if (tid < 128) {
@@ -151,7 +100,8 @@ __global__ __launch_bounds__(UP_NW * 64) void k_union_up(
         float hv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int rg = (2 * gg + h) * 4 + (j & 3), ln = b + 32 * (j >> 2);
+            const int n = gg * 16 + 8 * h + j;
+            const int rg = d_reg(n), ln = d_lane(n, b);
             float a = 0.f, g = 0.f;
 #pragma unroll
             for (int w = 0; w < UP_NW; ++w) {

@@ -147,6 +147,9 @@ PredPlan plan_pred(int d, int r, int F, int B) {
     size_t off = COUNTER_BYTES;
     p.off_z = off;
     off = align_up(off + (size_t)B * r * sizeof(float), 256);
+    p.b_ntile = p.b_nks = 0;
+    p.off_zpart = 0;
+    if (B > 1) plan_pred_batch(p, d, r, F, off);
     p.bytes = off;
     return p;
 }
@@ -154,6 +157,11 @@ PredPlan plan_pred(int d, int r, int F, int B) {
 hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                           float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
                           char* ws, hipStream_t s) {
+    if (B > 1) {
+        hipError_t e = launch_predict_batch(p, pl, x, B, theta, logits, mask, ws, s);
+        if (e != hipSuccess || idx == nullptr) return e;
+        return launch_compact(mask, B, p.F, PI_PER_TOKEN, idx, count, s);
+    }
     unsigned* cnt = reinterpret_cast<unsigned*>(ws);
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     hipError_t e = launch_pred_stage1(p, pl, x, B, z, s);

@@ -1,0 +1,247 @@
+// Low-rank activation predictor for 1 < B <= 32 tokens at once, on MFMA (gfx950).
+//
+// PowerInfer, "Adaptive Sparsity Predictors": l = (x W_p1) W_p2 + b per token; a neuron
+// is predicted active when l > theta.  With B tokens both factors are dense
+// contractions with B columns:
+//   stage 1  z[b, j] = W1t[j, :] . x[b, :]      (W1t = W_p1^T, [r, d] fp16)
+//   stage 2  l[b, i] = W2t[i, :] . z[b, :] + b_i (W2t = W_p2^T, [F, r] fp16)
+// z stays in fp32 between the stages.  Stage 1 multiplies fp16 by fp16 (products exact in
+// fp32, fp32 accumulation).  Stage 2 needs z in fp32 precision on an fp16 MFMA: each token's
+// z is scaled by a power of two 2^e (largest |z| brought into [2^14, 2^15)) and split into
+// z_hi = fp16(z 2^e) and z_lo = fp16(z 2^e - z_hi), which carry z to 22 bits or better;
+// W2t . z_hi + W2t . z_lo is accumulated in fp32 and scaled back by 2^-e (exact).
+//
+//   stage 1  block = 32 rows of W1t x one of KS shares of d; 8 waves split the share in
+//            runs of 64 and stream rows and x through the staged 32 x 32 MFMA tile; the
+//            waves meet in LDS; the shares meet in the workspace, added in a fixed order
+//            by the last-arriving block of the row tile.
+//   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  All of
+//            the block's W2t loads are issued first, then z is scaled, split and staged in
+//            LDS; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
+//            and one wave ballot per 64 neurons of a token gives two mask words.
+#include "internal.h"
+#include "mfma_tile.h"
+
+namespace pi {
+namespace {
+
+constexpr int PB_NW = 8;      // waves per block (both stages)
+constexpr int ZC = 512;       // rank values of z staged per pass in stage 2
+
+// ------------------------------------------------------------------------------------ stage 1
+__global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__ x, int B,
+                                                    const uint16_t* __restrict__ W1t, int d, int r,
+                                                    int ntile, int nks, float* __restrict__ part,
+                                                    unsigned* __restrict__ counter,
+                                                    float* __restrict__ z) {
+    __shared__ uint4 s_st[PB_NW][2][32][8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile = blockIdx.x % ntile, ks = blockIdx.x / ntile;
+    const int lrow = lane >> 3;
+    long long offw[4], offx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = tile * 32 + 8 * q + lrow;
+        offw[q] = j < r ? (long long)j * d : -1;
+        const int tok = 8 * q + lrow;
+        offx[q] = tok < B ? (long long)tok * d : -1;
+    }
+    // this block's share of the runs of 64, then this wave's part of it
+    const int nrun = (d + 63) / 64, pb = (nrun + nks - 1) / nks;
+    const int b0 = min(nrun, ks * pb), b1 = min(nrun, b0 + pb);
+    const int pw = (b1 - b0 + PB_NW - 1) / PB_NW;
+    const int r0 = min(b1, b0 + wave * pw), r1 = min(b1, r0 + pw);
+    f32x16_t acc[1] = {};
+    const uint16_t* const Wm[1] = {W1t};
+    runs_mfma<1>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
+
+    float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) red[q * 64 + lane] = acc[0][q];
+    __syncthreads();
+    // outputs (row n of the tile, token b), two per thread, 32 consecutive rows per token
+    float v[2];
+    int ob[2], oj[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int o = tid + q * PB_NW * 64, b = o >> 5, n = o & 31;
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < PB_NW; ++w)
+            t += reinterpret_cast<const float*>(&s_st[w][0][0][0])[d_reg(n) * 64 + d_lane(n, b)];
+        v[q] = t;
+        ob[q] = b;
+        oj[q] = tile * 32 + n;
+    }
+    if (nks == 1) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (ob[q] < B && oj[q] < r) z[(size_t)ob[q] * r + oj[q]] = v[q];
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        if (ob[q] < B && oj[q] < r) st_agent(&part[((size_t)ks * 32 + ob[q]) * r + oj[q]], v[q]);
+    if (!last_block_arrive(&counter[tile], nks)) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (ob[q] >= B || oj[q] >= r) continue;
+        float t = 0.f;
+        for (int k2 = 0; k2 < nks; ++k2)
+            t += k2 == ks ? v[q] : ld_agent(&part[((size_t)k2 * 32 + ob[q]) * r + oj[q]]);
+        z[(size_t)ob[q] * r + oj[q]] = t;
+    }
+}
+
+// ------------------------------------------------------------------------------------ stage 2
+PI_DEV float absmax4(float m, const float4& v) {
+    return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z, int B,
+                                                    const uint16_t* __restrict__ W2t,
+                                                    const float* __restrict__ bias, int r, int F,
+                                                    float theta, float* __restrict__ logits,
+                                                    uint32_t* __restrict__ mask) {
+    __shared__ uint4 s_z[2][32][ZC / 8];     // z_hi, z_lo: [token][chunk of 8, swizzled]
+    __shared__ uint4 s_w[PB_NW][32][8];      // per wave: W2t staging, then its accumulator
+    __shared__ int s_e[32];                  // per-token exponent e
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 128;
+    const int mt = wave & 3, kh = wave >> 2;
+    const int lrow = lane >> 3, lch = lane & 7, mi = lane & 31, half = lane >> 5;
+    long long offw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = n0 + mt * 32 + 8 * q + lrow;
+        offw[q] = i < F ? (long long)i * r : -1;
+    }
+    // 1. per-token exponent: 16 threads per token
+    {
+        const int b = tid >> 4, sub = tid & 15;
+        float m = 0.f;
+        if (b < B)
+            for (int k = sub * 4; k < r; k += 64)
+                m = absmax4(m, *reinterpret_cast<const float4*>(z + (size_t)b * r + k));
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+        if (sub == 0) {
+            int E = 0;
+            if (m > 0.f) (void)frexpf(m, &E);     // m = f 2^E, f in [0.5, 1)
+            s_e[b] = m > 0.f ? 15 - E : 0;
+        }
+    }
+    f32x16_t acc = {};
+    for (int c0 = 0; c0 < r; c0 += ZC) {
+        // this wave's 4 runs of 64 rank values: all W2t loads in flight at once
+        uint4 wv[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int e = c0 + kh * 256 + rr * 64 + lch * 8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                wv[rr][q] = (e < r && offw[q] >= 0) ? ld16(W2t + offw[q] + e) : zero4();
+        }
+        __syncthreads();                       // s_e ready; previous pass's reads done
+        // 2. stage z_hi / z_lo of this pass: token b, chunks sub + 16 i
+        {
+            const int b = tid >> 4, sub = tid & 15;
+            const int e = s_e[b];
+#pragma unroll
+            for (int i = 0; i < ZC / 128; ++i) {
+                const int ch = sub + 16 * i, k = c0 + 8 * ch;
+                uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+                if (b < B && k < r) {
+                    const float4 a0 = *reinterpret_cast<const float4*>(z + (size_t)b * r + k);
+                    const float4 a1 = *reinterpret_cast<const float4*>(z + (size_t)b * r + k + 4);
+                    const float zz[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float s0 = ldexpf(zz[2 * p], e), s1 = ldexpf(zz[2 * p + 1], e);
+                        const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
+                        const _Float16 l0 = (_Float16)(s0 - (float)h0), l1 = (_Float16)(s1 - (float)h1);
+                        hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                    }
+                }
+                s_z[0][b][ch ^ (b & 7)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                s_z[1][b][ch ^ (b & 7)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            }
+        }
+        __syncthreads();
+        // 3. per run: stage the W2t tile rows, 4 k-steps x (z_hi, z_lo)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s_w[wave][8 * q + lrow][lch ^ lrow] = wv[rr][q];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 a = s_w[wave][mi][(2 * s + half) ^ (mi & 7)];
+                const int zc = (kh * 256 + rr * 64) / 8 + 2 * s + half;
+                acc = mfma16(a, s_z[0][mi][zc ^ (mi & 7)], acc);
+                acc = mfma16(a, s_z[1][mi][zc ^ (mi & 7)], acc);
+            }
+        }
+    }
+    // 4. the two halves of the rank meet in LDS
+    float* red = reinterpret_cast<float*>(&s_w[wave][0][0]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) red[q * 64 + lane] = acc[q];
+    __syncthreads();
+    const int W = (F + 31) >> 5;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int b = wave * 4 + (it >> 1), nh = it & 1;
+        const int n = nh * 64 + lane, i = n0 + n;
+        const int m = n >> 5, nl = n & 31;
+        const float* r0 = reinterpret_cast<const float*>(&s_w[m][0][0]);
+        const float* r1 = reinterpret_cast<const float*>(&s_w[m + 4][0][0]);
+        const int o = d_reg(nl) * 64 + d_lane(nl, b);
+        bool act = false;
+        if (b < B && i < F) {
+            const float l = ldexpf(r0[o] + r1[o], -s_e[b]) + bias[i];
+            act = l > theta;
+            if (logits) logits[(size_t)b * F + i] = l;
+        }
+        const unsigned long long bal = __ballot(act);
+        const int w0 = (n0 + nh * 64) >> 5;
+        if (lane == 0 && b < B) {
+            if (w0 < W) mask[(size_t)b * W + w0] = (uint32_t)bal;
+            if (w0 + 1 < W) mask[(size_t)b * W + w0 + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+}
+
+}  // namespace
+
+void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
+    (void)F;
+    const int nrun = (d + 63) / 64;
+    p.b_ntile = (r + 31) / 32;
+    int ks = (128 + p.b_ntile - 1) / p.b_ntile;        // >= 128 stage-1 blocks
+    if (ks > 16) ks = 16;
+    if (ks > nrun) ks = nrun;
+    if (ks < 1 || p.b_ntile > 256) ks = 1;              // one arrival counter per row tile
+    p.b_nks = ks;
+    p.off_zpart = off;
+    if (ks > 1) off = align_up(off + (size_t)ks * 32 * r * sizeof(float), 256);
+}
+
+hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
+                                int B, float theta, float* logits, uint32_t* mask, char* ws,
+                                hipStream_t s) {
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_PRED1;
+    float* z = reinterpret_cast<float*>(ws + pl.off_z);
+    float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
+    hipLaunchKernelGGL(k_pb1, dim3(pl.b_ntile * pl.b_nks), dim3(PB_NW * 64), 0, s, x, B, p.w_p1t,
+                       p.d, p.r, pl.b_ntile, pl.b_nks, part, cnt, z);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_pb2, dim3((p.F + 127) / 128), dim3(PB_NW * 64), 0, s, z, B, p.w_p2t,
+                       p.bias, p.r, p.F, theta, logits, mask);
+    return hipGetLastError();
+}
+
+}  // namespace pi

@@ -1,0 +1,83 @@
+// 32 x 32 MFMA tiles over rows of fp16 matrices, fed through a wave-private LDS area.
+//
+// v_mfma_f32_32x32x16_f16 (gfx950) lane layout, checked on the device:
+//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + j], j < 8
+//   B (16 x 32): lane l holds B[8 * (l / 32) + j][l % 32]
+//   D (32 x 32): lane l, register r holds D[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32]
+// The k slots of one MFMA may be any permutation shared by A and B.
+#pragma once
+
+#include "device_common.h"
+
+namespace pi {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+PI_DEV f32x16_t mfma16(const uint4& a, const uint4& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// D[n][b] of a 32 x 32 accumulator: register and lane
+PI_DEV int d_reg(int n) { return (n >> 3) * 4 + (n & 3); }
+PI_DEV int d_lane(int n, int b) { return b + 32 * ((n >> 2) & 1); }
+
+// acc[m] += W_m[rows] . x[rows]^T over runs [r0, r1) of 64 elements of d-element rows.
+// Rows are given per loader slot: load q (0..3) of a run brings row 8q + lane/8 (element
+// offsets offw[q] into every W_m, offx[q] into x; -1 = a zero row), 16 bytes at chunk
+// lane % 8 of the run, so every global load is 8 full 128-byte lines.  st is the wave's
+// staging area, [NM + 1][32][8] units of 16 bytes: row r keeps chunk c in slot c ^ (r % 8),
+// which leaves both the staging writes and the operand reads free of bank conflicts.
+// Two register sets keep the run after next in flight while one run is consumed.
+template <int NM>
+PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4],
+                      const uint16_t* const (&W)[NM], const long long (&offw)[4], int d, int r0,
+                      int r1, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
+    constexpr int NP = NM + 1;
+    const int lane = threadIdx.x & 63;
+    const int lrow = lane >> 3, lch = lane & 7;
+    const int mi = lane & 31, half = lane >> 5;
+    uint4 ra[NP][4], rb[NP][4];
+    auto load = [&](int rr, uint4(&v)[NP][4]) {
+        const int e = rr * 64 + lch * 8;
+        const bool ok = e < d;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[0][q] = (ok && offx[q] >= 0) ? ld16(x + offx[q] + e) : zero4();
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                v[m + 1][q] = (ok && offw[q] >= 0) ? ld16(W[m] + offw[q] + e) : zero4();
+        }
+    };
+    auto stage = [&](const uint4(&v)[NP][4]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) st[p][8 * q + lrow][lch ^ lrow] = v[p][q];
+    };
+    // k-step s takes chunk 2s + half of row mi: k-slot 8 half + j <-> element 16 s + 8 half + j
+    auto compute = [&]() {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int slot = (2 * s + half) ^ (mi & 7);
+            const uint4 bx = st[0][mi][slot];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[m] = mfma16(st[m + 1][mi][slot], bx, acc[m]);
+        }
+    };
+    if (r0 < r1) load(r0, ra);
+    if (r0 + 1 < r1) load(r0 + 1, rb);
+    for (int rr = r0; rr < r1; rr += 2) {
+        stage(ra);
+        if (rr + 2 < r1) load(rr + 2, ra);
+        compute();
+        if (rr + 1 < r1) {
+            stage(rb);
+            if (rr + 3 < r1) load(rr + 3, rb);
+            compute();
+        }
+    }
+}
+
+}  // namespace pi

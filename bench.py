@@ -82,14 +82,15 @@ def bytes_model(cfg, n):
 
 
 def bytes_model_batch(cfg, n_tok, U):
-    """Algorithmic bytes of one batch step (B tokens, per-token active counts n_tok,
-    union size U).  Predictor: 2dr + 2rF + 4F + B*2d (x) + B*F/8 (masks) + 4*sum(n) (tables).
+    """Algorithmic bytes of one batch step (B tokens, union size U; n_tok, the per-token
+    active counts, is not needed: the step writes no per-token tables).
+    Predictor: 2dr + 2rF + 4F + B*2d (x) + B*F/8 (masks).
     Union compaction: B*F/8 + 4U.  Union FFN (the two MFMA kernels): the U gathered rows of
     each matrix, m*U*d*2 (m = 3 for ReGLU, 2 for ReLU), x B*2d, the union table twice 8U,
     the masks B*F/8, H written and read 2*B*U*2, y 4*B*d."""
     d, F, r, B = cfg.d, cfg.F, cfg.r, cfg.B
     m = 3 if cfg.act == "reglu" else 2
-    pred = 2 * d * r + 2 * r * F + 4 * F + B * 2 * d + B * F / 8 + 4 * float(np.sum(n_tok))
+    pred = 2 * d * r + 2 * r * F + 4 * F + B * 2 * d + B * F / 8
     comp = B * F / 8 + 4 * U
     ffn = m * U * d * 2 + B * 2 * d + 8 * U + B * F / 8 + 4 * B * U + 4 * B * d
     return dict(pred=pred, compact=comp, ffn=ffn, total=pred + comp + ffn)
@@ -165,8 +166,8 @@ def cpu_baseline_batch(inputs, budget_s):
 
 
 def bench_batch(a, cfg):
-    """Small-batch decode: one step = pi_predict(B) -> pi_compact(UNION) -> pi_sparse_ffn(B)
-    over one batch of B independent tokens (the union FFN runs on MFMA)."""
+    """Small-batch decode: one step = pi_predict(B, masks only) -> pi_compact(UNION) ->
+    pi_sparse_ffn(B) over one batch of B independent tokens (the union FFN runs on MFMA)."""
     import torch
 
     from activation_sparse_pi_amd.layer import DeviceLayer
@@ -192,8 +193,8 @@ def bench_batch(a, cfg):
     def step(s, ev=None):
         t, rep = s % T, s % R
         xp = xd[t].data_ptr()
-        layer.predict(xp, B, None, bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
-                      bufs["count"].data_ptr(), rep)
+        # masks only: the union FFN needs the per-token masks and their union list
+        layer.predict(xp, B, None, bufs["mask"].data_ptr(), None, None, rep)
         layer.compact(bufs["mask"].data_ptr(), B, 1, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr())
         if ev is not None:
             ev[0].record()

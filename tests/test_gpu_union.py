@@ -162,3 +162,69 @@ def test_union_c4_sampled():
                             ffn_tokens=[0, 5, 9, 14, 18, 23, 27, 31])
         say(f"[gpu] c4 t={t}: union {g['uidx'].size} of {cfg.F}, "
             f"mean per-token {np.mean([len(i) for i in g['idx']]):.0f}, worst rel-L2 {worst:.2e}")
+
+
+PRED_CASES = [
+    configs.tiny("relu", "f16", d=640, F=1000, r=1040, B=4, T=1, seed=31),     # 3 passes of the rank
+    configs.tiny("relu", "f16", d=8, F=8, r=8, B=32, T=1, seed=32, mean_rate=0.5),
+    configs.tiny("relu", "f16", d=1032, F=2056, r=96, B=17, T=1, seed=33),
+]
+
+
+def _predict_only(cfg, inp, B, want_idx=True):
+    """pi_predict at batch B straight through the C ABI (predictor weights only)."""
+    from activation_sparse_pi_amd import _lib as L
+    dev = torch.device("cuda")
+    w1 = torch.from_numpy(np.ascontiguousarray(inp["w_p1"].T)).to(dev)
+    w2 = torch.from_numpy(np.ascontiguousarray(inp["w_p2"].T)).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    x = torch.from_numpy(inp["x"][0].copy()).to(dev)
+    pred = L.PredDesc(w1.data_ptr(), w2.data_ptr(), bias.data_ptr(), cfg.d, cfg.r, cfg.F, 0.5)
+    nb = L.pi_workspace_bytes(pred, None, B)
+    assert nb > 0, L.pi_last_error()
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    L.check(L.pi_workspace_init(ws.data_ptr(), nb, stream))
+    W = (cfg.F + 31) // 32
+    logits = torch.empty((B, cfg.F), dtype=torch.float32, device=dev)
+    mask = torch.full((B, W), -1, dtype=torch.int32, device=dev)
+    idx = torch.full((B, cfg.F), -7, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(B, dtype=torch.int32, device=dev)
+    for _ in range(2):                          # twice: counters and partials are reused
+        L.check(L.pi_predict(pred, x.data_ptr(), B, logits.data_ptr(), mask.data_ptr(),
+                             idx.data_ptr() if want_idx else None,
+                             cnt.data_ptr() if want_idx else None, ws.data_ptr(), nb, stream))
+    torch.cuda.synchronize()
+    c = _np(cnt)
+    lists = [_np(idx[b, :c[b]]).astype(np.int64) for b in range(B)] if want_idx else None
+    return _np(logits), _np(mask).view(np.uint32), lists
+
+
+@pytest.mark.parametrize("cfg", PRED_CASES, ids=lambda c: f"{c.name}_b{c.B}")
+def test_predict_batch(cfg):
+    say(f"[gpu] batch predictor {cfg.name} B={cfg.B}")
+    inp = gen.make(cfg, ffn=False)
+    X = inp["x"][0]
+    lg, mk, lists = _predict_only(cfg, inp, cfg.B)
+    ref = O.predictor_logits(X, inp["w_p1"], inp["w_p2"], inp["bias"])
+    assert np.max(np.abs(lg - ref)) < 5e-5
+    for b in range(cfg.B):
+        P.check_index_set(lists[b], mk[b], ref[b], cfg.F, ctx=f"b={b}")
+
+
+def test_predict_batch_c5_shape():
+    """The batch predictor at the largest rank of the workloads (d=8192, r=1024,
+    F=28672), 32 tokens, masks only (no neuron tables)."""
+    import dataclasses
+    cfg = dataclasses.replace(configs.C5, B=32, T=1)
+    say(f"[gpu] batch predictor at {cfg.name} shape, B=32")
+    inp = gen.make(cfg, ffn=False)
+    X = inp["x"][0]
+    lg, mk, _ = _predict_only(cfg, inp, 32, want_idx=False)
+    ref = O.predictor_logits(X, inp["w_p1"], inp["w_p2"], inp["bias"])
+    err = np.max(np.abs(lg - ref))
+    say(f"[gpu] c5-shape batch predictor max |dl| {err:.2e}")
+    assert err < 5e-5
+    for b in range(32):
+        gpu_active = O.words_to_active(mk[b], cfg.F)
+        P.check_index_set(O.compact(gpu_active), mk[b], ref[b], cfg.F, ctx=f"b={b}")
