@@ -52,6 +52,13 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        try:
+            # torch ships its own HIP runtime (file libamdhip64.so, soname libamdhip64.so.7);
+            # loading it first lets libpi.so's libamdhip64.so.7 bind to that same copy, so
+            # the process holds one HIP runtime whatever the import order
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         L.pi_status_string.argtypes, L.pi_status_string.restype = [c_int], ctypes.c_char_p

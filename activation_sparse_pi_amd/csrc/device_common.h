@@ -187,50 +187,36 @@ PI_DEV uint32_t mask_word(const uint32_t* mask, int nrows, int stride, int w, in
     return v;
 }
 
+// Ascending ids of the set bits of the OR of nrows masks (F bits each, row stride `stride`
+// words) -> out[0 .. count).  Rounds of blockDim.x words, one word per thread; after the
+// block scan each wave writes its words' ids two words at a time (lanes 0-31 one word,
+// 32-63 the next, lane = bit), so a store instruction covers up to 64 consecutive ids.
 template <bool COHERENT>
 PI_DEV void block_compact(const uint32_t* mask, int nrows, int stride, int F, int32_t* out,
                           int32_t* count, int* s_tmp) {
-    constexpr int PERMAX = 8;   // words kept in registers per thread
     const int W = (F + 31) >> 5;
-    const int per = (W + (int)blockDim.x - 1) / (int)blockDim.x;
-    const int w0 = threadIdx.x * per;
-    uint32_t wr[PERMAX];
-    int c = 0;
-    if (per <= PERMAX) {
-#pragma unroll
-        for (int i = 0; i < PERMAX; ++i)    // all loads issued before any is used
-            wr[i] = (i < per && w0 + i < W) ? mask_word<COHERENT>(mask, nrows, stride, w0 + i, W, F) : 0u;
-#pragma unroll
-        for (int i = 0; i < PERMAX; ++i) c += __popc(wr[i]);
-    } else {
-        for (int i = 0; i < per; ++i)
-            if (w0 + i < W) c += __popc(mask_word<COHERENT>(mask, nrows, stride, w0 + i, W, F));
-    }
-    int total;
-    int pos = block_exclusive_scan(c, s_tmp, &total);
-    if (per <= PERMAX) {
-#pragma unroll
-        for (int i = 0; i < PERMAX; ++i) {
-            uint32_t v = wr[i];            // zero past this thread's words
-            while (v) {
-                const int b = __ffs(v) - 1;
-                out[pos++] = ((w0 + i) << 5) + b;
-                v &= v - 1u;
-            }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bit = lane & 31, sel = lane >> 5;
+    int base = 0;
+    for (int r0 = 0; r0 < W; r0 += (int)blockDim.x) {
+        const int w = r0 + (int)threadIdx.x;
+        const uint32_t v = w < W ? mask_word<COHERENT>(mask, nrows, stride, w, W, F) : 0u;
+        int total;
+        const int pos = base + block_exclusive_scan(__popc(v), s_tmp, &total);
+        const int wb = r0 + wave * 64;            // this wave's first word
+        for (int j = 0; j < 64; j += 2) {
+            const uint32_t v0 = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+            const uint32_t v1 = (uint32_t)__builtin_amdgcn_readlane((int)v, j + 1);
+            if ((v0 | v1) == 0u) continue;        // wave-uniform
+            const int p0 = __builtin_amdgcn_readlane(pos, j);
+            const int p1 = __builtin_amdgcn_readlane(pos, j + 1);
+            const uint32_t vv = sel ? v1 : v0;
+            if ((vv >> bit) & 1u)
+                out[(sel ? p1 : p0) + __popc(vv & ((1u << bit) - 1u))] = ((wb + j + sel) << 5) + bit;
         }
-    } else {
-        for (int i = 0; i < per; ++i) {
-            const int w = w0 + i;
-            if (w >= W) break;
-            uint32_t v = mask_word<COHERENT>(mask, nrows, stride, w, W, F);
-            while (v) {
-                const int b = __ffs(v) - 1;
-                out[pos++] = (w << 5) + b;
-                v &= v - 1u;
-            }
-        }
+        base += total;
     }
-    if (threadIdx.x == 0) *count = total;
+    if (threadIdx.x == 0) *count = base;
 }
 
 // ---- predictor stage 2 on one 64-neuron tile (blocks of NW waves) ------------------------------

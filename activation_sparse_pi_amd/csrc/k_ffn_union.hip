@@ -241,14 +241,27 @@ __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
     for (int q = 0; q < 4; ++q)
         if (ob[q] < B && oc[q] < d) st_agent(&part[((size_t)ks * 32 + ob[q]) * d + oc[q]], v[q]);
     if (!last_block_arrive(&counter[cgi], nks)) return;
+    // the other shares' partials, up to 16 loads in flight per round, added in share order
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nks; k0 += 4) {
+        float pv[4][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (ob[q] >= B || oc[q] >= d) continue;
-        float t = 0.f;
-        for (int k2 = 0; k2 < nks; ++k2)
-            t += k2 == ks ? v[q] : ld_agent(&part[((size_t)k2 * 32 + ob[q]) * d + oc[q]]);
-        y[(size_t)ob[q] * d + oc[q]] = t;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k2 = k0 + i;
+                pv[q][i] = (k2 < nks && k2 != ks && ob[q] < B && oc[q] < d)
+                               ? ld_agent(&part[((size_t)k2 * 32 + ob[q]) * d + oc[q]]) : 0.f;
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (k0 + i < nks) t[q] += k0 + i == ks ? v[q] : pv[q][i];
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (ob[q] < B && oc[q] < d) y[(size_t)ob[q] * d + oc[q]] = t[q];
 }
 
 }  // namespace

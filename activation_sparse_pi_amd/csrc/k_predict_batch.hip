@@ -83,12 +83,21 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
     for (int q = 0; q < 2; ++q)
         if (ob[q] < B && oj[q] < r) st_agent(&part[((size_t)ks * 32 + ob[q]) * r + oj[q]], v[q]);
     if (!last_block_arrive(&counter[tile], nks)) return;
+    // every share's partials in flight at once (nks <= 16), added in share order
+    float pv[2][16];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2)
+            pv[q][k2] = (k2 < nks && k2 != ks && ob[q] < B && oj[q] < r)
+                            ? ld_agent(&part[((size_t)k2 * 32 + ob[q]) * r + oj[q]]) : 0.f;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         if (ob[q] >= B || oj[q] >= r) continue;
         float t = 0.f;
-        for (int k2 = 0; k2 < nks; ++k2)
-            t += k2 == ks ? v[q] : ld_agent(&part[((size_t)k2 * 32 + ob[q]) * r + oj[q]]);
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2)
+            if (k2 < nks) t += k2 == ks ? v[q] : pv[q][k2];
         z[(size_t)ob[q] * r + oj[q]] = t;
     }
 }
@@ -116,25 +125,9 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
         const int i = n0 + mt * 32 + 8 * q + lrow;
         offw[q] = i < F ? (long long)i * r : -1;
     }
-    // 1. per-token exponent: 16 threads per token
-    {
-        const int b = tid >> 4, sub = tid & 15;
-        float m = 0.f;
-        if (b < B)
-            for (int k = sub * 4; k < r; k += 64)
-                m = absmax4(m, *reinterpret_cast<const float4*>(z + (size_t)b * r + k));
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-        if (sub == 0) {
-            int E = 0;
-            if (m > 0.f) (void)frexpf(m, &E);     // m = f 2^E, f in [0.5, 1)
-            s_e[b] = m > 0.f ? 15 - E : 0;
-        }
-    }
-    f32x16_t acc = {};
-    for (int c0 = 0; c0 < r; c0 += ZC) {
-        // this wave's 4 runs of 64 rank values: all W2t loads in flight at once
-        uint4 wv[4][4];
+    // W2t loads of one pass of the rank: this wave's 4 runs of 64, all in flight at once
+    uint4 wv[4][4];
+    auto load_w = [&](int c0) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int e = c0 + kh * 256 + rr * 64 + lch * 8;
@@ -142,33 +135,58 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
             for (int q = 0; q < 4; ++q)
                 wv[rr][q] = (e < r && offw[q] >= 0) ? ld16(W2t + offw[q] + e) : zero4();
         }
-        __syncthreads();                       // s_e ready; previous pass's reads done
-        // 2. stage z_hi / z_lo of this pass: token b, chunks sub + 16 i
-        {
-            const int b = tid >> 4, sub = tid & 15;
-            const int e = s_e[b];
+    };
+    // z of one pass: token b = tid / 16 holds chunks sub + 16 i (8 values each), i < 4
+    const int b = tid >> 4, sub = tid & 15;
+    float4 zr[2 * (ZC / 128)];
+    auto load_z = [&](int c0) {
 #pragma unroll
-            for (int i = 0; i < ZC / 128; ++i) {
-                const int ch = sub + 16 * i, k = c0 + 8 * ch;
-                uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
-                if (b < B && k < r) {
-                    const float4 a0 = *reinterpret_cast<const float4*>(z + (size_t)b * r + k);
-                    const float4 a1 = *reinterpret_cast<const float4*>(z + (size_t)b * r + k + 4);
-                    const float zz[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        for (int i = 0; i < ZC / 128; ++i) {
+            const int k = c0 + 8 * (sub + 16 * i);
+            const bool ok = b < B && k < r;
+            const float* p = z + (size_t)b * r + k;
+            zr[2 * i] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+            zr[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    load_w(0);
+    // 1. per-token exponent e: the largest |z| of the token brought into [2^14, 2^15)
+    float m = 0.f;
+    for (int c0 = 0; c0 < r; c0 += ZC) {       // a rank of at most ZC leaves its z in zr
+        load_z(c0);
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const float s0 = ldexpf(zz[2 * p], e), s1 = ldexpf(zz[2 * p + 1], e);
-                        const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
-                        const _Float16 l0 = (_Float16)(s0 - (float)h0), l1 = (_Float16)(s1 - (float)h1);
-                        hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                        lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-                    }
-                }
-                s_z[0][b][ch ^ (b & 7)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-                s_z[1][b][ch ^ (b & 7)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        for (int i = 0; i < 2 * (ZC / 128); ++i) m = absmax4(m, zr[i]);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    int E = 0;
+    if (m > 0.f) (void)frexpf(m, &E);           // m = f 2^E, f in [0.5, 1)
+    const int ez = m > 0.f ? 15 - E : 0;
+    if (sub == 0) s_e[b] = ez;
+    f32x16_t acc = {};
+    for (int c0 = 0; c0 < r; c0 += ZC) {
+        if (c0 > 0) load_w(c0);
+        if (r > ZC) load_z(c0);
+        __syncthreads();                       // previous pass's reads done
+        // 2. stage z_hi / z_lo of this pass
+#pragma unroll
+        for (int i = 0; i < ZC / 128; ++i) {
+            const int ch = sub + 16 * i;
+            const float zz[8] = {zr[2 * i].x, zr[2 * i].y, zr[2 * i].z, zr[2 * i].w,
+                                 zr[2 * i + 1].x, zr[2 * i + 1].y, zr[2 * i + 1].z, zr[2 * i + 1].w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float s0 = ldexpf(zz[2 * p], ez), s1 = ldexpf(zz[2 * p + 1], ez);
+                const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
+                const _Float16 l0 = (_Float16)(s0 - (float)h0), l1 = (_Float16)(s1 - (float)h1);
+                hi[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                lo[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
             }
+            s_z[0][b][ch ^ (b & 7)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            s_z[1][b][ch ^ (b & 7)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
         __syncthreads();
         // 3. per run: stage the W2t tile rows, 4 k-steps x (z_hi, z_lo)
@@ -193,23 +211,23 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     const int W = (F + 31) >> 5;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const int b = wave * 4 + (it >> 1), nh = it & 1;
+        const int tb = wave * 4 + (it >> 1), nh = it & 1;
         const int n = nh * 64 + lane, i = n0 + n;
         const int m = n >> 5, nl = n & 31;
         const float* r0 = reinterpret_cast<const float*>(&s_w[m][0][0]);
         const float* r1 = reinterpret_cast<const float*>(&s_w[m + 4][0][0]);
-        const int o = d_reg(nl) * 64 + d_lane(nl, b);
+        const int o = d_reg(nl) * 64 + d_lane(nl, tb);
         bool act = false;
-        if (b < B && i < F) {
-            const float l = ldexpf(r0[o] + r1[o], -s_e[b]) + bias[i];
+        if (tb < B && i < F) {
+            const float l = ldexpf(r0[o] + r1[o], -s_e[tb]) + bias[i];
             act = l > theta;
-            if (logits) logits[(size_t)b * F + i] = l;
+            if (logits) logits[(size_t)tb * F + i] = l;
         }
         const unsigned long long bal = __ballot(act);
         const int w0 = (n0 + nh * 64) >> 5;
-        if (lane == 0 && b < B) {
-            if (w0 < W) mask[(size_t)b * W + w0] = (uint32_t)bal;
-            if (w0 + 1 < W) mask[(size_t)b * W + w0 + 1] = (uint32_t)(bal >> 32);
+        if (lane == 0 && tb < B) {
+            if (w0 < W) mask[(size_t)tb * W + w0] = (uint32_t)bal;
+            if (w0 + 1 < W) mask[(size_t)tb * W + w0 + 1] = (uint32_t)(bal >> 32);
         }
     }
 }

@@ -112,7 +112,7 @@ def test_predict_validation(kw, code):
     (dict(desc=ffn(w_down=A + 4)), L.PI_ERR_ALIGN),
     (dict(B=2, token_mask=None), L.PI_ERR_NULL),
     (dict(B=2, token_mask=A, desc=ffn(wfmt=L.PI_W_I4G128, s_up=A, s_down=A)), L.PI_ERR_UNSUPPORTED),
-    (dict(B=32, token_mask=A, wsb=L.pi_workspace_bytes(None, ffn(), 1)), L.PI_ERR_WORKSPACE),
+    (dict(B=32, token_mask=A, wsb="batch1"), L.PI_ERR_WORKSPACE),
     (dict(token_mask=A), L.PI_ERR_SHAPE),
     (dict(idx=None), L.PI_ERR_NULL),
     (dict(count=None), L.PI_ERR_NULL),
@@ -124,6 +124,8 @@ def test_sparse_ffn_validation(kw, code):
     a = dict(desc=ffn(), x=A + 0x3000000, B=1, idx=A + 0x5000000, count=A + 0x6000000,
              token_mask=None, y=A + 0x7000000, ws=WS, wsb=WSB)
     a.update(kw)
+    if a["wsb"] == "batch1":     # sized for batch 1 only (evaluated here, not at collection)
+        a["wsb"] = L.pi_workspace_bytes(None, ffn(), 1)
     st = L.pi_sparse_ffn(a["desc"], a["x"], a["B"], a["idx"], a["count"], a["token_mask"], a["y"],
                          a["ws"], a["wsb"], None)
     assert st == code, L.pi_last_error()
