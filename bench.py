@@ -119,6 +119,19 @@ def traffic_from_profiles(kernel_key: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def copy_probe(mb, dev):
+    """Three plain device copies of mb MiB: the reference dispatches for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of the same run."""
+    if not mb:
+        return
+    import torch
+    src = torch.empty(mb << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(inputs, budget_s):
     import numpy as np
@@ -223,6 +236,7 @@ def bench_batch(a, cfg):
     achieved = ffn_bytes / (float(ffn_ms.mean()) * 1e-3) / 1e9
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
     kernel_key = f"k_union_up[{cfg.act}] + k_union_down {cfg.name}"
+    copy_probe(a.copy_probe_mb, dev)
     out = {
         "metric": f"sparse-FFN decode tokens/sec at batch {B} (union path) + effective HBM GB/s (% of peak)",
         "value": round(K * B / (total_ms / 1e3), 1),
@@ -383,12 +397,7 @@ def main():
                   else f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}")
     traffic = traffic_from_profiles(kernel_key)
 
-    if a.copy_probe_mb:
-        src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    copy_probe(a.copy_probe_mb, dev)
 
     out = {
         "metric": "sparse-FFN decode tokens/sec at batch 1 + effective HBM GB/s (% of peak)",
