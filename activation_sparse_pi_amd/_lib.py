@@ -18,6 +18,7 @@ PI_ERR_UNSUPPORTED, PI_ERR_WORKSPACE, PI_ERR_HIP = 5, 6, 7
 PI_ACT_RELU, PI_ACT_REGLU = 0, 1
 PI_W_F16, PI_W_I4G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
+PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS = 0, 1, 2
 PI_MAX_BATCH = 32
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
@@ -82,8 +83,8 @@ def lib() -> ctypes.CDLL:
                                   c_size_t, c_void_p]
         L.pi_ffn_down.restype = c_int
         L.pi_decode_run.argtypes = [P(PredDesc), P(FfnDesc), c_int, c_void_p, c_int,
-                                    ctypes.c_longlong, c_int, c_void_p, c_void_p, c_void_p,
-                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                    ctypes.c_longlong, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.pi_decode_run.restype = c_int
         L.pi_ffn_dense_ref_gpu.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p,
                                            c_size_t, c_void_p]
@@ -136,12 +137,13 @@ def pi_ffn_down(ffn, idx, count, h, y, ws, ws_bytes, stream) -> int:
     return lib().pi_ffn_down(_p(ffn), idx, count, h, y, ws, ws_bytes, stream)
 
 
-def pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mask, idx, count, y, events,
-                  ws, ws_bytes, stream) -> int:
-    """preds / ffns: ctypes arrays of PredDesc / FfnDesc; events: ctypes array of
-    hipEvent_t handles (c_void_p) or None."""
-    return lib().pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mask, idx, count, y,
-                               events, ws, ws_bytes, stream)
+def pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count, y, events,
+                  kernel_events, ws, ws_bytes, stream) -> int:
+    """preds / ffns: ctypes arrays of PredDesc / FfnDesc; events: ctypes array of two
+    hipEvent_t handles (c_void_p) or None; kernel_events: ctypes array of 2*nsteps
+    handles or None."""
+    return lib().pi_decode_run(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count, y,
+                               events, kernel_events, ws, ws_bytes, stream)
 
 
 def pi_ffn_dense_ref_gpu(ffn, x, B, y, ws, ws_bytes, stream) -> int:

@@ -109,21 +109,26 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const size_t rb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
     for (int it0 = wave * IPW; it0 < items; it0 += B_WAVES * IPW) {
         uint4 wr[IPW][Q];
-        float sc[IPW][Q];
+        uint32_t sr[IPW][Q];   // raw fp16 scales, one per register
+        // Every load is issued unconditionally, from chunk 0 of the row (row 0 for an empty
+        // slot) where a lane has nothing to read, and its value is discarded at use: a load
+        // guarded by a branch is waited for at the end of the branch, which would turn the
+        // round's loads into one memory round trip each.
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int it = it0 + i;
             const bool valid = it < items;
             const int k = GLU ? (it >> 1) : it;
             const int mat = GLU ? (it & 1) : 1;        // 0 = gate, 1 = up
-            const size_t row = valid ? (size_t)(tile * 64 + s_list[k]) : 0;
+            const size_t row = valid ? (size_t)(tile * 64 + s_list[k < 64 ? k : 63]) : 0;
             const uint8_t* base = static_cast<const uint8_t*>(mat ? Wu : Wg) + row * rb;
+            const uint16_t* sbase = WF == 1 ? (mat ? Su : Sg) + row * G : nullptr;
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
                 const int c = lane + 64 * q;
-                const bool ok = valid && c < nc;
-                wr[i][q] = ok ? ld16(base + 16 * (size_t)c) : zero4();
-                if (WF == 1) sc[i][q] = ok ? h2f((mat ? Su : Sg)[row * G + (c >> 2)]) : 0.f;
+                const int cc = c < nc ? c : 0;
+                wr[i][q] = ld16(base + 16 * (size_t)cc);
+                if (WF == 1) sr[i][q] = (uint32_t)sbase[cc >> 2];
             }
         }
 #pragma unroll
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
                             const uint4 t = s_x[4 * c + m];
                             xp[4 * m] = t.x; xp[4 * m + 1] = t.y; xp[4 * m + 2] = t.z; xp[4 * m + 3] = t.w;
                         }
-                        dot = fmaf(dot32_i4(wr[i][q], xp), sc[i][q], dot);
+                        dot = fmaf(dot32_i4(wr[i][q], xp), h2f((uint16_t)sr[i][q]), dot);
                     }
                 }
             }
@@ -245,26 +250,25 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     for (int v = 0; v < Gm::V; ++v) acc[v] = 0.f;
     float soff = 0.f;
     for (int k0 = wave; k0 < n_loc; k0 += DN_NW * U) {
-        float hv[U], sv[U];
+        float hv[U];
+        uint32_t sr[U];        // raw fp16 scales, one per register
         uint4 w16[U];
         uint2 w8[U];
+        // unconditional loads (row 0 / column 0 where there is nothing to read; the value is
+        // zeroed at use): a branch-guarded load would be waited for at the end of its branch
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + u * DN_NW;
-            hv[u] = 0.f;
-            sv[u] = 0.f;
-            if (WF == 0) w16[u] = zero4(); else w8[u] = make_uint2(0u, 0u);
-            if (k < n_loc) {
-                const size_t row = (size_t)__builtin_amdgcn_readfirstlane(s_ids[k]);
-                hv[u] = h[row];
-                if (cok) {
-                    if (WF == 0) {
-                        w16[u] = ld16(Wb + row * rowb + boff);
-                    } else {
-                        w8[u] = *reinterpret_cast<const uint2*>(Wb + row * rowb + boff);
-                        sv[u] = h2f(Sd[row * G + sg]);
-                    }
-                }
+            const bool valid = k < n_loc;
+            const size_t row = valid ? (size_t)__builtin_amdgcn_readfirstlane(s_ids[k < DEC_IDCAP ? k : 0]) : 0;
+            const size_t off = row * rowb + (cok ? boff : 0);
+            const float hr = h[row];
+            hv[u] = valid && cok ? hr : 0.f;
+            if (WF == 0) {
+                w16[u] = ld16(Wb + off);
+            } else {
+                w8[u] = *reinterpret_cast<const uint2*>(Wb + off);
+                sr[u] = (uint32_t)Sd[row * G + (cok ? sg : 0)];
             }
         }
 #pragma unroll
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
                     acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
                 }
             } else {
-                const float hs = hv[u] * sv[u];
+                const float hs = hv[u] * h2f((uint16_t)sr[u]);
                 soff += hs;
                 const uint32_t ws[2] = {w8[u].x, w8[u].y};
 #pragma unroll

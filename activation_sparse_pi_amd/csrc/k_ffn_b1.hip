@@ -118,23 +118,27 @@ __global__ __launch_bounds__(256) void k_up_i4(const uint16_t* __restrict__ x,
         }
         const size_t row = (size_t)irow;
         uint4 wu[Q], wg[Q];
-        float su[Q], sg[Q];
+        uint32_t su[Q], sg[Q];   // raw fp16 scales, one per register
+        // unconditional loads (chunk 0 where a lane has nothing to read, discarded at use):
+        // a branch-guarded load is waited for at the end of its branch
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int c = lane + 64 * q;
-            const bool ok = c < nc;
-            wu[q] = ok ? ld16(Uq + row * rb + 16 * c) : zero4();
-            su[q] = ok ? h2f(Us[row * G + (c >> 2)]) : 0.f;
+            const int cc = c < nc ? c : 0;
+            wu[q] = ld16(Uq + row * rb + 16 * cc);
+            su[q] = Us[row * G + (cc >> 2)];
             if (GLU) {
-                wg[q] = ok ? ld16(Gq + row * rb + 16 * c) : zero4();
-                sg[q] = ok ? h2f(Gs[row * G + (c >> 2)]) : 0.f;
+                wg[q] = ld16(Gq + row * rb + 16 * cc);
+                sg[q] = Gs[row * G + (cc >> 2)];
             }
         }
         float au = 0.f, ag = 0.f;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            au = fmaf(dot32_i4(wu[q], xp[q]), su[q], au);
-            if (GLU) ag = fmaf(dot32_i4(wg[q], xp[q]), sg[q], ag);
+            if (lane + 64 * q < nc) {
+                au = fmaf(dot32_i4(wu[q], xp[q]), h2f((uint16_t)su[q]), au);
+                if (GLU) ag = fmaf(dot32_i4(wg[q], xp[q]), h2f((uint16_t)sg[q]), ag);
+            }
         }
         au = wave_sum(au);
         if (GLU) ag = wave_sum(ag);
@@ -251,31 +255,35 @@ __global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
     float soff = 0.f;
     for (int k0 = split * NW + wave; k0 < n; k0 += stride * U) {
         uint4 w[U];
-        float hs[U];
+        float hr[U];
+        uint32_t sr[U];          // raw fp16 scales, one per register
+        bool ok[U];
+        // unconditional loads (row 0 / column 0 where there is nothing to read, zeroed at
+        // use): a branch-guarded load is waited for at the end of its branch
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kk = k0 + u * stride;
-            const int irow = (kk < n && cok) ? (dense_F > 0 ? kk : idx[kk]) : -1;
-            if ((unsigned)irow < (unsigned)F) {
-                const size_t row = (size_t)irow;
-                w[u] = ld16(Dq + row * rb + 16 * c);
-                hs[u] = h[kk] * h2f(Ds[row * G + (c >> 2)]);
-            } else {
-                w[u] = zero4();
-                hs[u] = 0.f;
-            }
+            const bool in = kk < n;
+            const int irow = in ? (dense_F > 0 ? kk : idx[kk]) : 0;
+            ok[u] = in && cok && (unsigned)irow < (unsigned)F;
+            const size_t row = ok[u] ? (size_t)irow : 0;
+            const int cc = cok ? c : 0;
+            w[u] = ld16(Dq + row * rb + 16 * cc);
+            sr[u] = Ds[row * G + (cc >> 2)];
+            hr[u] = h[in ? kk : 0];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            soff += hs[u];
+            const float hsu = ok[u] ? hr[u] * h2f((uint16_t)sr[u]) : 0.f;
+            soff += hsu;
             const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    acc[8 * m + 2 * b] = fmaf(hs[u], (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
-                    acc[8 * m + 2 * b + 1] = fmaf(hs[u], (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
+                    acc[8 * m + 2 * b] = fmaf(hsu, (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
+                    acc[8 * m + 2 * b + 1] = fmaf(hsu, (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
                 }
             }
         }

@@ -1,6 +1,7 @@
 // C ABI of the predictor-gated sparse FFN: host-side validation, workspace
 // planning and launches.  Every check runs before the first HIP call, so an
 // invalid request enqueues nothing and leaves the outputs untouched.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -135,7 +136,9 @@ size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int 
         }
     }
     if (pred && ffn && pred->d == ffn->d && pred->F == ffn->F) {
-        const size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
+        size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
+        if (b > need) need = b;
+        b = plan_run(pred->d, pred->r, pred->F, ffn->wfmt, 512).bytes;   // independent of the grid
         if (b > need) need = b;
     }
     return need;
@@ -232,12 +235,15 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
 }
 
 int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
-                  int T, long long s0, int nsteps, uint32_t* mask, int32_t* idx, int32_t* count,
-                  float* y, void* const* events, void* ws, size_t ws_bytes, void* stream) {
+                  int T, long long s0, int nsteps, int mode, uint32_t* mask, int32_t* idx,
+                  int32_t* count, float* y, void* const* events, void* const* kernel_events,
+                  void* ws, size_t ws_bytes, void* stream) {
     int st;
     if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
     if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
     if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
+    if (mode != PI_RUN_AUTO && mode != PI_RUN_PERSISTENT && mode != PI_RUN_KERNELS)
+        return fail(PI_ERR_DTYPE, "unknown run mode %d", mode);
     if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
     if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
     if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
@@ -250,25 +256,102 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
             return fail(PI_ERR_SHAPE, "replica %d does not match replica 0 / its ffn", i);
     }
     if (preds[0].F > 131072) return fail(PI_ERR_UNSUPPORTED, "pi_decode_run supports F <= 131072");
-    if (events)
+    if (events && (!events[0] || !events[1])) return fail(PI_ERR_NULL, "events must hold two events");
+    if (kernel_events) {
+        if (mode == PI_RUN_PERSISTENT) return fail(PI_ERR_SHAPE, "kernel_events need the three-kernel schedule");
         for (int i = 0; i < 2 * nsteps; ++i)
-            if (!events[i]) return fail(PI_ERR_NULL, "events[%d] is NULL", i);
-    const DecPlan pl = plan_decode(preds[0].d, preds[0].r, preds[0].F, ffns[0].wfmt);
-    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+            if (!kernel_events[i]) return fail(PI_ERR_NULL, "kernel_events[%d] is NULL", i);
+    }
+    const int d = preds[0].d, r = preds[0].r, F = preds[0].F;
+    const int act = ffns[0].act, wfmt = ffns[0].wfmt;
+    // persistent launch when the shape fits it (and the device holds the whole grid at once)
+    // PI_RUN_AUTO takes the three-kernel schedule: on MI355X every hand-off inside the
+    // persistent launch costs more than a kernel boundary (measured on all five workloads)
+    bool persistent = false;
+    RunPlan rp{};
+    if (mode == PI_RUN_PERSISTENT) {
+        const RunPlan probe = plan_run(d, r, F, wfmt, 512);
+        const int G = run_grid(wfmt, act, probe.q, probe.lds);
+        if (G > 0) {
+            rp = plan_run(d, r, F, wfmt, G);
+            persistent = run_fits(rp, d, r, F, wfmt);
+        }
+        if (!persistent)
+            return fail(PI_ERR_UNSUPPORTED, "this layer shape does not fit the persistent decode launch "
+                        "(d=%d r=%d F=%d, %d co-resident blocks)", d, r, F, G);
+    }
+    const DecPlan pl = plan_decode(d, r, F, wfmt);
+    if ((st = check_ws(ws, ws_bytes, persistent ? rp.bytes : pl.bytes)) != PI_OK) return st;
     const double tau = preds[0].threshold;
     const float theta = (float)std::log(tau / (1.0 - tau));
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
-    const int d = preds[0].d;
-    for (int i = 0; i < nsteps; ++i) {
-        const long long g = s0 + i;
-        const int t = (int)(g % T), rep = (int)(g % nrep);
-        hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[2 * i]) : nullptr;
-        hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[2 * i + 1]) : nullptr;
-        hipError_t e = launch_decode_step(preds[rep], ffns[rep], pl, x + (size_t)t * d, theta,
-                                          nullptr, mask, idx, count, y, w, s, e0, e1);
-        if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
+    hipError_t e;
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+        return hip_fail(e, "pi_decode_run start event");
+    if (persistent) {
+        RunArgs ra{};
+        ra.x = x;
+        ra.T = T;
+        ra.d = d;
+        ra.r = r;
+        ra.F = F;
+        ra.act = act;
+        ra.wfmt = wfmt;
+        ra.theta = theta;
+        ra.mask = mask;
+        ra.idx = idx;
+        ra.count = count;
+        ra.y = y;
+        ra.ws = w;
+        ra.pl = rp;
+        auto fill = [&](int slot, int rep) {
+            RunRep& R = ra.rep[slot];
+            R.w1t = preds[rep].w_p1t;
+            R.w2t = preds[rep].w_p2t;
+            R.bias = preds[rep].bias;
+            R.wg = ffns[rep].w_gate;
+            R.wu = ffns[rep].w_up;
+            R.wd = ffns[rep].w_down;
+            R.sg = ffns[rep].s_gate;
+            R.su = ffns[rep].s_up;
+            R.sd = ffns[rep].s_down;
+        };
+        // up to RUN_NTAB replicas fit one launch's table; more are walked in launches of
+        // RUN_NTAB steps whose table lists the replicas of exactly those steps
+        const bool whole = nrep <= RUN_NTAB;
+        if (whole) {
+            for (int i = 0; i < nrep; ++i) fill(i, i);
+            ra.tabn = nrep;
+        }
+        const int chunk = whole ? RUN_MAX_STEPS : RUN_NTAB;
+        for (long long i = 0; i < nsteps; i += chunk) {
+            const long long g0 = s0 + i;
+            const int L = (int)std::min<long long>(chunk, nsteps - i);
+            ra.g0 = g0;
+            ra.L = L;
+            if (whole) {
+                ra.e0 = (int)(g0 % nrep);
+            } else {
+                for (int j = 0; j < L; ++j) fill(j, (int)((g0 + j) % nrep));
+                ra.e0 = 0;
+                ra.tabn = L;
+            }
+            if ((e = launch_run(ra, s)) != hipSuccess) return hip_fail(e, "pi_decode_run persistent launch");
+        }
+    } else {
+        for (int i = 0; i < nsteps; ++i) {
+            const long long g = s0 + i;
+            const int t = (int)(g % T), rep = (int)(g % nrep);
+            hipEvent_t k0 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i]) : nullptr;
+            hipEvent_t k1 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i + 1]) : nullptr;
+            e = launch_decode_step(preds[rep], ffns[rep], pl, x + (size_t)t * d, theta, nullptr, mask,
+                                   idx, count, y, w, s, k0, k1);
+            if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
+        }
     }
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
+        return hip_fail(e, "pi_decode_run end event");
     return ok();
 }
 

@@ -89,20 +89,27 @@ class DeviceLayer:
         L.check(L.pi_ffn_dense_ref_gpu(self.ffn[rep], x, B, y, self.ws.data_ptr(), self.ws_bytes,
                                        self.stream()))
 
-    def decode_run(self, x, T: int, s0: int, nsteps: int, bufs: dict, events=None) -> None:
-        """Enqueue nsteps fused batch-1 steps from native code (token (s0+i) % T, replica
-        (s0+i) % R).  events: None or a list of 2*nsteps recorded torch.cuda.Event objects."""
+    def decode_run(self, x, T: int, s0: int, nsteps: int, bufs: dict, events=None,
+                   mode: int = L.PI_RUN_AUTO, kernel_events=None) -> None:
+        """Enqueue nsteps batch-1 steps from native code (token (s0+i) % T, replica
+        (s0+i) % R).  events: None or two torch.cuda.Event objects recorded around the
+        enqueued work; kernel_events: None or 2*nsteps events attached to the stage-2
+        kernel of every step (three-kernel schedule).  Events must have been recorded
+        once already (torch creates the HIP event on first record).
+        mode: PI_RUN_AUTO / PI_RUN_KERNELS / PI_RUN_PERSISTENT."""
         import ctypes
         if not hasattr(self, "_pred_arr"):
             self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
             self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
-        ev = None
-        if events is not None:
-            ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+
+        def handles(evs):
+            return None if evs is None else (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+
         L.check(L.pi_decode_run(self._pred_arr, self._ffn_arr, self.replicas, x, T, s0, nsteps,
-                                bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
+                                mode, bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
                                 bufs["count"].data_ptr(), bufs["y"].data_ptr(),
-                                ev, self.ws.data_ptr(), self.ws_bytes, self.stream()))
+                                handles(events), handles(kernel_events), self.ws.data_ptr(),
+                                self.ws_bytes, self.stream()))
 
     def step(self, x, bufs: dict, rep: int = 0, logits: bool = True) -> None:
         """One batch-1 decode step: predict + compact (fused), then the sparse FFN.

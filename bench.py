@@ -1,10 +1,11 @@
 """Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
 
 One step = one batch-1 decode token through the whole hot path of one FFN
-layer: predictor stage 1 + stage 2 with fused threshold and neuron-table
-compaction (pi_predict), the row operator over the active up/gate rows
-(pi_ffn_up) and the column operator over the active down rows (pi_ffn_down).
-Tokens are consumed strictly one after another (no batching across tokens).
+layer: predictor stage 1 and stage 2 with the strict threshold, the neuron
+table, the row operator over the predicted-active up/gate rows and the column
+operator over their down rows.  Tokens are consumed strictly one after another:
+a step starts only when the previous step's y is complete (no batching across
+tokens).
 
 Default workload: the LLaMA-7B-shaped ReGLU layer (d=4096, ffn=11008, predictor
 rank 256, fp16 weights, fp32 accumulation, Zipf(1.2) rates with a 5% hot set,
@@ -13,11 +14,17 @@ and token s uses replica s mod R, standing in for the distinct layers of a real
 model: the touched bytes of consecutive steps never share cache lines, so they
 come from HBM and not from the 256 MB Infinity Cache.
 
-The token loop is captured once in a HIP graph (through torch.cuda.CUDAGraph)
-and replayed; inputs are resident in HBM before the timed region starts.
-Events around every pi_ffn_up launch inside the graph give the dominant
-kernel's average duration; its algorithmic bytes (the active rows, x, the
-neuron table and h) over that duration give the roofline fraction.
+Modes (--mode): "kernels" (default) enqueues the K timed steps with one
+pi_decode_run call, three kernels per step; "persistent" runs the same call as one
+cooperative launch (slower on MI355X: its in-launch hand-offs cost more than kernel
+boundaries); "eager" makes one Python call per ABI function.  Inputs are resident in
+HBM before the timed region starts; two events recorded on the library's stream
+around the enqueued steps time them.  The roofline figure is the stage-2 kernel (the
+one that moves the most bytes): its algorithmic bytes over its average duration,
+taken in a second pass over the same stream in which that kernel of every step
+carries its own start/end events (those events slow the step down, so the headline
+value comes from the first pass, which has none).  In persistent mode the launch is
+the only kernel and its bytes over its duration are the roofline figure.
 
 Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
@@ -47,9 +54,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1088)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to bust the caches")
-    ap.add_argument("--mode", choices=("native", "graph", "eager"), default="native",
-                    help="native: one pi_decode_run call enqueues the timed steps (default); "
-                         "graph: torch HIP-graph replay; eager: one Python call per kernel")
+    ap.add_argument("--mode", choices=("kernels", "persistent", "eager"), default="kernels",
+                    help="kernels: one pi_decode_run call, three kernels per step (default); "
+                         "persistent: one pi_decode_run call, one cooperative launch; "
+                         "eager: one Python call per ABI function")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget, 0 = skip")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling runs)")
@@ -61,24 +69,21 @@ parse_defaults = {"steps": 5440, "warmup": 1088}
 
 # ------------------------------------------------------------------------------- byte accounting
 def bytes_model(cfg, n):
-    """Algorithmic bytes of one step with n active neurons.
-
-    Whole step: predictor weights 2dr + 2rF, bias 4F, active rows m*n*d*w_b (m = 3 for
-    ReGLU, 2 for ReLU; w_b = 2 for fp16, 0.5 + 2/128 for int4 with its scales), x 2d,
-    y 4d, the neuron table 4n and the mask F/8.  Per kernel of the fused step:
-      A (stage-1 partials): 2dr + 2d;
-      B (stage 2 + up/gate of the active rows): 2rF + 4F + (m-1)*n*d*w_b + 2d + F/8 + 4n;
-      C (down from the mask, neuron table): n*d*w_b + F/8 + 4n (h) + 4n (table) + 4d.
-    Per kernel of the unfused operators: up = (m-1)*n*d*w_b + 2d + 8n.
-    """
+    """Algorithmic bytes of one batch-1 step with n active neurons: predictor weights
+    2dr + 2rF, bias 4F, the active rows m*n*d*w_b (m = 3 for ReGLU, 2 for ReLU; w_b = 2
+    for fp16, 0.5 + 2/128 for int4 with its scales), x 2d, y 4d, the mask F/8 and the
+    neuron table 4n.  (The unfused up operator alone: (m-1)*n*d*w_b + 2d + 8n.)"""
     d, F, r = cfg.d, cfg.F, cfg.r
     wb = 2.0 if cfg.wfmt == "f16" else 0.5 + 2.0 / 128.0
-    m_up = 2 if cfg.act == "reglu" else 1
-    a = 2 * d * r + 2 * d
-    b = 2 * r * F + 4 * F + m_up * n * d * wb + 2 * d + F / 8 + 4 * n
-    c = n * d * wb + F / 8 + 8 * n + 4 * d
-    up = m_up * n * d * wb + 2 * d + 8 * n
-    return dict(A=a, B=b, C=c, up=up, total=a + b + c)
+    m = 3 if cfg.act == "reglu" else 2
+    pred = 2 * d * r + 2 * r * F + 4 * F
+    ffn = m * n * d * wb
+    total = pred + ffn + 2 * d + 4 * d + F / 8 + 4 * n
+    up = (m - 1) * n * d * wb + 2 * d + 8 * n
+    # the stage-2 kernel of the three-kernel step: W2t + bias, z, x, the up (and gate) rows of
+    # the active neurons, the mask words and h written
+    stage2 = 2 * r * F + 4 * F + 4 * r + 2 * d + (m - 1) * n * d * wb + F / 8 + 4 * n
+    return dict(pred=pred, ffn=ffn, up=up, stage2=stage2, total=total)
 
 
 def bytes_model_batch(cfg, n_tok, U):
@@ -284,6 +289,7 @@ def main():
     import numpy as np
     import torch
 
+    from activation_sparse_pi_amd import _lib as L
     from activation_sparse_pi_amd.layer import DeviceLayer
     from synth import configs, gen
 
@@ -307,8 +313,6 @@ def main():
         layer.predict(xd[t].data_ptr(), 1, None, mask, idx, cnt)
         counts[t] = int(bufs["count"][0].item())
 
-    L = R * math.ceil(T / R)            # graph length: whole replica cycles, phase-continuous
-
     def step(s, ev=None):
         t, rep = s % T, s % R
         xp = xd[t].data_ptr()
@@ -321,81 +325,63 @@ def main():
         layer.ffn_down(idx, cnt, h, y, rep)
 
     K, Wm = a.steps, a.warmup
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if a.mode == "native":
-        # timed region: one native call enqueues all K fused steps; the stage-2 + up kernel
-        # of every step (the one that moves the most bytes) carries its own start/end events
-        ev_up = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
-        for e in ev_up:                        # materialise the events before handing them over
+    up_ms = []
+    if a.mode in ("persistent", "kernels"):
+        mode = L.PI_RUN_PERSISTENT if a.mode == "persistent" else L.PI_RUN_KERNELS
+        layer.decode_run(xd.data_ptr(), T, 0, Wm, bufs, mode=mode)            # untimed warmup
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in ev:                 # torch creates the HIP event on first record
             e.record()
-        layer.decode_run(xd.data_ptr(), T, 0, Wm, bufs)          # untimed warmup
         torch.cuda.synchronize()
-        t0.record()
-        layer.decode_run(xd.data_ptr(), T, Wm, K, bufs, events=ev_up)
-        t1.record()
+        layer.decode_run(xd.data_ptr(), T, Wm, K, bufs, events=ev, mode=mode)  # timed: K steps
         torch.cuda.synchronize()
-        up_ms = [ev_up[2 * i].elapsed_time(ev_up[2 * i + 1]) for i in range(K)]
-        ev_steps = timed_steps = [Wm + i for i in range(K)]
-    elif a.mode == "eager":
+        total_ms = ev[0].elapsed_time(ev[1])
+        if a.mode == "kernels":
+            # roofline pass: the stage-2 kernel of every step carries its own start/end events
+            Kr = min(K, 1088)
+            kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
+            for e in kev:
+                e.record()
+            torch.cuda.synchronize()
+            layer.decode_run(xd.data_ptr(), T, Wm + K, Kr, bufs, mode=mode, kernel_events=kev)
+            torch.cuda.synchronize()
+            up_ms = [kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(Kr)]
+            roof_steps = (Wm + K + np.arange(Kr)) % T
+    else:
         for s in range(Wm):
             step(s)
         ev_up = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(K)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record()
         for s in range(K):
             step(Wm + s, ev_up[s])
         t1.record()
         torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
         up_ms = [e0.elapsed_time(e1) for e0, e1 in ev_up]
-        ev_steps = timed_steps = [Wm + s for s in range(K)]
-    else:                                       # graph: whole-step throughput only
-        for s in range(Wm):
-            step(s)
-        nfull, tail = divmod(K, L)
-        s_cap = torch.cuda.Stream(dev)
-        s_cap.wait_stream(torch.cuda.current_stream(dev))
-        graphs = []
-        with torch.cuda.stream(s_cap):
-            for length in (L, tail):
-                g = None
-                if length:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=s_cap):
-                        for s in range(length):
-                            step(Wm + s)
-                graphs.append(g)
-        torch.cuda.current_stream(dev).wait_stream(s_cap)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(nfull):
-            graphs[0].replay()
-        if tail:
-            graphs[1].replay()
-        t1.record()
-        torch.cuda.synchronize()
-        up_ms = []
-        ev_steps = []
-        timed_steps = [Wm + s for s in range(L)] * nfull + [Wm + s for s in range(tail)]
-    total_ms = t0.elapsed_time(t1)
+    timed = (Wm + np.arange(K)) % T
     ms_per_step = total_ms / K
     tok_s = K / (total_ms / 1e3)
-
-    dom = "B" if a.mode == "native" else "up"
-    if up_ms:
-        n_ev = counts[np.array(ev_steps) % T].astype(np.float64)
-        up_bytes = float(np.mean(bytes_model(cfg, n_ev)[dom]))
-        up_avg_ms = float(np.mean(up_ms))
-        achieved = up_bytes / (up_avg_ms * 1e-3) / 1e9
-    else:
-        up_bytes = up_avg_ms = achieved = float("nan")
-    n_all = counts[np.array(timed_steps) % T]
-    path_bytes = float(np.mean(bytes_model(cfg, n_all.astype(np.float64))["total"]))
+    n_all = counts[timed].astype(np.float64)
+    bm = bytes_model(cfg, n_all)
+    path_bytes = float(np.mean(bm["total"]))
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
-
-    kernel_key = (f"k_dec_stage2_up[{cfg.wfmt},{cfg.act}] {cfg.name}" if dom == "B"
-                  else f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}")
-    traffic = traffic_from_profiles(kernel_key)
+    ffn_gbs = float(np.mean(bm["ffn"])) / (ms_per_step * 1e-3) / 1e9
+    if a.mode == "persistent":
+        # the launch is the whole path: its bytes (K steps) over its duration
+        kernel_key = f"k_run[{cfg.wfmt},{cfg.act}] {cfg.name}"
+        launch_bytes, launch_ms = path_bytes * K, total_ms
+    elif a.mode == "eager":
+        kernel_key = f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}"
+        launch_bytes, launch_ms = float(np.mean(bm["up"])), float(np.mean(up_ms))
+    else:
+        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act}] {cfg.name}"
+        launch_bytes = float(np.mean(bytes_model(cfg, counts[roof_steps].astype(np.float64))["stage2"]))
+        launch_ms = float(np.mean(up_ms))
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(kernel_key) if kernel_key else None
 
     copy_probe(a.copy_probe_mb, dev)
 
@@ -418,20 +404,23 @@ def main():
                         f"{T}-token stream",
             "batch": 1, "d": cfg.d, "ffn": cfg.F, "rank": cfg.r, "replicas": R,
             "mean_active": round(float(counts.mean()), 1),
-            "launch": {"native": "one pi_decode_run call (native loop, events on the up kernel)",
-                       "graph": f"torch HIP graph of {L} steps, replayed",
+            "launch": {"persistent": "one pi_decode_run call: one cooperative launch per run "
+                                     "(per 32 steps when there are more than 32 replicas)",
+                       "kernels": "one pi_decode_run call: three kernels per step",
                        "eager": "one Python call per ABI function"}[a.mode],
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
-                          "bytes_per_step": round(path_bytes)},
+                          "bytes_per_step": round(path_bytes),
+                          "sparse_ffn_GB/s": round(ffn_gbs, 1),
+                          "sparse_ffn_bytes_per_step": round(float(np.mean(bm["ffn"])))},
         "roofline": {
             "bound": "hbm", "kernel": kernel_key,
             "achieved": None if math.isnan(achieved) else round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": None if math.isnan(achieved) else round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_us": None if math.isnan(up_avg_ms) else round(up_avg_ms * 1e3, 3),
-            "bytes_per_launch": None if math.isnan(up_bytes) else round(up_bytes),
+            "avg_us": None if math.isnan(launch_ms) else round(launch_ms * 1e3, 3),
+            "bytes_per_launch": None if math.isnan(launch_bytes) else round(launch_bytes),
         },
     }
     if a.cpu_seconds > 0:

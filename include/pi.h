@@ -178,24 +178,40 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  * Enqueues nsteps consecutive decode steps on `stream` from native code.  Step
  * i uses token x[(s0 + i) % T] (x fp16 [T, d]) and the layer of replica
  * (s0 + i) % nrep (preds[nrep], ffns[nrep]: layers of one shape, e.g. the layers
- * of a model or byte-identical copies).  A step is the same computation as
- * pi_predict + pi_sparse_ffn, fused into three kernels:
- *   1. predictor stage 1, z = x W_p1 (one wave per predictor column);
- *   2. per 64-neuron tile: z, logits, strict threshold, mask words, and h of the
- *      tile's own predicted-active neurons (their up/gate rows);
- *   3. the down projection read straight from the mask, which also writes the
- *      ascending neuron table.
+ * of a model or byte-identical copies).  A step is the computation of
+ * pi_predict + pi_sparse_ffn at batch 1 (PowerInfer online engine): predictor,
+ * strict threshold, the neuron table, the row operator on the predicted-active
+ * up/gate rows and the column operator on their down rows.  Steps run strictly one
+ * after another: a step starts only when the previous step's y is complete.
+ *   mode PI_RUN_KERNELS: three kernels per step (predictor stage 1; logits + mask
+ *        + up/gate rows per 64-neuron tile; down projection from the mask).
+ *   mode PI_RUN_PERSISTENT: the whole run is one cooperative launch (a launch per
+ *        32 steps when nrep > 32); inside it, the phases of a step and the steps
+ *        themselves hand over through flags in the workspace, with no kernel boundary.
+ *        Needs r <= 1024, d <= 8192 (fp16) and at most 64 neurons per block of the
+ *        co-resident grid (F <= 32768 on a 256-CU device); PI_ERR_UNSUPPORTED otherwise.
+ *        A hand-off that never completes (only possible if co-residency were broken)
+ *        ends the launch after a spin limit and leaves y all NaN and *count = -1.
+ *        On MI355X each of its hand-offs costs more than a kernel boundary, so it is
+ *        the slower schedule on every workload measured; it is kept as an alternative.
+ *   mode PI_RUN_AUTO: the three-kernel schedule.
  * mask u32 [ceil(F/32)], idx int32 [F] + count int32 [1] (both NULL or both set)
  * and y fp32 [d] hold the LAST step's results.  The summation order of z differs
  * from pi_predict's, so logits agree to fp32 rounding, not bit for bit.
- * events: NULL, or 2*nsteps hipEvent_t created with timing enabled; then kernel 2
- * of step i (the one that moves the most bytes) is launched with events[2i] /
- * events[2i+1] attached to its own start / end (hipExtLaunchKernelGGL), so their
- * elapsed time is exactly that kernel's execution time.                                 */
+ * events: NULL, or 2 hipEvent_t: events[0] is recorded on the stream before the
+ * first launch and events[1] after the last, so their elapsed time is the run's.
+ * kernel_events: NULL, or 2*nsteps hipEvent_t (three-kernel schedule only): kernel 2
+ * of step i (the one that moves the most bytes) is launched with kernel_events[2i] /
+ * [2i+1] attached to its own start / end, so their elapsed time is that kernel's
+ * execution time.  Attaching them slows the run down; time a run without them.       */
+#define PI_RUN_AUTO        0
+#define PI_RUN_PERSISTENT  1
+#define PI_RUN_KERNELS     2
 int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
-                  const uint16_t* x, int T, long long s0, int nsteps,
+                  const uint16_t* x, int T, long long s0, int nsteps, int mode,
                   uint32_t* mask, int32_t* idx, int32_t* count, float* y,
-                  void* const* events, void* ws, size_t ws_bytes, void* stream);
+                  void* const* events, void* const* kernel_events,
+                  void* ws, size_t ws_bytes, void* stream);
 
 /* ---- pi_ffn_dense_ref_gpu ------------------------------------------------------------------
  * The same FFN over all F neurons (no predictor, no skipping): the dense

@@ -165,38 +165,112 @@ def test_config_end_to_end(name):
     say(f"[gpu] {name}: band disagreements {band_total}, worst rel-L2 {worst:.2e}")
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
-def test_decode_run_fused(name):
-    """pi_decode_run (fused three-kernel step, native loop over replicas) against the
-    oracle: index set, neuron table, mask and y of single steps; a multi-step run ends
-    with exactly the single-step result of its last token."""
-    cfg = configs.get(name)
-    say(f"[gpu] fused decode_run on {cfg.name}")
-    inp = _full(name)
-    W = O.Weights.from_inputs(inp)
-    layer = _layer(inp, replicas=3)
-    bufs, ref = layer.buffers(1), layer.buffers(1)
+def _run_modes():
+    from activation_sparse_pi_amd import _lib as L
+    return {"persistent": L.PI_RUN_PERSISTENT, "kernels": L.PI_RUN_KERNELS}
+
+
+def _decode_single_steps(layer, inp, W, xd, tokens, mode, ctx):
+    """Each token as a one-step run, checked against the oracle (index set, table, mask, y)."""
+    cfg = inp["cfg"]
     X = inp["x"][:, 0, :]
-    xd = torch.from_numpy(X.copy()).to(layer.device)
-    tokens = sorted(set(np.linspace(0, cfg.T - 1, 5).astype(int).tolist()))
     ref_L = O.predictor_logits(X[tokens], inp["w_p1"], inp["w_p2"], inp["bias"])
+    bufs = layer.buffers(1)
     for i, t in enumerate(tokens):
-        layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs)
+        layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs, mode=mode)
         torch.cuda.synchronize()
         n = int(bufs["count"][0].item())
+        assert n >= 0, f"{ctx} t={t}: the run reported a failed hand-off"
         gidx = _to_np(bufs["idx"][0, :n]).astype(np.int64)
         gmask = _to_np(bufs["mask"][0]).view(np.uint32)
-        P.check_index_set(gidx, gmask, ref_L[i], cfg.F, ctx=f"{name} fused t={t}")
-        P.check_ffn(_to_np(bufs["y"][0]), W, X[t], gidx, ctx=f"{name} fused t={t}")
-    # 17 steps from s0 = 40 end on token 56 of replica 56 % 3; deterministic kernels
-    layer.decode_run(xd.data_ptr(), cfg.T, 40, 17, bufs)
-    layer.decode_run(xd.data_ptr(), cfg.T, 56, 1, ref)
+        P.check_index_set(gidx, gmask, ref_L[i], cfg.F, ctx=f"{ctx} t={t}")
+        P.check_ffn(_to_np(bufs["y"][0]), W, X[t], gidx, ctx=f"{ctx} t={t}")
+
+
+def _decode_long_run(layer, cfg, xd, s0, nsteps, mode):
+    """A multi-step run ends with exactly what a one-step run of its last token gives
+    (the kernels are deterministic and a step does not depend on earlier ones)."""
+    bufs, ref = layer.buffers(1), layer.buffers(1)
+    layer.decode_run(xd.data_ptr(), cfg.T, s0, nsteps, bufs, mode=mode)
+    layer.decode_run(xd.data_ptr(), cfg.T, s0 + nsteps - 1, 1, ref, mode=mode)
     torch.cuda.synchronize()
     c = int(ref["count"][0].item())
-    assert int(bufs["count"][0].item()) == c
+    assert c >= 0 and int(bufs["count"][0].item()) == c
     assert torch.equal(bufs["idx"][0, :c], ref["idx"][0, :c])
     assert torch.equal(bufs["mask"], ref["mask"])
     assert torch.equal(bufs["y"], ref["y"])
+
+
+@pytest.mark.parametrize("mode", ["persistent", "kernels"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_decode_run(name, mode):
+    """pi_decode_run, in its persistent launch and as three kernels per step, against
+    the oracle on single steps; a 17-step run over 3 replicas ends with the one-step
+    result of its last token."""
+    cfg = configs.get(name)
+    say(f"[gpu] decode_run {mode} on {cfg.name}")
+    inp = _full(name)
+    W = O.Weights.from_inputs(inp)
+    layer = _layer(inp, replicas=3)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    tokens = sorted(set(np.linspace(0, cfg.T - 1, 5).astype(int).tolist()))
+    m = _run_modes()[mode]
+    _decode_single_steps(layer, inp, W, xd, tokens, m, f"{name} {mode}")
+    _decode_long_run(layer, cfg, xd, 40, 17, m)
+
+
+@pytest.mark.parametrize("cfg", TINY, ids=lambda c: c.name)
+def test_decode_run_tiny(cfg):
+    """The persistent launch on ragged shapes (tails in d, F and r; F = 8): every token as
+    a one-step run against the oracle, then a 300-step run (past the wrap of the 8-bit
+    hand-off counters at 256) that must end on the one-step result of its last token."""
+    say(f"[gpu] decode_run persistent tiny {cfg.name}")
+    inp = gen.make(cfg)
+    W = O.Weights.from_inputs(inp)
+    layer = _layer(inp, replicas=2)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    m = _run_modes()["persistent"]
+    _decode_single_steps(layer, inp, W, xd, list(range(cfg.T)), m, f"{cfg.name} persistent")
+    _decode_long_run(layer, cfg, xd, 3, 300, m)
+
+
+def test_decode_run_many_replicas():
+    """More replicas than one launch's table holds (40 > 32): the run goes out as launches
+    of 32 steps; 70 steps must end on the one-step result of the last token."""
+    cfg = configs.C1
+    say("[gpu] decode_run persistent, 40 replicas")
+    inp = _full("c1")
+    layer = _layer(inp, replicas=40)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    m = _run_modes()["persistent"]
+    _decode_long_run(layer, cfg, xd, 5, 70, m)
+    W = O.Weights.from_inputs(inp)
+    _decode_single_steps(layer, inp, W, xd, [74 % cfg.T], m, "c1 40 replicas")
+
+
+def test_decode_run_modes_agree_on_tables():
+    """Both schedules produce the same neuron tables on c2 tokens (outside the band)."""
+    inp = _full("c2")
+    cfg = inp["cfg"]
+    layer = _layer(inp, replicas=1)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    X = inp["x"][:, 0, :]
+    modes = _run_modes()
+    for t in (0, 100, 255):
+        out = {}
+        for mname, m in modes.items():
+            b = layer.buffers(1)
+            layer.decode_run(xd.data_ptr(), cfg.T, t, 1, b, mode=m)
+            torch.cuda.synchronize()
+            n = int(b["count"][0].item())
+            out[mname] = (_to_np(b["idx"][0, :n]).astype(np.int64), _to_np(b["y"][0]).copy())
+        ref_l = O.predictor_logits(X[t], inp["w_p1"], inp["w_p2"], inp["bias"])
+        band = O.exclusion_band(ref_l)
+        a = np.zeros(cfg.F, bool); a[out["persistent"][0]] = True
+        k = np.zeros(cfg.F, bool); k[out["kernels"][0]] = True
+        assert not np.any((a ^ k) & ~band), f"t={t}: the two schedules differ outside the band"
+        if np.array_equal(a, k):
+            assert P.rel_l2(out["persistent"][1], out["kernels"][1]) <= 1e-5
 
 
 def test_operators_match_sparse_ffn():
