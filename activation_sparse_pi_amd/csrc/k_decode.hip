@@ -44,7 +44,10 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h) {
     constexpr int NT = B_WAVES * 64;
-    constexpr int IPW = Q <= 8 ? 2 : 1;        // row items per wave in flight
+    // row items per wave in flight: as many as the register budget of two blocks per CU
+    // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
+    // items needs one memory round trip
+    constexpr int IPW = Q <= 4 ? 4 : Q <= 8 ? (WF == 0 ? 3 : 2) : 1;
     extern __shared__ __align__(16) char smem[];
     float* s_z = reinterpret_cast<float*>(smem);
     uint4* s_x = reinterpret_cast<uint4*>(smem + align16i(r * 4));
@@ -56,9 +59,11 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const int tile = blockIdx.x;
     const int W = (F + 31) >> 5;
 
-    // --- logits of the tile: the first segment of its W2t rows goes out before z is staged
+    // --- logits of the tile: the first segment of its W2t rows (and the tile's bias) goes
+    // out before z is staged
     TileRows<B_WAVES> tr;
     tile_rows_load<B_WAVES>(tr, W2t, r, F, tile, 0);
+    const float bv = (wave == 0 && tile * 64 + lane < F) ? bias[tile * 64 + lane] : 0.f;
     for (int j = tid; j < r; j += NT) s_z[j] = z[j];
     const int nc8 = d >> 3;
     for (int c = tid; c < nc8; c += NT) {
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         const int n = tile * 64 + lane;
         bool act = false;
         if (n < F) {
-            const float l = s_red[lane] + bias[n];
+            const float l = s_red[lane] + bv;
             act = l > theta;
             if (logits) logits[n] = l;
         }

@@ -88,6 +88,8 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x;
     const int W = (F + 31) >> 5;
+    // the tile's bias, loaded once for every token and not on the threshold's critical path
+    const float bv = (wave == 0 && tile * 64 + lane < F) ? bias[tile * 64 + lane] : 0.f;
     for (int b0 = 0; b0 < B; b0 += nbz) {
         const int nb = min(nbz, B - b0);
         for (int i = tid; i < nb * r; i += P2_WAVES * 64) s_z[i] = z[(size_t)b0 * r + i];
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
                 const int b = b0 + t;
                 bool act = false;
                 if (n < F) {
-                    const float l = s_l[lane] + bias[n];
+                    const float l = s_l[lane] + bv;
                     act = l > theta;
                     if (logits) logits[(size_t)b * F + n] = l;
                 }
