@@ -120,6 +120,19 @@ PI_DEV uint32_t ld_agent(const uint32_t* p) {
     return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- exact cross-block sums: int64 fixed point ---------------------------------------------
+// A float v is carried as round(v * 2^32) (|v| clamped to 2^26, so even 64 such terms
+// cannot overflow); integer addition is exact and associative, so sums accumulated with
+// atomic adds in any order are bit-reproducible.  The one rounding is at the way in.
+PI_DEV long long to_fx(float v) {
+    const float c = fminf(fmaxf(v, -67108864.f), 67108864.f);   // 2^26
+    return (long long)llrintf(c * 4294967296.f);                  // exact power-of-two scaling
+}
+PI_DEV float from_fx(long long q) { return (float)((double)q * (1.0 / 4294967296.0)); }
+PI_DEV void fx_add(long long* acc, float v) {
+    __hip_atomic_fetch_add(acc, to_fx(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Every block calls this once, after all its threads issued their st_agent
 // partials.  The barrier drains the stores (vmcnt(0)) before thread 0 bumps the
 // arrival counter, so the block that sees the final count reads complete

@@ -14,7 +14,6 @@ constexpr int CNT_PRED1 = 0;      // one per predictor column group (r / 64 <= 2
 constexpr int CNT_PRED2 = 256;    // one for stage 2's compaction
 constexpr int CNT_DOWN = 512;     // one per down-projection column slice (<= 512)
 constexpr int CNT_UNION = 1024;   // union path (<= 512)
-constexpr int CNT_DECODE = 1536;  // fused decode step, one per down slice (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
@@ -59,13 +58,18 @@ struct DecPlan {
     int ntile, q;              // stage-2 tiles of 64 neurons, chunks per lane per row
     size_t lds_b;              // dynamic LDS of the stage-2 + up kernel
     int nslices, nsplit, wps;  // down: column slices, neuron-range splits, mask words per split
-    size_t off_z, off_h, off_part, bytes;
+    size_t off_z, off_h, off_yacc, bytes;
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
+// One step.  Its down projection adds into the fixed-point accumulators (d int64 in the
+// workspace, zero before the first step of a run); when convert_prev is set, its first
+// kernel turns the previous step's accumulators into y and clears them.
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
-                              int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s,
-                              hipEvent_t e0, hipEvent_t e1);
+                              int32_t* idx, int32_t* count, float* y, bool convert_prev,
+                              char* ws, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+// After the last step: y = the accumulators, which are cleared.
+hipError_t launch_decode_finish(const DecPlan& pl, int d, float* y, char* ws, hipStream_t s);
 
 // ---- persistent batch-1 decode (a run of steps in one cooperative launch) -----------------
 constexpr int RUN_NTAB = 32;          // replicas one launch can address
@@ -128,8 +132,11 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
                                 hipStream_t s);
 
+// yacc / y (batch-1 decode executor only): also turn the previous step's fixed-point y
+// accumulators (d of them) into y and clear them
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
-                              float* z, hipStream_t s);
+                              float* z, hipStream_t s, long long* yacc = nullptr,
+                              float* y = nullptr);
 
 hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
                           int32_t* count, hipStream_t s);

@@ -174,10 +174,10 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
 // slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte loads, or 1024 int4
 // columns with 8-byte loads) and the neuron ids of a range of mask words.  It compacts
 // its range in LDS, its 16 waves take interleaved active neurons (U rows in flight per
-// wave; each row's h and scale are wave-uniform scalar loads), the waves' sums meet in
-// LDS, and the block's partial row goes out with agent-coherent stores; the last block
-// to arrive on a slice adds the splits' partials in split order (deterministic).  The
-// slice-0 blocks also write the global ascending neuron table for their range.
+// wave), the waves' sums meet in LDS in a fixed order, and each column sum is added to
+// that column's int64 fixed-point accumulator with an atomic add (exact, so the result
+// does not depend on the order of the splits).  The slice-0 blocks also write the global
+// ascending neuron table for their range.
 constexpr int DN_NW = 16;
 
 template <int WF>
@@ -228,8 +228,7 @@ template <int WF, int U>
 __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
     const void* __restrict__ Wd, const uint16_t* __restrict__ Sd, int d, int wps,
-    float* __restrict__ part, float* __restrict__ y, unsigned* __restrict__ counters,
-    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    long long* __restrict__ yacc, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
     using Gm = DnGeom<WF>;
     __shared__ int s_ids[DEC_IDCAP];
     __shared__ __align__(16) float s_red[DN_NW * Gm::SC];
@@ -327,24 +326,18 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
 #pragma unroll
         for (int w = 0; w < DN_NW; ++w) s += s_red[w * Gm::SC + col];
     }
+    // the block's column sums go straight into the exact fixed-point accumulators: no
+    // partial rows, no arrival counter, no second pass (the next kernel reads them)
     const int gcol = slice * Gm::SC + col;
     const bool writer = WF == 0 ? (tid < 512) : true;
-    if (writer && gcol < d) st_agent(&part[(size_t)split * d + gcol], s);
-    if (last_block_arrive(&counters[slice], (unsigned)nsplit)) {
-        float t = 0.f;
-        if (writer && gcol < d) {
-            for (int base = 0; base < nsplit; base += 16) {      // 16 partials in flight
-                float v[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int sp = base + j;
-                    v[j] = sp < nsplit ? ld_agent(&part[(size_t)sp * d + gcol]) : 0.f;
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) t += v[j];
-            }
-            y[gcol] = t;
-        }
+    if (writer && gcol < d) fx_add(&yacc[gcol], s);
+}
+
+// y = the accumulators of the last step, which are cleared for the next run
+__global__ __launch_bounds__(256) void k_fx_out(long long* __restrict__ yacc, float* __restrict__ y, int d) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) {
+        y[i] = from_fx(yacc[i]);
+        yacc[i] = 0;
     }
 }
 
@@ -396,11 +389,11 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
     p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
-    // about 128 down blocks: enough waves to keep each one's rows (U in flight) streaming,
-    // few enough partials for the last block of a slice to sum them in one batch of loads
-    int ns = (128 + p.nslices - 1) / p.nslices;
+    // about 256 down blocks (one per CU): the splits' sums meet in atomic adds, so more
+    // splits cost nothing but fewer rows per block
+    int ns = (256 + p.nslices - 1) / p.nslices;
     const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
-    if (ns > 16) ns = 16;
+    if (ns > 32) ns = 32;
     if (ns > W) ns = W;
     if (ns < ns_min) ns = ns_min;
     if (ns < 1) ns = 1;
@@ -411,19 +404,20 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     off = align_up(off + (size_t)r * sizeof(float), 256);
     p.off_h = off;
     off = align_up(off + (size_t)F * sizeof(float), 256);
-    p.off_part = off;
-    off = align_up(off + (size_t)p.nsplit * d * sizeof(float), 256);
+    p.off_yacc = off;
+    off = align_up(off + (size_t)d * sizeof(long long), 256);
     p.bytes = off;
     return p;
 }
 
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
-                              int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s,
-                              hipEvent_t e0, hipEvent_t e1) {
+                              int32_t* idx, int32_t* count, float* y, bool convert_prev,
+                              char* ws, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
-    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s);
+    long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
+    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y);
     if (e != hipSuccess) return e;
     const bool glu = f.act == PI_ACT_REGLU;
     const dim3 gb(pl.ntile);
@@ -434,15 +428,19 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
         e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
                 : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
     if (e != hipSuccess) return e;
-    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DECODE;
-    float* part = reinterpret_cast<float*>(ws + pl.off_part);
     const dim3 gc(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16)
         hipLaunchKernelGGL((k_dec_down<0, 8>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, part, y, cnt, idx, count);
+                           f.s_down, f.d, pl.wps, yacc, idx, count);
     else
         hipLaunchKernelGGL((k_dec_down<1, 12>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, part, y, cnt, idx, count);
+                           f.s_down, f.d, pl.wps, yacc, idx, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_finish(const DecPlan& pl, int d, float* y, char* ws, hipStream_t s) {
+    long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
+    hipLaunchKernelGGL(k_fx_out, dim3((d + 255) / 256), dim3(256), 0, s, yacc, y, d);
     return hipGetLastError();
 }
 

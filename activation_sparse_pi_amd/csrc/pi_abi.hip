@@ -339,16 +339,22 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
             }
             if ((e = launch_run(ra, s)) != hipSuccess) return hip_fail(e, "pi_decode_run persistent launch");
         }
-    } else {
+    } else if (nsteps > 0) {
+        // y of every step accumulates exactly in int64 fixed point; the next step's first
+        // kernel turns it into y, and a small kernel does so after the last step
+        if ((e = launch_zero(w + pl.off_yacc, (size_t)d * sizeof(long long), s)) != hipSuccess)
+            return hip_fail(e, "pi_decode_run accumulator clear");
         for (int i = 0; i < nsteps; ++i) {
             const long long g = s0 + i;
             const int t = (int)(g % T), rep = (int)(g % nrep);
             hipEvent_t k0 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i]) : nullptr;
             hipEvent_t k1 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i + 1]) : nullptr;
             e = launch_decode_step(preds[rep], ffns[rep], pl, x + (size_t)t * d, theta, nullptr, mask,
-                                   idx, count, y, w, s, k0, k1);
+                                   idx, count, y, i > 0, w, s, k0, k1);
             if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
         }
+        if ((e = launch_decode_finish(pl, d, y, w, s)) != hipSuccess)
+            return hip_fail(e, "pi_decode_run final y");
     }
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
         return hip_fail(e, "pi_decode_run end event");
