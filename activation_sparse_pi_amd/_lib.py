@@ -18,7 +18,7 @@ PI_ERR_UNSUPPORTED, PI_ERR_WORKSPACE, PI_ERR_HIP = 5, 6, 7
 PI_ACT_RELU, PI_ACT_REGLU = 0, 1
 PI_W_F16, PI_W_I4G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
-PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS = 0, 1, 2
+PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 1, 2, 3, 4
 PI_MAX_BATCH = 32
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 #define PI_DEV __device__ __forceinline__
@@ -131,6 +133,21 @@ PI_DEV long long to_fx(float v) {
 PI_DEV float from_fx(long long q) { return (float)((double)q * (1.0 / 4294967296.0)); }
 PI_DEV void fx_add(long long* acc, float v) {
     __hip_atomic_fetch_add(acc, to_fx(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The sum of the DEC_NCOPY accumulator copies of element i (copies d elements apart), each
+// copy cleared.  Producers spread their atomic adds over the copies so that no address
+// sees more than a few dozen of them.
+PI_DEV long long fx_take(long long* acc, int d, int i) {
+    long long v[pi::DEC_NCOPY];
+#pragma unroll
+    for (int c = 0; c < pi::DEC_NCOPY; ++c) v[c] = acc[(size_t)c * d + i];
+    long long t = 0;
+#pragma unroll
+    for (int c = 0; c < pi::DEC_NCOPY; ++c) {
+        t += v[c];
+        acc[(size_t)c * d + i] = 0;
+    }
+    return t;
 }
 
 // Every block calls this once, after all its threads issued their st_agent

@@ -17,6 +17,9 @@ constexpr int CNT_UNION = 1024;   // union path (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
+// Copies of the batch-1 decode's fixed-point y accumulators (d int64 each): tile t adds into
+// copy t % DEC_NCOPY, which bounds the atomic adds any one address sees per step.
+constexpr int DEC_NCOPY = 16;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -54,22 +57,27 @@ size_t plan_union(FfnPlan& p, int d, int F, size_t off);
 
 // ---- fused batch-1 decode step (three kernels) --------------------------------------------
 struct DecPlan {
-    PredPlan pred;             // stage 1 is the predictor's row GEMV (batch 1)
-    int ntile, q;              // stage-2 tiles of 64 neurons, chunks per lane per row
-    size_t lds_b;              // dynamic LDS of the stage-2 + up kernel
-    int nslices, nsplit, wps;  // down: column slices, neuron-range splits, mask words per split
+    PredPlan pred;
+    int ntile, q;              // tiles of 64 neurons, chunks per lane per up/gate row
+    size_t lds_b;              // dynamic LDS of the tile kernel
+    bool fused_default;        // the schedule chosen for this shape
+    int nslices, nsplit, wps;  // split schedule's down grid: column slices, ranges, mask words per range
     size_t off_z, off_h, off_yacc, bytes;
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
-// One step.  Its down projection adds into the fixed-point accumulators (d int64 in the
-// workspace, zero before the first step of a run); when convert_prev is set, its first
-// kernel turns the previous step's accumulators into y and clears them.
-hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
+// One step: two kernels (fused: the tile blocks add their own down partial sums) or three
+// (split: a down kernel over ranges of the mask).  The down projection adds into the
+// fixed-point y accumulators (DEC_NCOPY copies of d int64 in the workspace, zero before the
+// first step of a run); when convert_prev is set, the first kernel turns the previous step's
+// accumulators into y and clears them.
+hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl, bool fused,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
-                              int32_t* idx, int32_t* count, float* y, bool convert_prev,
-                              char* ws, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-// After the last step: y = the accumulators, which are cleared.
-hipError_t launch_decode_finish(const DecPlan& pl, int d, float* y, char* ws, hipStream_t s);
+                              float* y, bool convert_prev, char* ws, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1);
+// After the last step: y = the accumulators (cleared), and the last step's neuron table
+// (idx, count; skipped when idx is NULL) from its mask.
+hipError_t launch_decode_finish(const DecPlan& pl, int d, int F, const uint32_t* mask, int32_t* idx,
+                                int32_t* count, float* y, char* ws, hipStream_t s);
 
 // ---- persistent batch-1 decode (a run of steps in one cooperative launch) -----------------
 constexpr int RUN_NTAB = 32;          // replicas one launch can address

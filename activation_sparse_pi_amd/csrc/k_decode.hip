@@ -1,25 +1,33 @@
-// Fused batch-1 decode step on gfx950: three kernels per token.
+// Batch-1 decode step on gfx950: two or three kernels per token.
 //
 // PowerInfer (online engine, "Adaptive Sparsity Predictors", "Neuron Placement
 // and Management", "Neuron-aware Operator"): predict the neurons a token will
 // fire, compute only their rows of up/gate and their output vectors of down,
 // and keep a table of their original positions.
 //
-// On this GPU a kernel boundary costs ~2-3 us of timeline and a grid-wide
-// barrier costs as much, so the step is cut where a global dependency forces a
-// cut, and nowhere else:
-//   A  predictor stage 1, z_j = W1t[j, :] . x (one wave per predictor column,
-//      the same kernel pi_predict uses).
-//   B  one block per 64-neuron tile: the tile's 64 contiguous W2t rows are
-//      already in flight while z is staged in LDS; l = W2t[tile] . z + b,
-//      active = l > theta, a wave ballot writes the tile's two mask words, and
-//      the block then computes h for ITS OWN active neurons (gate/up rows dotted
-//      with x staged in LDS).  No global neuron list is needed for that.
-//   C  down projection straight from the mask: block (slice, split) owns a
-//      column slice and a range of neuron ids, compacts its range in LDS, and
-//      accumulates h_i * W_down[i, slice]; the last-arriving block of a slice
-//      adds the splits' partials in split order.  The slice-0 blocks also write
-//      the global ascending neuron table (idx, count) for their range.
+// On this GPU a kernel boundary costs 1.1-1.4 us of timeline between dependent
+// kernels, so the step is cut only where a global dependency forces it (every
+// tile's logits need all of z):
+//   A  predictor stage 1, z_j = W1t[j, :] . x (one wave per predictor column, the
+//      kernel pi_predict uses); its grid also turns the previous step's fixed-point
+//      y accumulators into y and clears them.
+//   B  one block per 64-neuron tile: the tile's 64 contiguous W2t rows (and biases)
+//      are already in flight while z is staged in LDS; l = W2t[tile] . z + b,
+//      active = l > theta, a wave ballot writes the tile's two mask words and lists
+//      its active neurons; the block computes h for them from their gate/up rows
+//      (x staged in LDS).
+// The down projection y = sum_k h_k W_down[k, :] is added to int64 fixed-point y
+// accumulators with atomic adds (exact, so the order of the adds does not matter),
+// in one of two ways:
+//   fused (two kernels per step): B itself reads its active neurons' down rows and adds
+//      its d partial sums, one set per tile.
+//   split (three kernels per step): B writes h; C, a 2-D grid of (column slice, range
+//      of mask words) blocks, compacts its range of the mask in LDS, reduces its rows
+//      over 16 waves and adds one set of partial sums per range.
+// The fused step saves a kernel boundary but issues ntile * d atomic adds, against
+// nsplit * d for the split step, so it is chosen where ntile * d is small.
+// After the last step a small kernel turns the accumulators into y and writes the
+// last step's ascending neuron table from its mask.
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
@@ -28,7 +36,7 @@
 namespace pi {
 namespace {
 
-constexpr int DEC_IDCAP = 4096;   // neuron ids one down block can hold (128 mask words)
+constexpr int DEC_IDCAP = 4096;   // neuron ids one split-schedule down block holds (128 mask words)
 
 // --------------------------------------------------------------------------------------- B
 // WF: 0 = fp16 rows, 1 = int4 group-128 rows.  Q: 16-byte chunks per lane per row.
@@ -36,13 +44,14 @@ constexpr int DEC_IDCAP = 4096;   // neuron ids one down block can hold (128 mas
 // (x0,x4),(x1,x5),(x2,x6),(x3,x7) to match the nibble pairs one AND/OR extracts).
 constexpr int B_WAVES = 8;   // waves per tile block (two blocks fit on a CU)
 
-template <int WF, bool GLU, int Q>
+template <int WF, bool GLU, int Q, bool FUSED>
 __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const float* __restrict__ z, const uint16_t* __restrict__ W2t,
     const float* __restrict__ bias, int r, int F, float theta, float* __restrict__ logits,
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
-    const uint16_t* __restrict__ Su, int d, float* __restrict__ h) {
+    const uint16_t* __restrict__ Su, int d, float* __restrict__ h, const void* __restrict__ Wd,
+    const uint16_t* __restrict__ Sd, long long* __restrict__ yacc) {
     constexpr int NT = B_WAVES * 64;
     // row items per wave in flight: as many as the register budget of two blocks per CU
     // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
@@ -163,21 +172,114 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         }
     }
     __syncthreads();
+    if constexpr (!FUSED) {
+        for (int k = tid; k < na; k += NT) {
+            const float a = s_dot[1][k];
+            h[tile * 64 + s_list[k]] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
+        }
+        return;
+    }
+    __shared__ float s_h[64];
     for (int k = tid; k < na; k += NT) {
         const float a = s_dot[1][k];
-        h[tile * 64 + s_list[k]] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
+        s_h[k] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
+    }
+    __syncthreads();
+    if (na == 0) return;
+
+    // --- down: y += sum over the tile's active neurons of h_k W_down[row_k, :].  Wave w takes
+    // column chunks w, w + 8, ... (512 fp16 or 1024 int4 columns: 16 or 8 bytes per lane of
+    // each row) and reads that chunk of every active row at once (DN_ROWS in flight; empty
+    // slots re-read the first row's chunk, an L2 hit, and count zero).  Its column sums go
+    // into one of DEC_NCOPY fixed-point accumulator copies (copy = tile % DEC_NCOPY) with
+    // atomic adds: exact, so the order of the tiles does not matter.
+    constexpr int CH = WF == 0 ? 512 : 1024;
+    constexpr int V = CH / 64;                       // columns per lane
+    constexpr int DN_ROWS = 16;
+    __shared__ __align__(16) float s_acc[B_WAVES * CH];
+    const int nch = (d + CH - 1) / CH;
+    const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
+    long long* accc = yacc + (size_t)(tile % DEC_NCOPY) * d;
+    const uint8_t* Wb = static_cast<const uint8_t*>(Wd);
+    for (int j = wave; j < nch; j += B_WAVES) {
+        const int col0 = j * CH + lane * V;
+        const bool cok = col0 < d;                  // d % 8 (fp16) / % 128 (int4): all V or none
+        const size_t boff = cok ? (WF == 0 ? (size_t)col0 * 2 : (size_t)(col0 >> 1)) : 0;
+        const int sg = cok ? (col0 >> 7) : 0;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.f;
+        float soff = 0.f;
+        for (int k0 = 0; k0 < na; k0 += DN_ROWS) {
+            uint4 w16[DN_ROWS];
+            uint2 w8[DN_ROWS];
+            uint32_t sr[DN_ROWS];
+            float hv[DN_ROWS];
+#pragma unroll
+            for (int u = 0; u < DN_ROWS; ++u) {
+                const int k = k0 + u;
+                const int kk = k < na ? k : 0;
+                const size_t row = (size_t)(tile * 64 + s_list[kk]);
+                hv[u] = (k < na && cok) ? s_h[kk] : 0.f;
+                if (WF == 0) {
+                    w16[u] = ld16(Wb + row * rowb + boff);
+                } else {
+                    w8[u] = *reinterpret_cast<const uint2*>(Wb + row * rowb + boff);
+                    sr[u] = (uint32_t)Sd[row * G + sg];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < DN_ROWS; ++u) {
+                if (WF == 0) {
+                    const uint32_t ww[4] = {w16[u].x, w16[u].y, w16[u].z, w16[u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
+                        acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
+                    }
+                } else {
+                    const float hs = hv[u] * h2f((uint16_t)sr[u]);
+                    soff += hs;
+                    const uint32_t wv[2] = {w8[u].x, w8[u].y};
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const uint32_t lo = wv[m] & 0x0F0F0F0Fu, hi = (wv[m] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                        for (int bb = 0; bb < 4; ++bb) {
+                            acc[8 * m + 2 * bb] = fmaf(hs, (float)((lo >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb]);
+                            acc[8 * m + 2 * bb + 1] = fmaf(hs, (float)((hi >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb + 1]);
+                        }
+                    }
+                }
+            }
+        }
+        // transpose through the wave's LDS slice so that each atomic instruction covers 64
+        // consecutive columns (512 contiguous bytes) instead of 64 lanes 8 * V bytes apart
+        float* sa = s_acc + wave * CH;
+#pragma unroll
+        for (int v = 0; v < V; v += 4)
+            *reinterpret_cast<float4*>(sa + lane * V + v) =
+                WF == 1 ? make_float4(fmaf(-8.f, soff, acc[v]), fmaf(-8.f, soff, acc[v + 1]),
+                                      fmaf(-8.f, soff, acc[v + 2]), fmaf(-8.f, soff, acc[v + 3]))
+                        : make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int col = j * CH + v * 64 + lane;
+            if (col < d) fx_add(&accc[col], sa[v * 64 + lane]);
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
 // --------------------------------------------------------------------------------------- C
-// Down projection straight from the mask, 2-D tiled.  Block (slice, split) owns a column
-// slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte loads, or 1024 int4
-// columns with 8-byte loads) and the neuron ids of a range of mask words.  It compacts
-// its range in LDS, its 16 waves take interleaved active neurons (U rows in flight per
-// wave), the waves' sums meet in LDS in a fixed order, and each column sum is added to
-// that column's int64 fixed-point accumulator with an atomic add (exact, so the result
-// does not depend on the order of the splits).  The slice-0 blocks also write the global
-// ascending neuron table for their range.
+// Split schedule: the down projection straight from the mask, 2-D tiled.  Block (slice,
+// split) owns a column slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte
+// loads, or 1024 int4 columns with 8-byte loads) and the neuron ids of a range of mask
+// words.  It compacts its range in LDS, its 16 waves take interleaved active neurons (U rows
+// in flight per wave), the waves' sums meet in LDS in a fixed order, and each column sum is
+// added to that column's fixed-point accumulator (copy split % DEC_NCOPY) with an atomic
+// add.
 constexpr int DN_NW = 16;
 
 template <int WF>
@@ -208,40 +310,21 @@ PI_DEV int range_compact(const uint32_t* __restrict__ mask, int w0, int w1, int 
     return total;
 }
 
-// The global table for the slice-0 blocks: prefix = popcount of all words before w0.
-PI_DEV void write_table(const uint32_t* __restrict__ mask, int w0, int n_loc, bool last_split,
-                        const int* s_ids, int32_t* __restrict__ idx, int32_t* __restrict__ count,
-                        int* s_acc) {
-    if (threadIdx.x == 0) *s_acc = 0;
-    __syncthreads();
-    int c = 0;
-    for (int w = threadIdx.x; w < w0; w += blockDim.x) c += __popc(mask[w]);
-    c = (int)wave_sum((float)c);   // exact: counts stay far below 2^24
-    if ((threadIdx.x & 63) == 0 && c) atomicAdd(s_acc, c);
-    __syncthreads();
-    const int P = *s_acc;
-    for (int i = threadIdx.x; i < n_loc; i += blockDim.x) idx[P + i] = s_ids[i];
-    if (last_split && threadIdx.x == 0) *count = P + n_loc;
-}
-
 template <int WF, int U>
 __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
     const void* __restrict__ Wd, const uint16_t* __restrict__ Sd, int d, int wps,
-    long long* __restrict__ yacc, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    long long* __restrict__ yacc) {
     using Gm = DnGeom<WF>;
     __shared__ int s_ids[DEC_IDCAP];
     __shared__ __align__(16) float s_red[DN_NW * Gm::SC];
     __shared__ float s_half[512];
     __shared__ int s_tmp[DN_NW + 1];
-    __shared__ int s_acc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slice = blockIdx.x, split = blockIdx.y, nsplit = gridDim.y;
+    const int slice = blockIdx.x, split = blockIdx.y;
     const int W = (F + 31) >> 5;
     const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
     const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
-    if (slice == 0 && idx != nullptr)
-        write_table(mask, w0, n_loc, split == nsplit - 1, s_ids, idx, count, &s_acc);
 
     const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
     const size_t boff = ((size_t)slice * 64 + lane) * Gm::LB;
@@ -330,37 +413,40 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     // partial rows, no arrival counter, no second pass (the next kernel reads them)
     const int gcol = slice * Gm::SC + col;
     const bool writer = WF == 0 ? (tid < 512) : true;
-    if (writer && gcol < d) fx_add(&yacc[gcol], s);
+    if (writer && gcol < d) fx_add(&yacc[(size_t)(split % DEC_NCOPY) * d + gcol], s);
 }
 
-// y = the accumulators of the last step, which are cleared for the next run
-__global__ __launch_bounds__(256) void k_fx_out(long long* __restrict__ yacc, float* __restrict__ y, int d) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) {
-        y[i] = from_fx(yacc[i]);
-        yacc[i] = 0;
-    }
+// After the last step: y = the sum of the accumulator copies (cleared for the next run); block
+// 0 also writes the last step's ascending neuron table from its mask.
+__global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc, float* __restrict__ y,
+                                                    int d, const uint32_t* __restrict__ mask, int F,
+                                                    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    __shared__ int s_tmp[256 / 64 + 1];
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) y[i] = from_fx(fx_take(yacc, d, i));
+    if (blockIdx.x == 0 && idx != nullptr) block_compact<false>(mask, 1, (F + 31) >> 5, F, idx, count, s_tmp);
 }
 
 // --------------------------------------------------------------------------------------- dispatch
-template <int WF, bool GLU, int Q>
+template <int WF, bool GLU, int Q, bool FUSED>
 void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-              const uint16_t* x, const pi_ffn_desc& f, float* h) {
+              const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc) {
     if (e0)
-        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(B_WAVES * 64), (uint32_t)lds, s, e0, e1, 0,
-                              z, p.w_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
-                              f.s_gate, f.w_up, f.s_up, f.d, h);
+        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), (uint32_t)lds, s, e0,
+                              e1, 0, z, p.w_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
+                              f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc);
     else
-        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
+        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
                            p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
-                           f.s_up, f.d, h);
+                           f.s_up, f.d, h, f.w_down, f.s_down, yacc);
 }
 
-template <int WF, bool GLU>
+template <int WF, bool GLU, bool FUSED>
 hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                       const float* z, const pi_pred_desc& p, float theta, float* logits,
-                      uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h) {
-#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h); break;
+                      uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h,
+                      long long* yacc) {
+#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc); break;
     if constexpr (WF == 0) {
         switch (q) {
             PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
@@ -377,6 +463,19 @@ hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, h
     return hipGetLastError();
 }
 
+template <bool FUSED>
+hipError_t dispatch_b_fmt(const DecPlan& pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
+                          const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
+                          const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc) {
+    const bool glu = f.act == PI_ACT_REGLU;
+    const dim3 gb(pl.ntile);
+    if (f.wfmt == PI_W_F16)
+        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)
+                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
+    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)
+               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
+}
+
 }  // namespace
 
 DecPlan plan_decode(int d, int r, int F, int wfmt) {
@@ -386,6 +485,10 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     const bool f16 = wfmt == PI_W_F16;
     p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
     p.lds_b = (size_t)align16i(r * 4) + (size_t)(d / 8) * 16;
+    // fused down: ntile * d atomic adds per step; the split schedule's nsplit * d adds and
+    // extra kernel boundary win above about 2^20 adds (between the LLaMA-7B-shaped layer,
+    // 0.7M adds, faster fused, and the OPT-30B-shaped one, 3.2M, faster split)
+    p.fused_default = (long long)p.ntile * d <= (1LL << 20);
     const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
     p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
@@ -405,42 +508,37 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     p.off_h = off;
     off = align_up(off + (size_t)F * sizeof(float), 256);
     p.off_yacc = off;
-    off = align_up(off + (size_t)d * sizeof(long long), 256);
+    off = align_up(off + (size_t)DEC_NCOPY * d * sizeof(long long), 256);
     p.bytes = off;
     return p;
 }
 
-hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl,
+hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl, bool fused,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
-                              int32_t* idx, int32_t* count, float* y, bool convert_prev,
-                              char* ws, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                              float* y, bool convert_prev, char* ws, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
     hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y);
     if (e != hipSuccess) return e;
-    const bool glu = f.act == PI_ACT_REGLU;
-    const dim3 gb(pl.ntile);
-    if (f.wfmt == PI_W_F16)
-        e = glu ? dispatch_b<0, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
-                : dispatch_b<0, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
-    else
-        e = glu ? dispatch_b<1, true>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h)
-                : dispatch_b<1, false>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h);
-    if (e != hipSuccess) return e;
+    if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
+    if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)) != hipSuccess)
+        return e;
     const dim3 gc(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16)
         hipLaunchKernelGGL((k_dec_down<0, 8>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, yacc, idx, count);
+                           f.s_down, f.d, pl.wps, yacc);
     else
         hipLaunchKernelGGL((k_dec_down<1, 12>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, yacc, idx, count);
+                           f.s_down, f.d, pl.wps, yacc);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_finish(const DecPlan& pl, int d, float* y, char* ws, hipStream_t s) {
+hipError_t launch_decode_finish(const DecPlan& pl, int d, int F, const uint32_t* mask, int32_t* idx,
+                                int32_t* count, float* y, char* ws, hipStream_t s) {
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipLaunchKernelGGL(k_fx_out, dim3((d + 255) / 256), dim3(256), 0, s, yacc, y, d);
+    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, y, d, mask, F, idx, count);
     return hipGetLastError();
 }
 

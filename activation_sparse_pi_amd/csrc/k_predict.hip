@@ -26,17 +26,15 @@ namespace {
 // z[b, j] = W1t[j, :] . x[b, :].  Block: 4 waves = 4 rows.  The row is read in segments of
 // QS 16-byte chunks per lane (all loads of a segment in flight together).
 // CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
-// y accumulators into y and clears them for this step's down projection.
+// y accumulators (DEC_NCOPY copies) into y and clears them for this step's down projection.
 template <int QS, bool CONV>
 __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
                                             const uint16_t* __restrict__ W1t, int d, int r,
                                             float* __restrict__ z, long long* __restrict__ yacc,
                                             float* __restrict__ y) {
     if (CONV) {
-        for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) {
-            y[i] = from_fx(yacc[i]);
-            yacc[i] = 0;
-        }
+        for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
+            y[i] = from_fx(fx_take(yacc, d, i));
     }
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);

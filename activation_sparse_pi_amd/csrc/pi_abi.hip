@@ -242,7 +242,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
     if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
     if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
-    if (mode != PI_RUN_AUTO && mode != PI_RUN_PERSISTENT && mode != PI_RUN_KERNELS)
+    if (mode != PI_RUN_AUTO && mode != PI_RUN_PERSISTENT && mode != PI_RUN_KERNELS &&
+        mode != PI_RUN_FUSED && mode != PI_RUN_SPLIT)
         return fail(PI_ERR_DTYPE, "unknown run mode %d", mode);
     if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
     if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
@@ -258,15 +259,15 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     if (preds[0].F > 131072) return fail(PI_ERR_UNSUPPORTED, "pi_decode_run supports F <= 131072");
     if (events && (!events[0] || !events[1])) return fail(PI_ERR_NULL, "events must hold two events");
     if (kernel_events) {
-        if (mode == PI_RUN_PERSISTENT) return fail(PI_ERR_SHAPE, "kernel_events need the three-kernel schedule");
+        if (mode == PI_RUN_PERSISTENT) return fail(PI_ERR_SHAPE, "kernel_events need a kernel-per-phase schedule");
         for (int i = 0; i < 2 * nsteps; ++i)
             if (!kernel_events[i]) return fail(PI_ERR_NULL, "kernel_events[%d] is NULL", i);
     }
     const int d = preds[0].d, r = preds[0].r, F = preds[0].F;
     const int act = ffns[0].act, wfmt = ffns[0].wfmt;
-    // persistent launch when the shape fits it (and the device holds the whole grid at once)
-    // PI_RUN_AUTO takes the three-kernel schedule: on MI355X every hand-off inside the
-    // persistent launch costs more than a kernel boundary (measured on all five workloads)
+    // PI_RUN_AUTO and PI_RUN_KERNELS take the fused or the split kernel schedule by shape: on
+    // MI355X every hand-off inside the persistent launch costs more than a kernel boundary
+    // (measured on all five workloads)
     bool persistent = false;
     RunPlan rp{};
     if (mode == PI_RUN_PERSISTENT) {
@@ -281,6 +282,7 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
                         "(d=%d r=%d F=%d, %d co-resident blocks)", d, r, F, G);
     }
     const DecPlan pl = plan_decode(d, r, F, wfmt);
+    const bool fused = mode == PI_RUN_FUSED || (mode != PI_RUN_SPLIT && pl.fused_default);
     if ((st = check_ws(ws, ws_bytes, persistent ? rp.bytes : pl.bytes)) != PI_OK) return st;
     const double tau = preds[0].threshold;
     const float theta = (float)std::log(tau / (1.0 - tau));
@@ -342,18 +344,18 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     } else if (nsteps > 0) {
         // y of every step accumulates exactly in int64 fixed point; the next step's first
         // kernel turns it into y, and a small kernel does so after the last step
-        if ((e = launch_zero(w + pl.off_yacc, (size_t)d * sizeof(long long), s)) != hipSuccess)
+        if ((e = launch_zero(w + pl.off_yacc, (size_t)DEC_NCOPY * d * sizeof(long long), s)) != hipSuccess)
             return hip_fail(e, "pi_decode_run accumulator clear");
         for (int i = 0; i < nsteps; ++i) {
             const long long g = s0 + i;
             const int t = (int)(g % T), rep = (int)(g % nrep);
             hipEvent_t k0 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i]) : nullptr;
             hipEvent_t k1 = kernel_events ? static_cast<hipEvent_t>(kernel_events[2 * i + 1]) : nullptr;
-            e = launch_decode_step(preds[rep], ffns[rep], pl, x + (size_t)t * d, theta, nullptr, mask,
-                                   idx, count, y, i > 0, w, s, k0, k1);
+            e = launch_decode_step(preds[rep], ffns[rep], pl, fused, x + (size_t)t * d, theta, nullptr, mask,
+                                   y, i > 0, w, s, k0, k1);
             if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
         }
-        if ((e = launch_decode_finish(pl, d, y, w, s)) != hipSuccess)
+        if ((e = launch_decode_finish(pl, d, F, mask, idx, count, y, w, s)) != hipSuccess)
             return hip_fail(e, "pi_decode_run final y");
     }
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)

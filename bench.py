@@ -15,12 +15,15 @@ model: the touched bytes of consecutive steps never share cache lines, so they
 come from HBM and not from the 256 MB Infinity Cache.
 
 Modes (--mode): "kernels" (default) enqueues the K timed steps with one
-pi_decode_run call, three kernels per step; "persistent" runs the same call as one
-cooperative launch (slower on MI355X: its in-launch hand-offs cost more than kernel
-boundaries); "eager" makes one Python call per ABI function.  Inputs are resident in
-HBM before the timed region starts; two events recorded on the library's stream
-around the enqueued steps time them.  The roofline figure is the stage-2 kernel (the
-one that moves the most bytes): its algorithmic bytes over its average duration,
+pi_decode_run call in the kernel schedule the library picks for the shape: "fused"
+(two kernels per step, the tile kernel also does the down rows) where
+ceil(F/64) * d <= 2^20, else "split" (three kernels per step, the down projection
+its own kernel); "fused" and "split" force one of them; "persistent" runs the same
+call as one cooperative launch (slower on MI355X: its in-launch hand-offs cost more
+than kernel boundaries); "eager" makes one Python call per ABI function.  Inputs are
+resident in HBM before the timed region starts; two events recorded on the library's
+stream around the enqueued steps time them.  The roofline figure is the tile kernel
+(the one that moves the most bytes): its algorithmic bytes over its average duration,
 taken in a second pass over the same stream in which that kernel of every step
 carries its own start/end events (those events slow the step down, so the headline
 value comes from the first pass, which has none).  In persistent mode the launch is
@@ -54,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1088)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to bust the caches")
-    ap.add_argument("--mode", choices=("kernels", "persistent", "eager"), default="kernels",
+    ap.add_argument("--mode", choices=("kernels", "fused", "split", "persistent", "eager"), default="kernels",
                     help="kernels: one pi_decode_run call, three kernels per step (default); "
                          "persistent: one pi_decode_run call, one cooperative launch; "
                          "eager: one Python call per ABI function")
@@ -80,10 +83,17 @@ def bytes_model(cfg, n):
     ffn = m * n * d * wb
     total = pred + ffn + 2 * d + 4 * d + F / 8 + 4 * n
     up = (m - 1) * n * d * wb + 2 * d + 8 * n
-    # the stage-2 kernel of the three-kernel step: W2t + bias, z, x, the up (and gate) rows of
-    # the active neurons, the mask words and h written
+    # the tile kernel of the split step: W2t + bias, z, x, the up (and gate) rows of the
+    # active neurons, the mask words and h written
     stage2 = 2 * r * F + 4 * F + 4 * r + 2 * d + (m - 1) * n * d * wb + F / 8 + 4 * n
-    return dict(pred=pred, ffn=ffn, up=up, stage2=stage2, total=total)
+    # the tile kernel of the fused step: the same without h, plus the down rows and y
+    tile_fused = stage2 - 4 * n + n * d * wb + 4 * d
+    return dict(pred=pred, ffn=ffn, up=up, stage2=stage2, tile_fused=tile_fused, total=total)
+
+
+def kernel_schedule(cfg) -> str:
+    """The schedule PI_RUN_KERNELS takes for this shape (documented in include/pi.h)."""
+    return "fused" if ((cfg.F + 63) // 64) * cfg.d <= (1 << 20) else "split"
 
 
 def bytes_model_batch(cfg, n_tok, U):
@@ -326,8 +336,12 @@ def main():
 
     K, Wm = a.steps, a.warmup
     up_ms = []
-    if a.mode in ("persistent", "kernels"):
-        mode = L.PI_RUN_PERSISTENT if a.mode == "persistent" else L.PI_RUN_KERNELS
+    sched = a.mode if a.mode in ("fused", "split") else kernel_schedule(cfg)
+    sched_desc = ("two kernels per step (fused down)" if sched == "fused"
+                  else "three kernels per step (split down)")
+    if a.mode in ("persistent", "kernels", "fused", "split"):
+        mode = {"persistent": L.PI_RUN_PERSISTENT, "kernels": L.PI_RUN_KERNELS,
+                "fused": L.PI_RUN_FUSED, "split": L.PI_RUN_SPLIT}[a.mode]
         layer.decode_run(xd.data_ptr(), T, 0, Wm, bufs, mode=mode)            # untimed warmup
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in ev:                 # torch creates the HIP event on first record
@@ -336,8 +350,8 @@ def main():
         layer.decode_run(xd.data_ptr(), T, Wm, K, bufs, events=ev, mode=mode)  # timed: K steps
         torch.cuda.synchronize()
         total_ms = ev[0].elapsed_time(ev[1])
-        if a.mode == "kernels":
-            # roofline pass: the stage-2 kernel of every step carries its own start/end events
+        if a.mode != "persistent":
+            # roofline pass: the tile kernel of every step carries its own start/end events
             Kr = min(K, 1088)
             kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
             for e in kev:
@@ -377,8 +391,9 @@ def main():
         kernel_key = f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}"
         launch_bytes, launch_ms = float(np.mean(bm["up"])), float(np.mean(up_ms))
     else:
-        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act}] {cfg.name}"
-        launch_bytes = float(np.mean(bytes_model(cfg, counts[roof_steps].astype(np.float64))["stage2"]))
+        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act},{sched}] {cfg.name}"
+        bm_r = bytes_model(cfg, counts[roof_steps].astype(np.float64))
+        launch_bytes = float(np.mean(bm_r["tile_fused" if sched == "fused" else "stage2"]))
         launch_ms = float(np.mean(up_ms))
     achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(kernel_key) if kernel_key else None
@@ -406,7 +421,9 @@ def main():
             "mean_active": round(float(counts.mean()), 1),
             "launch": {"persistent": "one pi_decode_run call: one cooperative launch per run "
                                      "(per 32 steps when there are more than 32 replicas)",
-                       "kernels": "one pi_decode_run call: three kernels per step",
+                       "kernels": f"one pi_decode_run call: {sched_desc}",
+                       "fused": f"one pi_decode_run call: {sched_desc}",
+                       "split": f"one pi_decode_run call: {sched_desc}",
                        "eager": "one Python call per ABI function"}[a.mode],
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),

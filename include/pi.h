@@ -183,8 +183,13 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  * strict threshold, the neuron table, the row operator on the predicted-active
  * up/gate rows and the column operator on their down rows.  Steps run strictly one
  * after another: a step starts only when the previous step's y is complete.
- *   mode PI_RUN_KERNELS: three kernels per step (predictor stage 1; logits + mask
- *        + up/gate rows per 64-neuron tile; down projection from the mask).
+ *   mode PI_RUN_FUSED: two kernels per step (predictor stage 1; then one block per
+ *        64-neuron tile: its logits, mask words, up/gate rows and down rows, whose partial
+ *        sums are added to y).  Issues ceil(F/64) * d atomic adds per step.
+ *   mode PI_RUN_SPLIT: three kernels per step (predictor stage 1; logits + mask + up/gate
+ *        rows per tile; down projection from the mask over ranges of neurons).  Issues
+ *        about 256 * 512 atomic adds per step, whatever the shape.
+ *   mode PI_RUN_KERNELS: PI_RUN_FUSED where ceil(F/64) * d <= 2^20, else PI_RUN_SPLIT.
  *   mode PI_RUN_PERSISTENT: the whole run is one cooperative launch (a launch per
  *        32 steps when nrep > 32); inside it, the phases of a step and the steps
  *        themselves hand over through flags in the workspace, with no kernel boundary.
@@ -194,19 +199,25 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  *        ends the launch after a spin limit and leaves y all NaN and *count = -1.
  *        On MI355X each of its hand-offs costs more than a kernel boundary, so it is
  *        the slower schedule on every workload measured; it is kept as an alternative.
- *   mode PI_RUN_AUTO: the three-kernel schedule.
+ *   mode PI_RUN_AUTO: as PI_RUN_KERNELS.
+ * The kernel schedules add y in int64 fixed point (2^-32 units, each partial sum
+ * clamped to |v| <= 2^26), so their y does not depend on the order of the adds and is
+ * reproducible run to run; the persistent launch sums in fp32 in a fixed order.
  * mask u32 [ceil(F/32)], idx int32 [F] + count int32 [1] (both NULL or both set)
  * and y fp32 [d] hold the LAST step's results.  The summation order of z differs
  * from pi_predict's, so logits agree to fp32 rounding, not bit for bit.
  * events: NULL, or 2 hipEvent_t: events[0] is recorded on the stream before the
  * first launch and events[1] after the last, so their elapsed time is the run's.
- * kernel_events: NULL, or 2*nsteps hipEvent_t (three-kernel schedule only): kernel 2
- * of step i (the one that moves the most bytes) is launched with kernel_events[2i] /
- * [2i+1] attached to its own start / end, so their elapsed time is that kernel's
- * execution time.  Attaching them slows the run down; time a run without them.       */
+ * kernel_events: NULL, or 2*nsteps hipEvent_t (not with PI_RUN_PERSISTENT): kernel 2
+ * of step i (the tile kernel, the one that moves the most bytes) is launched with
+ * kernel_events[2i] / [2i+1] attached to its own start / end, so their elapsed time is
+ * that kernel's execution time.  Attaching them slows the run down; time a run without
+ * them.                                                                               */
 #define PI_RUN_AUTO        0
 #define PI_RUN_PERSISTENT  1
 #define PI_RUN_KERNELS     2
+#define PI_RUN_FUSED       3
+#define PI_RUN_SPLIT       4
 int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
                   const uint16_t* x, int T, long long s0, int nsteps, int mode,
                   uint32_t* mask, int32_t* idx, int32_t* count, float* y,

@@ -167,7 +167,7 @@ def test_config_end_to_end(name):
 
 def _run_modes():
     from activation_sparse_pi_amd import _lib as L
-    return {"persistent": L.PI_RUN_PERSISTENT, "kernels": L.PI_RUN_KERNELS}
+    return {"persistent": L.PI_RUN_PERSISTENT, "fused": L.PI_RUN_FUSED, "split": L.PI_RUN_SPLIT}
 
 
 def _decode_single_steps(layer, inp, W, xd, tokens, mode, ctx):
@@ -201,12 +201,12 @@ def _decode_long_run(layer, cfg, xd, s0, nsteps, mode):
     assert torch.equal(bufs["y"], ref["y"])
 
 
-@pytest.mark.parametrize("mode", ["persistent", "kernels"])
+@pytest.mark.parametrize("mode", ["persistent", "fused", "split"])
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_decode_run(name, mode):
-    """pi_decode_run, in its persistent launch and as three kernels per step, against
-    the oracle on single steps; a 17-step run over 3 replicas ends with the one-step
-    result of its last token."""
+    """pi_decode_run, in its persistent launch and as two (fused) or three (split) kernels
+    per step, against the oracle on single steps; a 17-step run over 3 replicas ends with
+    the one-step result of its last token, bit for bit."""
     cfg = configs.get(name)
     say(f"[gpu] decode_run {mode} on {cfg.name}")
     inp = _full(name)
@@ -219,19 +219,21 @@ def test_decode_run(name, mode):
     _decode_long_run(layer, cfg, xd, 40, 17, m)
 
 
+@pytest.mark.parametrize("mode", ["persistent", "fused", "split"])
 @pytest.mark.parametrize("cfg", TINY, ids=lambda c: c.name)
-def test_decode_run_tiny(cfg):
-    """The persistent launch on ragged shapes (tails in d, F and r; F = 8): every token as
-    a one-step run against the oracle, then a 300-step run (past the wrap of the 8-bit
-    hand-off counters at 256) that must end on the one-step result of its last token."""
-    say(f"[gpu] decode_run persistent tiny {cfg.name}")
+def test_decode_run_tiny(cfg, mode):
+    """Every schedule on ragged shapes (tails in d, F and r; F = 8): every token as a
+    one-step run against the oracle, then a long run that must end on the one-step result
+    of its last token (300 steps for the persistent launch: past the wrap of its 8-bit
+    hand-off counters at 256)."""
+    say(f"[gpu] decode_run {mode} tiny {cfg.name}")
     inp = gen.make(cfg)
     W = O.Weights.from_inputs(inp)
     layer = _layer(inp, replicas=2)
     xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
-    m = _run_modes()["persistent"]
-    _decode_single_steps(layer, inp, W, xd, list(range(cfg.T)), m, f"{cfg.name} persistent")
-    _decode_long_run(layer, cfg, xd, 3, 300, m)
+    m = _run_modes()[mode]
+    _decode_single_steps(layer, inp, W, xd, list(range(cfg.T)), m, f"{cfg.name} {mode}")
+    _decode_long_run(layer, cfg, xd, 3, 300 if mode == "persistent" else 40, m)
 
 
 def test_decode_run_many_replicas():
@@ -249,7 +251,9 @@ def test_decode_run_many_replicas():
 
 
 def test_decode_run_modes_agree_on_tables():
-    """Both schedules produce the same neuron tables on c2 tokens (outside the band)."""
+    """The schedules produce the same neuron tables on c2 tokens: the two kernel schedules
+    share their mask kernel and agree exactly, the persistent launch agrees outside the
+    band; y agrees where the tables do."""
     inp = _full("c2")
     cfg = inp["cfg"]
     layer = _layer(inp, replicas=1)
@@ -266,11 +270,13 @@ def test_decode_run_modes_agree_on_tables():
             out[mname] = (_to_np(b["idx"][0, :n]).astype(np.int64), _to_np(b["y"][0]).copy())
         ref_l = O.predictor_logits(X[t], inp["w_p1"], inp["w_p2"], inp["bias"])
         band = O.exclusion_band(ref_l)
+        assert np.array_equal(out["fused"][0], out["split"][0]), f"t={t}: fused and split tables differ"
+        assert P.rel_l2(out["fused"][1], out["split"][1]) <= 1e-5
         a = np.zeros(cfg.F, bool); a[out["persistent"][0]] = True
-        k = np.zeros(cfg.F, bool); k[out["kernels"][0]] = True
-        assert not np.any((a ^ k) & ~band), f"t={t}: the two schedules differ outside the band"
+        k = np.zeros(cfg.F, bool); k[out["fused"][0]] = True
+        assert not np.any((a ^ k) & ~band), f"t={t}: the schedules differ outside the band"
         if np.array_equal(a, k):
-            assert P.rel_l2(out["persistent"][1], out["kernels"][1]) <= 1e-5
+            assert P.rel_l2(out["persistent"][1], out["fused"][1]) <= 1e-5
 
 
 def test_operators_match_sparse_ffn():
