@@ -28,25 +28,63 @@ PI_DEV float dot8(const uint4& a, const uint4& b, float acc) {
 
 __host__ __device__ constexpr int align16i(int v) { return (v + 15) & ~15; }
 
+// (a & m) | c in one v_and_or_b32 (the compiler splits it in two when both constants are
+// literals, which gfx9 VOP3 encodings cannot hold); m in an SGPR, c in a VGPR
+PI_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
 // sum over the 32 int4 weights of one 16-byte chunk of (u - 8) * x, with x given as the 16
-// fp16 pairs (x[8m+p], x[8m+p+4]), m = word, p = nibble pair: each pair is widened exactly by
-// OR-ing the nibbles into the mantissa of fp16 1024.0 and subtracting 1032, then dotted with
-// v_dot2_f32_f16 (fp32 accumulation).
+// fp16 pairs (x[8m+p], x[8m+p+4]), m = word, p = nibble pair.  Each pair is widened exactly by
+// OR-ing it into the mantissa of fp16 1024.0: the nibbles at bits 0-3 (pairs 0 and 2, the
+// latter after a shift by 8) give 1024 + u, those at bits 4-7 (pairs 1 and 3) 1024 + 16 u; one
+// packed fp16 subtraction makes that u - 8 or 16 (u - 8), both exact, and v_dot2_f32_f16
+// dots them with x in fp32 (the factor 16 comes out of the second sum exactly at the end).
 PI_DEV float dot32_i4(const uint4& w, const uint32_t* xp) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    float acc = 0.f;
+    const h2_t o0 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2_t o1 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t mg = 0x64006400u;
+    float a1 = 0.f, a16 = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t v = ws[m];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t bits = ((v >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-            const h2_t qv = __builtin_bit_cast(h2_t, bits) - off;   // (u - 8) exactly
-            acc = __builtin_amdgcn_fdot2(qv, __builtin_bit_cast(h2_t, xp[4 * m + p]), acc, false);
-        }
+        const uint32_t v = ws[m], v8 = v >> 8;
+        const h2_t q0 = __builtin_bit_cast(h2_t, and_or(v, 0x000F000Fu, mg)) - o0;
+        const h2_t q1 = __builtin_bit_cast(h2_t, and_or(v, 0x00F000F0u, mg)) - o1;
+        const h2_t q2 = __builtin_bit_cast(h2_t, and_or(v8, 0x000F000Fu, mg)) - o0;
+        const h2_t q3 = __builtin_bit_cast(h2_t, and_or(v8, 0x00F000F0u, mg)) - o1;
+        a1 = __builtin_amdgcn_fdot2(q0, __builtin_bit_cast(h2_t, xp[4 * m]), a1, false);
+        a16 = __builtin_amdgcn_fdot2(q1, __builtin_bit_cast(h2_t, xp[4 * m + 1]), a16, false);
+        a1 = __builtin_amdgcn_fdot2(q2, __builtin_bit_cast(h2_t, xp[4 * m + 2]), a1, false);
+        a16 = __builtin_amdgcn_fdot2(q3, __builtin_bit_cast(h2_t, xp[4 * m + 3]), a16, false);
     }
-    return acc;
+    return fmaf(a16, 0.0625f, a1);
+}
+
+// acc[n] += hs * (u_n - 8) for the 8 int4 weights u_n of word v (nibble n = column n; hs16 =
+// hs / 16).  Each nibble pair (n, n + 4) is widened exactly by OR-ing it into the mantissa of
+// fp16 1024.0: the nibbles at bits 0-3 give 1024 + u, those at bits 4-7 give 1024 + 16 u, and
+// one packed fp16 subtraction of 1032 or 1152 makes that u - 8 or 16 (u - 8), both exact; the
+// fp32 FMAs take the fp16 operand directly (v_fma_mix_f32), the 16 folded into hs16.
+PI_DEV void axpy8_i4(float* acc, uint32_t v, float hs, float hs16) {
+    const h2_t o0 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2_t o1 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t v8 = v >> 8;
+    const uint32_t mg = 0x64006400u;
+    const h2_t q0 = __builtin_bit_cast(h2_t, and_or(v, 0x000F000Fu, mg)) - o0;
+    const h2_t q1 = __builtin_bit_cast(h2_t, and_or(v, 0x00F000F0u, mg)) - o1;
+    const h2_t q2 = __builtin_bit_cast(h2_t, and_or(v8, 0x000F000Fu, mg)) - o0;
+    const h2_t q3 = __builtin_bit_cast(h2_t, and_or(v8, 0x00F000F0u, mg)) - o1;
+    acc[0] = fmaf(hs, (float)q0.x, acc[0]);
+    acc[4] = fmaf(hs, (float)q0.y, acc[4]);
+    acc[1] = fmaf(hs16, (float)q1.x, acc[1]);
+    acc[5] = fmaf(hs16, (float)q1.y, acc[5]);
+    acc[2] = fmaf(hs, (float)q2.x, acc[2]);
+    acc[6] = fmaf(hs, (float)q2.y, acc[6]);
+    acc[3] = fmaf(hs16, (float)q3.x, acc[3]);
+    acc[7] = fmaf(hs16, (float)q3.y, acc[7]);
 }
 
 // sum of the 8 fp16 values of w times 8 fp32 values (za, zb), fp32 FMAs
@@ -60,6 +98,14 @@ PI_DEV float dot8_f32(const uint4& w, const float4& za, const float4& zb) {
     a = fmaf(lo_f(w.w), zb.z, a);
     return fmaf(hi_f(w.w), zb.w, a);
 }
+
+// An empty use of a loaded value, placed after the loop that consumes it under a uniform
+// condition: with a use outside the condition the compiler cannot sink the load into the
+// conditional block (where it would be waited for at once, one memory round trip per row).
+PI_DEV void keep(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+PI_DEV void keep(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+PI_DEV void keep(uint32_t& v) { asm volatile("" : "+v"(v)); }
+PI_DEV void keep(float& v) { asm volatile("" : "+v"(v)); }
 
 // 16-byte global load
 PI_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -134,10 +180,15 @@ PI_DEV float from_fx(long long q) { return (float)((double)q * (1.0 / 4294967296
 PI_DEV void fx_add(long long* acc, float v) {
     __hip_atomic_fetch_add(acc, to_fx(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// The sum of the DEC_NCOPY accumulator copies of element i (copies d elements apart), each
-// copy cleared.  Producers spread their atomic adds over the copies so that no address
+// The sum of the accumulator copies of element i (ncopy = 1 or DEC_NCOPY copies, d elements
+// apart), each copy cleared.  Producers spread their atomic adds over the copies so that no address
 // sees more than a few dozen of them.
-PI_DEV long long fx_take(long long* acc, int d, int i) {
+PI_DEV long long fx_take(long long* acc, int d, int i, int ncopy) {
+    if (ncopy == 1) {
+        const long long t = acc[i];
+        acc[i] = 0;
+        return t;
+    }
     long long v[pi::DEC_NCOPY];
 #pragma unroll
     for (int c = 0; c < pi::DEC_NCOPY; ++c) v[c] = acc[(size_t)c * d + i];

@@ -17,8 +17,8 @@ constexpr int CNT_UNION = 1024;   // union path (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
-// Copies of the batch-1 decode's fixed-point y accumulators (d int64 each): tile t adds into
-// copy t % DEC_NCOPY, which bounds the atomic adds any one address sees per step.
+// Copies of the fused batch-1 decode step's fixed-point y accumulators (d int64 each): tile t
+// adds into copy t % DEC_NCOPY, which bounds the atomic adds any one address sees per step.
 constexpr int DEC_NCOPY = 16;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -67,8 +67,8 @@ struct DecPlan {
 DecPlan plan_decode(int d, int r, int F, int wfmt);
 // One step: two kernels (fused: the tile blocks add their own down partial sums) or three
 // (split: a down kernel over ranges of the mask).  The down projection adds into the
-// fixed-point y accumulators (DEC_NCOPY copies of d int64 in the workspace, zero before the
-// first step of a run); when convert_prev is set, the first kernel turns the previous step's
+// fixed-point y accumulators (d int64 in the workspace, DEC_NCOPY copies of them for the fused
+// step, zero before the first step of a run); when convert_prev is set, the first kernel turns the previous step's
 // accumulators into y and clears them.
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl, bool fused,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
@@ -76,8 +76,8 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
                               hipEvent_t e0, hipEvent_t e1);
 // After the last step: y = the accumulators (cleared), and the last step's neuron table
 // (idx, count; skipped when idx is NULL) from its mask.
-hipError_t launch_decode_finish(const DecPlan& pl, int d, int F, const uint32_t* mask, int32_t* idx,
-                                int32_t* count, float* y, char* ws, hipStream_t s);
+hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
+                                int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s);
 
 // ---- persistent batch-1 decode (a run of steps in one cooperative launch) -----------------
 constexpr int RUN_NTAB = 32;          // replicas one launch can address
@@ -144,7 +144,7 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
 // accumulators (d of them) into y and clear them
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                               float* z, hipStream_t s, long long* yacc = nullptr,
-                              float* y = nullptr);
+                              float* y = nullptr, int ncopy = 1);
 
 hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
                           int32_t* count, hipStream_t s);

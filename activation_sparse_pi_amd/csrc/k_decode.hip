@@ -209,7 +209,6 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         float acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.f;
-        float soff = 0.f;
         for (int k0 = 0; k0 < na; k0 += DN_ROWS) {
             uint4 w16[DN_ROWS];
             uint2 w8[DN_ROWS];
@@ -230,6 +229,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
             }
 #pragma unroll
             for (int u = 0; u < DN_ROWS; ++u) {
+                if (k0 + u >= na) continue;              // empty slots: loaded, never used
                 if (WF == 0) {
                     const uint32_t ww[4] = {w16[u].x, w16[u].y, w16[u].z, w16[u].w};
 #pragma unroll
@@ -239,17 +239,17 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
                     }
                 } else {
                     const float hs = hv[u] * h2f((uint16_t)sr[u]);
-                    soff += hs;
-                    const uint32_t wv[2] = {w8[u].x, w8[u].y};
+                    axpy8_i4(acc, w8[u].x, hs, hs * 0.0625f);
+                    axpy8_i4(acc + 8, w8[u].y, hs, hs * 0.0625f);
+                }
+            }
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const uint32_t lo = wv[m] & 0x0F0F0F0Fu, hi = (wv[m] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) {
-                            acc[8 * m + 2 * bb] = fmaf(hs, (float)((lo >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb]);
-                            acc[8 * m + 2 * bb + 1] = fmaf(hs, (float)((hi >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb + 1]);
-                        }
-                    }
+            for (int u = 0; u < DN_ROWS; ++u) {
+                if (WF == 0) {
+                    keep(w16[u]);
+                } else {
+                    keep(w8[u]);
+                    keep(sr[u]);
                 }
             }
         }
@@ -258,10 +258,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         float* sa = s_acc + wave * CH;
 #pragma unroll
         for (int v = 0; v < V; v += 4)
-            *reinterpret_cast<float4*>(sa + lane * V + v) =
-                WF == 1 ? make_float4(fmaf(-8.f, soff, acc[v]), fmaf(-8.f, soff, acc[v + 1]),
-                                      fmaf(-8.f, soff, acc[v + 2]), fmaf(-8.f, soff, acc[v + 3]))
-                        : make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+            *reinterpret_cast<float4*>(sa + lane * V + v) = make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int v = 0; v < V; ++v) {
@@ -278,8 +275,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
 // loads, or 1024 int4 columns with 8-byte loads) and the neuron ids of a range of mask
 // words.  It compacts its range in LDS, its 16 waves take interleaved active neurons (U rows
 // in flight per wave), the waves' sums meet in LDS in a fixed order, and each column sum is
-// added to that column's fixed-point accumulator (copy split % DEC_NCOPY) with an atomic
-// add.
+// added to that column's fixed-point accumulator with an atomic add.
 constexpr int DN_NW = 16;
 
 template <int WF>
@@ -335,22 +331,26 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     float acc[Gm::V];
 #pragma unroll
     for (int v = 0; v < Gm::V; ++v) acc[v] = 0.f;
-    float soff = 0.f;
     for (int k0 = wave; k0 < n_loc; k0 += DN_NW * U) {
-        float hv[U];
+        float hr[U];
         uint32_t sr[U];        // raw fp16 scales, one per register
         uint4 w16[U];
         uint2 w8[U];
-        // unconditional loads (row 0 / column 0 where there is nothing to read; the value is
-        // zeroed at use): a branch-guarded load would be waited for at the end of its branch
+        // unconditional loads (row 0 / column 0 where there is nothing to read), and no use
+        // of a loaded value until all of them are issued: a branch-guarded load, or one whose
+        // value is consumed at once (even by a select), is waited for on the spot, and in-order
+        // completion then makes every row of the round a memory round trip of its own
+        int rid[U];            // the round's row ids (row 0 for an empty slot; n_loc >= 1 here)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + u * DN_NW;
-            const bool valid = k < n_loc;
-            const size_t row = valid ? (size_t)__builtin_amdgcn_readfirstlane(s_ids[k < DEC_IDCAP ? k : 0]) : 0;
+            rid[u] = s_ids[k < n_loc ? k : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t row = (size_t)__builtin_amdgcn_readfirstlane(rid[u]);
             const size_t off = row * rowb + (cok ? boff : 0);
-            const float hr = h[row];
-            hv[u] = valid && cok ? hr : 0.f;
+            hr[u] = h[row];
             if (WF == 0) {
                 w16[u] = ld16(Wb + off);
             } else {
@@ -358,8 +358,12 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
                 sr[u] = (uint32_t)Sd[row * G + (cok ? sg : 0)];
             }
         }
+        float hv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) hv[u] = (k0 + u * DN_NW < n_loc && cok) ? hr[u] : 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (k0 + u * DN_NW >= n_loc) continue;     // empty slots: loaded, never used
             if (WF == 0) {
                 const uint32_t ww[4] = {w16[u].x, w16[u].y, w16[u].z, w16[u].w};
 #pragma unroll
@@ -369,23 +373,19 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
                 }
             } else {
                 const float hs = hv[u] * h2f((uint16_t)sr[u]);
-                soff += hs;
-                const uint32_t ws[2] = {w8[u].x, w8[u].y};
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                    for (int bb = 0; bb < 4; ++bb) {
-                        acc[8 * m + 2 * bb] = fmaf(hs, (float)((lo >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb]);
-                        acc[8 * m + 2 * bb + 1] = fmaf(hs, (float)((hi >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb + 1]);
-                    }
-                }
+                axpy8_i4(acc, w8[u].x, hs, hs * 0.0625f);
+                axpy8_i4(acc + 8, w8[u].y, hs, hs * 0.0625f);
             }
         }
-    }
-    if (WF == 1) {
 #pragma unroll
-        for (int v = 0; v < Gm::V; ++v) acc[v] = fmaf(-8.f, soff, acc[v]);   // stored u = q + 8
+        for (int u = 0; u < U; ++u) {
+            if (WF == 0) {
+                keep(w16[u]);
+            } else {
+                keep(w8[u]);
+                keep(sr[u]);
+            }
+        }
     }
     {
         float4* dst = reinterpret_cast<float4*>(&s_red[wave * Gm::SC + lane * Gm::V]);
@@ -413,16 +413,16 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     // partial rows, no arrival counter, no second pass (the next kernel reads them)
     const int gcol = slice * Gm::SC + col;
     const bool writer = WF == 0 ? (tid < 512) : true;
-    if (writer && gcol < d) fx_add(&yacc[(size_t)(split % DEC_NCOPY) * d + gcol], s);
+    if (writer && gcol < d) fx_add(&yacc[gcol], s);
 }
 
 // After the last step: y = the sum of the accumulator copies (cleared for the next run); block
 // 0 also writes the last step's ascending neuron table from its mask.
-__global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc, float* __restrict__ y,
+__global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc, int ncopy, float* __restrict__ y,
                                                     int d, const uint32_t* __restrict__ mask, int F,
                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
     __shared__ int s_tmp[256 / 64 + 1];
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) y[i] = from_fx(fx_take(yacc, d, i));
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) y[i] = from_fx(fx_take(yacc, d, i, ncopy));
     if (blockIdx.x == 0 && idx != nullptr) block_compact<false>(mask, 1, (F + 31) >> 5, F, idx, count, s_tmp);
 }
 
@@ -520,7 +520,8 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y);
+    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y,
+                                      fused ? DEC_NCOPY : 1);
     if (e != hipSuccess) return e;
     if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
     if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)) != hipSuccess)
@@ -535,10 +536,11 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
     return hipGetLastError();
 }
 
-hipError_t launch_decode_finish(const DecPlan& pl, int d, int F, const uint32_t* mask, int32_t* idx,
-                                int32_t* count, float* y, char* ws, hipStream_t s) {
+hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
+                                int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s) {
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, y, d, mask, F, idx, count);
+    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, fused ? DEC_NCOPY : 1, y, d,
+                       mask, F, idx, count);
     return hipGetLastError();
 }
 

@@ -252,7 +252,6 @@ __global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
     float acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0.f;
-    float soff = 0.f;
     for (int k0 = split * NW + wave; k0 < n; k0 += stride * U) {
         uint4 w[U];
         float hr[U];
@@ -274,25 +273,23 @@ __global__ __launch_bounds__(512) void k_down_i4(const uint8_t* __restrict__ Dq,
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if (k0 + u * stride >= n) continue;        // empty slots: loaded, never used
             const float hsu = ok[u] ? hr[u] * h2f((uint16_t)sr[u]) : 0.f;
-            soff += hsu;
-            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+            axpy8_i4(acc, w[u].x, hsu, hsu * 0.0625f);
+            axpy8_i4(acc + 8, w[u].y, hsu, hsu * 0.0625f);
+            axpy8_i4(acc + 16, w[u].z, hsu, hsu * 0.0625f);
+            axpy8_i4(acc + 24, w[u].w, hsu, hsu * 0.0625f);
+        }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    acc[8 * m + 2 * b] = fmaf(hsu, (float)((lo >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b]);
-                    acc[8 * m + 2 * b + 1] = fmaf(hsu, (float)((hi >> (8 * b)) & 0xFFu), acc[8 * m + 2 * b + 1]);
-                }
-            }
+        for (int u = 0; u < U; ++u) {
+            keep(w[u]);
+            keep(sr[u]);
+            keep(hr[u]);
         }
     }
 #pragma unroll
     for (int j = 0; j < 32; j += 4)
-        s_red[wave][8 * lane + j / 4] =
-            make_float4(fmaf(-8.f, soff, acc[j]), fmaf(-8.f, soff, acc[j + 1]),
-                        fmaf(-8.f, soff, acc[j + 2]), fmaf(-8.f, soff, acc[j + 3]));
+        s_red[wave][8 * lane + j / 4] = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
     __syncthreads();
     // 512 threads x 4 columns each
     float4 s = s_red[0][tid];

@@ -26,15 +26,15 @@ namespace {
 // z[b, j] = W1t[j, :] . x[b, :].  Block: 4 waves = 4 rows.  The row is read in segments of
 // QS 16-byte chunks per lane (all loads of a segment in flight together).
 // CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
-// y accumulators (DEC_NCOPY copies) into y and clears them for this step's down projection.
+// y accumulators (ncopy copies) into y and clears them for this step's down projection.
 template <int QS, bool CONV>
 __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
                                             const uint16_t* __restrict__ W1t, int d, int r,
                                             float* __restrict__ z, long long* __restrict__ yacc,
-                                            float* __restrict__ y) {
+                                            float* __restrict__ y, int ncopy) {
     if (CONV) {
         for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
-            y[i] = from_fx(fx_take(yacc, d, i));
+            y[i] = from_fx(fx_take(yacc, d, i, ncopy));
     }
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
-                              float* z, hipStream_t s, long long* yacc, float* y) {
+                              float* z, hipStream_t s, long long* yacc, float* y, int ncopy) {
 #define PI_P1(QQ) case QQ: \
-    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, yacc, y); \
-    else hipLaunchKernelGGL((k_p1<QQ, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, nullptr, nullptr); \
+    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, yacc, y, ncopy); \
+    else hipLaunchKernelGGL((k_p1<QQ, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
     break;
     switch (pl.qs) {
         PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)

@@ -403,7 +403,6 @@ PI_DEV void run_step(const RunArgs& a, int k, int tid, int b, uint4 (&wa)[4], co
         float acc[Gm::V];
 #pragma unroll
         for (int v = 0; v < Gm::V; ++v) acc[v] = 0.f;
-        float soff = 0.f;
         uint4 w16[U];
         uint2 w8[U];
         uint32_t sr[U];            // raw fp16 scales, one per register
@@ -448,24 +447,11 @@ PI_DEV void run_step(const RunArgs& a, int k, int tid, int b, uint4 (&wa)[4], co
                     }
                 } else {
                     const float hs = hu * h2f((uint16_t)sr[u]);
-                    soff += hs;
-                    const uint32_t wv[2] = {w8[u].x, w8[u].y};
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const uint32_t lo = wv[m] & 0x0F0F0F0Fu, hi = (wv[m] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) {
-                            acc[8 * m + 2 * bb] = fmaf(hs, (float)((lo >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb]);
-                            acc[8 * m + 2 * bb + 1] = fmaf(hs, (float)((hi >> (8 * bb)) & 0xFFu), acc[8 * m + 2 * bb + 1]);
-                        }
-                    }
+                    axpy8_i4(acc, w8[u].x, hs, hs * 0.0625f);
+                    axpy8_i4(acc + 8, w8[u].y, hs, hs * 0.0625f);
                 }
             }
             if (k0 + RN_NW * U < n_loc) load_round(k0 + RN_NW * U, true);
-        }
-        if (WF == 1) {
-#pragma unroll
-            for (int v = 0; v < Gm::V; ++v) acc[v] = fmaf(-8.f, soff, acc[v]);   // stored u = q + 8
         }
         __syncthreads();                      // the ids are dead: their LDS takes the sums
         {

@@ -355,7 +355,7 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
                                    y, i > 0, w, s, k0, k1);
             if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
         }
-        if ((e = launch_decode_finish(pl, d, F, mask, idx, count, y, w, s)) != hipSuccess)
+        if ((e = launch_decode_finish(pl, fused, d, F, mask, idx, count, y, w, s)) != hipSuccess)
             return hip_fail(e, "pi_decode_run final y");
     }
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
