@@ -32,31 +32,39 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
                                             const uint16_t* __restrict__ W1t, int d, int r,
                                             float* __restrict__ z, long long* __restrict__ yacc,
                                             float* __restrict__ y, int ncopy) {
-    if (CONV) {
-        for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
-            y[i] = from_fx(fx_take(yacc, d, i, ncopy));
-    }
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (j >= r) return;
     const int nc = d >> 3;
-    const uint16_t* row = W1t + (size_t)j * d;
     if (B == 1 && nc <= 64 * QS) {
-        // one segment: row and x chunks all in flight together
+        // one segment: row and x chunks all in flight together, issued before the conversion
+        // (whose loads would otherwise hold the row loads back by a memory round trip)
+        const uint16_t* row = W1t + (size_t)(j < r ? j : 0) * d;
         uint4 w[QS], xr[QS];
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
             const int c = lane + 64 * q;
-            w[q] = c < nc ? ld16(row + 8 * c) : zero4();
-            xr[q] = c < nc ? ld16(x + 8 * c) : zero4();
+            w[q] = ld16(row + 8 * (c < nc ? c : 0));
+            xr[q] = ld16(x + 8 * (c < nc ? c : 0));
         }
+        if (CONV) {
+            for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
+                y[i] = from_fx(fx_take(yacc, d, i, ncopy));
+        }
+        if (j >= r) return;
         float acc = 0.f;
 #pragma unroll
-        for (int q = 0; q < QS; ++q) acc = dot8(w[q], xr[q], acc);
+        for (int q = 0; q < QS; ++q)
+            if (lane + 64 * q < nc) acc = dot8(w[q], xr[q], acc);
         acc = wave_sum(acc);
         if (lane == 0) z[j] = acc;
         return;
     }
+    if (CONV) {
+        for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
+            y[i] = from_fx(fx_take(yacc, d, i, ncopy));
+    }
+    if (j >= r) return;
+    const uint16_t* row = W1t + (size_t)j * d;
     for (int b = 0; b < B; ++b) {
         float acc = 0.f;
         for (int c0 = 0; c0 < nc; c0 += 64 * QS) {
