@@ -17,9 +17,10 @@ constexpr int CNT_UNION = 1024;   // union path (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
-// Copies of the fused batch-1 decode step's fixed-point y accumulators (d int64 each): tile t
-// adds into copy t % DEC_NCOPY, which bounds the atomic adds any one address sees per step.
-constexpr int DEC_NCOPY = 16;
+// Most copies of the fused batch-1 decode step's fixed-point y accumulators (d int64 each):
+// tile t adds into copy t % ncopy, which bounds the atomic adds any one address sees per step,
+// at the price of ncopy loads and stores per element when the copies are turned into y.
+constexpr int DEC_NCOPY = 4;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -61,15 +62,16 @@ struct DecPlan {
     int ntile, q;              // tiles of 64 neurons, chunks per lane per up/gate row
     size_t lds_b;              // dynamic LDS of the tile kernel
     bool fused_default;        // the schedule chosen for this shape
+    int ncopy;                 // accumulator copies of the fused schedule (1 or DEC_NCOPY)
     int nslices, nsplit, wps;  // split schedule's down grid: column slices, ranges, mask words per range
     size_t off_z, off_h, off_yacc, bytes;
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
 // One step: two kernels (fused: the tile blocks add their own down partial sums) or three
 // (split: a down kernel over ranges of the mask).  The down projection adds into the
-// fixed-point y accumulators (d int64 in the workspace, DEC_NCOPY copies of them for the fused
-// step, zero before the first step of a run); when convert_prev is set, the first kernel turns the previous step's
-// accumulators into y and clears them.
+// fixed-point y accumulators (pl.ncopy copies of d int64 in the workspace for the fused step,
+// one for the split step; zero before the first step of a run); when convert_prev is set,
+// the first kernel turns the previous step's accumulators into y and clears them.
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl, bool fused,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
                               float* y, bool convert_prev, char* ws, hipStream_t s,

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h, const void* __restrict__ Wd,
-    const uint16_t* __restrict__ Sd, long long* __restrict__ yacc) {
+    const uint16_t* __restrict__ Sd, long long* __restrict__ yacc, int ncopy) {
     constexpr int NT = B_WAVES * 64;
     // row items per wave in flight: as many as the register budget of two blocks per CU
     // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     // column chunks w, w + 8, ... (512 fp16 or 1024 int4 columns: 16 or 8 bytes per lane of
     // each row) and reads that chunk of every active row at once (DN_ROWS in flight; empty
     // slots re-read the first row's chunk, an L2 hit, and count zero).  Its column sums go
-    // into one of DEC_NCOPY fixed-point accumulator copies (copy = tile % DEC_NCOPY) with
+    // into one of ncopy fixed-point accumulator copies (copy = tile % ncopy) with
     // atomic adds: exact, so the order of the tiles does not matter.
     constexpr int CH = WF == 0 ? 512 : 1024;
     constexpr int V = CH / 64;                       // columns per lane
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     __shared__ __align__(16) float s_acc[B_WAVES * CH];
     const int nch = (d + CH - 1) / CH;
     const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
-    long long* accc = yacc + (size_t)(tile % DEC_NCOPY) * d;
+    long long* accc = yacc + (size_t)(tile % ncopy) * d;
     const uint8_t* Wb = static_cast<const uint8_t*>(Wd);
     for (int j = wave; j < nch; j += B_WAVES) {
         const int col0 = j * CH + lane * V;
@@ -430,23 +430,23 @@ __global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc
 template <int WF, bool GLU, int Q, bool FUSED>
 void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-              const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc) {
+              const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
     if (e0)
         hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), (uint32_t)lds, s, e0,
                               e1, 0, z, p.w_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
-                              f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc);
+                              f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
     else
         hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
                            p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
-                           f.s_up, f.d, h, f.w_down, f.s_down, yacc);
+                           f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
 }
 
 template <int WF, bool GLU, bool FUSED>
 hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                       const float* z, const pi_pred_desc& p, float theta, float* logits,
                       uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h,
-                      long long* yacc) {
-#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc); break;
+                      long long* yacc, int ncopy) {
+#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy); break;
     if constexpr (WF == 0) {
         switch (q) {
             PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
@@ -466,14 +466,14 @@ hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, h
 template <bool FUSED>
 hipError_t dispatch_b_fmt(const DecPlan& pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
                           const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-                          const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc) {
+                          const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
     const bool glu = f.act == PI_ACT_REGLU;
     const dim3 gb(pl.ntile);
     if (f.wfmt == PI_W_F16)
-        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)
-                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
-    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)
-               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
+        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy)
+                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
+    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy)
+               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
 }
 
 }  // namespace
@@ -489,6 +489,10 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     // extra kernel boundary win above about 2^20 adds (between the LLaMA-7B-shaped layer,
     // 0.7M adds, faster fused, and the OPT-30B-shaped one, 3.2M, faster split)
     p.fused_default = (long long)p.ntile * d <= (1LL << 20);
+    // fused: spreading the adds over copies pays where turning the copies into y is cheap
+    // (tiny ReLU layer, d = 1024: 4 copies 10.9 us/step, 1 copy 11.3); at d = 4096 one copy
+    // wins (LLaMA-7B-shaped: 17.2 us against 17.7 with 4 and 18.6 with 16)
+    p.ncopy = d <= 2048 ? DEC_NCOPY : 1;
     const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
     p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
@@ -520,11 +524,11 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y,
-                                      fused ? DEC_NCOPY : 1);
+    const int ncopy = fused ? pl.ncopy : 1;
+    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y, ncopy);
     if (e != hipSuccess) return e;
-    if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc);
-    if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc)) != hipSuccess)
+    if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
+    if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, 1)) != hipSuccess)
         return e;
     const dim3 gc(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16)
@@ -539,7 +543,7 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
 hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s) {
     long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, fused ? DEC_NCOPY : 1, y, d,
+    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, fused ? pl.ncopy : 1, y, d,
                        mask, F, idx, count);
     return hipGetLastError();
 }
