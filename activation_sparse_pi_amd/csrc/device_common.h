@@ -106,9 +106,32 @@ PI_DEV void keep(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), 
 PI_DEV void keep(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
 PI_DEV void keep(uint32_t& v) { asm volatile("" : "+v"(v)); }
 PI_DEV void keep(float& v) { asm volatile("" : "+v"(v)); }
+// keep() for the NB loaded bytes of an ld_n value
+template <int NB>
+PI_DEV void keep_n(uint4& v) {
+    if constexpr (NB == 16) {
+        keep(v);
+    } else if constexpr (NB == 8) {
+        asm volatile("" : "+v"(v.x), "+v"(v.y));
+    } else {
+        asm volatile("" : "+v"(v.x));
+    }
+}
 
 // 16-byte global load
 PI_DEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// NB-byte (16, 8 or 4) global load into the low words of a uint4 (the rest zero)
+template <int NB>
+PI_DEV uint4 ld_n(const void* p) {
+    if constexpr (NB == 16) {
+        return *reinterpret_cast<const uint4*>(p);
+    } else if constexpr (NB == 8) {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        return make_uint4(t.x, t.y, 0u, 0u);
+    } else {
+        return make_uint4(*reinterpret_cast<const uint32_t*>(p), 0u, 0u, 0u);
+    }
+}
 PI_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // ---- wave-level (DPP: cross-lane moves inside the VALU, no LDS round trip) ----------------------

@@ -44,6 +44,12 @@ constexpr int DEC_IDCAP = 4096;   // neuron ids one split-schedule down block ho
 // (x0,x4),(x1,x5),(x2,x6),(x3,x7) to match the nibble pairs one AND/OR extracts).
 constexpr int B_WAVES = 8;   // waves per tile block (two blocks fit on a CU)
 
+// Columns per lane of the fused down chunks: 8 fp16 (16-byte loads) or 16 int4 (8-byte loads)
+// where the layer is wide enough to give each of the 8 waves a chunk, fewer below that.
+constexpr int down_cols_per_lane(int wf, int q) {
+    return wf == 0 ? (q <= 2 ? 2 : q <= 4 ? 4 : 8) : (q <= 2 ? 8 : 16);
+}
+
 template <int WF, bool GLU, int Q, bool FUSED>
 __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const float* __restrict__ z, const uint16_t* __restrict__ W2t,
@@ -188,13 +194,14 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     if (na == 0) return;
 
     // --- down: y += sum over the tile's active neurons of h_k W_down[row_k, :].  Wave w takes
-    // column chunks w, w + 8, ... (512 fp16 or 1024 int4 columns: 16 or 8 bytes per lane of
-    // each row) and reads that chunk of every active row at once (DN_ROWS in flight; empty
-    // slots re-read the first row's chunk, an L2 hit, and count zero).  Its column sums go
-    // into one of ncopy fixed-point accumulator copies (copy = tile % ncopy) with
-    // atomic adds: exact, so the order of the tiles does not matter.
-    constexpr int CH = WF == 0 ? 512 : 1024;
-    constexpr int V = CH / 64;                       // columns per lane
+    // column chunks w, w + 8, ... (64 V columns: V fp16 or int4 weights per lane of each row,
+    // V as large as leaves no wave without a chunk) and reads that chunk of every active row
+    // at once (DN_ROWS in flight; empty slots re-read the first row's chunk, an L2 hit, and
+    // count zero).  Its column sums go into one of ncopy fixed-point accumulator copies (copy
+    // = tile % ncopy) with atomic adds: exact, so the order of the tiles does not matter.
+    constexpr int V = down_cols_per_lane(WF, Q);     // columns per lane
+    constexpr int CH = 64 * V;
+    constexpr int NB = WF == 0 ? 2 * V : V / 2;      // bytes per lane per row
     constexpr int DN_ROWS = 16;
     __shared__ __align__(16) float s_acc[B_WAVES * CH];
     const int nch = (d + CH - 1) / CH;
@@ -210,8 +217,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.f;
         for (int k0 = 0; k0 < na; k0 += DN_ROWS) {
-            uint4 w16[DN_ROWS];
-            uint2 w8[DN_ROWS];
+            uint4 wv[DN_ROWS];         // NB bytes used
             uint32_t sr[DN_ROWS];
             float hv[DN_ROWS];
 #pragma unroll
@@ -220,45 +226,41 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
                 const int kk = k < na ? k : 0;
                 const size_t row = (size_t)(tile * 64 + s_list[kk]);
                 hv[u] = (k < na && cok) ? s_h[kk] : 0.f;
-                if (WF == 0) {
-                    w16[u] = ld16(Wb + row * rowb + boff);
-                } else {
-                    w8[u] = *reinterpret_cast<const uint2*>(Wb + row * rowb + boff);
-                    sr[u] = (uint32_t)Sd[row * G + sg];
-                }
+                wv[u] = ld_n<NB>(Wb + row * rowb + boff);
+                if (WF == 1) sr[u] = (uint32_t)Sd[row * G + sg];
             }
 #pragma unroll
             for (int u = 0; u < DN_ROWS; ++u) {
                 if (k0 + u >= na) continue;              // empty slots: loaded, never used
+                const uint32_t ww[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
                 if (WF == 0) {
-                    const uint32_t ww[4] = {w16[u].x, w16[u].y, w16[u].z, w16[u].w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
+                    for (int e = 0; e < V / 2; ++e) {
                         acc[2 * e] = fmaf(hv[u], lo_f(ww[e]), acc[2 * e]);
                         acc[2 * e + 1] = fmaf(hv[u], hi_f(ww[e]), acc[2 * e + 1]);
                     }
                 } else {
                     const float hs = hv[u] * h2f((uint16_t)sr[u]);
-                    axpy8_i4(acc, w8[u].x, hs, hs * 0.0625f);
-                    axpy8_i4(acc + 8, w8[u].y, hs, hs * 0.0625f);
+#pragma unroll
+                    for (int e = 0; e < V / 8; ++e) axpy8_i4(acc + 8 * e, ww[e], hs, hs * 0.0625f);
                 }
             }
 #pragma unroll
             for (int u = 0; u < DN_ROWS; ++u) {
-                if (WF == 0) {
-                    keep(w16[u]);
-                } else {
-                    keep(w8[u]);
-                    keep(sr[u]);
-                }
+                keep_n<NB>(wv[u]);
+                if (WF == 1) keep(sr[u]);
             }
         }
         // transpose through the wave's LDS slice so that each atomic instruction covers 64
         // consecutive columns (512 contiguous bytes) instead of 64 lanes 8 * V bytes apart
         float* sa = s_acc + wave * CH;
+        if constexpr (V == 2) {
+            *reinterpret_cast<float2*>(sa + lane * V) = make_float2(acc[0], acc[1]);
+        } else {
 #pragma unroll
-        for (int v = 0; v < V; v += 4)
-            *reinterpret_cast<float4*>(sa + lane * V + v) = make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+            for (int v = 0; v < V; v += 4)
+                *reinterpret_cast<float4*>(sa + lane * V + v) = make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+        }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int v = 0; v < V; ++v) {
