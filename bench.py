@@ -148,26 +148,49 @@ def copy_probe(mb, dev):
 
 
 # ------------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(inputs, budget_s):
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_rate(inputs, W, X, budget_s, limit):
+    import oracle.pi_oracle as O
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s and n < limit:
+        O.token_step(inputs, W, X[n % X.shape[0]])
+        n += 1
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(inputs, budget_s):
+    """The oracle on the host: about two thirds of the budget with every BLAS thread, the rest
+    with one thread (reported beside it)."""
     import oracle.pi_oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     W = O.Weights.from_inputs(inputs)
     X = inputs["x"][:, 0, :]
-    t0 = time.perf_counter()
-    n = 0
-    while time.perf_counter() - t0 < budget_s and n < X.shape[0] * 4:
-        O.token_step(inputs, W, X[n % X.shape[0]])
-        n += 1
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} tokens of the same stream (wrapping), one at a time, "
-                      f"numpy float64, {dt:.1f} s"}
+    n, dt = _oracle_rate(inputs, W, X, budget_s * 2 / 3, X.shape[0] * 4)
+    out = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {n} tokens of the same stream (wrapping), one at a time, "
+                     f"numpy float64, {dt:.1f} s", "cpu_model": cpu_model()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, dt1 = _oracle_rate(inputs, W, X, budget_s / 3, X.shape[0] * 4)
+        out["single_thread"] = {"value": n1 / dt1, "unit": "tokens/s",
+                                "sample": f"first {n1} tokens, one BLAS thread, {dt1:.1f} s"}
+    return out
 
 
 # ------------------------------------------------------------------------------- batch path
