@@ -294,3 +294,37 @@ def test_operators_match_sparse_ffn():
                        bufs["y"].data_ptr())
         torch.cuda.synchronize()
         assert torch.equal(bufs["y"], ref["y"])
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_decode_run_graph_replay(mode):
+    """A run captured into a HIP graph (the library records kernels only: no memset, no host
+    sync) replays bit-identically to the same run enqueued eagerly, three times, with eager
+    runs of other steps in between."""
+    cfg = configs.C1
+    inp = _full("c1")
+    layer = _layer(inp, replicas=3)
+    xd = torch.from_numpy(inp["x"][:, 0, :].copy()).to(layer.device)
+    m = _run_modes()[mode]
+    bufs = layer.buffers(1)
+    layer.decode_run(xd.data_ptr(), cfg.T, 5, 9, bufs, mode=m)
+    torch.cuda.synchronize()
+    ref = {k: bufs[k].clone() for k in ("y", "mask", "idx", "count")}
+    side = torch.cuda.Stream(device=layer.device)
+    side.wait_stream(torch.cuda.current_stream(layer.device))
+    with torch.cuda.stream(side):
+        layer.decode_run(xd.data_ptr(), cfg.T, 0, 2, bufs, mode=m)
+    torch.cuda.current_stream(layer.device).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.decode_run(xd.data_ptr(), cfg.T, 5, 9, bufs, mode=m)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        c = int(ref["count"][0].item())
+        assert int(bufs["count"][0].item()) == c, f"replay {rep}: count"
+        assert torch.equal(bufs["idx"][0, :c], ref["idx"][0, :c]), f"replay {rep}: table"
+        assert torch.equal(bufs["mask"], ref["mask"]) and torch.equal(bufs["y"], ref["y"]), f"replay {rep}"
+        layer.decode_run(xd.data_ptr(), cfg.T, 20 + rep, 4, bufs, mode=m)   # eager work in between
+        torch.cuda.synchronize()
