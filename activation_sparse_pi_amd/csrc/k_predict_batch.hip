@@ -15,9 +15,9 @@
 //            runs of 64 and stream rows and x through the staged 32 x 32 MFMA tile; the
 //            waves meet in LDS; the shares meet in the workspace, added in a fixed order
 //            by the last-arriving block of the row tile.
-//   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  All of
-//            the block's W2t loads are issued first, then z is scaled, split and staged in
-//            LDS; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
+//   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  The
+//            block's z loads, then all of its W2t loads are issued first; z is scaled, split
+//            and staged in LDS while the W2t rows are in flight; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
 //            and one wave ballot per 64 neurons of a token gives two mask words.
 #include "internal.h"
 #include "mfma_tile.h"
@@ -149,11 +149,14 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
             zr[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+    // z first: it is small and in L2, and a load waits for every load issued before it,
+    // so issued behind the W2t rows it would only arrive with them
+    if (r <= ZC) load_z(0);
     load_w(0);
     // 1. per-token exponent e: the largest |z| of the token brought into [2^14, 2^15)
     float m = 0.f;
     for (int c0 = 0; c0 < r; c0 += ZC) {       // a rank of at most ZC leaves its z in zr
-        load_z(c0);
+        if (r > ZC) load_z(c0);
 #pragma unroll
         for (int i = 0; i < 2 * (ZC / 128); ++i) m = absmax4(m, zr[i]);
     }
