@@ -19,14 +19,16 @@
 //         written in the down kernel's A-operand order ("H fragments": for each group
 //         of 16 union positions, 64 lanes x 16 bytes, lane l holding positions
 //         8 (l / 32) .. + 7 of token l % 32), so that operand is one 1 KB load.
-//   down  y[b, :] = sum_k H[b, k] W_down[u_k, :].  Block = 64 columns (one 128-byte
-//         line of every row) x one of KS interleaved shares of the union list; its 8
-//         waves take stages of 64 union positions round-robin.  Per stage a lane loads
-//         16 bytes of 8 consecutive rows, transposes the 8 x 8 fp16 block in registers
-//         into 8 column vectors of 8 positions (exactly B-operand units) and writes them
-//         to LDS; then 4 K-steps x 2 column tiles of MFMA.  The waves meet in LDS; with
-//         KS > 1 the shares meet in the workspace and the last-arriving block of the
-//         column group adds them in a fixed order (bitwise reproducible).
+//   down  y[b, :] = sum_k H[b, k] W_down[u_k, :].  Block = 256 columns (512 contiguous
+//         bytes of every row) x one of KS interleaved shares of the union list; its 8 waves
+//         take stages of 16 union positions round-robin.  Per stage a lane loads 16 bytes of
+//         8 consecutive rows, transposes the 8 x 8 fp16 block in registers into 8 column
+//         vectors of 8 positions (exactly B-operand units) and writes them to LDS; then one
+//         MFMA per 32-column tile (8 per stage) with the stage's H fragment as A.  Wide
+//         blocks read long pieces of each row and re-read the H fragments (from L2) for
+//         fewer columns.  The waves meet in LDS; with KS > 1 the shares meet in the
+//         workspace and the last-arriving block of the column group adds them in a fixed
+//         order (bitwise reproducible).
 #include "internal.h"
 #include "mfma_tile.h"
 
@@ -34,8 +36,9 @@ namespace pi {
 namespace {
 
 constexpr int UP_NW = 8;      // waves per up block
-constexpr int DN_NWU = 8;     // waves per down block
-constexpr int DN_COLS = 64;   // columns per down block
+constexpr int DN_NWU = 4;     // waves per down block (one per SIMD)
+constexpr int DN_COLS = 256;  // columns per down block
+constexpr int DN_TILES = DN_COLS / 32;   // 32-column MFMA tiles per down block
 
 PI_DEV bool bit_of(const uint32_t* __restrict__ mask, int W, int b, int i) {
     return (mask[(size_t)b * W + (i >> 5)] >> (i & 31)) & 1u;
@@ -125,143 +128,232 @@ __global__ __launch_bounds__(UP_NW * 64) void k_union_up(
 }
 
 // ------------------------------------------------------------------------------------ down
-// column c of a stage keeps k-block kb in unit kb * 64 + (c ^ ((c >> 3) & 7))
-PI_DEV int dn_slot(int c) { return c ^ ((c >> 3) & 7); }
+// Loads: one instruction brings 512 contiguous bytes (the block's 256 columns) of one row,
+// 8 bytes per lane, from a wave-uniform row address (row ids move to scalar registers) and a
+// fixed per-lane offset.  Loader lane l takes column chunk pl(l) (4 columns); after 16 rows
+// (a stage) it holds 4 columns x 16 positions, transposed in registers into 8 B-operand
+// units (column 4 pl + e, k-half hh: 8 positions).
+// Stage layout (16-byte units): unit(4 m + e, hh) = hh * DN_HS + 65 e + q(m), with
+//   q(m) = g(m / 8) + z(m % 8),  g(t) = 2 (t % 2) + 16 (t / 2),  z(i) = 4 (i % 4) + i / 4,
+// so a staging write is base(l) + hh * DN_HS + 65 e and the operand read of tile t is
+// base(n) + g(t): one address register each, the rest immediate offsets.  With
+//   pl(l) = 8 t + i,  t = 2 (l / 16) + (l / 4) % 2,  i = l % 2 + 2 ((l / 8) % 2) + 4 ((l / 2) % 2)
+// both the writes and the reads touch distinct banks within every group of 8 and of 16 lanes.
+constexpr int DN_HS = 4 * 65;                 // units per k-half
+constexpr int DN_NB = 3;                      // stages in flight per wave
+PI_DEV int dn_g(int t) { return 2 * (t & 1) + 16 * (t >> 1); }
+PI_DEV int dn_z(int i) { return 4 * (i & 3) + (i >> 2); }
 
+// Pipeline (per wave, its stages s, s + nw, s + 2 nw, ...): DN_NB stages of rows in flight;
+// the row ids of a stage are loaded 2 DN_NB - 1 stages ahead, before the rows of the stage
+// DN_NB - 1 ahead, so that (loads completing in order) waiting for ids never waits for rows
+// in flight.  The steady loop issues every load unconditionally and is unrolled DN_NB times
+// so the buffers rotate without copies; the last stages run in a drain whose waits may be
+// conservative.
 __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
     const uint4* __restrict__ Hf, int B, const uint16_t* __restrict__ Wd, int d, int F,
     const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucount, int ncg, int nks,
     float* __restrict__ part, unsigned* __restrict__ counter, float* __restrict__ y) {
-    __shared__ uint4 s_t[DN_NWU][8][64];             // per wave: k-block, swizzled column unit
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NB = DN_NB;
+    __shared__ uint4 s_t[DN_NWU][2 * DN_HS];         // per wave: two k-halves x 256 column units
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cgi = blockIdx.x % ncg, ks = blockIdx.x / ncg;
     const int U = min(*ucount, F);
     const int c0 = cgi * DN_COLS;
-    const int nst = (U + 63) / 64;                    // stages of 64 union positions
+    const int nst = (U + 15) / 16;                    // stages of 16 union positions
     const int nw = nks * DN_NWU;                      // waves sharing the list
-    // loader role: lane -> rows 8 rbk .. 8 rbk + 7 of a stage, columns 8 ch .. 8 ch + 7
-    const int rbk = lane >> 3, ch = lane & 7;
-    const bool col_ok = c0 + ch * 8 < d;
+    // loader role: columns 4 pl .. 4 pl + 3 of the block (byte offset voff of each row piece;
+    // columns past d read the block's first columns and only reach outputs never written)
+    const int pl = 8 * (2 * (lane >> 4) + ((lane >> 2) & 1)) + (lane & 1) + 2 * ((lane >> 3) & 1) +
+                   4 * ((lane >> 1) & 1);
+    const uint32_t voff = c0 + 4 * pl < d ? 8u * pl : 0u;
     // MFMA role: B column n of each 32-column tile, k half h
     const int n = lane & 31, h = lane >> 5;
-    const int slot0 = dn_slot(n), slot1 = dn_slot(32 + n);
-    uint4(*st)[64] = s_t[wave];
+    uint4* const stw = s_t[wave] + dn_g(pl >> 3) + dn_z(pl & 7);                        // writes
+    const uint4* const str = s_t[wave] + h * DN_HS + 65 * (n & 3) + dn_z(n >> 2);        // reads
 
-    f32x16_t acc0 = {}, acc1 = {};
-    int rows[8];
-    uint4 R[8], Rn[8], A[4], An[4];
-    auto load_rows = [&](int s) {
+    f32x16_t acc[DN_TILES];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int k = s * 64 + rbk * 8 + j;
-            int r = (s < nst && k < U) ? uidx[k] : -1;
-            rows[j] = (unsigned)r < (unsigned)F ? r : -1;
+    for (int t = 0; t < DN_TILES; ++t) acc[t] = f32x16_t{};
+    // a stage's 16 row ids: lane l holds the id at position l % 16 (clamped into the list)
+    auto load_ids = [&](int st_) { return uidx[min(st_ * 16 + (lane & 15), U - 1)]; };
+    // issue the rows of stage st_ and return its (wave-uniform) mask of rows to zero: a
+    // position past the union, or holding an id outside [0, F), reads row 0
+    auto load_w = [&](int st_, int ids, uint2(&v)[16]) {
+        unsigned bad = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int id = __builtin_amdgcn_readlane(ids, j);
+            const bool ok = st_ * 16 + j < U && (unsigned)id < (unsigned)F;
+            bad |= ok ? 0u : 1u << j;
+            const char* row = reinterpret_cast<const char*>(Wd + ((size_t)(ok ? id : 0) * d + c0));
+            v[j] = *reinterpret_cast<const uint2*>(row + voff);
         }
+        return bad;
     };
-    auto load_w = [&](uint4(&v)[8]) {
+    auto load_a = [&](int st_) { return Hf[(size_t)st_ * 64 + lane]; };
+    // stage: zero the invalid rows, transpose into 8 units (column 4 pl + e, k-half hh), write
+    // them to the wave's LDS area, one MFMA per 32-column tile
+    auto stage = [&](unsigned bad, uint2(&R)[16], const uint4& A) {
+        if (bad) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = (rows[j] >= 0 && col_ok) ? ld16(Wd + (size_t)rows[j] * d + c0 + ch * 8) : zero4();
-    };
-    auto load_a = [&](int s, uint4(&a)[4]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int g = s * 4 + q;                  // group of 16 positions
-            a[q] = g * 16 < U ? Hf[(size_t)g * 64 + lane] : zero4();
+            for (int j = 0; j < 16; ++j)
+                if ((bad >> j) & 1u) R[j] = make_uint2(0u, 0u);
         }
-    };
-    int s = ks * DN_NWU + wave;
-    if (s < nst) {
-        load_rows(s);
-        load_w(R);
-        load_a(s, A);
-        load_rows(s + nw);
-    }
-    for (; s < nst; s += nw) {
-        const int sn = s + nw;
-        if (sn < nst) {
-            load_w(Rn);
-            load_a(sn, An);
-            load_rows(sn + nw);
-        }
-        // 8 x 8 transpose: unit e = column 8 ch + e over rows 8 rbk .. 8 rbk + 7
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t o[4];
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t lo = (&R[2 * p].x)[e >> 1], hi = (&R[2 * p + 1].x)[e >> 1];
-                o[p] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+            for (int e = 0; e < 4; ++e) {
+                uint32_t o[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint2& lo = R[8 * hh + 2 * p];
+                    const uint2& hi = R[8 * hh + 2 * p + 1];
+                    o[p] = __builtin_amdgcn_perm((e >> 1) ? hi.y : hi.x, (e >> 1) ? lo.y : lo.x,
+                                                 (e & 1) ? 0x07060302u : 0x05040100u);
+                }
+                stw[hh * DN_HS + 65 * e] = make_uint4(o[0], o[1], o[2], o[3]);
             }
-            st[rbk][8 * ch + (e ^ ch)] = make_uint4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+        for (int t = 0; t < DN_TILES; ++t) acc[t] = mfma16(A, str[dn_g(t)], acc[t]);
+    };
+
+    int s = ks * DN_NWU + wave;
+    uint2 R[NB][16];
+    uint4 A[NB];
+    unsigned bad[NB];
+    int ids[NB];
+    if (s + (2 * NB - 1) * nw < nst) {
+        // ids slot b holds the ids of stage s + (b + NB) nw, buffer b the rows of s + b nw
+        int id0[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) id0[b] = load_ids(s + b * nw);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ids[b] = load_ids(s + (b + NB) * nw);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            bad[b] = load_w(s + b * nw, id0[b], R[b]);
+            A[b] = load_a(s + b * nw);
+        }
+        do {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                // stage s + b nw: refill its buffer with stage s + (b + NB) nw (ids in slot b),
+                // then load the ids of stage s + (b + 2 NB) nw into slot b
+                stage(bad[b], R[b], A[b]);
+                const int nid = load_ids(s + (b + 2 * NB) * nw);
+                asm volatile("" ::: "memory");
+                bad[b] = load_w(s + (b + NB) * nw, ids[b], R[b]);
+                A[b] = load_a(s + (b + NB) * nw);
+                ids[b] = nid;
+            }
+            s += NB * nw;
+        } while (s + (2 * NB - 1) * nw < nst);
+        // drain: buffers hold stages s .. s + (NB - 1) nw, slots the ids of the next NB
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (s + b * nw < nst) stage(bad[b], R[b], A[b]);
+            if (s + (b + NB) * nw < nst) {
+                bad[b] = load_w(s + (b + NB) * nw, ids[b], R[b]);
+                A[b] = load_a(s + (b + NB) * nw);
+            }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int kb = 2 * q + h;
-            acc0 = mfma16(A[q], st[kb][slot0], acc0);
-            acc1 = mfma16(A[q], st[kb][slot1], acc1);
+        for (int b = 0; b < NB; ++b)
+            if (s + (b + NB) * nw < nst) stage(bad[b], R[b], A[b]);
+    } else {
+        // fewer than 2 NB - 1 stages: one at a time
+        for (; s < nst; s += nw) {
+            bad[0] = load_w(s, load_ids(s), R[0]);
+            A[0] = load_a(s);
+            stage(bad[0], R[0], A[0]);
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) R[j] = Rn[j];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) A[q] = An[q];
     }
 
-    // the waves meet in LDS
-    float* red = reinterpret_cast<float*>(&s_t[wave][0][0]);
+    // the waves meet in LDS, one column tile at a time (32 tokens x 32 columns); thread o of
+    // a tile takes outputs o + q * DN_NWU * 64 (q < DN_OPT): register (o / 64) % 16, lane o % 64
+    constexpr int OPT = 1024 / (DN_NWU * 64);         // outputs per thread per tile
+    float v[OPT * DN_TILES];
+    int ob[OPT], oc[OPT];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        red[r * 64 + lane] = acc0[r];
-        red[1024 + r * 64 + lane] = acc1[r];
-    }
-    __syncthreads();
-    // 32 tokens x 64 columns, four per thread; output o: tile o / 1024, register
-    // (o / 64) % 16, lane o % 64
-    float v[4];
-    int ob[4], oc[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int o = tid + q * DN_NWU * 64;
-        const int nt = o >> 10, r = (o >> 6) & 15, l = o & 63;
-        float t = 0.f;
-#pragma unroll
-        for (int w = 0; w < DN_NWU; ++w)
-            t += reinterpret_cast<const float*>(&s_t[w][0][0])[nt * 1024 + r * 64 + l];
-        v[q] = t;
+    for (int q = 0; q < OPT; ++q) {
+        const int o = tid + q * DN_NWU * 64, r = (o >> 6) & 15, l = o & 63;
         ob[q] = (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
-        oc[q] = c0 + nt * 32 + (l & 31);
+        oc[q] = l & 31;
     }
+    float* red = reinterpret_cast<float*>(&s_t[0][0]);    // DN_NWU waves x 1024 floats
+#pragma unroll
+    for (int t = 0; t < DN_TILES; ++t) {
+        __syncthreads();                              // staging (or the previous tile) read
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lane] = acc[t][r];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < OPT; ++q) {
+            const int o = tid + q * DN_NWU * 64;
+            float a = 0.f;
+#pragma unroll
+            for (int w = 0; w < DN_NWU; ++w) a += red[w * 1024 + o];
+            v[OPT * t + q] = a;
+        }
+    }
+    auto row_of = [&](int i) { return ob[i % OPT]; };                              // token
+    auto col = [&](int i) { return c0 + (i / OPT) * 32 + oc[i % OPT]; };          // column
+    constexpr int NV = OPT * DN_TILES;
     if (nks == 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (ob[q] < B && oc[q] < d) y[(size_t)ob[q] * d + oc[q]] = v[q];
+        for (int i = 0; i < NV; ++i)
+            if (row_of(i) < B && col(i) < d) y[(size_t)row_of(i) * d + col(i)] = v[i];
         return;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (ob[q] < B && oc[q] < d) st_agent(&part[((size_t)ks * 32 + ob[q]) * d + oc[q]], v[q]);
+    for (int i = 0; i < NV; ++i)
+        if (row_of(i) < B && col(i) < d) st_agent(&part[((size_t)ks * 32 + row_of(i)) * d + col(i)], v[i]);
     if (!last_block_arrive(&counter[cgi], nks)) return;
-    // the other shares' partials, up to 16 loads in flight per round, added in share order
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < nks; k0 += 4) {
-        float pv[4][4];
+    // The last block of the column group adds every share's partial (its own included) in
+    // share order.  Chunk q = tid + 256 m (m < 8) is token q / 64 (wave-uniform), columns
+    // c0 + 4 (q % 64) .. + 3; 32 coherent 16-byte loads are in flight per round (4 chunks x
+    // 8 shares).  Loads past the buffer (shares >= nks) return zeros; columns past d are
+    // summed but never stored.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        part, 0, (int)((size_t)nks * 32 * d * sizeof(float)), 0x00020000);
+    const int j4 = 4 * (tid & 63);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+    for (int m0 = 0; m0 < 8; m0 += 4) {
+        if (wave + 4 * m0 >= B) break;                // tokens of this round: none left
+        float4 t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k0 = 0; k0 < nks; k0 += 8) {
+            float4 pv[4][8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int k2 = k0 + i;
-                pv[q][i] = (k2 < nks && k2 != ks && ob[q] < B && oc[q] < d)
-                               ? ld_agent(&part[((size_t)k2 * 32 + ob[q]) * d + oc[q]]) : 0.f;
+                const int b = wave + 4 * (m0 + i);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int off = (((k0 + kk) * 32 + b) * d + c0 + j4) * (int)sizeof(float);
+                    const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);   // sc1
+                    pv[i][kk] = __builtin_bit_cast(float4, r);
+                }
             }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (k0 + i < nks) t[q] += k0 + i == ks ? v[q] : pv[q][i];
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (ob[q] < B && oc[q] < d) y[(size_t)ob[q] * d + oc[q]] = t[q];
+                for (int kk = 0; kk < 8; ++kk) {
+                    t[i].x += pv[i][kk].x;
+                    t[i].y += pv[i][kk].y;
+                    t[i].z += pv[i][kk].z;
+                    t[i].w += pv[i][kk].w;
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = wave + 4 * (m0 + i);
+            if (b < B && c0 + j4 < d) *reinterpret_cast<float4*>(&y[(size_t)b * d + c0 + j4]) = t[i];
+        }
+    }
 }
 
 }  // namespace
