@@ -23,7 +23,8 @@ PI_MAX_BATCH = 32
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
-           "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu")
+           "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
+           "pi_place_neurons", "pi_permute_rows", "pi_map_ids")
 
 
 class PredDesc(ctypes.Structure):
@@ -89,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.pi_ffn_dense_ref_gpu.argtypes = [P(FfnDesc), c_void_p, c_int, c_void_p, c_void_p,
                                            c_size_t, c_void_p]
         L.pi_ffn_dense_ref_gpu.restype = c_int
+        L.pi_place_neurons.argtypes = [c_void_p, c_int, c_void_p]
+        L.pi_place_neurons.restype = c_int
+        L.pi_permute_rows.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_size_t, c_void_p]
+        L.pi_permute_rows.restype = c_int
+        L.pi_map_ids.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
+        L.pi_map_ids.restype = c_int
         _LIB = L
     return _LIB
 
@@ -154,3 +161,16 @@ def check(status: int) -> None:
     """Raise PiError with the library's message for a non-zero status."""
     if status != PI_OK:
         raise PiError(status, f"{pi_status_string(status)}: {pi_last_error()}")
+
+
+def pi_place_neurons(counts: int, F: int, perm: int) -> int:
+    """counts and perm are host addresses (int32 [F]), e.g. ndarray.ctypes.data."""
+    return lib().pi_place_neurons(counts, F, perm)
+
+
+def pi_permute_rows(src, dst, perm, n, row_bytes, stream) -> int:
+    return lib().pi_permute_rows(src, dst, perm, n, row_bytes, stream)
+
+
+def pi_map_ids(idx, count, B, F, perm, out, stream) -> int:
+    return lib().pi_map_ids(idx, count, B, F, perm, out, stream)

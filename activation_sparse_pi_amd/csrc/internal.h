@@ -170,5 +170,9 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
                             float* y, char* ws, hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* perm, int n,
+                               size_t row_bytes, hipStream_t s);
+hipError_t launch_map_ids(const int32_t* idx, const int32_t* count, int B, int F,
+                          const int32_t* perm, int32_t* out, hipStream_t s);
 
 }  // namespace pi

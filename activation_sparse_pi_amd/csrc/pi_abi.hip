@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -379,6 +380,52 @@ int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_dense_ref_gpu launch");
     }
     return ok();
+}
+
+int pi_place_neurons(const int32_t* counts, int F, int32_t* perm) {
+    if (!counts || !perm) return fail(PI_ERR_NULL, "counts / perm NULL");
+    if (F <= 0) return fail(PI_ERR_SHAPE, "F must be positive (F=%d)", F);
+    for (int i = 0; i < F; ++i)
+        if (counts[i] < 0) return fail(PI_ERR_SHAPE, "negative count %d at neuron %d", counts[i], i);
+    // rank: descending count, ties by ascending original index
+    std::vector<int32_t> order(F);
+    for (int i = 0; i < F; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+    // deal the ranks over the 64-neuron tiles in serpentine order, skipping full tiles
+    const int T = (F + 63) / 64;
+    std::vector<int> fill(T, 0);
+    auto cap = [&](int t) { return t == T - 1 ? F - 64 * (T - 1) : 64; };
+    int t = 0, dir = 1;
+    auto advance = [&]() {
+        t += dir;
+        if (t == T) { t = T - 1; dir = -1; }
+        if (t < 0) { t = 0; dir = 1; }
+    };
+    for (int k = 0; k < F; ++k) {
+        while (fill[t] == cap(t)) advance();
+        perm[t * 64 + fill[t]] = order[k];
+        ++fill[t];
+        advance();
+    }
+    return ok();
+}
+
+int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size_t row_bytes,
+                    void* stream) {
+    if (!src || !dst || !perm) return fail(PI_ERR_NULL, "src / dst / perm NULL");
+    if (n <= 0 || row_bytes == 0) return fail(PI_ERR_SHAPE, "need n > 0 and row_bytes > 0 (n=%d)", n);
+    const hipError_t e = launch_permute_rows(src, dst, perm, n, row_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pi_permute_rows");
+}
+
+int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int32_t* perm,
+               int32_t* out, void* stream) {
+    if (!idx || !count || !perm || !out) return fail(PI_ERR_NULL, "idx / count / perm / out NULL");
+    if (F <= 0) return fail(PI_ERR_SHAPE, "F must be positive (F=%d)", F);
+    if (int st = check_batch(B); st != PI_OK) return st;
+    const hipError_t e = launch_map_ids(idx, count, B, F, perm, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pi_map_ids");
 }
 
 }  // extern "C"

@@ -20,7 +20,10 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 class DeviceLayer:
     def __init__(self, inputs: dict, replicas: int = 1, B_max: int = 1, device="cuda",
-                 threshold: float = 0.5):
+                 threshold: float = 0.5, perm: np.ndarray | None = None):
+        """perm: optional neuron placement (int32 [F], placed position p holds original
+        neuron perm[p], from ``pi_place_neurons``): every per-neuron array is permuted on the
+        device with ``pi_permute_rows``; ``map_ids`` turns placed ids back into original ones."""
         cfg = inputs["cfg"]
         self.cfg, self.d, self.F, self.r = cfg, cfg.d, cfg.F, cfg.r
         self.act = L.PI_ACT_REGLU if cfg.act == "reglu" else L.PI_ACT_RELU
@@ -35,6 +38,20 @@ class DeviceLayer:
         host["w_p1"] = np.ascontiguousarray(inputs["w_p1"].T)    # [r, d]
         host["w_p2"] = np.ascontiguousarray(inputs["w_p2"].T)    # [F, r]
         base = {k: _dev(v, self.device) for k, v in host.items()}
+        self.perm = None
+        if perm is not None:
+            perm = np.ascontiguousarray(perm, dtype=np.int32)
+            if perm.shape != (cfg.F,):
+                raise ValueError(f"perm must be int32 [{cfg.F}]")
+            self.perm = _dev(perm, self.device)
+            for k in names:                     # every array here is one row per neuron but W_p1^T
+                if k == "w_p1":
+                    continue
+                src = base[k]
+                dst = torch.empty_like(src)
+                L.check(L.pi_permute_rows(src.data_ptr(), dst.data_ptr(), self.perm.data_ptr(), cfg.F,
+                                          src.numel() * src.element_size() // cfg.F, self.stream()))
+                base[k] = dst
         self.tensors = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
         self.pred, self.ffn = [], []
         for t in self.tensors:
@@ -84,6 +101,28 @@ class DeviceLayer:
     def ffn_down(self, idx, count, h, y, rep: int = 0) -> None:
         L.check(L.pi_ffn_down(self.ffn[rep], idx, count, h, y, self.ws.data_ptr(), self.ws_bytes,
                               self.stream()))
+
+    def map_ids(self, idx, count, B: int, out) -> None:
+        """Neuron table of a placed layer: out[b, k] = perm[idx[b, k]] for k < count[b]."""
+        if self.perm is None:
+            raise ValueError("the layer has no placement")
+        L.check(L.pi_map_ids(idx, count, B, self.F, self.perm.data_ptr(), out, self.stream()))
+
+    def activation_counts(self, x: torch.Tensor) -> np.ndarray:
+        """Profiling run: how often each neuron (in this layer's order) is predicted active over
+        the tokens x (fp16 [n, d] on the device), in batches of up to 32 tokens through
+        pi_predict.  Returns int32 [F] on the host."""
+        n = x.shape[0]
+        W = (self.F + 31) // 32
+        mask = torch.empty((L.PI_MAX_BATCH, W), dtype=torch.int32, device=self.device)
+        counts = np.zeros(self.F, dtype=np.int64)
+        for t0 in range(0, n, L.PI_MAX_BATCH):
+            B = min(L.PI_MAX_BATCH, n - t0)
+            self.predict(x[t0:t0 + B].data_ptr(), B, None, mask.data_ptr(), None, None)
+            m = mask[:B].cpu().numpy().view(np.uint32)
+            bits = np.unpackbits(m.view(np.uint8), axis=1, bitorder="little")[:, :self.F]
+            counts += bits.sum(axis=0, dtype=np.int64)
+        return counts.astype(np.int32)
 
     def dense(self, x, B, y, rep: int = 0) -> None:
         L.check(L.pi_ffn_dense_ref_gpu(self.ffn[rep], x, B, y, self.ws.data_ptr(), self.ws_bytes,

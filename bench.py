@@ -62,6 +62,10 @@ def parse():
                          "persistent: one pi_decode_run call, one cooperative launch; "
                          "eager: one Python call per ABI function")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget, 0 = skip")
+    ap.add_argument("--placement", choices=("none", "dealt"), default="none",
+                    help="dealt: neurons dealt over the 64-neuron tiles by their activation counts "
+                         "on calibration tokens (pi_place_neurons), batch 1 only")
+    ap.add_argument("--calib-tokens", type=int, default=256, help="calibration tokens for --placement")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling runs)")
     return ap.parse_args()
@@ -334,7 +338,18 @@ def main():
     inputs = gen.make(cfg)
     probe = bytes_model(cfg, cfg.mean_rate * cfg.F)
     R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
-    layer = DeviceLayer(inputs, replicas=R, device=dev)
+    perm = None
+    if a.placement == "dealt":
+        # profiling run on calibration tokens of their own (none of the timed stream), then
+        # the placement; the timed layer holds the placed weights
+        prof = DeviceLayer(inputs, replicas=1, B_max=L.PI_MAX_BATCH, device=dev)
+        cal = torch.from_numpy(gen.calibration_x(cfg, a.calib_tokens)).to(dev)
+        cal_counts = prof.activation_counts(cal)
+        del prof, cal
+        torch.cuda.empty_cache()
+        perm = np.empty(cfg.F, dtype=np.int32)
+        L.check(L.pi_place_neurons(cal_counts.ctypes.data, cfg.F, perm.ctypes.data))
+    layer = DeviceLayer(inputs, replicas=R, device=dev, perm=perm)
     T = cfg.T
     xd = torch.from_numpy(inputs["x"][:, 0, :].copy()).to(dev)     # [T, d] resident in HBM
     bufs = layer.buffers(1)
@@ -448,6 +463,9 @@ def main():
                        "fused": f"one pi_decode_run call: {sched_desc}",
                        "split": f"one pi_decode_run call: {sched_desc}",
                        "eager": "one Python call per ABI function"}[a.mode],
+            "placement": ("none" if perm is None else
+                          f"neurons dealt over the 64-neuron tiles by their activation counts on "
+                          f"{a.calib_tokens} calibration tokens (pi_place_neurons)"),
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_step": round(path_bytes),

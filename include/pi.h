@@ -230,6 +230,40 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
 int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float* y,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* ---- neuron placement ----------------------------------------------------------------------
+ * PowerInfer, "Neuron Placement and Management" (with its offline profiling of how often each
+ * neuron fires): neurons are laid out by activation frequency, and a neuron table maps every
+ * placed neuron back to its position in the original matrices.  On one GPU the layout serves
+ * the balance of the batch-1 kernels, which give each block 64 consecutive neurons: the
+ * neurons, ranked by profiled activation count, are dealt over those 64-neuron tiles in
+ * serpentine order (ranks 0 .. T-1 to tiles 0 .. T-1, the next T ranks to tiles T-1 .. 0,
+ * and so on; the last tile holds F - 64 (T - 1)), so every tile expects about the same number
+ * of active neurons.  Placement permutes rows only: predictor logits, masks, the FFN output y
+ * and the active sets (mapped back through the table) are those of the original layer.
+ *
+ * pi_place_neurons (host only, no HIP call): counts int32 [F] on the host, >= 0 (activation
+ * counts of a calibration run); perm int32 [F] on the host, written: placed position p holds
+ * original neuron perm[p].  Ties rank by ascending original index.  Errors: PI_ERR_NULL,
+ * PI_ERR_SHAPE (F <= 0 or a negative count); perm untouched on error.                       */
+int pi_place_neurons(const int32_t* counts, int F, int32_t* perm);
+
+/* Applies a placement to one per-neuron array on `stream`: row i of dst (row_bytes bytes) is
+ * row perm[i] of src, for i < n.  src and dst are device buffers of n rows and must not
+ * overlap; perm is a device int32 [n] permutation of 0 .. n-1 (a row whose entry lies
+ * outside [0, n) is zero-filled).  Use it for W_up, W_gate, W_down (fp16 [F, d]; int4
+ * u8 [F, d/2] and scales fp16 [F, d/128]), W2t (fp16 [F, r], the transposed W_p2) and the
+ * bias (fp32 [F], row_bytes 4).  Errors: PI_ERR_NULL, PI_ERR_SHAPE (n <= 0, row_bytes == 0),
+ * PI_ERR_HIP.                                                                                */
+int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size_t row_bytes,
+                    void* stream);
+
+/* The neuron table: out[b, k] = perm[idx[b, k]] for k < count[b] (rows of F entries), so the
+ * active list of a placed layer names original neurons (in placed order, not ascending).
+ * idx, count (int32 [B]) and out are device buffers; an id outside [0, F) maps to -1; out
+ * may be idx itself.  1 <= B <= PI_MAX_BATCH.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_HIP. */
+int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int32_t* perm,
+               int32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

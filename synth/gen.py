@@ -33,7 +33,7 @@ from scipy.special import ndtri
 from .configs import FFNConfig
 
 GEN_VERSION = 1
-_STREAMS = ("perm", "w_p1", "w_p2", "w_gate", "w_up", "w_down", "x")
+_STREAMS = ("perm", "w_p1", "w_p2", "w_gate", "w_up", "w_down", "x", "x_cal")
 GROUP = 128  # int4 group size along d
 
 
@@ -165,3 +165,9 @@ def make(cfg: FFNConfig, *, ffn: bool = True, tokens: bool = True) -> dict:
 def expected_union(rates: np.ndarray, B: int) -> float:
     """Expected size of the OR of B independent token masks with these rates."""
     return float(np.sum(1.0 - (1.0 - rates) ** B))
+
+
+def calibration_x(cfg: FFNConfig, n: int) -> np.ndarray:
+    """n calibration tokens fp16 [n, d], x ~ N(0, 1), from a stream of their own (no token of
+    the workload's stream): the profiling run behind a neuron placement."""
+    return _normal_f16(_rngs(cfg.seed)["x_cal"], (n, cfg.d), 1.0)
