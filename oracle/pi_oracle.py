@@ -22,7 +22,8 @@ spun copy and its Japanese translation):
   output vector one contiguous row.
 * Intel Extension for Transformers LLM Runtime, "01 LLM Runtime" and
   "04 Accuracy": weight-only int4 with per-group scales (group 32 or 128)
-  produced by round-to-nearest.
+  produced by round-to-nearest; the same per-group weight-only scheme at 8 bits
+  stores the optional int8 predictor.
 
 Readings where the pages are silent (each listed in the design notes):
 predictor = linear low-rank pair l = (x W_p1) W_p2 + b with no hidden
@@ -66,6 +67,25 @@ def unpack_int4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     s = np.repeat(f64(scales), GROUP, axis=1)
     assert s.shape == q.shape, "scale count must be d / 128"
     return q * s
+
+
+# ---------------------------------------------------------------------------
+# int8 group-128 predictor factors (LLM Runtime page, "Model Quantization": weight-only
+# per-group quantization, here at 8 bits)
+# ---------------------------------------------------------------------------
+def dequant_int8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise rows of int8: W[i, k] = q[i, k] * s[i, k // 128], q the stored signed
+    byte.  q: int8 [rows, cols]; scales: fp16 [rows, cols/128]."""
+    q = np.asarray(q, dtype=np.int8).astype(np.float64)
+    s = np.repeat(f64(scales), GROUP, axis=1)
+    assert s.shape == q.shape, "scale count must be cols / 128"
+    return q * s
+
+
+def predictor_from_int8(q_p1t, s_p1t, q_p2t, s_p2t):
+    """The fp64 factors (W_p1 [d, r], W_p2 [r, F]) of a predictor stored transposed in
+    int8 group-128: the same predictor_logits then applies."""
+    return dequant_int8(q_p1t, s_p1t).T, dequant_int8(q_p2t, s_p2t).T
 
 
 # ---------------------------------------------------------------------------

@@ -119,6 +119,29 @@ def quantize_int4_g128(w: np.ndarray):
     return packed, scales
 
 
+def quantize_int8_g128(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric int8 weight-only quantization with one fp16 scale per 128 columns:
+    s = max|w| / 127 over the group (rounded to fp16), q = clip(rint(w / s), -127, 127).
+    Returns (q int8 [rows, cols], scales fp16 [rows, cols/128])."""
+    rows, cols = w.shape
+    if cols % GROUP:
+        raise ValueError("int8 rows need cols % 128 == 0")
+    g = np.asarray(w, np.float32).reshape(rows, cols // GROUP, GROUP)
+    s16 = (np.abs(g).max(axis=2) / np.float32(127.0)).astype(np.float16)
+    s = s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(g / np.where(s > 0, s, 1)), 0)
+    return np.clip(q, -127, 127).astype(np.int8).reshape(rows, cols), s16
+
+
+def predictor_int8(inputs: dict) -> dict:
+    """The layer's predictor factors, transposed (one row per output) and quantized to int8
+    group-128: q_p1t [r, d], s_p1t [r, d/128], q_p2t [F, r], s_p2t [F, r/128]."""
+    q1, s1 = quantize_int8_g128(np.ascontiguousarray(inputs["w_p1"].T))
+    q2, s2 = quantize_int8_g128(np.ascontiguousarray(inputs["w_p2"].T))
+    return dict(q_p1t=q1, s_p1t=s1, q_p2t=q2, s_p2t=s2)
+
+
 def _normal_i4(rng, shape, std):
     rows, d = shape
     packed = np.empty((rows, d // 2), dtype=np.uint8)
