@@ -17,6 +17,7 @@ PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_DTYPE = 0, 1, 2, 3, 4
 PI_ERR_UNSUPPORTED, PI_ERR_WORKSPACE, PI_ERR_HIP = 5, 6, 7
 PI_ACT_RELU, PI_ACT_REGLU = 0, 1
 PI_W_F16, PI_W_I4G128 = 0, 1
+PI_P_F16, PI_P_I8G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
 PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 1, 2, 3, 4
 PI_MAX_BATCH = 32
@@ -29,7 +30,8 @@ EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_byte
 
 class PredDesc(ctypes.Structure):
     _fields_ = [("w_p1t", c_void_p), ("w_p2t", c_void_p), ("bias", c_void_p),
-                ("d", c_int32), ("r", c_int32), ("F", c_int32), ("threshold", c_float)]
+                ("d", c_int32), ("r", c_int32), ("F", c_int32), ("threshold", c_float),
+                ("pfmt", c_int32), ("s_p1t", c_void_p), ("s_p2t", c_void_p)]
 
 
 class FfnDesc(ctypes.Structure):

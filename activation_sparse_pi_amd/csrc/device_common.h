@@ -99,6 +99,39 @@ PI_DEV float dot8_f32(const uint4& w, const float4& za, const float4& zb) {
     return fmaf(hi_f(w.w), zb.w, a);
 }
 
+// ---- int8 predictor rows (one 16-byte chunk = 16 signed weights) -----------------------------
+PI_DEV float i8f(uint32_t w, int k) { return (float)(int8_t)(uint8_t)(w >> (8 * k)); }
+
+// sum over the 16 bytes of w of (signed byte) * v, v = a, b, c, e (fp32, in byte order)
+PI_DEV float dot16_i8_f32(const uint4& w, const float4& a, const float4& b, const float4& c,
+                          const float4& e) {
+    float s = 0.f;
+    s = fmaf(i8f(w.x, 0), a.x, s); s = fmaf(i8f(w.x, 1), a.y, s);
+    s = fmaf(i8f(w.x, 2), a.z, s); s = fmaf(i8f(w.x, 3), a.w, s);
+    s = fmaf(i8f(w.y, 0), b.x, s); s = fmaf(i8f(w.y, 1), b.y, s);
+    s = fmaf(i8f(w.y, 2), b.z, s); s = fmaf(i8f(w.y, 3), b.w, s);
+    s = fmaf(i8f(w.z, 0), c.x, s); s = fmaf(i8f(w.z, 1), c.y, s);
+    s = fmaf(i8f(w.z, 2), c.z, s); s = fmaf(i8f(w.z, 3), c.w, s);
+    s = fmaf(i8f(w.w, 0), e.x, s); s = fmaf(i8f(w.w, 1), e.y, s);
+    s = fmaf(i8f(w.w, 2), e.z, s); s = fmaf(i8f(w.w, 3), e.w, s);
+    return s;
+}
+
+// the same with 16 fp16 values (x0: elements 0-7, x1: 8-15)
+PI_DEV float dot16_i8_f16(const uint4& w, const uint4& x0, const uint4& x1) {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s = fmaf(i8f(ww[i], 0), lo_f(xx[2 * i]), s);
+        s = fmaf(i8f(ww[i], 1), hi_f(xx[2 * i]), s);
+        s = fmaf(i8f(ww[i], 2), lo_f(xx[2 * i + 1]), s);
+        s = fmaf(i8f(ww[i], 3), hi_f(xx[2 * i + 1]), s);
+    }
+    return s;
+}
+
 // An empty use of a loaded value, placed after the loop that consumes it under a uniform
 // condition: with a use outside the condition the compiler cannot sink the load into the
 // conditional block (where it would be waited for at once, one memory round trip per row).
@@ -326,44 +359,79 @@ PI_DEV void block_compact(const uint32_t* mask, int nrows, int stride, int F, in
 // ---- predictor stage 2 on one 64-neuron tile (blocks of NW waves) ------------------------------
 // Wave w owns rows n0 + w*RPW .. n0 + w*RPW + RPW - 1 of W2t [F, r] (row n = neuron n's
 // predictor weights, contiguous), RPW = 64 / NW.  A row is read by all 64 lanes in segments
-// of 128 16-byte chunks (1024 predictor columns), so a segment's loads are all in flight.
-template <int NW>
+// of 128 16-byte chunks (1024 predictor columns in fp16, 2048 in int8), so a segment's loads
+// are all in flight.  P8: int8 rows with one fp16 scale per 128 columns (per 8 chunks).
+template <bool P8>
+PI_DEV int tile_chunks(int r) { return P8 ? (r >> 4) : (r >> 3); }
+// chunks per lane per row in one segment (int8 rows are half as long: one chunk a lane
+// covers 1024 columns), and chunks per segment
+template <bool P8> constexpr int TILE_QC = P8 ? 1 : 2;
+template <bool P8> constexpr int TILE_SEG = 64 * TILE_QC<P8>;
+
+template <int NW, bool P8 = false>
 struct TileRows {
     static constexpr int RPW = 64 / NW;
     uint4 w[RPW][2];
 };
 
 template <int NW>
-PI_DEV void tile_rows_load(TileRows<NW>& tr, const uint16_t* __restrict__ W2t, int r, int F,
-                           int tile, int c0) {
-    constexpr int RPW = TileRows<NW>::RPW;
+struct TileRows<NW, true> {
+    static constexpr int RPW = 64 / NW;
+    uint4 w[RPW][1];
+    uint32_t s[RPW][1];                           // raw fp16 scales (int8 rows)
+};
+
+template <int NW, bool P8 = false>
+PI_DEV void tile_rows_load(TileRows<NW, P8>& tr, const void* __restrict__ W2t,
+                           const uint16_t* __restrict__ S2, int r, int F, int tile, int c0) {
+    constexpr int RPW = TileRows<NW, P8>::RPW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nr = r >> 3;
+    const int nr = tile_chunks<P8>(r);
 #pragma unroll
     for (int m = 0; m < RPW; ++m) {
         const int n = tile * 64 + wave * RPW + m;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < TILE_QC<P8>; ++q) {
             const int c = c0 + lane + 64 * q;
-            tr.w[m][q] = (n < F && c < nr) ? ld16(W2t + (size_t)n * r + 8 * c) : zero4();
+            if constexpr (P8) {
+                // the row's bases are wave-uniform (scalar registers); lanes add their offsets
+                // the scale load is unconditional (clamped row and chunk): a load merged with
+                // a constant under a lane condition is waited for on the spot
+                const int nu = __builtin_amdgcn_readfirstlane(n);
+                const int8_t* W8 = static_cast<const int8_t*>(W2t) + (size_t)nu * r;
+                const uint16_t* s8 = S2 + (size_t)(nu < F ? nu : 0) * (r >> 7);
+                tr.w[m][q] = (nu < F && c < nr) ? ld16(W8 + 16 * c) : zero4();
+                tr.s[m][q] = (uint32_t)s8[(c < nr ? c : 0) >> 3];
+            } else {
+                const uint16_t* W16 = static_cast<const uint16_t*>(W2t);
+                tr.w[m][q] = (n < F && c < nr) ? ld16(W16 + (size_t)n * r + 8 * c) : zero4();
+            }
         }
     }
 }
 
 // acc[m] += row m . z over the segment starting at chunk c0 (z in LDS, fp32)
-template <int NW>
-PI_DEV void tile_rows_fma(const TileRows<NW>& tr, const float* s_z, int r, int c0, float* acc) {
-    constexpr int RPW = TileRows<NW>::RPW;
+template <int NW, bool P8 = false>
+PI_DEV void tile_rows_fma(const TileRows<NW, P8>& tr, const float* s_z, int r, int c0, float* acc) {
+    constexpr int RPW = TileRows<NW, P8>::RPW;
     const int lane = threadIdx.x & 63;
-    const int nr = r >> 3;
+    const int nr = tile_chunks<P8>(r);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < TILE_QC<P8>; ++q) {
         const int c = c0 + lane + 64 * q;
         if (c < nr) {
-            const float4 za = *reinterpret_cast<const float4*>(&s_z[8 * c]);
-            const float4 zb = *reinterpret_cast<const float4*>(&s_z[8 * c + 4]);
+            if constexpr (P8) {
+                const float4* zp = reinterpret_cast<const float4*>(&s_z[16 * c]);
+                const float4 za = zp[0], zb = zp[1], zc = zp[2], zd = zp[3];
 #pragma unroll
-            for (int m = 0; m < RPW; ++m) acc[m] += dot8_f32(tr.w[m][q], za, zb);
+                for (int m = 0; m < RPW; ++m)
+                    acc[m] = fmaf(h2f((uint16_t)tr.s[m][q]), dot16_i8_f32(tr.w[m][q], za, zb, zc, zd), acc[m]);
+            } else {
+                const float4 za = *reinterpret_cast<const float4*>(&s_z[8 * c]);
+                const float4 zb = *reinterpret_cast<const float4*>(&s_z[8 * c + 4]);
+#pragma unroll
+                for (int m = 0; m < RPW; ++m) acc[m] += dot8_f32(tr.w[m][q], za, zb);
+            }
         }
     }
 }
@@ -381,14 +449,14 @@ PI_DEV void tile_rows_store(const float* acc, float* s_l) {
 }
 
 // s_l[k] = W2t[tile*64 + k, :] . z for k < 64 (before the bias); z in LDS.  Caller syncs after.
-template <int NW>
-PI_DEV void tile_logits(const uint16_t* __restrict__ W2t, const float* s_z, int r, int F, int tile,
-                        float* s_l) {
-    float acc[TileRows<NW>::RPW] = {};
-    for (int c0 = 0; c0 < (r >> 3); c0 += 128) {
-        TileRows<NW> tr;
-        tile_rows_load<NW>(tr, W2t, r, F, tile, c0);
-        tile_rows_fma<NW>(tr, s_z, r, c0, acc);
+template <int NW, bool P8 = false>
+PI_DEV void tile_logits(const void* __restrict__ W2t, const uint16_t* __restrict__ S2, const float* s_z,
+                        int r, int F, int tile, float* s_l) {
+    float acc[TileRows<NW, P8>::RPW] = {};
+    for (int c0 = 0; c0 < tile_chunks<P8>(r); c0 += TILE_SEG<P8>) {
+        TileRows<NW, P8> tr;
+        tile_rows_load<NW, P8>(tr, W2t, S2, r, F, tile, c0);
+        tile_rows_fma<NW, P8>(tr, s_z, r, c0, acc);
     }
     tile_rows_store<NW>(acc, s_l);
 }

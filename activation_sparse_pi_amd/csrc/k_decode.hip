@@ -50,9 +50,11 @@ constexpr int down_cols_per_lane(int wf, int q) {
     return wf == 0 ? (q <= 2 ? 2 : q <= 4 ? 4 : 8) : (q <= 2 ? 8 : 16);
 }
 
-template <int WF, bool GLU, int Q, bool FUSED>
-__global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
-    const float* __restrict__ z, const uint16_t* __restrict__ W2t,
+// P8: int8 predictor rows W2t with fp16 scales S2 (one per 128 columns); held to four
+// waves per SIMD (128 VGPRs) so that two tile blocks share a CU.
+template <int WF, bool GLU, int Q, bool FUSED, bool P8>
+__global__ __launch_bounds__(B_WAVES * 64, P8 ? 4 : 2) void k_dec_stage2_up(
+    const float* __restrict__ z, const void* __restrict__ W2t, const uint16_t* __restrict__ S2,
     const float* __restrict__ bias, int r, int F, float theta, float* __restrict__ logits,
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
@@ -76,8 +78,8 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
 
     // --- logits of the tile: the first segment of its W2t rows (and the tile's bias) goes
     // out before z is staged
-    TileRows<B_WAVES> tr;
-    tile_rows_load<B_WAVES>(tr, W2t, r, F, tile, 0);
+    TileRows<B_WAVES, P8> tr;
+    tile_rows_load<B_WAVES, P8>(tr, W2t, S2, r, F, tile, 0);
     const float bv = (wave == 0 && tile * 64 + lane < F) ? bias[tile * 64 + lane] : 0.f;
     for (int j = tid; j < r; j += NT) s_z[j] = z[j];
     const int nc8 = d >> 3;
@@ -91,11 +93,11 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         }
     }
     __syncthreads();
-    float acc[TileRows<B_WAVES>::RPW] = {};
-    tile_rows_fma<B_WAVES>(tr, s_z, r, 0, acc);
-    for (int c0 = 128; c0 < (r >> 3); c0 += 128) {
-        tile_rows_load<B_WAVES>(tr, W2t, r, F, tile, c0);
-        tile_rows_fma<B_WAVES>(tr, s_z, r, c0, acc);
+    float acc[TileRows<B_WAVES, P8>::RPW] = {};
+    tile_rows_fma<B_WAVES, P8>(tr, s_z, r, 0, acc);
+    for (int c0 = TILE_SEG<P8>; c0 < tile_chunks<P8>(r); c0 += TILE_SEG<P8>) {
+        tile_rows_load<B_WAVES, P8>(tr, W2t, S2, r, F, tile, c0);
+        tile_rows_fma<B_WAVES, P8>(tr, s_z, r, c0, acc);
     }
     tile_rows_store<B_WAVES>(acc, s_red);
     __syncthreads();
@@ -271,6 +273,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     }
 }
 
+
 // --------------------------------------------------------------------------------------- C
 // Split schedule: the down projection straight from the mask, 2-D tiled.  Block (slice,
 // split) owns a column slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte
@@ -429,18 +432,28 @@ __global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc
 }
 
 // --------------------------------------------------------------------------------------- dispatch
+template <int WF, bool GLU, int Q, bool FUSED, bool P8>
+void launch_b8(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
+               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
+               const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
+    if (e0)
+        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), (uint32_t)lds, s,
+                              e0, e1, 0, z, p.w_p2t, p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x,
+                              f.w_gate, f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+    else
+        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
+                           p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
+                           f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+}
+
 template <int WF, bool GLU, int Q, bool FUSED>
 void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
               const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
-    if (e0)
-        hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), (uint32_t)lds, s, e0,
-                              e1, 0, z, p.w_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate,
-                              f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+    if (p.pfmt == PI_P_I8G128)
+        launch_b8<WF, GLU, Q, FUSED, true>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
     else
-        hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
-                           p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
-                           f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+        launch_b8<WF, GLU, Q, FUSED, false>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
 }
 
 template <int WF, bool GLU, bool FUSED>

@@ -27,24 +27,39 @@ namespace {
 // QS 16-byte chunks per lane (all loads of a segment in flight together).
 // CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
 // y accumulators (ncopy copies) into y and clears them for this step's down projection.
-template <int QS, bool CONV>
+// P8: int8 rows (a chunk = 16 weights, one fp16 scale per 8 chunks), x read 32 bytes a chunk.
+template <int QS, bool CONV, bool P8>
 __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
-                                            const uint16_t* __restrict__ W1t, int d, int r,
+                                            const void* __restrict__ W1t,
+                                            const uint16_t* __restrict__ S1, int d, int r,
                                             float* __restrict__ z, long long* __restrict__ yacc,
                                             float* __restrict__ y, int ncopy) {
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nc = d >> 3;
+    constexpr int EPC = P8 ? 16 : 8;                  // elements per 16-byte chunk
+    const int nc = d / EPC;
+    const size_t rowb = P8 ? (size_t)d : (size_t)d * 2;
+    const uint8_t* Wb = static_cast<const uint8_t*>(W1t);
+    const int ng = d >> 7;                            // int8: scale groups per row
     if (B == 1 && nc <= 64 * QS) {
         // one segment: row and x chunks all in flight together, issued before the conversion
         // (whose loads would otherwise hold the row loads back by a memory round trip)
-        const uint16_t* row = W1t + (size_t)(j < r ? j : 0) * d;
-        uint4 w[QS], xr[QS];
+        const int jj = j < r ? j : 0;
+        const uint8_t* row = Wb + (size_t)jj * rowb;
+        uint4 w[QS], xr[QS], xr2[P8 ? QS : 1];
+        uint32_t sr[P8 ? QS : 1];
 #pragma unroll
         for (int q = 0; q < QS; ++q) {
             const int c = lane + 64 * q;
-            w[q] = ld16(row + 8 * (c < nc ? c : 0));
-            xr[q] = ld16(x + 8 * (c < nc ? c : 0));
+            const int cc = c < nc ? c : 0;
+            w[q] = ld16(row + 16 * (size_t)cc);
+            if constexpr (P8) {
+                xr[q] = ld16(x + 16 * cc);
+                xr2[q] = ld16(x + 16 * cc + 8);
+                sr[q] = S1[(size_t)jj * ng + (cc >> 3)];
+            } else {
+                xr[q] = ld16(x + 8 * cc);
+            }
         }
         if (CONV) {
             for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
@@ -54,7 +69,12 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
         float acc = 0.f;
 #pragma unroll
         for (int q = 0; q < QS; ++q)
-            if (lane + 64 * q < nc) acc = dot8(w[q], xr[q], acc);
+            if (lane + 64 * q < nc) {
+                if constexpr (P8)
+                    acc = fmaf(h2f((uint16_t)sr[q]), dot16_i8_f16(w[q], xr[q], xr2[q]), acc);
+                else
+                    acc = dot8(w[q], xr[q], acc);
+            }
         acc = wave_sum(acc);
         if (lane == 0) z[j] = acc;
         return;
@@ -64,19 +84,33 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
             y[i] = from_fx(fx_take(yacc, d, i, ncopy));
     }
     if (j >= r) return;
-    const uint16_t* row = W1t + (size_t)j * d;
+    const uint8_t* row = Wb + (size_t)j * rowb;
     for (int b = 0; b < B; ++b) {
+        const uint16_t* xb = x + (size_t)b * d;
         float acc = 0.f;
         for (int c0 = 0; c0 < nc; c0 += 64 * QS) {
-            uint4 w[QS], xr[QS];
+            uint4 w[QS], xr[QS], xr2[P8 ? QS : 1];
+            uint32_t sr[P8 ? QS : 1];
 #pragma unroll
             for (int q = 0; q < QS; ++q) {
                 const int c = c0 + lane + 64 * q;
-                w[q] = c < nc ? ld16(row + 8 * c) : zero4();
-                xr[q] = c < nc ? ld16(x + (size_t)b * d + 8 * c) : zero4();
+                const bool ok = c < nc;
+                w[q] = ok ? ld16(row + 16 * (size_t)c) : zero4();
+                if constexpr (P8) {
+                    xr[q] = ok ? ld16(xb + 16 * c) : zero4();
+                    xr2[q] = ok ? ld16(xb + 16 * c + 8) : zero4();
+                    sr[q] = (uint32_t)S1[(size_t)j * ng + ((ok ? c : 0) >> 3)];
+                } else {
+                    xr[q] = ok ? ld16(xb + 8 * c) : zero4();
+                }
             }
 #pragma unroll
-            for (int q = 0; q < QS; ++q) acc = dot8(w[q], xr[q], acc);
+            for (int q = 0; q < QS; ++q) {
+                if constexpr (P8)
+                    acc = fmaf(h2f((uint16_t)sr[q]), dot16_i8_f16(w[q], xr[q], xr2[q]), acc);
+                else
+                    acc = dot8(w[q], xr[q], acc);
+            }
         }
         acc = wave_sum(acc);
         if (lane == 0) z[(size_t)b * r + j] = acc;
@@ -89,8 +123,10 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
 // at a time sits in dynamic LDS.
 constexpr int P2_WAVES = 8;
 
+template <bool P8>
 __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ z, int B,
-                                             const uint16_t* __restrict__ W2t,
+                                             const void* __restrict__ W2t,
+                                             const uint16_t* __restrict__ S2,
                                              const float* __restrict__ bias, int r, int F,
                                              float theta, int nbz, float* __restrict__ logits,
                                              uint32_t* __restrict__ mask,
@@ -110,7 +146,7 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
         for (int i = tid; i < nb * r; i += P2_WAVES * 64) s_z[i] = z[(size_t)b0 * r + i];
         __syncthreads();
         for (int t = 0; t < nb; ++t) {
-            tile_logits<P2_WAVES>(W2t, s_z + t * r, r, F, tile, s_l);
+            tile_logits<P2_WAVES, P8>(W2t, S2, s_z + t * r, r, F, tile, s_l);
             __syncthreads();
             if (wave == 0) {
                 const int n = tile * 64 + lane;
@@ -140,9 +176,24 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
 
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
                               float* z, hipStream_t s, long long* yacc, float* y, int ncopy) {
+    if (p.pfmt == PI_P_I8G128) {
+        int q = (p.d / 16 + 63) / 64;
+        q = q < 1 ? 1 : (q > 16 ? 16 : q);
 #define PI_P1(QQ) case QQ: \
-    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, yacc, y, ncopy); \
-    else hipLaunchKernelGGL((k_p1<QQ, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
+    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
+    else hipLaunchKernelGGL((k_p1<QQ, false, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
+    break;
+        switch (q) {
+            PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)
+            PI_P1(9) PI_P1(10) PI_P1(11) PI_P1(12) PI_P1(13) PI_P1(14) PI_P1(15) PI_P1(16)
+            default: return hipErrorInvalidValue;
+        }
+#undef PI_P1
+        return hipGetLastError();
+    }
+#define PI_P1(QQ) case QQ: \
+    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
+    else hipLaunchKernelGGL((k_p1<QQ, false, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 1); \
     break;
     switch (pl.qs) {
         PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)
@@ -186,8 +237,12 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     hipError_t e = launch_pred_stage1(p, pl, x, B, z, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_p2, dim3(pl.nblk2), dim3(P2_WAVES * 64), pl.lds2, s, z, B, p.w_p2t, p.bias, p.r,
-                       p.F, theta, pl.nbz, logits, mask, idx, count, cnt + CNT_PRED2);
+    if (p.pfmt == PI_P_I8G128)
+        hipLaunchKernelGGL(k_p2<true>, dim3(pl.nblk2), dim3(P2_WAVES * 64), pl.lds2, s, z, B, p.w_p2t, p.s_p2t,
+                           p.bias, p.r, p.F, theta, pl.nbz, logits, mask, idx, count, cnt + CNT_PRED2);
+    else
+        hipLaunchKernelGGL(k_p2<false>, dim3(pl.nblk2), dim3(P2_WAVES * 64), pl.lds2, s, z, B, p.w_p2t, nullptr,
+                           p.bias, p.r, p.F, theta, pl.nbz, logits, mask, idx, count, cnt + CNT_PRED2);
     return hipGetLastError();
 }
 

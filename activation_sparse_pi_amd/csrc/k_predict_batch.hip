@@ -256,11 +256,13 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_PRED1;
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
-    hipLaunchKernelGGL(k_pb1, dim3(pl.b_ntile * pl.b_nks), dim3(PB_NW * 64), 0, s, x, B, p.w_p1t,
+    hipLaunchKernelGGL(k_pb1, dim3(pl.b_ntile * pl.b_nks), dim3(PB_NW * 64), 0, s, x, B,
+                       static_cast<const uint16_t*>(p.w_p1t),
                        p.d, p.r, pl.b_ntile, pl.b_nks, part, cnt, z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pb2, dim3((p.F + 127) / 128), dim3(PB_NW * 64), 0, s, z, B, p.w_p2t,
+    hipLaunchKernelGGL(k_pb2, dim3((p.F + 127) / 128), dim3(PB_NW * 64), 0, s, z, B,
+                       static_cast<const uint16_t*>(p.w_p2t),
                        p.bias, p.r, p.F, theta, logits, mask);
     return hipGetLastError();
 }

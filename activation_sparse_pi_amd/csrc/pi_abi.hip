@@ -49,6 +49,15 @@ int check_pred(const pi_pred_desc* p) {
         return fail(PI_ERR_ALIGN, "predictor weights must be 16-byte aligned");
     if (!(p->threshold > 0.f && p->threshold < 1.f))
         return fail(PI_ERR_SHAPE, "threshold must be a probability in (0,1), got %g", (double)p->threshold);
+    if (p->pfmt != PI_P_F16 && p->pfmt != PI_P_I8G128)
+        return fail(PI_ERR_DTYPE, "unknown predictor format %d", p->pfmt);
+    if (p->pfmt == PI_P_I8G128) {
+        if (!p->s_p1t || !p->s_p2t) return fail(PI_ERR_NULL, "int8 predictor needs s_p1t / s_p2t");
+        if (p->d % 128 || p->r % 128)
+            return fail(PI_ERR_SHAPE, "int8 predictor needs d, r %% 128 == 0 (d=%d r=%d)", p->d, p->r);
+        if ((reinterpret_cast<uintptr_t>(p->s_p1t) | reinterpret_cast<uintptr_t>(p->s_p2t)) & 1u)
+            return fail(PI_ERR_ALIGN, "predictor scales must be 2-byte aligned");
+    }
     return PI_OK;
 }
 
@@ -162,6 +171,8 @@ int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B, float* logits
     if (!x || !mask) return fail(PI_ERR_NULL, "x and mask are required");
     if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
     if (!aligned16(x)) return fail(PI_ERR_ALIGN, "x must be 16-byte aligned");
+    if (pred->pfmt == PI_P_I8G128 && B > 1)
+        return fail(PI_ERR_UNSUPPORTED, "the int8 predictor runs at batch 1 (B=%d)", B);
     const PredPlan pl = plan_pred(pred->d, pred->r, pred->F, B);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
     const double tau = pred->threshold;
@@ -254,7 +265,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
         if ((st = check_ffn(&ffns[i], 1)) != PI_OK) return st;
         if (preds[i].d != ffns[i].d || preds[i].F != ffns[i].F || preds[i].d != preds[0].d ||
             preds[i].F != preds[0].F || preds[i].r != preds[0].r || ffns[i].act != ffns[0].act ||
-            ffns[i].wfmt != ffns[0].wfmt || preds[i].threshold != preds[0].threshold)
+            ffns[i].wfmt != ffns[0].wfmt || preds[i].threshold != preds[0].threshold ||
+            preds[i].pfmt != preds[0].pfmt)
             return fail(PI_ERR_SHAPE, "replica %d does not match replica 0 / its ffn", i);
     }
     if (preds[0].F > 131072) return fail(PI_ERR_UNSUPPORTED, "pi_decode_run supports F <= 131072");
@@ -271,6 +283,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     // (measured on all five workloads)
     bool persistent = false;
     RunPlan rp{};
+    if (mode == PI_RUN_PERSISTENT && preds[0].pfmt != PI_P_F16)
+        return fail(PI_ERR_UNSUPPORTED, "the persistent decode launch takes an fp16 predictor");
     if (mode == PI_RUN_PERSISTENT) {
         const RunPlan probe = plan_run(d, r, F, wfmt, 512);
         const int G = run_grid(wfmt, act, probe.q, probe.lds);
@@ -310,8 +324,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
         ra.pl = rp;
         auto fill = [&](int slot, int rep) {
             RunRep& R = ra.rep[slot];
-            R.w1t = preds[rep].w_p1t;
-            R.w2t = preds[rep].w_p2t;
+            R.w1t = static_cast<const uint16_t*>(preds[rep].w_p1t);
+            R.w2t = static_cast<const uint16_t*>(preds[rep].w_p2t);
             R.bias = preds[rep].bias;
             R.wg = ffns[rep].w_gate;
             R.wu = ffns[rep].w_up;

@@ -20,23 +20,29 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 class DeviceLayer:
     def __init__(self, inputs: dict, replicas: int = 1, B_max: int = 1, device="cuda",
-                 threshold: float = 0.5, perm: np.ndarray | None = None):
+                 threshold: float = 0.5, perm: np.ndarray | None = None, pred_format: str = "f16"):
         """perm: optional neuron placement (int32 [F], placed position p holds original
         neuron perm[p], from ``pi_place_neurons``): every per-neuron array is permuted on the
-        device with ``pi_permute_rows``; ``map_ids`` turns placed ids back into original ones."""
+        device with ``pi_permute_rows``; ``map_ids`` turns placed ids back into original ones.
+        pred_format: "f16", or "i8g128" for the int8 group-128 predictor, whose factors come in
+        ``inputs`` as q_p1t, s_p1t, q_p2t, s_p2t (one row per predictor output)."""
         cfg = inputs["cfg"]
         self.cfg, self.d, self.F, self.r = cfg, cfg.d, cfg.F, cfg.r
         self.act = L.PI_ACT_REGLU if cfg.act == "reglu" else L.PI_ACT_RELU
         self.wfmt = L.PI_W_F16 if cfg.wfmt == "f16" else L.PI_W_I4G128
         self.device = torch.device(device)
-        names = ["w_p1", "w_p2", "bias"]
+        if pred_format not in ("f16", "i8g128"):
+            raise ValueError(f"unknown predictor format {pred_format}")
+        self.pfmt = L.PI_P_I8G128 if pred_format == "i8g128" else L.PI_P_F16
+        names = ["w_p1", "w_p2", "bias"] if pred_format == "f16" else ["q_p1t", "s_p1t", "q_p2t", "s_p2t", "bias"]
         mats = ("gate", "up", "down") if cfg.act == "reglu" else ("up", "down")
         for m in mats:
             names += ["w_" + m] if cfg.wfmt == "f16" else ["q_" + m, "s_" + m]
         host = {k: inputs[k] for k in names}
         # predictor factors go to the device transposed: one contiguous row per output
-        host["w_p1"] = np.ascontiguousarray(inputs["w_p1"].T)    # [r, d]
-        host["w_p2"] = np.ascontiguousarray(inputs["w_p2"].T)    # [F, r]
+        if pred_format == "f16":
+            host["w_p1"] = np.ascontiguousarray(inputs["w_p1"].T)    # [r, d]
+            host["w_p2"] = np.ascontiguousarray(inputs["w_p2"].T)    # [F, r]
         base = {k: _dev(v, self.device) for k, v in host.items()}
         self.perm = None
         if perm is not None:
@@ -45,7 +51,7 @@ class DeviceLayer:
                 raise ValueError(f"perm must be int32 [{cfg.F}]")
             self.perm = _dev(perm, self.device)
             for k in names:                     # every array here is one row per neuron but W_p1^T
-                if k == "w_p1":
+                if k in ("w_p1", "q_p1t", "s_p1t"):
                     continue
                 src = base[k]
                 dst = torch.empty_like(src)
@@ -55,8 +61,13 @@ class DeviceLayer:
         self.tensors = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
         self.pred, self.ffn = [], []
         for t in self.tensors:
-            self.pred.append(L.PredDesc(t["w_p1"].data_ptr(), t["w_p2"].data_ptr(), t["bias"].data_ptr(),
-                                        cfg.d, cfg.r, cfg.F, threshold))
+            if pred_format == "f16":
+                self.pred.append(L.PredDesc(t["w_p1"].data_ptr(), t["w_p2"].data_ptr(), t["bias"].data_ptr(),
+                                            cfg.d, cfg.r, cfg.F, threshold))
+            else:
+                self.pred.append(L.PredDesc(t["q_p1t"].data_ptr(), t["q_p2t"].data_ptr(), t["bias"].data_ptr(),
+                                            cfg.d, cfg.r, cfg.F, threshold, L.PI_P_I8G128,
+                                            t["s_p1t"].data_ptr(), t["s_p2t"].data_ptr()))
             if cfg.wfmt == "f16":
                 g = t["w_gate"].data_ptr() if "w_gate" in t else None
                 self.ffn.append(L.FfnDesc(g, t["w_up"].data_ptr(), t["w_down"].data_ptr(), None, None,
@@ -110,14 +121,15 @@ class DeviceLayer:
 
     def activation_counts(self, x: torch.Tensor) -> np.ndarray:
         """Profiling run: how often each neuron (in this layer's order) is predicted active over
-        the tokens x (fp16 [n, d] on the device), in batches of up to 32 tokens through
-        pi_predict.  Returns int32 [F] on the host."""
+        the tokens x (fp16 [n, d] on the device), in batches of up to 32 tokens (1 with the int8
+        predictor) through pi_predict.  Returns int32 [F] on the host."""
         n = x.shape[0]
         W = (self.F + 31) // 32
-        mask = torch.empty((L.PI_MAX_BATCH, W), dtype=torch.int32, device=self.device)
+        bmax = 1 if self.pfmt == L.PI_P_I8G128 else L.PI_MAX_BATCH      # int8: batch 1 only
+        mask = torch.empty((bmax, W), dtype=torch.int32, device=self.device)
         counts = np.zeros(self.F, dtype=np.int64)
-        for t0 in range(0, n, L.PI_MAX_BATCH):
-            B = min(L.PI_MAX_BATCH, n - t0)
+        for t0 in range(0, n, bmax):
+            B = min(bmax, n - t0)
             self.predict(x[t0:t0 + B].data_ptr(), B, None, mask.data_ptr(), None, None)
             m = mask[:B].cpu().numpy().view(np.uint32)
             bits = np.unpackbits(m.view(np.uint8), axis=1, bitorder="little")[:, :self.F]

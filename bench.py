@@ -66,6 +66,8 @@ def parse():
                     help="dealt: neurons dealt over the 64-neuron tiles by their activation counts "
                          "on calibration tokens (pi_place_neurons), batch 1 only")
     ap.add_argument("--calib-tokens", type=int, default=256, help="calibration tokens for --placement")
+    ap.add_argument("--pred-format", choices=("f16", "i8g128"), default="f16",
+                    help="i8g128: the predictor factors in int8 with one fp16 scale per 128 (batch 1)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling runs)")
     return ap.parse_args()
@@ -75,21 +77,21 @@ parse_defaults = {"steps": 5440, "warmup": 1088}
 
 
 # ------------------------------------------------------------------------------- byte accounting
-def bytes_model(cfg, n):
+def bytes_model(cfg, n, pb=2.0):
     """Algorithmic bytes of one batch-1 step with n active neurons: predictor weights
-    2dr + 2rF, bias 4F, the active rows m*n*d*w_b (m = 3 for ReGLU, 2 for ReLU; w_b = 2
+    pb*(dr + rF) (pb = 2 for fp16, 1 + 2/128 for int8 with its scales), bias 4F, the active rows m*n*d*w_b (m = 3 for ReGLU, 2 for ReLU; w_b = 2
     for fp16, 0.5 + 2/128 for int4 with its scales), x 2d, y 4d, the mask F/8 and the
     neuron table 4n.  (The unfused up operator alone: (m-1)*n*d*w_b + 2d + 8n.)"""
     d, F, r = cfg.d, cfg.F, cfg.r
     wb = 2.0 if cfg.wfmt == "f16" else 0.5 + 2.0 / 128.0
     m = 3 if cfg.act == "reglu" else 2
-    pred = 2 * d * r + 2 * r * F + 4 * F
+    pred = pb * d * r + pb * r * F + 4 * F
     ffn = m * n * d * wb
     total = pred + ffn + 2 * d + 4 * d + F / 8 + 4 * n
     up = (m - 1) * n * d * wb + 2 * d + 8 * n
     # the tile kernel of the split step: W2t + bias, z, x, the up (and gate) rows of the
     # active neurons, the mask words and h written
-    stage2 = 2 * r * F + 4 * F + 4 * r + 2 * d + (m - 1) * n * d * wb + F / 8 + 4 * n
+    stage2 = pb * r * F + 4 * F + 4 * r + 2 * d + (m - 1) * n * d * wb + F / 8 + 4 * n
     # the tile kernel of the fused step: the same without h, plus the down rows and y
     tile_fused = stage2 - 4 * n + n * d * wb + 4 * d
     return dict(pred=pred, ffn=ffn, up=up, stage2=stage2, tile_fused=tile_fused, total=total)
@@ -109,7 +111,7 @@ def bytes_model_batch(cfg, n_tok, U):
     the masks B*F/8, H written and read 2*B*U*2, y 4*B*d."""
     d, F, r, B = cfg.d, cfg.F, cfg.r, cfg.B
     m = 3 if cfg.act == "reglu" else 2
-    pred = 2 * d * r + 2 * r * F + 4 * F + B * 2 * d + B * F / 8
+    pred = pb * d * r + pb * r * F + 4 * F + B * 2 * d + B * F / 8
     comp = B * F / 8 + 4 * U
     ffn = m * U * d * 2 + B * 2 * d + 8 * U + B * F / 8 + 4 * B * U + 4 * B * d
     return dict(pred=pred, compact=comp, ffn=ffn, total=pred + comp + ffn)
@@ -336,20 +338,25 @@ def main():
         return bench_batch(a, cfg)
     dev = torch.device("cuda:0")
     inputs = gen.make(cfg)
-    probe = bytes_model(cfg, cfg.mean_rate * cfg.F)
+    p8 = a.pred_format == "i8g128"
+    pb = 1.0 + 2.0 / 128.0 if p8 else 2.0
+    if p8:
+        inputs.update(gen.predictor_int8(inputs))
+    probe = bytes_model(cfg, cfg.mean_rate * cfg.F, pb)
     R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
     perm = None
     if a.placement == "dealt":
         # profiling run on calibration tokens of their own (none of the timed stream), then
         # the placement; the timed layer holds the placed weights
-        prof = DeviceLayer(inputs, replicas=1, B_max=L.PI_MAX_BATCH, device=dev)
+        prof = DeviceLayer(inputs, replicas=1, B_max=1 if p8 else L.PI_MAX_BATCH, device=dev,
+                           pred_format=a.pred_format)
         cal = torch.from_numpy(gen.calibration_x(cfg, a.calib_tokens)).to(dev)
         cal_counts = prof.activation_counts(cal)
         del prof, cal
         torch.cuda.empty_cache()
         perm = np.empty(cfg.F, dtype=np.int32)
         L.check(L.pi_place_neurons(cal_counts.ctypes.data, cfg.F, perm.ctypes.data))
-    layer = DeviceLayer(inputs, replicas=R, device=dev, perm=perm)
+    layer = DeviceLayer(inputs, replicas=R, device=dev, perm=perm, pred_format=a.pred_format)
     T = cfg.T
     xd = torch.from_numpy(inputs["x"][:, 0, :].copy()).to(dev)     # [T, d] resident in HBM
     bufs = layer.buffers(1)
@@ -417,7 +424,7 @@ def main():
     ms_per_step = total_ms / K
     tok_s = K / (total_ms / 1e3)
     n_all = counts[timed].astype(np.float64)
-    bm = bytes_model(cfg, n_all)
+    bm = bytes_model(cfg, n_all, pb)
     path_bytes = float(np.mean(bm["total"]))
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbs = float(np.mean(bm["ffn"])) / (ms_per_step * 1e-3) / 1e9
@@ -429,8 +436,8 @@ def main():
         kernel_key = f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}"
         launch_bytes, launch_ms = float(np.mean(bm["up"])), float(np.mean(up_ms))
     else:
-        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act},{sched}] {cfg.name}"
-        bm_r = bytes_model(cfg, counts[roof_steps].astype(np.float64))
+        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act},{sched}{',p8' if p8 else ''}] {cfg.name}"
+        bm_r = bytes_model(cfg, counts[roof_steps].astype(np.float64), pb)
         launch_bytes = float(np.mean(bm_r["tile_fused" if sched == "fused" else "stage2"]))
         launch_ms = float(np.mean(up_ms))
     achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
@@ -463,6 +470,7 @@ def main():
                        "fused": f"one pi_decode_run call: {sched_desc}",
                        "split": f"one pi_decode_run call: {sched_desc}",
                        "eager": "one Python call per ABI function"}[a.mode],
+            "predictor": "int8 group-128, fp16 scales" if p8 else "fp16",
             "placement": ("none" if perm is None else
                           f"neurons dealt over the 64-neuron tiles by their activation counts on "
                           f"{a.calib_tokens} calibration tokens (pi_place_neurons)"),

@@ -73,14 +73,24 @@ extern "C" {
  * evaluated as l_i > ln(threshold / (1 - threshold)) in fp32 (strict; 0 for
  * threshold 0.5).  z = x W_p1 is accumulated and kept in fp32 (never rounded to
  * fp16).                                                                       */
+#define PI_P_F16     0   /* predictor factors fp16                                      */
+#define PI_P_I8G128  1   /* predictor factors int8 weight-only, one fp16 scale per group of
+                            128 along each row: w = q * s (q the stored signed byte), the
+                            per-group weight-only scheme of the LLM Runtime page ("Model
+                            Quantization") at 8 bits.  Batch-1 paths only: pi_predict with
+                            B = 1 and pi_decode_run's kernel schedules; d % 128 == 0 and
+                            r % 128 == 0.                                                  */
 typedef struct pi_pred_desc {
-    const uint16_t* w_p1t;  /* fp16 [r, d] row-major (= W_p1 transposed)  */
-    const uint16_t* w_p2t;  /* fp16 [F, r] row-major (= W_p2 transposed)  */
+    const void*     w_p1t;  /* [r, d] row-major (= W_p1 transposed): fp16, or int8 (PI_P_I8G128) */
+    const void*     w_p2t;  /* [F, r] row-major (= W_p2 transposed): fp16, or int8 (PI_P_I8G128) */
     const float*    bias;   /* fp32 [F]                                   */
     int32_t d;              /* model width, d % 8 == 0                    */
     int32_t r;              /* predictor rank, r % 8 == 0                 */
     int32_t F;              /* ffn width (neurons), F % 8 == 0            */
     float   threshold;      /* probability in (0, 1); 0.5 is the default  */
+    int32_t pfmt;           /* PI_P_F16 (0, a zero-filled descriptor) or PI_P_I8G128      */
+    const uint16_t* s_p1t;  /* PI_P_I8G128: fp16 [r, d/128] scales of w_p1t; else NULL     */
+    const uint16_t* s_p2t;  /* PI_P_I8G128: fp16 [F, r/128] scales of w_p2t; else NULL     */
 } pi_pred_desc;
 
 /* FFN weights of one layer, every matrix neuron-major [F, d]: row i of
