@@ -111,7 +111,7 @@ def bytes_model_batch(cfg, n_tok, U):
     the masks B*F/8, H written and read 2*B*U*2, y 4*B*d."""
     d, F, r, B = cfg.d, cfg.F, cfg.r, cfg.B
     m = 3 if cfg.act == "reglu" else 2
-    pred = pb * d * r + pb * r * F + 4 * F + B * 2 * d + B * F / 8
+    pred = 2 * d * r + 2 * r * F + 4 * F + B * 2 * d + B * F / 8
     comp = B * F / 8 + 4 * U
     ffn = m * U * d * 2 + B * 2 * d + 8 * U + B * F / 8 + 4 * B * U + 4 * B * d
     return dict(pred=pred, compact=comp, ffn=ffn, total=pred + comp + ffn)
