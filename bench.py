@@ -29,7 +29,7 @@ carries its own start/end events (those events slow the step down, so the headli
 value comes from the first pass, which has none).  In persistent mode the launch is
 the only kernel and its bytes over its duration are the roofline figure.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the layer runs on one GPU.
 """
 from __future__ import annotations
 
@@ -322,7 +322,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
-              "the sparse FFN layer is not sharded in this build.", file=sys.stderr)
+              "the sparse FFN layer is not sharded over GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

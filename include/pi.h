@@ -46,7 +46,7 @@ extern "C" {
 #define PI_ERR_SHAPE       2  /* a size is out of range or inconsistent              */
 #define PI_ERR_ALIGN       3  /* a pointer is not 16-byte aligned                    */
 #define PI_ERR_DTYPE       4  /* unknown activation / weight format / mode enum      */
-#define PI_ERR_UNSUPPORTED 5  /* valid request this build does not implement         */
+#define PI_ERR_UNSUPPORTED 5  /* valid request the library does not implement        */
 #define PI_ERR_WORKSPACE   6  /* workspace missing, too small or misaligned          */
 #define PI_ERR_HIP         7  /* a HIP runtime call failed                           */
 

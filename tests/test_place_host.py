@@ -44,9 +44,9 @@ def test_serpentine_rounds():
     st, perm = place(counts)
     assert st == L.PI_OK
     for t in range(T):
-        assert perm[t * 64] == t                          # round 0, left to right
-        assert perm[t * 64 + 1] == 2 * T - 1 - t          # round 1, right to left
-        assert perm[t * 64 + 2] == 2 * T + t              # round 2, left to right
+        assert perm[t * 64] == t                          # pass 0, left to right
+        assert perm[t * 64 + 1] == 2 * T - 1 - t          # pass 1, right to left
+        assert perm[t * 64 + 2] == 2 * T + t              # pass 2, left to right
 
 
 def test_equal_counts_give_the_original_ids_dealt():
