@@ -50,10 +50,10 @@ constexpr int down_cols_per_lane(int wf, int q) {
     return wf == 0 ? (q <= 2 ? 2 : q <= 4 ? 4 : 8) : (q <= 2 ? 8 : 16);
 }
 
-// P8: int8 predictor rows W2t with fp16 scales S2 (one per 128 columns); held to four
-// waves per SIMD (128 VGPRs) so that two tile blocks share a CU.
+// P8: int8 predictor rows W2t with fp16 scales S2 (one per 128 columns).  (Holding the int8
+// variants to 128 VGPRs, for two tile blocks per CU, makes them spill: slower on every shape.)
 template <int WF, bool GLU, int Q, bool FUSED, bool P8>
-__global__ __launch_bounds__(B_WAVES * 64, P8 ? 4 : 2) void k_dec_stage2_up(
+__global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const float* __restrict__ z, const void* __restrict__ W2t, const uint16_t* __restrict__ S2,
     const float* __restrict__ bias, int r, int F, float theta, float* __restrict__ logits,
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
