@@ -308,17 +308,24 @@ PI_DEV int block_exclusive_scan(int v, int* s_tmp, int* total) {
 // thread its first output slot.
 template <bool COHERENT>
 PI_DEV uint32_t mask_word(const uint32_t* mask, int nrows, int stride, int w, int W, int F) {
+    auto ld = [&](int b) {
+        const uint32_t* p = mask + (size_t)b * stride + w;
+        return COHERENT ? ld_agent(p) : *p;
+    };
     uint32_t v = 0;
-    // the rows' words in groups of 16 independent loads (one memory round trip per group)
-    for (int b0 = 0; b0 < nrows; b0 += 16) {
-        uint32_t t[16];
+    if (nrows == 1) {
+        v = ld(0);
+    } else {
+        // the rows' words in groups of 16 loads, all issued before the first is used (one
+        // memory round trip per group); rows past the last repeat it, which leaves the OR as it
+        // is and keeps every load unconditional (a load under a condition is waited for at once)
+        for (int b0 = 0; b0 < nrows; b0 += 16) {
+            uint32_t t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t* p = mask + (size_t)(b0 + i) * stride + w;
-            t[i] = b0 + i < nrows ? (COHERENT ? ld_agent(p) : *p) : 0u;
+            for (int i = 0; i < 16; ++i) t[i] = ld(min(b0 + i, nrows - 1));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v |= t[i];
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v |= t[i];
     }
     if (w == W - 1 && (F & 31)) v &= (1u << (F & 31)) - 1u;
     return v;

@@ -29,6 +29,8 @@
 //         fewer columns.  The waves meet in LDS; with KS > 1 the shares meet in the
 //         workspace and the last-arriving block of the column group adds them in a fixed
 //         order (bitwise reproducible).
+#include <climits>
+
 #include "internal.h"
 #include "mfma_tile.h"
 
@@ -50,15 +52,17 @@ PI_DEV uint32_t pack_h2(float lo, float hi) {
 }
 
 // ------------------------------------------------------------------------------------ up
-template <bool GLU>
-__global__ __launch_bounds__(UP_NW * 64) void k_union_up(
+// ReLU with 32-bit offsets fits 128 registers: two blocks per CU
+template <bool GLU, bool OFF32>
+__global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
     const uint16_t* __restrict__ x, int B, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, int d, int F, const int32_t* __restrict__ uidx,
     const int32_t* __restrict__ ucount, const uint32_t* __restrict__ tmask,
     uint4* __restrict__ Hf) {
     constexpr int NM = GLU ? 2 : 1;                   // weight matrices: up [, gate]
     __shared__ uint4 s_st[UP_NW][NM + 1][32][8];      // per wave: x, up [, gate] staging
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int U = min(*ucount, F);
     const int tile = blockIdx.x;
     if (tile * 32 >= U) return;                       // whole block: past the union
@@ -69,21 +73,45 @@ __global__ __launch_bounds__(UP_NW * 64) void k_union_up(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int kp = tile * 32 + 8 * q + lrow;
-        int row = kp < U ? uidx[kp] : -1;
-        if ((unsigned)row >= (unsigned)F) row = -1;
-        offw[q] = row < 0 ? -1 : (long long)row * d;
+        const int row = kp < U ? uidx[kp] : -1;
+        offw[q] = (unsigned)row < (unsigned)F ? (long long)row * d : -1;
         const int tok = 8 * q + lrow;
         offx[q] = tok < B ? (long long)tok * d : -1;
     }
-    const int nrun = (d + 63) / 64, per = (nrun + UP_NW - 1) / UP_NW;
-    const int r0 = min(nrun, wave * per), r1 = min(nrun, r0 + per);
     f32x16_t acc[NM] = {};
-    if constexpr (GLU) {
-        const uint16_t* const Wm[2] = {Wu, Wg};
-        runs_mfma<2>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
+    if constexpr (OFF32) {
+        // full runs through buffer resources (byte offsets of F rows fit 31 bits): zero rows
+        // read row 0 of W and x instead, their h is zeroed below; the partial run, if any,
+        // goes the general way
+        const int flags = 0x00020000;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(x), 0, B * d * 2, flags);
+        __amdgpu_buffer_rsrc_t rw[NM];
+        rw[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wu), 0, F * d * 2, flags);
+        if constexpr (GLU)
+            rw[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg), 0, F * d * 2, flags);
+        uint32_t ox[4], ow[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
+            ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
+        }
+        const int nfull = d >> 6, per = (nfull + UP_NW - 1) / UP_NW;
+        const int r0 = min(nfull, wave * per), r1 = min(nfull, r0 + per);
+        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+        if ((d & 63) && wave == UP_NW - 1) {
+            const uint16_t* Wm[NM];
+            Wm[0] = Wu;
+            if constexpr (GLU) Wm[1] = Wg;
+            runs_mfma<NM>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);
+        }
     } else {
-        const uint16_t* const Wm[1] = {Wu};
-        runs_mfma<1>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
+        const int nrun = (d + 63) / 64, per = (nrun + UP_NW - 1) / UP_NW;
+        const int r0 = min(nrun, wave * per), r1 = min(nrun, r0 + per);
+        const uint16_t* Wm[NM];
+        Wm[0] = Wu;
+        if constexpr (GLU) Wm[1] = Wg;
+        runs_mfma<NM>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
     }
 
     // the waves meet in LDS (each wave's staging area holds its own accumulators)
@@ -376,12 +404,16 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
     const int tiles = (f.F + 31) / 32;
     const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
     const uint16_t* Wu = static_cast<const uint16_t*>(f.w_up);
+    // 32-bit buffer offsets when every byte of a weight matrix is within 2^31
+    const bool off32 = (size_t)f.F * f.d * 2 <= (size_t)INT_MAX;
+    auto up = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu, f.d, f.F, idx,
+                           count, token_mask, Hf);
+    };
     if (f.act == PI_ACT_REGLU)
-        hipLaunchKernelGGL((k_union_up<true>), dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu,
-                           f.d, f.F, idx, count, token_mask, Hf);
+        off32 ? up(k_union_up<true, true>) : up(k_union_up<true, false>);
     else
-        hipLaunchKernelGGL((k_union_up<false>), dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu,
-                           f.d, f.F, idx, count, token_mask, Hf);
+        off32 ? up(k_union_up<false, true>) : up(k_union_up<false, false>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_UNION;

@@ -35,10 +35,11 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
                                                     unsigned* __restrict__ counter,
                                                     float* __restrict__ z) {
     __shared__ uint4 s_st[PB_NW][2][32][8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x % ntile, ks = blockIdx.x / ntile;
     const int lrow = lane >> 3;
-    long long offw[4], offx[4];
+    long long offw[4], offx[4];                       // element offsets, -1 = zero row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int j = tile * 32 + 8 * q + lrow;
@@ -46,14 +47,31 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
         const int tok = 8 * q + lrow;
         offx[q] = tok < B ? (long long)tok * d : -1;
     }
-    // this block's share of the runs of 64, then this wave's part of it
-    const int nrun = (d + 63) / 64, pb = (nrun + nks - 1) / nks;
-    const int b0 = min(nrun, ks * pb), b1 = min(nrun, b0 + pb);
+    // this block's share of the full runs of 64, then this wave's part of it; the partial
+    // run, if any, goes to the last wave of the last share
+    const int nfull = d >> 6, pb = (nfull + nks - 1) / nks;
+    const int b0 = min(nfull, ks * pb), b1 = min(nfull, b0 + pb);
     const int pw = (b1 - b0 + PB_NW - 1) / PB_NW;
     const int r0 = min(b1, b0 + wave * pw), r1 = min(b1, r0 + pw);
     f32x16_t acc[1] = {};
-    const uint16_t* const Wm[1] = {W1t};
-    runs_mfma<1>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
+    // full runs through buffer resources (every byte offset below 2^31): rows past r read
+    // row 0, tokens past B token 0; neither reaches a stored output
+    const int flags = 0x00020000;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, B * d * 2, flags);
+    const __amdgpu_buffer_rsrc_t rw[1] = {
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W1t), 0, r * d * 2, flags)};
+    uint32_t ox[4], ow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
+        ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
+    }
+    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+    if ((d & 63) && ks == nks - 1 && wave == PB_NW - 1) {
+        const uint16_t* const Wm[1] = {W1t};
+        runs_mfma<1>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);
+    }
 
     float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
 #pragma unroll
@@ -107,6 +125,8 @@ PI_DEV float absmax4(float m, const float4& v) {
     return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// ONE: the rank fits one pass (r <= ZC), straight-line code, z loaded before W2t
+template <bool ONE>
 __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z, int B,
                                                     const uint16_t* __restrict__ W2t,
                                                     const float* __restrict__ bias, int r, int F,
@@ -119,46 +139,59 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     const int n0 = blockIdx.x * 128;
     const int mt = wave & 3, kh = wave >> 2;
     const int lrow = lane >> 3, lch = lane & 7, mi = lane & 31, half = lane >> 5;
-    long long offw[4];
+    // Every load below is unconditional (a load in a branch makes the next wait a full one):
+    // rows past F read row F - 1, rank positions past r read its last 8, tokens past B token
+    // 0.  z past r is zeroed before it is staged, so those W2t values meet zeros; rows past F
+    // and tokens past B only reach outputs that are never written.
+    const uint16_t* wrow[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = n0 + mt * 32 + 8 * q + lrow;
-        offw[q] = i < F ? (long long)i * r : -1;
-    }
+    for (int q = 0; q < 4; ++q)
+        wrow[q] = W2t + (size_t)min(n0 + mt * 32 + 8 * q + lrow, F - 1) * r;
     // W2t loads of one pass of the rank: this wave's 4 runs of 64, all in flight at once
     uint4 wv[4][4];
     auto load_w = [&](int c0) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const int e = c0 + kh * 256 + rr * 64 + lch * 8;
+            const int e = min(c0 + kh * 256 + rr * 64 + lch * 8, r - 8);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                wv[rr][q] = (e < r && offw[q] >= 0) ? ld16(W2t + offw[q] + e) : zero4();
+            for (int q = 0; q < 4; ++q) wv[rr][q] = ld16(wrow[q] + e);
         }
     };
     // z of one pass: token b = tid / 16 holds chunks sub + 16 i (8 values each), i < 4
     const int b = tid >> 4, sub = tid & 15;
+    const float* const zrow = z + (size_t)(b < B ? b : 0) * r;
     float4 zr[2 * (ZC / 128)];
+    bool zok[ZC / 128];
     auto load_z = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < ZC / 128; ++i) {
             const int k = c0 + 8 * (sub + 16 * i);
-            const bool ok = b < B && k < r;
-            const float* p = z + (size_t)b * r + k;
-            zr[2 * i] = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-            zr[2 * i + 1] = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            zok[i] = k < r;
+            const float* p = zrow + min(k, r - 8);
+            zr[2 * i] = *reinterpret_cast<const float4*>(p);
+            zr[2 * i + 1] = *reinterpret_cast<const float4*>(p + 4);
         }
     };
     // z first: it is small and in L2, and a load waits for every load issued before it,
     // so issued behind the W2t rows it would only arrive with them
-    if (r <= ZC) load_z(0);
-    load_w(0);
     // 1. per-token exponent e: the largest |z| of the token brought into [2^14, 2^15)
     float m = 0.f;
-    for (int c0 = 0; c0 < r; c0 += ZC) {       // a rank of at most ZC leaves its z in zr
-        if (r > ZC) load_z(c0);
+    auto zmax = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2 * (ZC / 128); ++i) m = absmax4(m, zr[i]);
+        for (int i = 0; i < 2 * (ZC / 128); ++i) m = zok[i / 2] ? absmax4(m, zr[i]) : m;
+    };
+    if constexpr (ONE) {                        // the pass's z stays in zr
+        load_z(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(0);
+        __builtin_amdgcn_sched_barrier(0);
+        zmax();
+    } else {
+        load_w(0);
+        for (int c0 = 0; c0 < r; c0 += ZC) {
+            load_z(c0);
+            zmax();
+        }
     }
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
@@ -167,16 +200,17 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     const int ez = m > 0.f ? 15 - E : 0;
     if (sub == 0) s_e[b] = ez;
     f32x16_t acc = {};
-    for (int c0 = 0; c0 < r; c0 += ZC) {
-        if (c0 > 0) load_w(c0);
-        if (r > ZC) load_z(c0);
+    for (int c0 = 0; c0 < (ONE ? 1 : r); c0 += ZC) {
+        if (!ONE && c0 > 0) load_w(c0);
+        if (!ONE) load_z(c0);
         __syncthreads();                       // previous pass's reads done
         // 2. stage z_hi / z_lo of this pass
 #pragma unroll
         for (int i = 0; i < ZC / 128; ++i) {
             const int ch = sub + 16 * i;
-            const float zz[8] = {zr[2 * i].x, zr[2 * i].y, zr[2 * i].z, zr[2 * i].w,
-                                 zr[2 * i + 1].x, zr[2 * i + 1].y, zr[2 * i + 1].z, zr[2 * i + 1].w};
+            const float4 za = zok[i] ? zr[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 zb = zok[i] ? zr[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -261,7 +295,8 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
                        p.d, p.r, pl.b_ntile, pl.b_nks, part, cnt, z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pb2, dim3((p.F + 127) / 128), dim3(PB_NW * 64), 0, s, z, B,
+    hipLaunchKernelGGL(p.r <= ZC ? k_pb2<true> : k_pb2<false>, dim3((p.F + 127) / 128),
+                       dim3(PB_NW * 64), 0, s, z, B,
                        static_cast<const uint16_t*>(p.w_p2t),
                        p.bias, p.r, p.F, theta, logits, mask);
     return hipGetLastError();

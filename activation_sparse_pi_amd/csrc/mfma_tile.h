@@ -80,4 +80,78 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
     }
 }
 
+// runs_mfma over full runs only (every run of [r0, r1) inside the rows), rows read through
+// buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and ow[q] into
+// every W_m (resource rw[m]), plus 128 bytes per run.  NB runs are in flight per wave: a
+// run's registers are refilled with the run NB ahead as soon as they are staged.  The
+// steady loop issues every load unconditionally and is unrolled NB times so the buffers
+// rotate without copies; a scheduling barrier after each run's loads keeps them together,
+// so that (vector loads completing in order) waiting for the oldest run never waits for
+// younger ones.
+template <int NM, int NB>
+PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
+                           const __amdgpu_buffer_rsrc_t (&rw)[NM], const uint32_t (&ow)[4],
+                           int r0, int r1, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
+    constexpr int NP = NM + 1;
+    const int lane = threadIdx.x & 63;
+    const int lrow = lane >> 3, lch = lane & 7;
+    const int mi = lane & 31, half = lane >> 5;
+    uint4 v[NB][NP][4];
+    auto load = [&](int rr, uint4(&b)[NP][4]) {
+        const int so = rr * 128;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            b[0][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[q], so, 0));
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                b[m + 1][q] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw[m], ow[q], so, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage = [&](const uint4(&b)[NP][4]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) st[p][8 * q + lrow][lch ^ lrow] = b[p][q];
+    };
+    auto compute = [&]() {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int slot = (2 * s + half) ^ (mi & 7);
+            const uint4 bx = st[0][mi][slot];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[m] = mfma16(st[m + 1][mi][slot], bx, acc[m]);
+        }
+    };
+    if (r1 - r0 < NB) {
+        for (int rr = r0; rr < r1; ++rr) {
+            load(rr, v[0]);
+            stage(v[0]);
+            compute();
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) load(r0 + k, v[k]);
+    int rr = r0;
+    for (; rr + 2 * NB - 1 < r1; rr += NB) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            stage(v[k]);
+            load(rr + k + NB, v[k]);
+            compute();
+        }
+    }
+    // fewer than 2 NB runs remain, the first NB of them loaded
+#pragma unroll
+    for (int k = 0; k < 2 * NB - 1; ++k) {
+        if (rr + k < r1) {
+            stage(v[k % NB]);
+            if (rr + k + NB < r1) load(rr + k + NB, v[k % NB]);
+            compute();
+        }
+    }
+}
+
 }  // namespace pi

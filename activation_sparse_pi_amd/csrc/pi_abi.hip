@@ -2,6 +2,7 @@
 // planning and launches.  Every check runs before the first HIP call, so an
 // invalid request enqueues nothing and leaves the outputs untouched.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -173,6 +174,9 @@ int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B, float* logits
     if (!aligned16(x)) return fail(PI_ERR_ALIGN, "x must be 16-byte aligned");
     if (pred->pfmt == PI_P_I8G128 && B > 1)
         return fail(PI_ERR_UNSUPPORTED, "the int8 predictor runs at batch 1 (B=%d)", B);
+    if (B > 1 && (size_t)pred->r * pred->d * 2 > (size_t)INT_MAX)
+        return fail(PI_ERR_UNSUPPORTED, "the batch predictor needs r * d * 2 < 2^31 bytes (r=%d d=%d)",
+                    pred->r, pred->d);
     const PredPlan pl = plan_pred(pred->d, pred->r, pred->F, B);
     if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
     const double tau = pred->threshold;

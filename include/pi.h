@@ -136,7 +136,9 @@ int pi_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   count  : int32 [B]   or NULL          ascending order in idx[b*F .. b*F+count[b])
  *                                         (the neuron table, "Neuron Placement and
  *                                         Management"); entries past count are not written
- * idx and count must both be given or both be NULL.  1 <= B <= PI_MAX_BATCH.       */
+ * idx and count must both be given or both be NULL.  1 <= B <= PI_MAX_BATCH.
+ * B > 1 takes an fp16 predictor with r * d * 2 < 2^31 bytes (PI_ERR_UNSUPPORTED
+ * otherwise).                                                                       */
 int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B,
                float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
                void* ws, size_t ws_bytes, void* stream);
