@@ -88,6 +88,8 @@ WSB = 1 << 30
     (dict(ws=None), L.PI_ERR_WORKSPACE),
     (dict(ws=WS + 16), L.PI_ERR_WORKSPACE),
     (dict(wsb=1024), L.PI_ERR_WORKSPACE),
+    # batch predictor: r * d * 2 must stay below 2^31 bytes
+    (dict(desc=pred(d=131072, r=8192), B=2), L.PI_ERR_UNSUPPORTED),
 ])
 def test_predict_validation(kw, code):
     a = dict(desc=pred(), x=A + 0x3000000, B=1, logits=None, mask=A + 0x4000000,
