@@ -167,6 +167,21 @@ PI_DEV uint4 ld_n(const void* p) {
 }
 PI_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// On the batch path weight rows are read once per step while x, the H fragments and the
+// partial sums are read many times: non-temporal loads of the rows (and buffer loads with
+// the nt cache-policy bit, PI_NT) keep them from evicting the reused data from L2.
+constexpr int PI_NT = 2;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+PI_DEV uint4 ld16_nt(const void* p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+PI_DEV uint2 ld8_nt(const void* p) {
+    const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(t.x, t.y);
+}
+
 // ---- wave-level (DPP: cross-lane moves inside the VALU, no LDS round trip) ----------------------
 // update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes whose source lane is
 // outside the row, or whose row is masked off, get `old`.

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
         }
         const int nfull = d >> 6, per = (nfull + UP_NW - 1) / UP_NW;
         const int r0 = min(nfull, wave * per), r1 = min(nfull, r0 + per);
-        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, 1, r1 - r0, s_st[wave], acc);
         if ((d & 63) && wave == UP_NW - 1) {
             const uint16_t* Wm[NM];
             Wm[0] = Wu;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
             const bool ok = st_ * 16 + j < U && (unsigned)id < (unsigned)F;
             bad |= ok ? 0u : 1u << j;
             const char* row = reinterpret_cast<const char*>(Wd + ((size_t)(ok ? id : 0) * d + c0));
-            v[j] = *reinterpret_cast<const uint2*>(row + voff);
+            v[j] = ld8_nt(row + voff);
         }
         return bad;
     };

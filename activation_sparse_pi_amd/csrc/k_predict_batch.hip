@@ -67,7 +67,7 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
         ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
         ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
     }
-    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, 1, r1 - r0, s_st[wave], acc);
     if ((d & 63) && ks == nks - 1 && wave == PB_NW - 1) {
         const uint16_t* const Wm[1] = {W1t};
         runs_mfma<1>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
         for (int rr = 0; rr < 4; ++rr) {
             const int e = min(c0 + kh * 256 + rr * 64 + lch * 8, r - 8);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) wv[rr][q] = ld16(wrow[q] + e);
+            for (int q = 0; q < 4; ++q) wv[rr][q] = ld16_nt(wrow[q] + e);
         }
     };
     // z of one pass: token b = tid / 16 holds chunks sub + 16 i (8 values each), i < 4

@@ -47,7 +47,7 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
             v[0][q] = (ok && offx[q] >= 0) ? ld16(x + offx[q] + e) : zero4();
 #pragma unroll
             for (int m = 0; m < NM; ++m)
-                v[m + 1][q] = (ok && offw[q] >= 0) ? ld16(W[m] + offw[q] + e) : zero4();
+                v[m + 1][q] = (ok && offw[q] >= 0) ? ld16_nt(W[m] + offw[q] + e) : zero4();
         }
     };
     auto stage = [&](const uint4(&v)[NP][4]) {
@@ -80,32 +80,34 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
     }
 }
 
-// runs_mfma over full runs only (every run of [r0, r1) inside the rows), rows read through
-// buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and ow[q] into
-// every W_m (resource rw[m]), plus 128 bytes per run.  NB runs are in flight per wave: a
-// run's registers are refilled with the run NB ahead as soon as they are staged.  The
-// steady loop issues every load unconditionally and is unrolled NB times so the buffers
-// rotate without copies; a scheduling barrier after each run's loads keeps them together,
-// so that (vector loads completing in order) waiting for the oldest run never waits for
-// younger ones.
+// runs_mfma over the nr full runs rbase + i rstep (every one inside the rows), rows read
+// through buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and
+// ow[q] into every W_m (resource rw[m], non-temporal), plus 128 bytes per run.  NB runs are
+// in flight per wave: a run's registers are refilled with the run NB ahead as soon as they
+// are staged.  The steady loop issues every load unconditionally and is unrolled NB times so
+// the buffers rotate without copies; a scheduling barrier after each run's loads keeps them
+// together, so that (vector loads completing in order) waiting for the oldest run never
+// waits for younger ones.
 template <int NM, int NB>
 PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
                            const __amdgpu_buffer_rsrc_t (&rw)[NM], const uint32_t (&ow)[4],
-                           int r0, int r1, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
+                           int rbase, int rstep, int nr, uint4 (*st)[32][8],
+                           f32x16_t (&acc)[NM]) {
+    const int r0 = 0, r1 = nr;
     constexpr int NP = NM + 1;
     const int lane = threadIdx.x & 63;
     const int lrow = lane >> 3, lch = lane & 7;
     const int mi = lane & 31, half = lane >> 5;
     uint4 v[NB][NP][4];
     auto load = [&](int rr, uint4(&b)[NP][4]) {
-        const int so = rr * 128;
+        const int so = (rbase + rr * rstep) * 128;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             b[0][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[q], so, 0));
 #pragma unroll
             for (int m = 0; m < NM; ++m)
                 b[m + 1][q] =
-                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw[m], ow[q], so, 0));
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw[m], ow[q], so, PI_NT));
         }
         __builtin_amdgcn_sched_barrier(0);
     };
