@@ -21,11 +21,12 @@ PI_P_F16, PI_P_I8G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
 PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 1, 2, 3, 4
 PI_MAX_BATCH = 32
+PI_BATCH_TOKENS, PI_BATCH_UNION = 0, 1
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
-           "pi_place_neurons", "pi_permute_rows", "pi_map_ids")
+           "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan")
 
 
 class PredDesc(ctypes.Structure):
@@ -38,6 +39,12 @@ class FfnDesc(ctypes.Structure):
     _fields_ = [("w_gate", c_void_p), ("w_up", c_void_p), ("w_down", c_void_p),
                 ("s_gate", c_void_p), ("s_up", c_void_p), ("s_down", c_void_p),
                 ("d", c_int32), ("F", c_int32), ("act", c_int32), ("wfmt", c_int32)]
+
+
+class BatchPlan(ctypes.Structure):
+    _fields_ = [("n_mean", ctypes.c_double), ("u_mean", ctypes.c_double),
+                ("t_tokens_us", ctypes.c_double), ("t_union_us", ctypes.c_double),
+                ("choice", c_int32)]
 
 
 class PiError(RuntimeError):
@@ -98,6 +105,9 @@ def lib() -> ctypes.CDLL:
         L.pi_permute_rows.restype = c_int
         L.pi_map_ids.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
         L.pi_map_ids.restype = c_int
+        L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
+                                    ctypes.POINTER(BatchPlan)]
+        L.pi_batch_plan.restype = c_int
         _LIB = L
     return _LIB
 
@@ -168,6 +178,11 @@ def check(status: int) -> None:
 def pi_place_neurons(counts: int, F: int, perm: int) -> int:
     """counts and perm are host addresses (int32 [F]), e.g. ndarray.ctypes.data."""
     return lib().pi_place_neurons(counts, F, perm)
+
+
+def pi_batch_plan(desc, B: int, rate: int, hbm_gbs: float, plan) -> int:
+    """rate is a host address (float32 [F]); plan a BatchPlan, filled on success."""
+    return lib().pi_batch_plan(_p(desc), B, rate, hbm_gbs, _p(plan))
 
 
 def pi_permute_rows(src, dst, perm, n, row_bytes, stream) -> int:

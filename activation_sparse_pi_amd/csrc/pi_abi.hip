@@ -429,6 +429,43 @@ int pi_place_neurons(const int32_t* counts, int F, int32_t* perm) {
     return ok();
 }
 
+// Batch-size dispatch.  The fixed costs and bandwidth fractions are fitted to this library's
+// own measurements on MI355X (one FFN layer of d = 8192, F = 32768, fp16, ReLU, 8% of the
+// neurons per token, B = 1 .. 32): the batch-1 operators move a token's rows at ~40% of peak
+// after ~4 us of launches and ramps; the union path (compaction + two MFMA kernels) moves
+// the union's rows at ~63% after ~15 us.
+namespace {
+constexpr double BATCH_TOK_FIXED_US = 4.0, BATCH_TOK_EFF = 0.40;
+constexpr double BATCH_UNION_FIXED_US = 15.0, BATCH_UNION_EFF = 0.63;
+}  // namespace
+
+int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_gbs,
+                  pi_batch_plan_t* plan) {
+    int st;
+    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
+    if (!rate || !plan) return fail(PI_ERR_NULL, "rate / plan NULL");
+    if ((st = check_batch(B)) != PI_OK) return st;
+    if (!(hbm_gbs > 0.0)) return fail(PI_ERR_SHAPE, "hbm_gbs must be positive, got %g", hbm_gbs);
+    double n = 0.0, u = 0.0;
+    for (int i = 0; i < ffn->F; ++i) {
+        const double p = rate[i];
+        if (!(p >= 0.0 && p <= 1.0)) return fail(PI_ERR_SHAPE, "rate[%d] = %g outside [0, 1]", i, p);
+        n += p;
+        u += 1.0 - std::pow(1.0 - p, (double)B);
+    }
+    const int m = ffn->act == PI_ACT_REGLU ? 3 : 2;
+    const double w = ffn->wfmt == PI_W_F16 ? 2.0 : 0.5 + 2.0 / 128.0;
+    const double row = (double)m * ffn->d * w;                    // bytes per listed neuron
+    const double bw = hbm_gbs * 1e3;                               // bytes per us
+    plan->n_mean = n;
+    plan->u_mean = u;
+    plan->t_tokens_us = B * (BATCH_TOK_FIXED_US + n * row / (BATCH_TOK_EFF * bw));
+    const bool union_ok = B > 1 && ffn->wfmt == PI_W_F16;
+    plan->t_union_us = union_ok ? BATCH_UNION_FIXED_US + u * row / (BATCH_UNION_EFF * bw) : HUGE_VAL;
+    plan->choice = plan->t_union_us < plan->t_tokens_us ? PI_BATCH_UNION : PI_BATCH_TOKENS;
+    return ok();
+}
+
 int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size_t row_bytes,
                     void* stream) {
     if (!src || !dst || !perm) return fail(PI_ERR_NULL, "src / dst / perm NULL");

@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--calib-tokens", type=int, default=256, help="calibration tokens for --placement")
     ap.add_argument("--pred-format", choices=("f16", "i8g128"), default="f16",
                     help="i8g128: the predictor factors in int8 with one fp16 scale per 128 (batch 1)")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="batch workload: token-by-token vs union sparse FFN for B = 1, 2, 4, ...")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling runs)")
     return ap.parse_args()
@@ -316,6 +318,96 @@ def bench_batch(a, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_batch_sweep(a, cfg):
+    """Batch-size dispatch on the batch workload's layer: for B = 1, 2, 4, ... up to the
+    workload's batch, the sparse FFN of B tokens run (i) token by token through the batch-1
+    operators, each with its own list, and (ii) as one union pass on MFMA (compaction
+    included), next to pi_batch_plan's estimates from the tokens' activation rates.  The
+    predictor is common to both and left out of the timed region."""
+    import torch
+
+    from activation_sparse_pi_amd import _lib as L
+    from activation_sparse_pi_amd.layer import DeviceLayer
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    inputs = gen.make(cfg)
+    Bmax, F = cfg.B, cfg.F
+    S = min(cfg.T, 16)                                   # distinct steps cycled through
+    xd = torch.from_numpy(inputs["x"][:S].copy()).to(dev)                 # [S, Bmax, d]
+    R = a.replicas or 2
+    layer = DeviceLayer(inputs, replicas=R, B_max=Bmax, device=dev)
+    W = (F + 31) // 32
+    mask = torch.empty((S, Bmax, W), dtype=torch.int32, device=dev)
+    idx = torch.empty((S, Bmax, F), dtype=torch.int32, device=dev)
+    cnt = torch.empty((S, Bmax), dtype=torch.int32, device=dev)
+    for t in range(S):
+        layer.predict(xd[t].data_ptr(), Bmax, None, mask[t].data_ptr(), idx[t].data_ptr(),
+                      cnt[t].data_ptr())
+    torch.cuda.synchronize()
+    bits = np.unpackbits(mask.cpu().numpy().view(np.uint8), axis=-1, bitorder="little")[..., :F]
+    rate = np.ascontiguousarray(bits.reshape(-1, F).mean(axis=0), dtype=np.float32)
+    uidx = torch.empty((F,), dtype=torch.int32, device=dev)
+    ucnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    y = torch.empty((Bmax, cfg.d), dtype=torch.float32, device=dev)
+    K, Wm = 32, 4
+
+    def timed(run):
+        for s in range(Wm):
+            run(s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(K):
+            run(Wm + s)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3          # us per step
+
+    rows = []
+    B = 1
+    while B <= Bmax:
+        def tokens(s, B=B):
+            t, rep = s % S, s % R
+            for b in range(B):
+                layer.sparse_ffn(xd[t, b].data_ptr(), 1, idx[t, b].data_ptr(), cnt[t, b:].data_ptr(),
+                                 None, y[b].data_ptr(), rep)
+
+        def union(s, B=B):
+            t, rep = s % S, s % R
+            layer.compact(mask[t].data_ptr(), B, L.PI_UNION, uidx.data_ptr(), ucnt.data_ptr())
+            layer.sparse_ffn(xd[t].data_ptr(), B, uidx.data_ptr(), ucnt.data_ptr(), mask[t].data_ptr(),
+                             y.data_ptr(), rep)
+
+        t_tok = timed(tokens)
+        t_uni = timed(union) if B > 1 else None
+        u_meas = float(np.mean([bits[t, :B].any(axis=0).sum() for t in range(S)]))
+        p = L.BatchPlan()
+        L.check(L.pi_batch_plan(layer.ffn[0], B, rate.ctypes.data, HBM_PEAK_GBS, p))
+        best = "tokens" if t_uni is None or t_tok <= t_uni else "union"
+        rows.append({
+            "B": B, "tokens_us": round(t_tok, 2), "union_us": None if t_uni is None else round(t_uni, 2),
+            "best": best, "mean_union": round(u_meas, 1),
+            "plan": {"choice": "union" if p.choice == L.PI_BATCH_UNION else "tokens",
+                     "tokens_us": round(p.t_tokens_us, 2),
+                     "union_us": None if math.isinf(p.t_union_us) else round(p.t_union_us, 2),
+                     "n_mean": round(p.n_mean, 1), "u_mean": round(p.u_mean, 1)},
+        })
+        print(f"# B={B}: tokens {t_tok:.1f} us, union {t_uni} us, plan {rows[-1]['plan']}", file=sys.stderr,
+              flush=True)
+        B *= 2
+    out = {
+        "metric": "batch-size dispatch: sparse FFN of B tokens, token by token vs one union pass (us per step)",
+        "unit": "us", "n_gpus": 1, "data": "synthetic", "dtype": "f16",
+        "config": {"workload": f"{cfg.name}: one FFN layer, d={cfg.d}, ffn={F}, {cfg.act}, fp16 weights; "
+                               f"the first B of each step's {Bmax} tokens, {S} steps cycled, {R} replicas",
+                   "steps": K, "warmup": Wm},
+        "rows": rows,
+        "plan_agrees": sum(r["plan"]["choice"] == r["best"] for r in rows),
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------------------- main
 def main():
     a = parse()
@@ -334,6 +426,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = configs.get(a.config)
+    if a.batch_sweep:
+        if cfg.B == 1:
+            print("--batch-sweep needs a batch workload (c4)", file=sys.stderr)
+            sys.exit(2)
+        return bench_batch_sweep(a, cfg)
     if cfg.B != 1:
         return bench_batch(a, cfg)
     dev = torch.device("cuda:0")

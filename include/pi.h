@@ -276,6 +276,36 @@ int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size
 int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int32_t* perm,
                int32_t* out, void* stream);
 
+/* ---- batch-size dispatch ------------------------------------------------------------------
+ * Efficient, VRAM-Constrained xLM Inference on Clients, "Methodology" (planning phase): a
+ * roofline time estimate picks, for each number of tokens per step, one of several schedules
+ * prepared in advance.  Here the two schedules of the sparse FFN of B tokens on one GPU:
+ *   PI_BATCH_TOKENS  every token through the batch-1 operators with its own list
+ *                    (pi_sparse_ffn at B = 1, once per token): m n d w bytes per token;
+ *   PI_BATCH_UNION   one pass over the union of the B lists on MFMA (pi_compact PI_UNION,
+ *                    then pi_sparse_ffn at B): m U d w bytes for the B tokens together.
+ * m = 2 (ReLU) or 3 (ReGLU) matrices, w = bytes per weight.  With rate[i] the probability that
+ * neuron i is predicted active for one token (activation counts of a calibration run over
+ * its number of tokens) and tokens drawn independently:
+ *   n = sum_i rate[i],   U = sum_i (1 - (1 - rate[i])^B).
+ * Each schedule's time is a fixed cost per step or per token (its kernel launches) plus its
+ * bytes over its measured fraction of hbm_gbs (figures measured on MI355X, stated with the
+ * implementation).  B = 1 and int4 weights (no union path) give PI_BATCH_TOKENS.
+ * Host only, no HIP call.  rate: host float [F], each in [0, 1].  Errors: PI_ERR_NULL,
+ * PI_ERR_SHAPE (B outside 1..PI_MAX_BATCH, a rate outside [0, 1], hbm_gbs <= 0), and the
+ * descriptor checks of pi_sparse_ffn; *plan untouched on error.                             */
+#define PI_BATCH_TOKENS 0
+#define PI_BATCH_UNION  1
+typedef struct {
+    double n_mean;       /* expected active neurons per token                    */
+    double u_mean;       /* expected size of the union of B tokens' lists        */
+    double t_tokens_us;  /* estimated time of PI_BATCH_TOKENS for the B tokens    */
+    double t_union_us;   /* estimated time of PI_BATCH_UNION (B > 1, fp16)        */
+    int32_t choice;      /* PI_BATCH_TOKENS or PI_BATCH_UNION: the smaller time  */
+} pi_batch_plan_t;
+int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_gbs,
+                  pi_batch_plan_t* plan);
+
 #ifdef __cplusplus
 }
 #endif

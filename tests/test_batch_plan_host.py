@@ -1,0 +1,109 @@
+"""Batch-size dispatch planner (pi_batch_plan), host only.
+
+The expected per-token count n and union U of B independent tokens are pinned against an
+exhaustive enumeration of every outcome on a tiny layer and against a Monte-Carlo draw of
+token masks; the choice against the cases the model fixes (one token, int4 weights, a
+heavy overlap of the tokens' lists)."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from activation_sparse_pi_amd import _lib as L
+
+A = 0x7F0000000000
+
+
+def ffn(d=8192, F=64, act=L.PI_ACT_RELU, wfmt=L.PI_W_F16):
+    s = A + 0x2000000 if wfmt == L.PI_W_I4G128 else None
+    g = A + 0x3000000 if act == L.PI_ACT_REGLU else None
+    return L.FfnDesc(g, A, A + 0x1000000, s if g else None, s, s, d, F, act, wfmt)
+
+
+def plan(rate, B, desc=None, hbm=8000.0):
+    rate = np.ascontiguousarray(rate, dtype=np.float32)
+    desc = desc or ffn(F=rate.size)
+    p = L.BatchPlan()
+    st = L.pi_batch_plan(desc, B, rate.ctypes.data, hbm, p)
+    assert st == L.PI_OK, L.pi_last_error()
+    return p
+
+
+def test_expected_union_by_enumeration():
+    """Tiny layer: E[union] and E[n] by summing over every joint outcome of B tokens."""
+    rate = np.array([0.5, 0.25, 0.75, 0.0, 1.0, 0.125, 0.5, 0.625], np.float32)
+    F, B = rate.size, 2
+    eu = en = 0.0
+    for bits in itertools.product((0, 1), repeat=F * B):
+        m = np.array(bits).reshape(B, F)
+        pr = np.prod(np.where(m == 1, rate[None, :], 1.0 - rate[None, :]))
+        eu += pr * m.any(axis=0).sum()
+        en += pr * m[0].sum()
+    p = plan(rate, B)
+    assert p.u_mean == pytest.approx(eu, rel=1e-12, abs=1e-12)
+    assert p.n_mean == pytest.approx(en, rel=1e-12, abs=1e-12)
+
+
+def test_expected_union_by_sampling():
+    rng = np.random.default_rng(7)
+    F, B, T = 512, 12, 4000
+    rate = np.clip(rng.gamma(0.6, 0.12, F), 0.0, 1.0).astype(np.float32)
+    masks = rng.random((T, B, F)) < rate[None, None, :]
+    u = masks.any(axis=1).sum(axis=1)
+    p = plan(rate, B)
+    sem = u.std() / math.sqrt(T)
+    assert abs(u.mean() - p.u_mean) < 5 * sem
+    assert abs(masks[:, 0].sum(axis=1).mean() - p.n_mean) < 5 * masks[:, 0].sum(axis=1).std() / math.sqrt(T)
+
+
+def test_one_token_and_int4_take_the_token_path():
+    rate = np.full(256, 0.1, np.float32)
+    p1 = plan(rate, 1)
+    assert p1.choice == L.PI_BATCH_TOKENS and math.isinf(p1.t_union_us)
+    assert p1.u_mean == pytest.approx(p1.n_mean, rel=1e-12)
+    p4 = plan(rate, 8, ffn(F=256, wfmt=L.PI_W_I4G128))
+    assert p4.choice == L.PI_BATCH_TOKENS and math.isinf(p4.t_union_us)
+
+
+def test_overlap_decides():
+    """Identical lists (rates 0 or 1): the union costs one token's rows, so it wins at any
+    B > 1; disjoint-looking sparse rates at small B keep the token path's lower fixed cost."""
+    F = 32768
+    rate = np.zeros(F, np.float32)
+    rate[:2600] = 1.0
+    p = plan(rate, 2, ffn(F=F))
+    assert p.u_mean == pytest.approx(2600) and p.choice == L.PI_BATCH_UNION
+    sparse = np.full(F, 4.0 / F, np.float32)            # ~4 neurons per token
+    q = plan(sparse, 2, ffn(F=F))
+    assert q.choice == L.PI_BATCH_TOKENS
+
+
+def test_token_time_is_linear_in_batch():
+    rate = np.full(1024, 0.05, np.float32)
+    t = [plan(rate, B).t_tokens_us for B in (1, 2, 4, 8)]
+    assert t[1] == pytest.approx(2 * t[0]) and t[3] == pytest.approx(8 * t[0])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), L.PI_ERR_SHAPE),
+    (dict(B=33), L.PI_ERR_SHAPE),
+    (dict(hbm=0.0), L.PI_ERR_SHAPE),
+    (dict(bad=1.5), L.PI_ERR_SHAPE),
+    (dict(bad=float("nan")), L.PI_ERR_SHAPE),
+    (dict(bad=-0.1), L.PI_ERR_SHAPE),
+    (dict(null_rate=True), L.PI_ERR_NULL),
+    (dict(null_plan=True), L.PI_ERR_NULL),
+    (dict(null_desc=True), L.PI_ERR_NULL),
+])
+def test_validation(kw, code):
+    rate = np.full(64, 0.1, np.float32)
+    if "bad" in kw:
+        rate[5] = kw["bad"]
+    p = L.BatchPlan()
+    p.choice = 77
+    st = L.pi_batch_plan(None if kw.get("null_desc") else ffn(F=64), kw.get("B", 4),
+                         None if kw.get("null_rate") else rate.ctypes.data, kw.get("hbm", 8000.0),
+                         None if kw.get("null_plan") else p)
+    assert st == code, L.pi_last_error()
+    assert p.choice == 77                                  # untouched on error

@@ -228,3 +228,37 @@ def test_predict_batch_c5_shape():
     for b in range(32):
         gpu_active = O.words_to_active(mk[b], cfg.F)
         P.check_index_set(O.compact(gpu_active), mk[b], ref[b], cfg.F, ctx=f"b={b}")
+
+
+@pytest.mark.parametrize("cfg", [
+    configs.tiny("relu", "f16", d=1032, F=2056, r=96, B=6, T=1, seed=41),
+    configs.tiny("reglu", "f16", d=384, F=1000, r=40, B=3, T=1, seed=42),
+], ids=lambda c: f"{c.name}_b{c.B}")
+def test_batch_schedules_agree(cfg):
+    """The two schedules pi_batch_plan chooses between: every token through the batch-1
+    operators with its own list, and one union pass.  Both match the oracle on each token's
+    own list; pi_batch_plan takes the layer's descriptor (at rates of 0 and 1 its expected
+    union is the union's size)."""
+    from activation_sparse_pi_amd import _lib as L
+    say(f"[gpu] batch schedules {cfg.name} B={cfg.B}")
+    inp = gen.make(cfg)
+    W = O.Weights.from_inputs(inp)
+    layer = _layer(inp, B_max=cfg.B)
+    bufs = layer.buffers(cfg.B)
+    xd = torch.from_numpy(inp["x"]).to(layer.device)
+    g = run_batch(layer, xd[0], cfg.B, bufs)                 # union schedule
+    check_batch(g, inp, W, inp["x"][0], cfg.F, ctx=f"{cfg.name} union")
+    yt = torch.zeros((cfg.B, cfg.d), dtype=torch.float32, device=layer.device)
+    for b in range(cfg.B):                                   # token schedule, own lists
+        layer.sparse_ffn(xd[0, b].data_ptr(), 1, bufs["idx"][b].data_ptr(), bufs["count"][b:].data_ptr(),
+                         None, yt[b].data_ptr())
+    torch.cuda.synchronize()
+    y_tok = _np(yt)
+    for b in range(cfg.B):
+        P.check_ffn(y_tok[b], W, inp["x"][0, b], g["idx"][b], ctx=f"{cfg.name} tokens b={b}")
+    rate = np.zeros(cfg.F, np.float32)                       # every neuron at rate 0 or 1
+    for b in range(cfg.B):
+        rate[g["idx"][b]] = 1.0
+    p = L.BatchPlan()
+    L.check(L.pi_batch_plan(layer.ffn[0], cfg.B, rate.ctypes.data, 8000.0, p))
+    assert p.u_mean == pytest.approx(len(g["uidx"]))
