@@ -262,3 +262,54 @@ def test_batch_schedules_agree(cfg):
     p = L.BatchPlan()
     L.check(L.pi_batch_plan(layer.ffn[0], cfg.B, rate.ctypes.data, 8000.0, p))
     assert p.u_mean == pytest.approx(len(g["uidx"]))
+
+
+def test_union_past_2gb_rows():
+    """Weight matrices larger than 2^31 bytes (F = 131080, d = 8192: rows from 131072 on start
+    past 2 GB) take the union kernels' general loop; token lists that include the last rows,
+    checked against the oracle on each token's own list (the oracle holds only the listed
+    rows, renumbered)."""
+    from activation_sparse_pi_amd import _lib as L
+    F, d, B = 131080, 8192, 4
+    assert F * d * 2 > 2**31 - 1
+    say(f"[gpu] union past 2 GB: F={F} d={d} B={B}")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(51)
+    w_up = torch.empty((F, d), dtype=torch.float16, device=dev).normal_(0.0, 0.02, generator=g)
+    w_dn = torch.empty((F, d), dtype=torch.float16, device=dev).normal_(0.0, 0.02, generator=g)
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((B, d)).astype(np.float16)
+    act = np.zeros((B, F), bool)
+    for b in range(B):
+        act[b, rng.choice(F, 60, replace=False)] = True
+        act[b, F - 1 - b] = True                            # the last rows, past 2 GB
+        act[b, 131072 + 2 * b] = True
+    act[:, 5] = True                                         # one neuron shared by every token
+    desc = L.FfnDesc(None, w_up.data_ptr(), w_dn.data_ptr(), None, None, None, d, F,
+                     L.PI_ACT_RELU, L.PI_W_F16)
+    nws = L.pi_workspace_bytes(None, desc, B)
+    assert nws > 0, L.pi_last_error()
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    L.check(L.pi_workspace_init(ws.data_ptr(), nws, stream))
+    xd = torch.from_numpy(x).to(dev)
+    md = torch.from_numpy(O.mask_words(act).view(np.int32)).to(dev)
+    uidx = torch.empty((F,), dtype=torch.int32, device=dev)
+    ucnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    L.check(L.pi_compact(md.data_ptr(), B, F, L.PI_UNION, uidx.data_ptr(), ucnt.data_ptr(), None, 0, stream))
+    L.check(L.pi_sparse_ffn(desc, xd.data_ptr(), B, uidx.data_ptr(), ucnt.data_ptr(), md.data_ptr(),
+                            y.data_ptr(), ws.data_ptr(), nws, stream))
+    torch.cuda.synchronize()
+    un = O.compact(O.union_active(act))
+    assert np.array_equal(_np(uidx[: int(_np(ucnt)[0])]).astype(np.int64), un)
+    sel = torch.from_numpy(un).to(dev)
+    Wsmall = O.Weights("relu", "f16", {"w_up": _np(w_up[sel]), "w_down": _np(w_dn[sel])})
+    pos = {int(n): k for k, n in enumerate(un)}
+    yg = _np(y)
+    for b in range(B):
+        own = np.array([pos[int(n)] for n in O.compact(act[b])], np.int64)
+        P.check_ffn(yg[b], Wsmall, x[b], own, ctx=f"past 2 GB b={b}")
+    del w_up, w_dn
+    torch.cuda.empty_cache()
