@@ -171,6 +171,11 @@ PI_DEV uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 // partial sums are read many times: non-temporal loads of the rows (and buffer loads with
 // the nt cache-policy bit, PI_NT) keep them from evicting the reused data from L2.
 constexpr int PI_NT = 2;
+// A raw buffer resource over `bytes` bytes at p (loads past them return 0).  Word 3 names a
+// 32-bit data format: with a zero format every load would return 0.
+PI_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 PI_DEV uint4 ld16_nt(const void* p) {

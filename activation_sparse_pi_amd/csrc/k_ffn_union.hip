@@ -83,13 +83,10 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
         // full runs through buffer resources (byte offsets of F rows fit 31 bits): zero rows
         // read row 0 of W and x instead, their h is zeroed below; the partial run, if any,
         // goes the general way
-        const int flags = 0x00020000;
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(x), 0, B * d * 2, flags);
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, B * d * 2);
         __amdgpu_buffer_rsrc_t rw[NM];
-        rw[0] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wu), 0, F * d * 2, flags);
-        if constexpr (GLU)
-            rw[1] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg), 0, F * d * 2, flags);
+        rw[0] = buf_rsrc(Wu, F * d * 2);
+        if constexpr (GLU) rw[1] = buf_rsrc(Wg, F * d * 2);
         uint32_t ox[4], ow[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -98,7 +95,7 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
         }
         const int nfull = d >> 6, per = (nfull + UP_NW - 1) / UP_NW;
         const int r0 = min(nfull, wave * per), r1 = min(nfull, r0 + per);
-        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, 1, r1 - r0, s_st[wave], acc);
+        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
         if ((d & 63) && wave == UP_NW - 1) {
             const uint16_t* Wm[NM];
             Wm[0] = Wu;
@@ -345,8 +342,7 @@ __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
     // c0 + 4 (q % 64) .. + 3; 32 coherent 16-byte loads are in flight per round (4 chunks x
     // 8 shares).  Loads past the buffer (shares >= nks) return zeros; columns past d are
     // summed but never stored.
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        part, 0, (int)((size_t)nks * 32 * d * sizeof(float)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(part, (int)((size_t)nks * 32 * d * sizeof(float)));
     const int j4 = 4 * (tid & 63);
 #pragma unroll
     for (int m0 = 0; m0 < 8; m0 += 4) {

@@ -56,18 +56,15 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
     f32x16_t acc[1] = {};
     // full runs through buffer resources (every byte offset below 2^31): rows past r read
     // row 0, tokens past B token 0; neither reaches a stored output
-    const int flags = 0x00020000;
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, B * d * 2, flags);
-    const __amdgpu_buffer_rsrc_t rw[1] = {
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W1t), 0, r * d * 2, flags)};
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, B * d * 2);
+    const __amdgpu_buffer_rsrc_t rw[1] = {buf_rsrc(W1t, r * d * 2)};
     uint32_t ox[4], ow[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
         ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
     }
-    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, 1, r1 - r0, s_st[wave], acc);
+    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
     if ((d & 63) && ks == nks - 1 && wave == PB_NW - 1) {
         const uint16_t* const Wm[1] = {W1t};
         runs_mfma<1>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);

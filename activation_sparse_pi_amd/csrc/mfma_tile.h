@@ -80,7 +80,7 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
     }
 }
 
-// runs_mfma over the nr full runs rbase + i rstep (every one inside the rows), rows read
+// runs_mfma over the full runs [r0, r1) (every one inside the rows), rows read
 // through buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and
 // ow[q] into every W_m (resource rw[m], non-temporal), plus 128 bytes per run.  NB runs are
 // in flight per wave: a run's registers are refilled with the run NB ahead as soon as they
@@ -91,16 +91,14 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
 template <int NM, int NB>
 PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
                            const __amdgpu_buffer_rsrc_t (&rw)[NM], const uint32_t (&ow)[4],
-                           int rbase, int rstep, int nr, uint4 (*st)[32][8],
-                           f32x16_t (&acc)[NM]) {
-    const int r0 = 0, r1 = nr;
+                           int r0, int r1, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
     constexpr int NP = NM + 1;
     const int lane = threadIdx.x & 63;
     const int lrow = lane >> 3, lch = lane & 7;
     const int mi = lane & 31, half = lane >> 5;
     uint4 v[NB][NP][4];
     auto load = [&](int rr, uint4(&b)[NP][4]) {
-        const int so = (rbase + rr * rstep) * 128;
+        const int so = rr * 128;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             b[0][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[q], so, 0));
