@@ -107,3 +107,19 @@ def test_validation(kw, code):
                          None if kw.get("null_plan") else p)
     assert st == code, L.pi_last_error()
     assert p.choice == 77                                  # untouched on error
+
+
+def test_bytes_per_row_follow_matrices_and_format():
+    """The variable part of each estimate scales with the bytes of one listed neuron:
+    m d w, with m = 2 (ReLU) or 3 (ReGLU) and w = 2 (fp16) or 0.5 + 2/128 (int4 g128)."""
+    F, d, B = 4096, 4096, 4
+    rate = np.full(F, 0.1, np.float32)
+    base = plan(rate, B, ffn(d=d, F=F))
+    glu = plan(rate, B, ffn(d=d, F=F, act=L.PI_ACT_REGLU))
+    i4 = plan(rate, B, ffn(d=d, F=F, wfmt=L.PI_W_I4G128))
+    tiny = plan(np.full(F, 1e-9, np.float32), B, ffn(d=d, F=F))    # ~ the fixed costs alone
+    tok = lambda p: p.t_tokens_us - tiny.t_tokens_us                  # noqa: E731
+    uni = lambda p: p.t_union_us - tiny.t_union_us                    # noqa: E731
+    assert tok(glu) / tok(base) == pytest.approx(1.5, rel=1e-6)
+    assert uni(glu) / uni(base) == pytest.approx(1.5, rel=1e-6)
+    assert tok(i4) / tok(base) == pytest.approx((0.5 + 2 / 128) / 2, rel=1e-6)
