@@ -24,23 +24,61 @@ namespace {
 
 // ------------------------------------------------------------------------------------ stage 1
 // z[b, j] = W1t[j, :] . x[b, :].  Block: 4 waves = 4 rows.  The row is read in segments of
-// QS 16-byte chunks per lane (all loads of a segment in flight together).
+// QS 16-byte chunks per lane (all loads of a segment in flight together).  WPR = 4 (batch 1,
+// fp16, rows of at least 256 chunks): one row per block, its 4 waves taking a quarter of
+// the chunks each and meeting in LDS -- four times the blocks, each wave a quarter of the
+// loads.
 // CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
 // y accumulators (ncopy copies) into y and clears them for this step's down projection.
 // P8: int8 rows (a chunk = 16 weights, one fp16 scale per 8 chunks), x read 32 bytes a chunk.
-template <int QS, bool CONV, bool P8>
+template <int QS, bool CONV, bool P8, int WPR = 1>
 __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
                                             const void* __restrict__ W1t,
                                             const uint16_t* __restrict__ S1, int d, int r,
                                             float* __restrict__ z, long long* __restrict__ yacc,
                                             float* __restrict__ y, int ncopy) {
     const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int j = WPR == 1 ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
     constexpr int EPC = P8 ? 16 : 8;                  // elements per 16-byte chunk
     const int nc = d / EPC;
     const size_t rowb = P8 ? (size_t)d : (size_t)d * 2;
     const uint8_t* Wb = static_cast<const uint8_t*>(W1t);
     const int ng = d >> 7;                            // int8: scale groups per row
+    if constexpr (WPR > 1) {
+        // one row per block: wave p takes chunks (p QW + q) 64 + lane
+        constexpr int QW = (QS + WPR - 1) / WPR;
+        const int p = threadIdx.x >> 6;
+        const int jj = j < r ? j : 0;
+        const uint8_t* row = Wb + (size_t)jj * rowb;
+        uint4 w[QW], xr[QW];
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const int c = (p * QW + q) * 64 + lane;
+            const int cc = c < nc ? c : 0;
+            w[q] = ld16(row + 16 * (size_t)cc);
+            xr[q] = ld16(x + 8 * cc);
+        }
+        if (CONV) {
+            for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
+                y[i] = from_fx(fx_take(yacc, d, i, ncopy));
+        }
+        if (j >= r) return;                             // the whole block
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < QW; ++q)
+            if ((p * QW + q) * 64 + lane < nc) acc = dot8(w[q], xr[q], acc);
+        acc = wave_sum(acc);
+        __shared__ float s_part[WPR];
+        if (lane == 0) s_part[p] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = 0.f;
+#pragma unroll
+            for (int k = 0; k < WPR; ++k) t += s_part[k];
+            z[j] = t;
+        }
+        return;
+    }
     if (B == 1 && nc <= 64 * QS) {
         // one segment: row and x chunks all in flight together, issued before the conversion
         // (whose loads would otherwise hold the row loads back by a memory round trip)
@@ -192,7 +230,10 @@ hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const u
         return hipGetLastError();
     }
 #define PI_P1(QQ) case QQ: \
-    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
+    if (B == 1 && QQ >= 4 && p.d / 8 <= 64 * QQ) { \
+        if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
+        else hipLaunchKernelGGL((k_p1<QQ, false, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 1); \
+    } else if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
     else hipLaunchKernelGGL((k_p1<QQ, false, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 1); \
     break;
     switch (pl.qs) {
