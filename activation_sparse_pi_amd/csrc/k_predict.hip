@@ -25,9 +25,8 @@ namespace {
 // ------------------------------------------------------------------------------------ stage 1
 // z[b, j] = W1t[j, :] . x[b, :].  Block: 4 waves = 4 rows.  The row is read in segments of
 // QS 16-byte chunks per lane (all loads of a segment in flight together).  WPR = 4 (batch 1,
-// fp16, rows of at least 256 chunks): one row per block, its 4 waves taking a quarter of
-// the chunks each and meeting in LDS -- four times the blocks, each wave a quarter of the
-// loads.
+// rows of at least 256 chunks): one row per block, its 4 waves taking a quarter of the
+// chunks each and meeting in LDS -- four times the blocks, each wave a quarter of the loads.
 // CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
 // y accumulators (ncopy copies) into y and clears them for this step's down projection.
 // P8: int8 rows (a chunk = 16 weights, one fp16 scale per 8 chunks), x read 32 bytes a chunk.
@@ -50,13 +49,20 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
         const int p = threadIdx.x >> 6;
         const int jj = j < r ? j : 0;
         const uint8_t* row = Wb + (size_t)jj * rowb;
-        uint4 w[QW], xr[QW];
+        uint4 w[QW], xr[QW], xr2[P8 ? QW : 1];
+        uint32_t sr[P8 ? QW : 1];
 #pragma unroll
         for (int q = 0; q < QW; ++q) {
             const int c = (p * QW + q) * 64 + lane;
             const int cc = c < nc ? c : 0;
             w[q] = ld16(row + 16 * (size_t)cc);
-            xr[q] = ld16(x + 8 * cc);
+            if constexpr (P8) {
+                xr[q] = ld16(x + 16 * cc);
+                xr2[q] = ld16(x + 16 * cc + 8);
+                sr[q] = S1[(size_t)jj * ng + (cc >> 3)];
+            } else {
+                xr[q] = ld16(x + 8 * cc);
+            }
         }
         if (CONV) {
             for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
@@ -66,7 +72,12 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
         float acc = 0.f;
 #pragma unroll
         for (int q = 0; q < QW; ++q)
-            if ((p * QW + q) * 64 + lane < nc) acc = dot8(w[q], xr[q], acc);
+            if ((p * QW + q) * 64 + lane < nc) {
+                if constexpr (P8)
+                    acc = fmaf(h2f((uint16_t)sr[q]), dot16_i8_f16(w[q], xr[q], xr2[q]), acc);
+                else
+                    acc = dot8(w[q], xr[q], acc);
+            }
         acc = wave_sum(acc);
         __shared__ float s_part[WPR];
         if (lane == 0) s_part[p] = acc;
@@ -218,7 +229,10 @@ hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const u
         int q = (p.d / 16 + 63) / 64;
         q = q < 1 ? 1 : (q > 16 ? 16 : q);
 #define PI_P1(QQ) case QQ: \
-    if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
+    if (B == 1 && QQ >= 4 && p.d / 16 <= 64 * QQ) { \
+        if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
+        else hipLaunchKernelGGL((k_p1<QQ, false, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
+    } else if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
     else hipLaunchKernelGGL((k_p1<QQ, false, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
     break;
         switch (q) {
