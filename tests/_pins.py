@@ -287,6 +287,43 @@ def pin_int4_roundtrip(O, seed=8):
             assert abs(round(deq[i, k] / float(scales[i, j]))) == 7, "absmax -> |q| = 7"
 
 
+# ----------------------------------------------------------------------------- one decode step
+def pin_token_step(O):
+    """token_step composes predict -> strict threshold -> band -> table -> FFN on that table.
+
+    Against the hand-worked example: neurons 3 and 5 sit exactly on the threshold, so they are
+    inactive and form the exclusion band; the FFN runs on {0, 2, 4} only.  Against brute force
+    on tiny shapes: the table is the set of brute-force logits above 0, the band the set within
+    1e-4 of it, and y the brute-force FFN over that table (not the dense FFN).
+    """
+    ex = _load("worked_example.json")
+    inp = {"w_p1": np.array(ex["w_p1"], np.float16), "w_p2": np.array(ex["w_p2"], np.float16),
+           "bias": np.array(ex["bias"], np.float32)}
+    x = np.array(ex["x"], np.float16)
+    for a in ("relu", "reglu"):
+        W = O.Weights(a, "f16", _ffn_inputs(ex, a))
+        st = O.token_step(inp, W, x)
+        assert np.array_equal(st["logits"], np.array(ex["logits"], float)), (a, "step logits")
+        assert list(st["idx"]) == ex["active_idx"], (a, "step idx", st["idx"])
+        assert list(np.flatnonzero(st["active"])) == ex["active_idx"], (a, "step active")
+        assert list(np.flatnonzero(st["band"])) == [3, 5], (a, "step band", st["band"])
+        assert np.array_equal(st["y"], np.array(ex[a + "_y_pred"], float)), (a, "step y", st["y"])
+    for seed in (1, 2):
+        for act, wfmt, d in (("relu", "f16", 8), ("reglu", "f16", 8), ("reglu", "i4g128", 128)):
+            inp = _tiny_inputs(act, wfmt, seed, d=d, F=16, r=2)
+            W = O.Weights(act, wfmt, inp)
+            for t in range(inp["x"].shape[0]):
+                x = inp["x"][t, 0]
+                bl = _brute_logits(x, inp["w_p1"], inp["w_p2"], inp["bias"])
+                st = O.token_step(inp, W, x)
+                want = [i for i in range(16) if bl[i] > 0]
+                assert list(st["idx"]) == want, (act, wfmt, "step idx", st["idx"], want)
+                assert list(np.flatnonzero(st["band"])) == \
+                    [i for i in range(16) if abs(bl[i]) < 1e-4], (act, wfmt, "step band")
+                yb = _brute_ffn(inp, act, wfmt, x, want, d)
+                assert np.allclose(st["y"], yb, rtol=1e-11, atol=1e-12), (act, wfmt, "step y")
+
+
 ALL_PINS = [pin_worked_example, pin_int4_worked, pin_bruteforce, pin_support_and_ones,
             pin_additivity, pin_empty, pin_rate_closed_form, pin_compaction,
-            pin_threshold_strict, pin_int4_roundtrip]
+            pin_threshold_strict, pin_int4_roundtrip, pin_token_step]

@@ -132,6 +132,31 @@ def _mask_words_msb_first(active):
     return out.astype(np.uint32)
 
 
+_token_step_orig = O.token_step
+
+
+def _step_uses_band(inputs, W, x, theta=0.0, eps=1e-4):
+    out = _token_step_orig(inputs, W, x, theta, eps)
+    idx = O.compact(out["band"])
+    return dict(out, idx=idx, y=O.ffn_neurons(W, x, idx))
+
+
+def _step_runs_dense(inputs, W, x, theta=0.0, eps=1e-4):
+    out = _token_step_orig(inputs, W, x, theta, eps)
+    return dict(out, y=O.ffn_dense(W, x))
+
+
+def _step_mask_or_band(inputs, W, x, theta=0.0, eps=1e-4):
+    out = _token_step_orig(inputs, W, x, theta, eps)
+    idx = O.compact(out["active"] | out["band"])
+    return dict(out, idx=idx, y=O.ffn_neurons(W, x, idx))
+
+
+def _step_ffn_on_other_token(inputs, W, x, theta=0.0, eps=1e-4):
+    out = _token_step_orig(inputs, W, x, theta, eps)
+    return dict(out, y=O.ffn_neurons(W, -f64(x), out["idx"]))
+
+
 MUTANTS = {
     "predictor drops bias": ("predictor_logits", _pred_no_bias),
     "predictor bias sign": ("predictor_logits", _pred_minus_bias),
@@ -151,6 +176,10 @@ MUTANTS = {
     "ffn drops last neuron": ("ffn_neurons", _ffn_drops_last),
     "down rows shifted": ("ffn_neurons", _ffn_shifted_rows),
     "mask bit order": ("mask_words", _mask_words_msb_first),
+    "token_step thresholds the band": ("token_step", _step_uses_band),
+    "token_step runs the dense FFN": ("token_step", _step_runs_dense),
+    "token_step keeps the band neurons": ("token_step", _step_mask_or_band),
+    "token_step FFN on the wrong x": ("token_step", _step_ffn_on_other_token),
 }
 
 
@@ -164,4 +193,5 @@ def test_mutant_is_caught(name, monkeypatch):
             pin(O)
         except (AssertionError, IndexError, ValueError) as e:  # a pin tripped
             failed.append((pin.__name__, str(e)[:80]))
+            break                     # one failing pin is enough
     assert failed, f"mutant '{name}' passed every pin"
