@@ -26,7 +26,8 @@ PI_BATCH_TOKENS, PI_BATCH_UNION = 0, 1
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
-           "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan")
+           "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan",
+           "pi_count_active")
 
 
 class PredDesc(ctypes.Structure):
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.pi_permute_rows.restype = c_int
         L.pi_map_ids.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
         L.pi_map_ids.restype = c_int
+        L.pi_count_active.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p]
+        L.pi_count_active.restype = c_int
         L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
                                     ctypes.POINTER(BatchPlan)]
         L.pi_batch_plan.restype = c_int
@@ -191,3 +194,7 @@ def pi_permute_rows(src, dst, perm, n, row_bytes, stream) -> int:
 
 def pi_map_ids(idx, count, B, F, perm, out, stream) -> int:
     return lib().pi_map_ids(idx, count, B, F, perm, out, stream)
+
+
+def pi_count_active(mask, B, F, counts, stream) -> int:
+    return lib().pi_count_active(mask, B, F, counts, stream)

@@ -244,37 +244,49 @@ PI_DEV uint32_t ld_agent(const uint32_t* p) {
     return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- exact cross-block sums: int64 fixed point ---------------------------------------------
-// A float v is carried as round(v * 2^32) (|v| clamped to 2^26, so even 64 such terms
-// cannot overflow); integer addition is exact and associative, so sums accumulated with
-// atomic adds in any order are bit-reproducible.  The one rounding is at the way in.
-PI_DEV long long to_fx(float v) {
-    const float c = fminf(fmaxf(v, -67108864.f), 67108864.f);   // 2^26
-    return (long long)llrintf(c * 4294967296.f);                  // exact power-of-two scaling
-}
-PI_DEV float from_fx(long long q) { return (float)((double)q * (1.0 / 4294967296.0)); }
-PI_DEV void fx_add(long long* acc, float v) {
-    __hip_atomic_fetch_add(acc, to_fx(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The sum of the accumulator copies of element i (ncopy = 1 or DEC_NCOPY copies, d elements
-// apart), each copy cleared.  Producers spread their atomic adds over the copies so that no address
-// sees more than a few dozen of them.
-PI_DEV long long fx_take(long long* acc, int d, int i, int ncopy) {
-    if (ncopy == 1) {
-        const long long t = acc[i];
-        acc[i] = 0;
-        return t;
-    }
-    long long v[pi::DEC_NCOPY];
+// ---- deterministic cross-block sums: fp32 partial rows, reduced in a fixed order -------------
+// Producers (blocks that each own a share of the neurons) store their d column sums as one
+// partial row part[p, 0 .. d) with plain stores; a later kernel turns the P rows into y.  The
+// order of that sum is a function of P alone -- not of the grid that runs it -- so every
+// kernel that reduces the same rows gets the same bits, and repeated runs are bit-identical.
+// Values are fp32 throughout: relative (not absolute) precision, and NaN / Inf propagate.
+
+// y[c] = sum over p < P of part[p * d + c] (d % 4 == 0; part and y 16-byte aligned).  A unit is
+// one 4-column quad, taken by a whole wave: lane j adds the rows p = j, j + 64, j + 128, ... in
+// ascending order (all of a lane's loads in flight together, eight at a time), and the 64 lane
+// sums meet in wave_sum's fixed pattern.  gw / nw: this wave's index in the grid and the
+// grid's number of waves (quads are dealt out round-robin).  Every lane of the wave must call
+// it (it uses cross-lane moves).
+PI_DEV void reduce_partials(const float* __restrict__ part, int P, int d, float* __restrict__ y,
+                            int gw, int nw) {
+    const int lane = threadIdx.x & 63;
+    const int nq = d >> 2;
+    for (int q = gw; q < nq; q += nw) {
+        const float* src = part + (size_t)q * 4;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p0 = 0; p0 < P; p0 += 64 * 8) {
+            float4 v[8];
 #pragma unroll
-    for (int c = 0; c < pi::DEC_NCOPY; ++c) v[c] = acc[(size_t)c * d + i];
-    long long t = 0;
+            for (int k = 0; k < 8; ++k) {
+                const int p = p0 + 64 * k + lane;
+                v[k] = *reinterpret_cast<const float4*>(src + (size_t)(p < P ? p : 0) * d);
+            }
 #pragma unroll
-    for (int c = 0; c < pi::DEC_NCOPY; ++c) {
-        t += v[c];
-        acc[(size_t)c * d + i] = 0;
+            for (int k = 0; k < 8; ++k) {
+                if (p0 + 64 * k + lane < P) {
+                    s.x += v[k].x;
+                    s.y += v[k].y;
+                    s.z += v[k].z;
+                    s.w += v[k].w;
+                }
+            }
+        }
+        s.x = wave_sum(s.x);
+        s.y = wave_sum(s.y);
+        s.z = wave_sum(s.z);
+        s.w = wave_sum(s.w);
+        if (lane == 0) *reinterpret_cast<float4*>(y + 4 * q) = s;
     }
-    return t;
 }
 
 // Every block calls this once, after all its threads issued their st_agent

@@ -17,10 +17,6 @@ constexpr int CNT_UNION = 1024;   // union path (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
-// Most copies of the fused batch-1 decode step's fixed-point y accumulators (d int64 each):
-// tile t adds into copy t % ncopy, which bounds the atomic adds any one address sees per step,
-// at the price of ncopy loads and stores per element when the copies are turned into y.
-constexpr int DEC_NCOPY = 4;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -62,22 +58,20 @@ struct DecPlan {
     int ntile, q;              // tiles of 64 neurons, chunks per lane per up/gate row
     size_t lds_b;              // dynamic LDS of the tile kernel
     bool fused_default;        // the schedule chosen for this shape
-    int ncopy;                 // accumulator copies of the fused schedule (1 or DEC_NCOPY)
     int nslices, nsplit, wps;  // split schedule's down grid: column slices, ranges, mask words per range
-    size_t off_z, off_h, off_yacc, bytes;
+    size_t off_z, off_h, off_part, bytes;   // off_part: max(ntile, nsplit) partial rows of d floats
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
-// One step: two kernels (fused: the tile blocks add their own down partial sums) or three
-// (split: a down kernel over ranges of the mask).  The down projection adds into the
-// fixed-point y accumulators (pl.ncopy copies of d int64 in the workspace for the fused step,
-// one for the split step; zero before the first step of a run); when convert_prev is set,
-// the first kernel turns the previous step's accumulators into y and clears them.
+// One step: two kernels (fused: each tile block stores its down projection as one partial row
+// of d floats) or three (split: a down kernel over ranges of the mask, one partial row per
+// range).  When convert_prev is set, the first kernel sums the previous step's partial rows
+// into y (same schedule), in a fixed order.
 hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const DecPlan& pl, bool fused,
                               const uint16_t* x, float theta, float* logits, uint32_t* mask,
                               float* y, bool convert_prev, char* ws, hipStream_t s,
                               hipEvent_t e0, hipEvent_t e1);
-// After the last step: y = the accumulators (cleared), and the last step's neuron table
-// (idx, count; skipped when idx is NULL) from its mask.
+// After the last step: y = the fixed-order sum of its partial rows, and the last step's neuron
+// table (idx, count; skipped when idx is NULL) from its mask.
 hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s);
 
@@ -142,11 +136,11 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
                                 hipStream_t s);
 
-// yacc / y (batch-1 decode executor only): also turn the previous step's fixed-point y
-// accumulators (d of them) into y and clear them
+// part / y (batch-1 decode executor only): also sum the previous step's P partial rows of d
+// floats into y (reduce_partials)
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
-                              float* z, hipStream_t s, long long* yacc = nullptr,
-                              float* y = nullptr, int ncopy = 1);
+                              float* z, hipStream_t s, const float* part = nullptr,
+                              float* y = nullptr, int P = 0);
 
 hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
                           int32_t* count, hipStream_t s);
@@ -172,6 +166,7 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* perm, int n,
                                size_t row_bytes, hipStream_t s);
+hipError_t launch_count_active(const uint32_t* mask, int B, int F, int32_t* counts, hipStream_t s);
 hipError_t launch_map_ids(const int32_t* idx, const int32_t* count, int B, int F,
                           const int32_t* perm, int32_t* out, hipStream_t s);
 

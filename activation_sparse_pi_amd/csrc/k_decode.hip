@@ -9,26 +9,28 @@
 // kernels, so the step is cut only where a global dependency forces it (every
 // tile's logits need all of z):
 //   A  predictor stage 1, z_j = W1t[j, :] . x (one wave per predictor column, the
-//      kernel pi_predict uses); its grid also turns the previous step's fixed-point
-//      y accumulators into y and clears them.
+//      kernel pi_predict uses); its grid also sums the previous step's partial rows
+//      into y.
 //   B  one block per 64-neuron tile: the tile's 64 contiguous W2t rows (and biases)
 //      are already in flight while z is staged in LDS; l = W2t[tile] . z + b,
 //      active = l > theta, a wave ballot writes the tile's two mask words and lists
 //      its active neurons; the block computes h for them from their gate/up rows
 //      (x staged in LDS).
-// The down projection y = sum_k h_k W_down[k, :] is added to int64 fixed-point y
-// accumulators with atomic adds (exact, so the order of the adds does not matter),
-// in one of two ways:
-//   fused (two kernels per step): B itself reads its active neurons' down rows and adds
-//      its d partial sums, one set per tile.
-//   split (three kernels per step): B writes h; C, a 2-D grid of (column slice, range
-//      of mask words) blocks, compacts its range of the mask in LDS, reduces its rows
-//      over 16 waves and adds one set of partial sums per range.
-// The fused step saves a kernel boundary but issues ntile * d atomic adds, against
-// nsplit * d for the split step, so it is chosen where ntile * d is small.
-// After the last step a small kernel turns the accumulators into y and writes the
-// last step's ascending neuron table from its mask.
+// The down projection y = sum_k h_k W_down[k, :] is computed as P fp32 partial rows of d
+// columns (plain stores, no atomics), which the next step's first kernel -- or, after the last
+// step, a small finishing kernel -- sums in a fixed order into y (reduce_partials), in one of
+// two ways:
+//   fused (two kernels per step): B itself reads its active neurons' down rows and stores
+//      its d column sums as partial row `tile` (P = number of tiles).
+//   split (three kernels per step): B writes h; C, a 2-D grid of (range of mask words, column
+//      slice) blocks, compacts its range of the mask in LDS, reduces its rows over 16 waves and
+//      stores its slice of partial row `range` (P = number of ranges).
+// The fused step saves a kernel boundary but writes (and the reduction reads) ntile * d
+// partial sums, against nsplit * d for the split step, so it is chosen where ntile * d is
+// small.  The finishing kernel also writes the last step's ascending neuron table.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "device_common.h"
 #include "internal.h"
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h, const void* __restrict__ Wd,
-    const uint16_t* __restrict__ Sd, long long* __restrict__ yacc, int ncopy) {
+    const uint16_t* __restrict__ Sd, float* __restrict__ part) {
     constexpr int NT = B_WAVES * 64;
     // row items per wave in flight: as many as the register budget of two blocks per CU
     // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
@@ -193,22 +195,20 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         s_h[k] = GLU ? fmaxf(s_dot[0][k], 0.f) * a : fmaxf(a, 0.f);
     }
     __syncthreads();
-    if (na == 0) return;
 
-    // --- down: y += sum over the tile's active neurons of h_k W_down[row_k, :].  Wave w takes
-    // column chunks w, w + 8, ... (64 V columns: V fp16 or int4 weights per lane of each row,
-    // V as large as leaves no wave without a chunk) and reads that chunk of every active row
-    // at once (DN_ROWS in flight; empty slots re-read the first row's chunk, an L2 hit, and
-    // count zero).  Its column sums go into one of ncopy fixed-point accumulator copies (copy
-    // = tile % ncopy) with atomic adds: exact, so the order of the tiles does not matter.
+    // --- down: partial row `tile` = sum over the tile's active neurons of h_k W_down[row_k, :]
+    // (all zero for a tile with none).  Wave w takes column chunks w, w + 8, ... (64 V columns:
+    // V fp16 or int4 weights per lane of each row, V as large as leaves no wave without a
+    // chunk) and reads that chunk of every active row at once (DN_ROWS in flight; empty slots
+    // re-read the first row's chunk, an L2 hit, and count zero); a lane's V column sums are V
+    // consecutive floats of the partial row, so the wave's stores are contiguous.
     constexpr int V = down_cols_per_lane(WF, Q);     // columns per lane
     constexpr int CH = 64 * V;
     constexpr int NB = WF == 0 ? 2 * V : V / 2;      // bytes per lane per row
     constexpr int DN_ROWS = 16;
-    __shared__ __align__(16) float s_acc[B_WAVES * CH];
     const int nch = (d + CH - 1) / CH;
     const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
-    long long* accc = yacc + (size_t)(tile % ncopy) * d;
+    float* prow = part + (size_t)tile * d;
     const uint8_t* Wb = static_cast<const uint8_t*>(Wd);
     for (int j = wave; j < nch; j += B_WAVES) {
         const int col0 = j * CH + lane * V;
@@ -253,34 +253,29 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
                 if (WF == 1) keep(sr[u]);
             }
         }
-        // transpose through the wave's LDS slice so that each atomic instruction covers 64
-        // consecutive columns (512 contiguous bytes) instead of 64 lanes 8 * V bytes apart
-        float* sa = s_acc + wave * CH;
-        if constexpr (V == 2) {
-            *reinterpret_cast<float2*>(sa + lane * V) = make_float2(acc[0], acc[1]);
-        } else {
+        if (cok) {
+            if constexpr (V == 2) {
+                *reinterpret_cast<float2*>(prow + col0) = make_float2(acc[0], acc[1]);
+            } else {
 #pragma unroll
-            for (int v = 0; v < V; v += 4)
-                *reinterpret_cast<float4*>(sa + lane * V + v) = make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+                for (int v = 0; v < V; v += 4)
+                    *reinterpret_cast<float4*>(prow + col0 + v) =
+                        make_float4(acc[v], acc[v + 1], acc[v + 2], acc[v + 3]);
+            }
         }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int col = j * CH + v * 64 + lane;
-            if (col < d) fx_add(&accc[col], sa[v * 64 + lane]);
-        }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
 
 // --------------------------------------------------------------------------------------- C
-// Split schedule: the down projection straight from the mask, 2-D tiled.  Block (slice,
-// split) owns a column slice of y (64 lanes x one load each: 512 fp16 columns with 16-byte
-// loads, or 1024 int4 columns with 8-byte loads) and the neuron ids of a range of mask
-// words.  It compacts its range in LDS, its 16 waves take interleaved active neurons (U rows
-// in flight per wave), the waves' sums meet in LDS in a fixed order, and each column sum is
-// added to that column's fixed-point accumulator with an atomic add.
+// Split schedule: the down projection straight from the mask, 2-D tiled.  Block (split,
+// slice) owns the neuron ids of a range of mask words and a column slice of y (64 lanes x one
+// load each: 512 fp16 columns with 16-byte loads, or 1024 int4 columns with 8-byte loads).  It
+// compacts its range in LDS, its 16 waves take interleaved active neurons (U rows in flight
+// per wave), the waves' sums meet in LDS in a fixed order, and the block stores its slice of
+// partial row `split`.  The range is the grid's fast index, so the blocks of one range (which
+// read the same mask words, the same h entries and the same lines of int4 scales) go to the
+// same XCD and share its L2.
 constexpr int DN_NW = 16;
 
 template <int WF>
@@ -315,14 +310,14 @@ template <int WF, int U>
 __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
     const void* __restrict__ Wd, const uint16_t* __restrict__ Sd, int d, int wps,
-    long long* __restrict__ yacc) {
+    float* __restrict__ part) {
     using Gm = DnGeom<WF>;
     __shared__ int s_ids[DEC_IDCAP];
     __shared__ __align__(16) float s_red[DN_NW * Gm::SC];
     __shared__ float s_half[512];
     __shared__ int s_tmp[DN_NW + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slice = blockIdx.x, split = blockIdx.y;
+    const int split = blockIdx.x, slice = blockIdx.y;
     const int W = (F + 31) >> 5;
     const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
     const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
@@ -414,20 +409,19 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
 #pragma unroll
         for (int w = 0; w < DN_NW; ++w) s += s_red[w * Gm::SC + col];
     }
-    // the block's column sums go straight into the exact fixed-point accumulators: no
-    // partial rows, no arrival counter, no second pass (the next kernel reads them)
+    // the block's column sums are its slice of partial row `split` (a later kernel sums the rows)
     const int gcol = slice * Gm::SC + col;
     const bool writer = WF == 0 ? (tid < 512) : true;
-    if (writer && gcol < d) fx_add(&yacc[gcol], s);
+    if (writer && gcol < d) part[(size_t)split * d + gcol] = s;
 }
 
-// After the last step: y = the sum of the accumulator copies (cleared for the next run); block
-// 0 also writes the last step's ascending neuron table from its mask.
-__global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc, int ncopy, float* __restrict__ y,
+// After the last step: y = the fixed-order sum of the P partial rows; block 0 also writes the
+// last step's ascending neuron table from its mask.
+__global__ __launch_bounds__(256) void k_dec_finish(const float* __restrict__ part, int P, float* __restrict__ y,
                                                     int d, const uint32_t* __restrict__ mask, int F,
                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
     __shared__ int s_tmp[256 / 64 + 1];
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256) y[i] = from_fx(fx_take(yacc, d, i, ncopy));
+    reduce_partials(part, P, d, y, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
     if (blockIdx.x == 0 && idx != nullptr) block_compact<false>(mask, 1, (F + 31) >> 5, F, idx, count, s_tmp);
 }
 
@@ -435,33 +429,33 @@ __global__ __launch_bounds__(256) void k_dec_finish(long long* __restrict__ yacc
 template <int WF, bool GLU, int Q, bool FUSED, bool P8>
 void launch_b8(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
                const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-               const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
+               const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
     if (e0)
         hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), (uint32_t)lds, s,
                               e0, e1, 0, z, p.w_p2t, p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x,
-                              f.w_gate, f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+                              f.w_gate, f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, part);
     else
         hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
                            p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
-                           f.s_up, f.d, h, f.w_down, f.s_down, yacc, ncopy);
+                           f.s_up, f.d, h, f.w_down, f.s_down, part);
 }
 
 template <int WF, bool GLU, int Q, bool FUSED>
 void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-              const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
+              const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
     if (p.pfmt == PI_P_I8G128)
-        launch_b8<WF, GLU, Q, FUSED, true>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
+        launch_b8<WF, GLU, Q, FUSED, true>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
     else
-        launch_b8<WF, GLU, Q, FUSED, false>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
+        launch_b8<WF, GLU, Q, FUSED, false>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
 }
 
 template <int WF, bool GLU, bool FUSED>
 hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                       const float* z, const pi_pred_desc& p, float theta, float* logits,
                       uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h,
-                      long long* yacc, int ncopy) {
-#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy); break;
+                      float* part) {
+#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part); break;
     if constexpr (WF == 0) {
         switch (q) {
             PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
@@ -481,14 +475,14 @@ hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, h
 template <bool FUSED>
 hipError_t dispatch_b_fmt(const DecPlan& pl, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
                           const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
-                          const uint16_t* x, const pi_ffn_desc& f, float* h, long long* yacc, int ncopy) {
+                          const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
     const bool glu = f.act == PI_ACT_REGLU;
     const dim3 gb(pl.ntile);
     if (f.wfmt == PI_W_F16)
-        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy)
-                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
-    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy)
-               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
+        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
+                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
+               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
 }
 
 }  // namespace
@@ -500,19 +494,14 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     const bool f16 = wfmt == PI_W_F16;
     p.q = f16 ? (d + 511) / 512 : (d + 2047) / 2048;
     p.lds_b = (size_t)align16i(r * 4) + (size_t)(d / 8) * 16;
-    // fused down: ntile * d atomic adds per step; the split schedule's nsplit * d adds and
-    // extra kernel boundary win above about 2^20 adds (between the LLaMA-7B-shaped layer,
-    // 0.7M adds, faster fused, and the OPT-30B-shaped one, 3.2M, faster split)
+    // fused down: ntile * d partial sums per step; the split schedule's nsplit * d and its
+    // extra kernel boundary win above about 2^20 (between the LLaMA-7B-shaped layer, 0.7M,
+    // faster fused, and the OPT-30B-shaped one, 3.2M, faster split)
     p.fused_default = (long long)p.ntile * d <= (1LL << 20);
-    // fused: spreading the adds over copies pays where turning the copies into y is cheap
-    // (tiny ReLU layer, d = 1024: 4 copies 10.9 us/step, 1 copy 11.3); at d = 4096 one copy
-    // wins (LLaMA-7B-shaped: 17.2 us against 17.7 with 4 and 18.6 with 16)
-    p.ncopy = d <= 2048 ? DEC_NCOPY : 1;
     const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
     p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
-    // about 256 down blocks (one per CU): the splits' sums meet in atomic adds, so more
-    // splits cost nothing but fewer rows per block
+    // about 256 down blocks (one per CU); every range adds one partial row of d floats
     int ns = (256 + p.nslices - 1) / p.nslices;
     const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
     if (ns > 32) ns = 32;
@@ -526,8 +515,8 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     off = align_up(off + (size_t)r * sizeof(float), 256);
     p.off_h = off;
     off = align_up(off + (size_t)F * sizeof(float), 256);
-    p.off_yacc = off;
-    off = align_up(off + (size_t)DEC_NCOPY * d * sizeof(long long), 256);
+    p.off_part = off;          // partial rows of either schedule
+    off = align_up(off + (size_t)std::max(p.ntile, p.nsplit) * d * sizeof(float), 256);
     p.bytes = off;
     return p;
 }
@@ -538,28 +527,30 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
                               hipEvent_t e0, hipEvent_t e1) {
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* h = reinterpret_cast<float*>(ws + pl.off_h);
-    long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    const int ncopy = fused ? pl.ncopy : 1;
-    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? yacc : nullptr, y, ncopy);
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    // the previous step (same schedule) left its partial rows: stage 1 sums them into y
+    hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? part : nullptr, y,
+                                      fused ? pl.ntile : pl.nsplit);
     if (e != hipSuccess) return e;
-    if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, ncopy);
-    if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, yacc, 1)) != hipSuccess)
+    if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+    if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)) != hipSuccess)
         return e;
-    const dim3 gc(pl.nslices, pl.nsplit);
+    const dim3 gc(pl.nsplit, pl.nslices);     // range fastest: one range's blocks on one XCD
     if (f.wfmt == PI_W_F16)
         hipLaunchKernelGGL((k_dec_down<0, 8>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, yacc);
+                           f.s_down, f.d, pl.wps, part);
     else
         hipLaunchKernelGGL((k_dec_down<1, 12>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, yacc);
+                           f.s_down, f.d, pl.wps, part);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s) {
-    long long* yacc = reinterpret_cast<long long*>(ws + pl.off_yacc);
-    hipLaunchKernelGGL(k_dec_finish, dim3((d + 255) / 256), dim3(256), 0, s, yacc, fused ? pl.ncopy : 1, y, d,
-                       mask, F, idx, count);
+    const float* part = reinterpret_cast<const float*>(ws + pl.off_part);
+    const int nq = d / 4;                         // one 4-column quad per wave
+    hipLaunchKernelGGL(k_dec_finish, dim3((nq + 3) / 4), dim3(256), 0, s, part,
+                       fused ? pl.ntile : pl.nsplit, y, d, mask, F, idx, count);
     return hipGetLastError();
 }
 

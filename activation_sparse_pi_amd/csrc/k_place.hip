@@ -47,7 +47,31 @@ __global__ __launch_bounds__(256) void k_map_ids(const int32_t* idx,   // may be
     }
 }
 
+// counts[i] += number of the B masks (rows of W words) with bit i set, for i < F.  Thread
+// = neuron; the 32 lanes of a word read it together (one broadcast load), and every row's
+// word is issued before the first is used.
+__global__ __launch_bounds__(256) void k_count_active(const uint32_t* __restrict__ mask, int B,
+                                                      int F, int32_t* __restrict__ counts) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= F) return;
+    const int W = (F + 31) >> 5, w = i >> 5, bit = i & 31;
+    int c = 0;
+    for (int b0 = 0; b0 < B; b0 += 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = mask[(size_t)min(b0 + k, B - 1) * W + w];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c += (b0 + k < B) ? (int)((v[k] >> bit) & 1u) : 0;
+    }
+    counts[i] += c;
+}
+
 }  // namespace
+
+hipError_t launch_count_active(const uint32_t* mask, int B, int F, int32_t* counts, hipStream_t s) {
+    hipLaunchKernelGGL(k_count_active, dim3((F + 255) / 256), dim3(256), 0, s, mask, B, F, counts);
+    return hipGetLastError();
+}
 
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* perm, int n,
                                size_t row_bytes, hipStream_t s) {

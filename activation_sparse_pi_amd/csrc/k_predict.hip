@@ -27,15 +27,15 @@ namespace {
 // QS 16-byte chunks per lane (all loads of a segment in flight together).  WPR = 4 (batch 1,
 // rows of at least 256 chunks): one row per block, its 4 waves taking a quarter of the
 // chunks each and meeting in LDS -- four times the blocks, each wave a quarter of the loads.
-// CONV (the batch-1 decode executor): the grid first turns the previous step's fixed-point
-// y accumulators (ncopy copies) into y and clears them for this step's down projection.
+// CONV (the batch-1 decode executor): the grid also sums the previous step's P partial rows
+// into y (reduce_partials), after its own loads are issued.
 // P8: int8 rows (a chunk = 16 weights, one fp16 scale per 8 chunks), x read 32 bytes a chunk.
 template <int QS, bool CONV, bool P8, int WPR = 1>
 __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int B,
                                             const void* __restrict__ W1t,
                                             const uint16_t* __restrict__ S1, int d, int r,
-                                            float* __restrict__ z, long long* __restrict__ yacc,
-                                            float* __restrict__ y, int ncopy) {
+                                            float* __restrict__ z, const float* __restrict__ part,
+                                            float* __restrict__ y, int P) {
     const int lane = threadIdx.x & 63;
     const int j = WPR == 1 ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
     constexpr int EPC = P8 ? 16 : 8;                  // elements per 16-byte chunk
@@ -64,10 +64,7 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
                 xr[q] = ld16(x + 8 * cc);
             }
         }
-        if (CONV) {
-            for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
-                y[i] = from_fx(fx_take(yacc, d, i, ncopy));
-        }
+        if (CONV) reduce_partials(part, P, d, y, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
         if (j >= r) return;                             // the whole block
         float acc = 0.f;
 #pragma unroll
@@ -110,10 +107,7 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
                 xr[q] = ld16(x + 8 * cc);
             }
         }
-        if (CONV) {
-            for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
-                y[i] = from_fx(fx_take(yacc, d, i, ncopy));
-        }
+        if (CONV) reduce_partials(part, P, d, y, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
         if (j >= r) return;
         float acc = 0.f;
 #pragma unroll
@@ -128,10 +122,7 @@ __global__ __launch_bounds__(256) void k_p1(const uint16_t* __restrict__ x, int 
         if (lane == 0) z[j] = acc;
         return;
     }
-    if (CONV) {
-        for (int i = blockIdx.x * 256 + threadIdx.x; i < d; i += gridDim.x * 256)
-            y[i] = from_fx(fx_take(yacc, d, i, ncopy));
-    }
+    if (CONV) reduce_partials(part, P, d, y, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4);
     if (j >= r) return;
     const uint8_t* row = Wb + (size_t)j * rowb;
     for (int b = 0; b < B; ++b) {
@@ -224,16 +215,16 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
-                              float* z, hipStream_t s, long long* yacc, float* y, int ncopy) {
+                              float* z, hipStream_t s, const float* part, float* y, int P) {
     if (p.pfmt == PI_P_I8G128) {
         int q = (p.d / 16 + 63) / 64;
         q = q < 1 ? 1 : (q > 16 ? 16 : q);
 #define PI_P1(QQ) case QQ: \
     if (B == 1 && QQ >= 4 && p.d / 16 <= 64 * QQ) { \
-        if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
-        else hipLaunchKernelGGL((k_p1<QQ, false, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
-    } else if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, yacc, y, ncopy); \
-    else hipLaunchKernelGGL((k_p1<QQ, false, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 1); \
+        if (part) hipLaunchKernelGGL((k_p1<QQ, true, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, part, y, P); \
+        else hipLaunchKernelGGL((k_p1<QQ, false, true, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 0); \
+    } else if (part) hipLaunchKernelGGL((k_p1<QQ, true, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, part, y, P); \
+    else hipLaunchKernelGGL((k_p1<QQ, false, true>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, p.s_p1t, p.d, p.r, z, nullptr, nullptr, 0); \
     break;
         switch (q) {
             PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)
@@ -245,10 +236,10 @@ hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const u
     }
 #define PI_P1(QQ) case QQ: \
     if (B == 1 && QQ >= 4 && p.d / 8 <= 64 * QQ) { \
-        if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
-        else hipLaunchKernelGGL((k_p1<QQ, false, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 1); \
-    } else if (yacc) hipLaunchKernelGGL((k_p1<QQ, true, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, yacc, y, ncopy); \
-    else hipLaunchKernelGGL((k_p1<QQ, false, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 1); \
+        if (part) hipLaunchKernelGGL((k_p1<QQ, true, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, part, y, P); \
+        else hipLaunchKernelGGL((k_p1<QQ, false, false, 4>), dim3(p.r), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 0); \
+    } else if (part) hipLaunchKernelGGL((k_p1<QQ, true, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, part, y, P); \
+    else hipLaunchKernelGGL((k_p1<QQ, false, false>), dim3(pl.nblk1), dim3(256), 0, s, x, B, p.w_p1t, nullptr, p.d, p.r, z, nullptr, nullptr, 0); \
     break;
     switch (pl.qs) {
         PI_P1(1) PI_P1(2) PI_P1(3) PI_P1(4) PI_P1(5) PI_P1(6) PI_P1(7) PI_P1(8)

@@ -361,10 +361,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
             if ((e = launch_run(ra, s)) != hipSuccess) return hip_fail(e, "pi_decode_run persistent launch");
         }
     } else if (nsteps > 0) {
-        // y of every step accumulates exactly in int64 fixed point; the next step's first
-        // kernel turns it into y, and a small kernel does so after the last step
-        if ((e = launch_zero(w + pl.off_yacc, (size_t)DEC_NCOPY * d * sizeof(long long), s)) != hipSuccess)
-            return hip_fail(e, "pi_decode_run accumulator clear");
+        // every step leaves its down projection as fp32 partial rows; the next step's first
+        // kernel sums them into y in a fixed order, and a small kernel does so after the last
         for (int i = 0; i < nsteps; ++i) {
             const long long g = s0 + i;
             const int t = (int)(g % T), rep = (int)(g % nrep);
@@ -472,6 +470,14 @@ int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size
     if (n <= 0 || row_bytes == 0) return fail(PI_ERR_SHAPE, "need n > 0 and row_bytes > 0 (n=%d)", n);
     const hipError_t e = launch_permute_rows(src, dst, perm, n, row_bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "pi_permute_rows");
+}
+
+int pi_count_active(const uint32_t* mask, int B, int F, int32_t* counts, void* stream) {
+    if (!mask || !counts) return fail(PI_ERR_NULL, "mask / counts NULL");
+    if (F <= 0) return fail(PI_ERR_SHAPE, "F must be positive (F=%d)", F);
+    if (int st = check_batch(B); st != PI_OK) return st;
+    const hipError_t e = launch_count_active(mask, B, F, counts, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pi_count_active");
 }
 
 int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int32_t* perm,

@@ -122,19 +122,18 @@ class DeviceLayer:
     def activation_counts(self, x: torch.Tensor) -> np.ndarray:
         """Profiling run: how often each neuron (in this layer's order) is predicted active over
         the tokens x (fp16 [n, d] on the device), in batches of up to 32 tokens (1 with the int8
-        predictor) through pi_predict.  Returns int32 [F] on the host."""
+        predictor) through pi_predict, counted on the device by pi_count_active.  Returns
+        int32 [F] on the host."""
         n = x.shape[0]
         W = (self.F + 31) // 32
         bmax = 1 if self.pfmt == L.PI_P_I8G128 else L.PI_MAX_BATCH      # int8: batch 1 only
         mask = torch.empty((bmax, W), dtype=torch.int32, device=self.device)
-        counts = np.zeros(self.F, dtype=np.int64)
+        counts = torch.zeros((self.F,), dtype=torch.int32, device=self.device)
         for t0 in range(0, n, bmax):
             B = min(bmax, n - t0)
             self.predict(x[t0:t0 + B].data_ptr(), B, None, mask.data_ptr(), None, None)
-            m = mask[:B].cpu().numpy().view(np.uint32)
-            bits = np.unpackbits(m.view(np.uint8), axis=1, bitorder="little")[:, :self.F]
-            counts += bits.sum(axis=0, dtype=np.int64)
-        return counts.astype(np.int32)
+            L.check(L.pi_count_active(mask.data_ptr(), B, self.F, counts.data_ptr(), self.stream()))
+        return counts.cpu().numpy()
 
     def dense(self, x, B, y, rep: int = 0) -> None:
         L.check(L.pi_ffn_dense_ref_gpu(self.ffn[rep], x, B, y, self.ws.data_ptr(), self.ws_bytes,

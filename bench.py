@@ -7,9 +7,10 @@ operator over their down rows.  Tokens are consumed strictly one after another:
 a step starts only when the previous step's y is complete (no batching across
 tokens).
 
-Default workload: the LLaMA-7B-shaped ReGLU layer (d=4096, ffn=11008, predictor
-rank 256, fp16 weights, fp32 accumulation, Zipf(1.2) rates with a 5% hot set,
-~10% active, 256-token stream).  Weights are held in R byte-identical replicas
+Default workload: the largest batch-1 layer, LLaMA-70B-shaped ReGLU (d=8192,
+ffn=28672, weight-only int4 with one fp16 scale per 128 along d, fp16 predictor of
+rank 1024, fp32 accumulation, Zipf(1.2) rates, ~10% active, 128-token stream);
+--config c1 / c2 / c3 select the smaller batch-1 layers, c4 the batch-32 one.  Weights are held in R byte-identical replicas
 and token s uses replica s mod R, standing in for the distinct layers of a real
 model: the touched bytes of consecutive steps never share cache lines, so they
 come from HBM and not from the 256 MB Infinity Cache.
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5440)
     ap.add_argument("--warmup", type=int, default=1088)
-    ap.add_argument("--config", default="c2")
+    ap.add_argument("--config", default="c5")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to bust the caches")
     ap.add_argument("--mode", choices=("kernels", "fused", "split", "persistent", "eager"), default="kernels",
                     help="kernels: one pi_decode_run call, three kernels per step (default); "
@@ -70,6 +71,9 @@ def parse():
                     help="i8g128: the predictor factors in int8 with one fp16 scale per 128 (batch 1)")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="batch workload: token-by-token vs union sparse FFN for B = 1, 2, 4, ...")
+    ap.add_argument("--passes", type=int, default=5,
+                    help="also time this many whole passes over the T-token stream and report "
+                         "their median (0 = skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling runs)")
     return ap.parse_args()
@@ -157,6 +161,15 @@ def copy_probe(mb, dev):
 
 # ------------------------------------------------------------------------------- CPU baseline
 def cpu_model() -> str:
+    """The host CPU's model name as lscpu prints it (falling back to /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -165,6 +178,16 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def host_cpus() -> dict:
+    """CPUs the host has, and the ones this process may run on."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"host_cpus": os.cpu_count(), "usable_cpus": usable,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def _oracle_rate(inputs, W, X, budget_s, limit):
@@ -192,11 +215,12 @@ def cpu_baseline(inputs, budget_s):
     n, dt = _oracle_rate(inputs, W, X, budget_s * 2 / 3, X.shape[0] * 4)
     out = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
            "sample": f"first {n} tokens of the same stream (wrapping), one at a time, "
-                     f"numpy float64, {dt:.1f} s", "cpu_model": cpu_model()}
+                     f"numpy float64 with its BLAS pool of {threads} threads, {dt:.1f} s",
+           "cpu_model": cpu_model(), **host_cpus()}
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
             n1, dt1 = _oracle_rate(inputs, W, X, budget_s / 3, X.shape[0] * 4)
-        out["single_thread"] = {"value": n1 / dt1, "unit": "tokens/s",
+        out["single_thread"] = {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
                                 "sample": f"first {n1} tokens, one BLAS thread, {dt1:.1f} s"}
     return out
 
@@ -478,6 +502,7 @@ def main():
 
     K, Wm = a.steps, a.warmup
     up_ms = []
+    passes_ms = []
     sched = a.mode if a.mode in ("fused", "split") else kernel_schedule(cfg)
     sched_desc = ("two kernels per step (fused down)" if sched == "fused"
                   else "three kernels per step (split down)")
@@ -492,6 +517,16 @@ def main():
         layer.decode_run(xd.data_ptr(), T, Wm, K, bufs, events=ev, mode=mode)  # timed: K steps
         torch.cuda.synchronize()
         total_ms = ev[0].elapsed_time(ev[1])
+        passes_ms = []
+        for _ in range(a.passes):
+            # a whole pass over the stream: tokens 0 .. T-1, replicas rotating as in the timed run
+            pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for e in pe:
+                e.record()
+            torch.cuda.synchronize()
+            layer.decode_run(xd.data_ptr(), T, 0, T, bufs, events=pe, mode=mode)
+            torch.cuda.synchronize()
+            passes_ms.append(pe[0].elapsed_time(pe[1]))
         if a.mode != "persistent":
             # roofline pass: the tile kernel of every step carries its own start/end events
             Kr = min(K, 1088)
@@ -586,6 +621,15 @@ def main():
             "bytes_per_launch": None if math.isnan(launch_bytes) else round(launch_bytes),
         },
     }
+    if passes_ms:
+        med = float(np.median(passes_ms))
+        out["stream_passes"] = {
+            "passes": len(passes_ms), "tokens_per_pass": T,
+            "median_us_per_step": round(med / T * 1e3, 3),
+            "median_tokens_per_s": round(T / (med / 1e3), 1),
+            "us_per_step_each": [round(p / T * 1e3, 3) for p in passes_ms],
+            "GB/s_median": round(float(np.mean(bytes_model(cfg, counts.astype(np.float64), pb)["total"]))
+                                 / (med / T * 1e-3) / 1e9, 1)}
     if a.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inputs, a.cpu_seconds)
     print(json.dumps(out), flush=True)

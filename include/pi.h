@@ -144,10 +144,16 @@ int pi_predict(const pi_pred_desc* pred, const uint16_t* x, int B,
                void* ws, size_t ws_bytes, void* stream);
 
 /* ---- pi_compact ----------------------------------------------------------------------------
+ * PowerInfer, "Neuron Placement and Management": the engine keeps a neuron table that
+ * maps every neuron it computes to its original position in the weight matrix.  Here
+ * the table is the ascending list of the set bits of a predicted-active mask.
  * Turns masks (u32 [B, ceil(F/32)], as written by pi_predict) into ascending
  * neuron-id lists.  PI_PER_TOKEN: idx int32 [B, F], count int32 [B].
- * PI_UNION: the OR of the B masks -> idx int32 [F], count int32 [1].
- * Mask bits at positions >= F are ignored.  Needs no workspace (ws may be NULL). */
+ * PI_UNION: the OR of the B masks -> idx int32 [F], count int32 [1] (the table of the
+ * batch's union, which the B > 1 sparse FFN runs over).
+ * Mask bits at positions >= F are ignored.  Needs no workspace (ws may be NULL).
+ * Errors: PI_ERR_NULL (mask, idx or count NULL), PI_ERR_SHAPE (F <= 0, B outside
+ * 1..PI_MAX_BATCH), PI_ERR_DTYPE (mode), PI_ERR_HIP.                                          */
 int pi_compact(const uint32_t* mask, int B, int F, int mode,
                int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
@@ -212,9 +218,15 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  *        On MI355X each of its hand-offs costs more than a kernel boundary, so it is
  *        the slower schedule on every workload measured; it is kept as an alternative.
  *   mode PI_RUN_AUTO: as PI_RUN_KERNELS.
- * The kernel schedules add y in int64 fixed point (2^-32 units, each partial sum
- * clamped to |v| <= 2^26), so their y does not depend on the order of the adds and is
- * reproducible run to run; the persistent launch sums in fp32 in a fixed order.
+ * y of the kernel schedules: every block that owns a share of the step's neurons stores its
+ * d column sums as one fp32 partial row in the workspace (no atomics); a later kernel sums
+ * the rows into y in an order fixed by the number of rows and d alone.  So y is fp32 with
+ * relative (not absolute) rounding: each partial sum and each addition of the reduction
+ * rounds once in fp32, whatever the scale of x or of the weights; NaN and Inf propagate as
+ * in any fp32 sum (a non-finite h or weight of a listed neuron makes the affected columns of
+ * y non-finite); a run is bit-identical to itself, and a step's y does not depend on the
+ * steps before it.  The fused and split schedules group the sums differently and agree to
+ * fp32 rounding.  The persistent launch sums in fp32 in a fixed order of its own.
  * mask u32 [ceil(F/32)], idx int32 [F] + count int32 [1] (both NULL or both set)
  * and y fp32 [d] hold the LAST step's results.  The summation order of z differs
  * from pi_predict's, so logits agree to fp32 rounding, not bit for bit.
@@ -237,8 +249,15 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
                   void* ws, size_t ws_bytes, void* stream);
 
 /* ---- pi_ffn_dense_ref_gpu ------------------------------------------------------------------
- * The same FFN over all F neurons (no predictor, no skipping): the dense
- * reference and dense-time baseline.  y fp32 [B, d], overwritten.             */
+ * The dense FFN that skipping has to reproduce: PowerInfer ("Neuron-aware Operator"; the
+ * online engine's "skip the inactive neurons") computes only the predicted-active
+ * neurons, and the result equals the layer's full FFN whenever every neuron that would
+ * fire is in the predicted set.  This call computes that full FFN over all F neurons (no
+ * predictor, no skipping) with the same numerics as pi_sparse_ffn: the GPU reference of
+ * the "all neurons listed = dense" and "true support = dense" identities, and the
+ * dense-time baseline.  x fp16 [B, d]; y fp32 [B, d], overwritten.  The workspace holds
+ * its down projection's partial sums (pi_workspace_bytes with a NULL predictor).
+ * Errors: those of pi_sparse_ffn's descriptor checks, PI_ERR_WORKSPACE, PI_ERR_HIP.     */
 int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float* y,
                          void* ws, size_t ws_bytes, void* stream);
 
@@ -268,6 +287,16 @@ int pi_place_neurons(const int32_t* counts, int F, int32_t* perm);
  * PI_ERR_HIP.                                                                                */
 int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size_t row_bytes,
                     void* stream);
+
+/* PowerInfer, offline phase ("LLM Profiler"): the profiler runs requests through the model and
+ * records which neurons fire in every layer; the placement above ranks neurons by those counts.
+ * Here the profiling statistic on the device: counts[i] += the number of the B masks (u32
+ * [B, ceil(F/32)], as pi_predict writes them) in which neuron i is set, for i < F.  counts is
+ * a device int32 [F] accumulator owned by the caller (zero it before the first batch); a
+ * profiling run calls pi_predict and then this on each batch of calibration tokens, on one
+ * stream.  Mask bits at positions >= F are ignored.  Needs no workspace.
+ * Errors: PI_ERR_NULL, PI_ERR_SHAPE (F <= 0, B outside 1..PI_MAX_BATCH), PI_ERR_HIP.       */
+int pi_count_active(const uint32_t* mask, int B, int F, int32_t* counts, void* stream);
 
 /* The neuron table: out[b, k] = perm[idx[b, k]] for k < count[b] (rows of F entries), so the
  * active list of a placed layer names original neurons (in placed order, not ascending).

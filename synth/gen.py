@@ -27,6 +27,8 @@ most inputs, the cold majority fire rarely -- a power law):
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 from scipy.special import ndtri
 
@@ -46,12 +48,14 @@ def _normal_f16(rng, shape, std) -> np.ndarray:
     """fp32 N(0,1) draws times std, rounded to fp16; built in row chunks to bound memory."""
     out = np.empty(shape, dtype=np.float16)
     rows = shape[0]
-    step = max(1, (1 << 24) // max(1, int(np.prod(shape[1:]))))
+    step = max(1, (1 << 22) // max(1, int(np.prod(shape[1:]))))
+    blk = np.empty((min(step, rows),) + tuple(shape[1:]), dtype=np.float32)   # reused scratch
     for r0 in range(0, rows, step):
         r1 = min(rows, r0 + step)
-        blk = rng.standard_normal((r1 - r0,) + tuple(shape[1:]), dtype=np.float32)
-        blk *= np.float32(std)
-        out[r0:r1] = blk.astype(np.float16)
+        b = blk[:r1 - r0]
+        rng.standard_normal(dtype=np.float32, out=b)
+        b *= np.float32(std)
+        out[r0:r1] = b
     return out
 
 
@@ -105,16 +109,29 @@ def quantize_int4_g128(w: np.ndarray):
         raise ValueError("int4 rows need d % 128 == 0")
     packed = np.empty((rows, d // 2), dtype=np.uint8)
     scales = np.empty((rows, d // GROUP), dtype=np.float16)
-    step = max(1, (1 << 22) // d)
+    step = max(1, (1 << 20) // d)
+    # scratch reused across row blocks (large temporaries would be page-faulted in afresh
+    # for every block); the arithmetic is the one stated above, element by element
+    q = np.empty((step, d // GROUP, GROUP), dtype=np.float32)
+    u = np.empty((step, d), dtype=np.uint8)
     for r0 in range(0, rows, step):
         r1 = min(rows, r0 + step)
-        g = w[r0:r1].astype(np.float32).reshape(r1 - r0, d // GROUP, GROUP)
-        s16 = (np.abs(g).max(axis=2) / np.float32(7.0)).astype(np.float16)
+        n = r1 - r0
+        g = w[r0:r1].astype(np.float32, copy=False).reshape(n, d // GROUP, GROUP)
+        qn = q[:n]
+        np.abs(g, out=qn)
+        s16 = (qn.max(axis=2) / np.float32(7.0)).astype(np.float16)
         s = s16.astype(np.float32)[..., None]
+        pos = s > 0
         with np.errstate(divide="ignore", invalid="ignore"):
-            q = np.where(s > 0, np.rint(g / np.where(s > 0, s, 1)), 0)
-        u = (np.clip(q, -8, 7) + 8).astype(np.uint8).reshape(r1 - r0, d)
-        packed[r0:r1] = u[:, 0::2] | (u[:, 1::2] << 4)
+            np.divide(g, np.where(pos, s, np.float32(1)), out=qn)
+        np.rint(qn, out=qn)
+        np.multiply(qn, pos, out=qn)
+        np.clip(qn, -8, 7, out=qn)
+        qn += 8
+        un = u[:n]
+        un[...] = qn.reshape(n, d)
+        packed[r0:r1] = un[:, 0::2] | (un[:, 1::2] << 4)
         scales[r0:r1] = s16
     return packed, scales
 
@@ -146,11 +163,14 @@ def _normal_i4(rng, shape, std):
     rows, d = shape
     packed = np.empty((rows, d // 2), dtype=np.uint8)
     scales = np.empty((rows, d // GROUP), dtype=np.float16)
-    step = max(1, (1 << 24) // d)
+    step = max(1, (1 << 22) // d)
+    blk = np.empty((step, d), dtype=np.float32)         # reused: draws are sequential either way
     for r0 in range(0, rows, step):
         r1 = min(rows, r0 + step)
-        blk = rng.standard_normal((r1 - r0, d), dtype=np.float32) * np.float32(std)
-        packed[r0:r1], scales[r0:r1] = quantize_int4_g128(blk)
+        b = blk[:r1 - r0]
+        rng.standard_normal(dtype=np.float32, out=b)
+        b *= np.float32(std)
+        packed[r0:r1], scales[r0:r1] = quantize_int4_g128(b)
     return packed, scales
 
 
@@ -171,15 +191,22 @@ def make(cfg: FFNConfig, *, ffn: bool = True, tokens: bool = True) -> dict:
     bias = (sigma * ndtri(rates)).astype(np.float32)
     out = dict(cfg=cfg, perm=perm, w_p1=w_p1, w_p2=w_p2, bias=bias, rates=rates, sigma=sigma)
     if ffn:
+        if cfg.wfmt not in ("f16", "i4g128"):
+            raise ValueError(cfg.wfmt)
         mats = ("gate", "up", "down") if cfg.act == "reglu" else ("up", "down")
-        for name in mats:
+
+        def draw(name):
             rng = st["w_" + name]
             if cfg.wfmt == "f16":
-                out["w_" + name] = _normal_f16(rng, (cfg.F, cfg.d), cfg.w_std)
-            elif cfg.wfmt == "i4g128":
-                out["q_" + name], out["s_" + name] = _normal_i4(rng, (cfg.F, cfg.d), cfg.w_std)
-            else:
-                raise ValueError(cfg.wfmt)
+                return {"w_" + name: _normal_f16(rng, (cfg.F, cfg.d), cfg.w_std)}
+            q, sc = _normal_i4(rng, (cfg.F, cfg.d), cfg.w_std)
+            return {"q_" + name: q, "s_" + name: sc}
+
+        # every matrix has its own stream, so drawing them side by side (numpy fills without
+        # holding the interpreter lock) gives the same arrays as drawing them in turn
+        with ThreadPoolExecutor(max_workers=len(mats)) as ex:
+            for part in ex.map(draw, mats):
+                out.update(part)
     if tokens:
         out["x"] = _normal_f16(st["x"], (cfg.T, cfg.B, cfg.d), 1.0)
     return out

@@ -93,6 +93,44 @@ def test_map_ids_table_and_in_place():
     assert np.array_equal(_np(di), inplace)
 
 
+@pytest.mark.parametrize("F,B", [(1000, 1), (1000, 3), (33, 32), (4096, 32), (28672, 17)])
+def test_count_active_matches_oracle_masks(F, B):
+    """pi_count_active adds, per neuron, the number of masks in which it is set: bit-exact
+    against the column sums of oracle-built masks, accumulated over two calls, with garbage
+    bits above F in the last word ignored."""
+    L = _L()
+    say(f"[gpu] count_active F={F} B={B}")
+    rng = np.random.default_rng(F * 7 + B)
+    rate = rng.random(F) ** 3                                   # skewed, like the Zipf rates
+    acts = [rng.random((B, F)) < rate for _ in range(2)]
+    W = (F + 31) // 32
+    counts = torch.full((F,), 5, dtype=torch.int32, device="cuda")
+    for a in acts:
+        words = O.mask_words(a).astype(np.uint32)
+        if F % 32:
+            words[:, -1] |= np.uint32(0xFFFFFFFF) << np.uint32(F % 32)
+        md = torch.from_numpy(words.view(np.int32).reshape(B, W).copy()).cuda()
+        L.check(L.pi_count_active(md.data_ptr(), B, F, counts.data_ptr(), _stream()))
+    torch.cuda.synchronize()
+    want = 5 + sum(a.sum(axis=0) for a in acts)
+    assert np.array_equal(_np(counts), want.astype(np.int32))
+
+
+def test_activation_counts_profiling_run():
+    """The profiling run (pi_predict masks counted by pi_count_active) against the oracle's
+    predicted sets on the same calibration tokens, outside the exclusion band."""
+    cfg = configs.tiny("reglu", "f16", d=1032, F=2000, r=48, T=1, seed=9)
+    inp = gen.make(cfg)
+    L = _L()
+    prof = _layer(inp, B_max=L.PI_MAX_BATCH)
+    xc = gen.calibration_x(cfg, 70)
+    got = prof.activation_counts(torch.from_numpy(xc).cuda())
+    lg = O.predictor_logits(xc, inp["w_p1"], inp["w_p2"], inp["bias"])
+    want = O.predicted_active(lg).sum(axis=0)
+    slack = O.exclusion_band(lg).sum(axis=0)
+    assert np.all(np.abs(got.astype(np.int64) - want) <= slack), "counts outside the band slack"
+
+
 def _placement(inp, ncal=64):
     """pi_place_neurons from a profiling run of the unplaced layer on calibration tokens."""
     L = _L()
