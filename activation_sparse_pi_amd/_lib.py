@@ -27,7 +27,8 @@ EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_byte
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
            "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan",
-           "pi_count_active")
+           "pi_count_active", "pi_decode_run_noalloc")
+PI_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class PredDesc(ctypes.Structure):
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
         L.pi_permute_rows.restype = c_int
         L.pi_map_ids.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
         L.pi_map_ids.restype = c_int
+        L.pi_decode_run_noalloc.argtypes = [P(PredDesc), P(FfnDesc), c_int, c_void_p, c_int,
+                                            ctypes.c_longlong, c_int, c_int, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.pi_decode_run_noalloc.restype = c_int
         L.pi_count_active.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p]
         L.pi_count_active.restype = c_int
         L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
@@ -198,3 +203,10 @@ def pi_map_ids(idx, count, B, F, perm, out, stream) -> int:
 
 def pi_count_active(mask, B, F, counts, stream) -> int:
     return lib().pi_count_active(mask, B, F, counts, stream)
+
+
+def pi_decode_run_noalloc(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count, y, events,
+                          kernel_events, stream) -> int:
+    """pi_decode_run without a workspace (the library's static scratch); arguments as there."""
+    return lib().pi_decode_run_noalloc(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count,
+                                       y, events, kernel_events, stream)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -106,6 +107,42 @@ size_t ffn_bytes(const pi_ffn_desc& f, int B) {
     FfnPlan p = plan_ffn(f.d, f.F, f.wfmt, B);
     return p.bytes;
 }
+
+// ---- scratch of pi_decode_run_noalloc -------------------------------------------------------
+// The one entry point that allocates nothing keeps its scratch (z, h, the partial rows) in this
+// file-scope device array: PI_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held until
+// the process ends.  In host code `scratch` only names the array; its device address on the
+// current GPU comes from hipGetSymbolAddress, looked up once per device (with that device
+// current) and kept in g_scratch_ptr, and only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[PI_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<char*> g_scratch_ptr;    // indexed by device ordinal
+
+hipError_t scratch_ptr(char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u)) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// pi_decode_run and pi_decode_run_noalloc.  Every check, the workspace size included, runs
+// before the first HIP call.  noalloc: ws / ws_bytes are ignored and the scratch array above is
+// used (kernel schedules only).
+int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                    int T, long long s0, int nsteps, int mode, uint32_t* mask, int32_t* idx,
+                    int32_t* count, float* y, void* const* events, void* const* kernel_events,
+                    void* ws, size_t ws_bytes, void* stream, bool noalloc);
 
 }  // namespace
 
@@ -250,10 +287,14 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
     return ok();
 }
 
-int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
-                  int T, long long s0, int nsteps, int mode, uint32_t* mask, int32_t* idx,
-                  int32_t* count, float* y, void* const* events, void* const* kernel_events,
-                  void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                    int T, long long s0, int nsteps, int mode, uint32_t* mask, int32_t* idx,
+                    int32_t* count, float* y, void* const* events, void* const* kernel_events,
+                    void* ws, size_t ws_bytes, void* stream, bool noalloc) {
     int st;
     if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
     if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
@@ -261,6 +302,8 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     if (mode != PI_RUN_AUTO && mode != PI_RUN_PERSISTENT && mode != PI_RUN_KERNELS &&
         mode != PI_RUN_FUSED && mode != PI_RUN_SPLIT)
         return fail(PI_ERR_DTYPE, "unknown run mode %d", mode);
+    if (noalloc && mode == PI_RUN_PERSISTENT)
+        return fail(PI_ERR_UNSUPPORTED, "pi_decode_run_noalloc runs the kernel schedules only");
     if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
     if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
     if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
@@ -302,7 +345,22 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     }
     const DecPlan pl = plan_decode(d, r, F, wfmt);
     const bool fused = mode == PI_RUN_FUSED || (mode != PI_RUN_SPLIT && pl.fused_default);
-    if ((st = check_ws(ws, ws_bytes, persistent ? rp.bytes : pl.bytes)) != PI_OK) return st;
+    // the kernel schedules use the partial rows of the schedule they run (the workspace from
+    // pi_workspace_bytes holds those of either)
+    const size_t need = persistent ? rp.bytes
+                                   : pl.off_part + (size_t)(fused ? pl.ntile : pl.nsplit) * d * sizeof(float);
+    if (noalloc) {
+        if (need > (size_t)PI_NOALLOC_SCRATCH_BYTES)
+            return fail(PI_ERR_WORKSPACE, "this layer's decode scratch is %zu bytes, more than the %u "
+                        "bytes of the static scratch (d=%d r=%d F=%d, %s schedule)", need,
+                        (unsigned)PI_NOALLOC_SCRATCH_BYTES, d, r, F, fused ? "fused" : "split");
+        char* sp = nullptr;
+        hipError_t e = scratch_ptr(&sp);          // the first HIP call of this path
+        if (e != hipSuccess) return hip_fail(e, "static scratch address");
+        ws = sp;
+        ws_bytes = PI_NOALLOC_SCRATCH_BYTES;
+    }
+    if ((st = check_ws(ws, ws_bytes, need)) != PI_OK) return st;
     const double tau = preds[0].threshold;
     const float theta = (float)std::log(tau / (1.0 - tau));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -378,6 +436,26 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, 
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
         return hip_fail(e, "pi_decode_run end event");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                  int T, long long s0, int nsteps, int mode, uint32_t* mask, int32_t* idx,
+                  int32_t* count, float* y, void* const* events, void* const* kernel_events,
+                  void* ws, size_t ws_bytes, void* stream) {
+    return decode_run_impl(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count, y, events,
+                           kernel_events, ws, ws_bytes, stream, false);
+}
+
+int pi_decode_run_noalloc(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
+                          const uint16_t* x, int T, long long s0, int nsteps, int mode,
+                          uint32_t* mask, int32_t* idx, int32_t* count, float* y,
+                          void* const* events, void* const* kernel_events, void* stream) {
+    return decode_run_impl(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count, y, events,
+                           kernel_events, nullptr, 0, stream, true);
 }
 
 int pi_ffn_dense_ref_gpu(const pi_ffn_desc* ffn, const uint16_t* x, int B, float* y, void* ws,

@@ -161,6 +161,18 @@ class DeviceLayer:
                                 handles(events), handles(kernel_events), self.ws.data_ptr(),
                                 self.ws_bytes, self.stream()))
 
+    def decode_run_noalloc(self, x, T: int, s0: int, nsteps: int, bufs: dict,
+                           mode: int = L.PI_RUN_AUTO) -> None:
+        """decode_run through pi_decode_run_noalloc: the library's static scratch instead of this
+        layer's workspace (kernel schedules only)."""
+        if not hasattr(self, "_pred_arr"):
+            self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
+            self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
+        L.check(L.pi_decode_run_noalloc(self._pred_arr, self._ffn_arr, self.replicas, x, T, s0, nsteps,
+                                        mode, bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
+                                        bufs["count"].data_ptr(), bufs["y"].data_ptr(), None, None,
+                                        self.stream()))
+
     def step(self, x, bufs: dict, rep: int = 0, logits: bool = True) -> None:
         """One batch-1 decode step: predict + compact (fused), then the sparse FFN.
 

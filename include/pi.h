@@ -248,6 +248,27 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
                   void* const* events, void* const* kernel_events,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* ---- pi_decode_run_noalloc ---------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  pi_decode_run in one of its kernel schedules
+ * (PI_RUN_AUTO, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT) with no workspace argument: its
+ * scratch (z, h and the down projection's partial rows) lives in a static device array of
+ * PI_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library routine); the caller
+ * still owns x and the outputs.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU -- different streams or threads -- race, so the caller orders them.
+ * Scratch a layer needs: 256-aligned (16384 + 4 r) + 256-aligned (4 F) + 4 d P bytes, with
+ * P = ceil(F/64) for the fused schedule and the split schedule's range count (at most 32)
+ * otherwise; a layer that needs more than PI_NOALLOC_SCRATCH_BYTES is rejected with
+ * PI_ERR_WORKSPACE, and PI_RUN_PERSISTENT with PI_ERR_UNSUPPORTED, both before any HIP call.
+ * Every other argument, output, check and error is that of pi_decode_run.                  */
+#define PI_NOALLOC_SCRATCH_BYTES (4u << 20)
+int pi_decode_run_noalloc(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
+                          const uint16_t* x, int T, long long s0, int nsteps, int mode,
+                          uint32_t* mask, int32_t* idx, int32_t* count, float* y,
+                          void* const* events, void* const* kernel_events, void* stream);
+
 /* ---- pi_ffn_dense_ref_gpu ------------------------------------------------------------------
  * The dense FFN that skipping has to reproduce: PowerInfer ("Neuron-aware Operator"; the
  * online engine's "skip the inactive neurons") computes only the predicted-active
