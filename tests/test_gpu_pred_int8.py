@@ -52,6 +52,9 @@ TINY8 = [
     configs.tiny("reglu", "f16", d=1024, F=2000, r=256, seed=52),
     configs.tiny("reglu", "i4g128", d=384, F=1000, r=128, seed=53),
     configs.tiny("relu", "f16", d=128, F=8, r=128, seed=54, mean_rate=0.5),
+    # d >= 3200: stage 1 takes one row per block with four waves (208 chunks of 16 weights,
+    # split raggedly: the fourth wave holds 16), also in the multi-step conversion variant
+    configs.tiny("reglu", "f16", d=3328, F=1000, r=256, seed=55),
 ]
 
 
@@ -133,6 +136,21 @@ def test_int8_decode_full(name):
         band += P.check_index_set(gidx, _np(bufs["mask"][0]).view(np.uint32), ref_L[i], cfg.F, ctx=f"{name} t={t}")
         P.check_ffn(_np(bufs["y"][0]), W, X[t], gidx, ctx=f"{name} t={t}")
     say(f"[gpu] {name}: band disagreements {band}")
+    # a 17-step run (every step after the first sums its predecessor's partial rows in the
+    # stage-1 kernel) ends bit-identical to a one-step run of its last token, against the oracle
+    s0, n = 5, 17
+    last = s0 + n - 1
+    ref = layer.buffers(1)
+    layer.decode_run(xd.data_ptr(), cfg.T, s0, n, bufs, mode=L.PI_RUN_KERNELS)
+    layer.decode_run(xd.data_ptr(), cfg.T, last, 1, ref, mode=L.PI_RUN_KERNELS)
+    torch.cuda.synchronize()
+    c = int(ref["count"][0].item())
+    assert int(bufs["count"][0].item()) == c and torch.equal(bufs["idx"][0, :c], ref["idx"][0, :c])
+    assert torch.equal(bufs["mask"], ref["mask"]) and torch.equal(bufs["y"], ref["y"])
+    gidx = _np(bufs["idx"][0, :c]).astype(np.int64)
+    ref_last = O.predictor_logits(X[last % cfg.T], W1, W2, inp["bias"])
+    P.check_index_set(gidx, _np(bufs["mask"][0]).view(np.uint32), ref_last, cfg.F, ctx=f"{name} run")
+    P.check_ffn(_np(bufs["y"][0]), W, X[last % cfg.T], gidx, ctx=f"{name} run")
 
 
 def test_int8_placed():
