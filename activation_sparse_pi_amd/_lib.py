@@ -27,7 +27,7 @@ EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_byte
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
            "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan",
-           "pi_count_active", "pi_decode_run_noalloc")
+           "pi_count_active", "pi_decode_run_noalloc", "pi_place_neurons_hot")
 PI_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -40,7 +40,8 @@ class PredDesc(ctypes.Structure):
 class FfnDesc(ctypes.Structure):
     _fields_ = [("w_gate", c_void_p), ("w_up", c_void_p), ("w_down", c_void_p),
                 ("s_gate", c_void_p), ("s_up", c_void_p), ("s_down", c_void_p),
-                ("d", c_int32), ("F", c_int32), ("act", c_int32), ("wfmt", c_int32)]
+                ("d", c_int32), ("F", c_int32), ("act", c_int32), ("wfmt", c_int32),
+                ("nhot", c_int32)]
 
 
 class BatchPlan(ctypes.Structure):
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_longlong, c_int, c_int, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.pi_decode_run_noalloc.restype = c_int
+        L.pi_place_neurons_hot.argtypes = [c_void_p, c_int, c_int, c_float, c_void_p, c_void_p]
+        L.pi_place_neurons_hot.restype = c_int
         L.pi_count_active.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p]
         L.pi_count_active.restype = c_int
         L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
@@ -210,3 +213,8 @@ def pi_decode_run_noalloc(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, 
     """pi_decode_run without a workspace (the library's static scratch); arguments as there."""
     return lib().pi_decode_run_noalloc(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, count,
                                        y, events, kernel_events, stream)
+
+
+def pi_place_neurons_hot(counts: int, F: int, ntok: int, hot_rate: float, perm: int, nhot) -> int:
+    """counts / perm host addresses (int32 [F]); nhot a ctypes.c_int32, set on success."""
+    return lib().pi_place_neurons_hot(counts, F, ntok, hot_rate, perm, ctypes.byref(nhot))

@@ -62,6 +62,16 @@ struct DecPlan {
     size_t off_z, off_h, off_part, bytes;   // off_part: max(ntile, nsplit) partial rows of d floats
 };
 DecPlan plan_decode(int d, int r, int F, int wfmt);
+// The split schedule's down ranges: Rh ranges of wps_hot mask words over the hot block's words
+// [0, Wh), then ranges of wps_cold words over the rest; P partial rows in all.
+struct DownRanges {
+    int Wh, wps_hot, Rh, P, wps_cold;
+};
+DownRanges down_ranges(const DecPlan& pl, int nhot, int F);
+// Dynamic LDS of the split schedule's hot-block slots: ceil(nhot / ntile) waves per tile block,
+// one 1 KB-aligned row slot per matrix (gate, up); 0 without a hot block.
+size_t hot_lds_bytes(const pi_ffn_desc& f, int ntile);
+constexpr int DEC_LDS_MAX = 160 * 1024;   // LDS of a gfx950 CU
 // One step: two kernels (fused: each tile block stores its down projection as one partial row
 // of d floats) or three (split: a down kernel over ranges of the mask, one partial row per
 // range).  When convert_prev is set, the first kernel sums the previous step's partial rows
@@ -72,7 +82,7 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
                               hipEvent_t e0, hipEvent_t e1);
 // After the last step: y = the fixed-order sum of its partial rows, and the last step's neuron
 // table (idx, count; skipped when idx is NULL) from its mask.
-hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
+hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int nhot, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s);
 
 // ---- persistent batch-1 decode (a run of steps in one cooperative launch) -----------------

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     uint32_t* __restrict__ mask, const uint16_t* __restrict__ x, const void* __restrict__ Wg,
     const uint16_t* __restrict__ Sg, const void* __restrict__ Wu,
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h, const void* __restrict__ Wd,
-    const uint16_t* __restrict__ Sd, float* __restrict__ part) {
+    const uint16_t* __restrict__ Sd, float* __restrict__ part, int nhot) {
     constexpr int NT = B_WAVES * 64;
     // row items per wave in flight: as many as the register budget of two blocks per CU
     // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
@@ -77,6 +77,38 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile = blockIdx.x;
     const int W = (F + 31) >> 5;
+
+    // --- hot block (split schedule): neurons [0, nhot) are computed densely, whether or not the
+    // predictor marks them, so their up/gate rows need not wait for the logits.  Wave w of block
+    // b takes hot neuron b + ntile w (at most one per wave); its rows go straight into the
+    // wave's LDS slot (no registers held), issued before the W2t rows, and are used after the
+    // logits, by which time they have landed.  h of a hot neuron is written unmasked: the down
+    // projection reads h only for neurons set in the mask.
+    constexpr int M = GLU ? 2 : 1;
+    const int nc = WF == 0 ? (d >> 3) : (d >> 5);   // 16-byte chunks per row
+    const int G = d >> 7;
+    const size_t rb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
+    const size_t hslot = (rb + 1023) & ~(size_t)1023;       // one row's LDS slot
+    const int hn = tile + (int)gridDim.x * wave;              // this wave's hot neuron
+    const bool hot_w = !FUSED && hn < nhot;                   // wave-uniform
+    char* s_hot = smem + align16i(r * 4) + (size_t)(d / 8) * 16 + (size_t)wave * M * hslot;
+    uint32_t hsc[M][WF == 1 ? Q : 1];                         // int4 scales of the hot rows
+    if (hot_w) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int mat = GLU ? m : 1;                      // 0 = gate, 1 = up
+            const uint8_t* rowp = static_cast<const uint8_t*>(mat ? Wu : Wg) + (size_t)hn * rb;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int c = lane + 64 * q;
+                if (c < nc)        // lane c of instruction q lands at slot offset 16 c
+                    __builtin_amdgcn_global_load_lds(rowp + 16 * (size_t)c,
+                        (__attribute__((address_space(3))) void*)(s_hot + m * hslot + 1024 * q), 16, 0, 0);
+                if constexpr (WF == 1)
+                    hsc[m][q] = (uint32_t)((mat ? Su : Sg) + (size_t)hn * G)[(c < nc ? c : 0) >> 2];
+            }
+        }
+    }
 
     // --- logits of the tile: the first segment of its W2t rows (and the tile's bias) goes
     // out before z is staged
@@ -104,6 +136,38 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     tile_rows_store<B_WAVES>(acc, s_red);
     __syncthreads();
 
+    // --- the wave's hot neuron: its rows are in LDS by now (issued before the W2t rows, whose
+    // data the logits have consumed); the wait below makes that explicit
+    if (hot_w) {
+        __builtin_amdgcn_s_waitcnt(0);
+        float hd[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float dot = 0.f;
+            const char* slot = s_hot + m * hslot;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int c = lane + 64 * q;
+                if (c < nc) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(slot + 16 * c);
+                    if (WF == 0) {
+                        dot = dot8(w, s_x[c], dot);
+                    } else {
+                        uint32_t xp[16];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint4 t = s_x[4 * c + k];
+                            xp[4 * k] = t.x; xp[4 * k + 1] = t.y; xp[4 * k + 2] = t.z; xp[4 * k + 3] = t.w;
+                        }
+                        dot = fmaf(dot32_i4(w, xp), h2f((uint16_t)hsc[m][q]), dot);
+                    }
+                }
+            }
+            hd[m] = wave_sum(dot);
+        }
+        if (lane == 0) h[hn] = GLU ? fmaxf(hd[0], 0.f) * hd[M - 1] : fmaxf(hd[0], 0.f);
+    }
+
     // --- threshold, mask words, the tile's active list (wave 0: lane = neuron of the tile)
     if (wave == 0) {
         const int n = tile * 64 + lane;
@@ -114,23 +178,22 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
             if (logits) logits[n] = l;
         }
         const unsigned long long bal = __ballot(act);
-        const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
         if (lane == 0) {
-            mask[2 * tile] = lo;
-            if (2 * tile + 1 < W) mask[2 * tile + 1] = hi;
-            s_n = __popcll(bal);
+            mask[2 * tile] = (uint32_t)bal;
+            if (2 * tile + 1 < W) mask[2 * tile + 1] = (uint32_t)(bal >> 32);
         }
-        if (act) s_list[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = lane;
+        // the row list holds the active neurons outside the hot block (all of them when fused)
+        const bool listed = act && (FUSED || n >= nhot);
+        const unsigned long long bl = __ballot(listed);
+        const uint32_t lo = (uint32_t)bl, hi = (uint32_t)(bl >> 32);
+        if (lane == 0) s_n = __popcll(bl);
+        if (listed) s_list[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = lane;
     }
     __syncthreads();
 
     // --- rows of the active neurons: (neuron, matrix) items, IPW per wave in flight
     const int na = s_n;
-    constexpr int M = GLU ? 2 : 1;
     const int items = na * M;
-    const int nc = WF == 0 ? (d >> 3) : (d >> 5);   // 16-byte chunks per row
-    const int G = d >> 7;
-    const size_t rb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
     for (int it0 = wave * IPW; it0 < items; it0 += B_WAVES * IPW) {
         uint4 wr[IPW][Q];
         uint32_t sr[IPW][Q];   // raw fp16 scales, one per register
@@ -310,7 +373,7 @@ template <int WF, int U>
 __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const uint32_t* __restrict__ mask, int F, const float* __restrict__ h,
     const void* __restrict__ Wd, const uint16_t* __restrict__ Sd, int d, int wps,
-    float* __restrict__ part) {
+    float* __restrict__ part, int Wh, int wps_hot, int Rh) {
     using Gm = DnGeom<WF>;
     __shared__ int s_ids[DEC_IDCAP];
     __shared__ __align__(16) float s_red[DN_NW * Gm::SC];
@@ -319,7 +382,10 @@ __global__ __launch_bounds__(DN_NW * 64) void k_dec_down(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.x, slice = blockIdx.y;
     const int W = (F + 31) >> 5;
-    const int w0 = min(W, split * wps), w1 = min(W, w0 + wps);
+    // ranges: the first Rh cover the hot block's mask words [0, Wh) wps_hot at a time (a hot
+    // word holds ~8 times the active neurons of a cold one), the rest the cold words wps at a time
+    const int w0 = split < Rh ? split * wps_hot : min(W, Wh + (split - Rh) * wps);
+    const int w1 = split < Rh ? min(Wh, w0 + wps_hot) : min(W, w0 + wps);   // wps: the cold width
     const int n_loc = range_compact(mask, w0, w1, F, s_ids, s_tmp);
 
     const size_t rowb = WF == 0 ? (size_t)d * 2 : (size_t)(d >> 1);
@@ -427,27 +493,39 @@ __global__ __launch_bounds__(256) void k_dec_finish(const float* __restrict__ pa
 
 // --------------------------------------------------------------------------------------- dispatch
 template <int WF, bool GLU, int Q, bool FUSED, bool P8>
-void launch_b8(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
+hipError_t launch_b8(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
                const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
                const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
+    if (lds > 65536) {
+        // a hot block's LDS slots can take the tile block past the default 64 KB of dynamic
+        // LDS (a gfx950 CU has 160 KB); raise this kernel's limit to what the launch needs
+        static size_t raised = 65536;
+        if (lds > raised) {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&k_dec_stage2_up<WF, GLU, Q, FUSED, P8>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            raised = lds;
+        }
+    }
     if (e0)
         hipExtLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), (uint32_t)lds, s,
                               e0, e1, 0, z, p.w_p2t, p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x,
-                              f.w_gate, f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, part);
+                              f.w_gate, f.s_gate, f.w_up, f.s_up, f.d, h, f.w_down, f.s_down, part, FUSED ? 0 : f.nhot);
     else
         hipLaunchKernelGGL((k_dec_stage2_up<WF, GLU, Q, FUSED, P8>), g, dim3(B_WAVES * 64), lds, s, z, p.w_p2t,
                            p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, x, f.w_gate, f.s_gate, f.w_up,
-                           f.s_up, f.d, h, f.w_down, f.s_down, part);
+                           f.s_up, f.d, h, f.w_down, f.s_down, part, FUSED ? 0 : f.nhot);
+    return hipSuccess;
 }
 
 template <int WF, bool GLU, int Q, bool FUSED>
-void launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
+hipError_t launch_b(dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const float* z,
               const pi_pred_desc& p, float theta, float* logits, uint32_t* mask,
               const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
     if (p.pfmt == PI_P_I8G128)
-        launch_b8<WF, GLU, Q, FUSED, true>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
-    else
-        launch_b8<WF, GLU, Q, FUSED, false>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+        return launch_b8<WF, GLU, Q, FUSED, true>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+    return launch_b8<WF, GLU, Q, FUSED, false>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
 }
 
 template <int WF, bool GLU, bool FUSED>
@@ -455,7 +533,9 @@ hipError_t dispatch_b(int q, dim3 g, size_t lds, hipStream_t s, hipEvent_t e0, h
                       const float* z, const pi_pred_desc& p, float theta, float* logits,
                       uint32_t* mask, const uint16_t* x, const pi_ffn_desc& f, float* h,
                       float* part) {
-#define PI_B(QQ) case QQ: launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part); break;
+#define PI_B(QQ) case QQ: { \
+        const hipError_t le = launch_b<WF, GLU, QQ, FUSED>(g, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part); \
+        if (le != hipSuccess) return le; } break;
     if constexpr (WF == 0) {
         switch (q) {
             PI_B(1) PI_B(2) PI_B(3) PI_B(4) PI_B(5) PI_B(6) PI_B(7) PI_B(8)
@@ -478,14 +558,57 @@ hipError_t dispatch_b_fmt(const DecPlan& pl, hipStream_t s, hipEvent_t e0, hipEv
                           const uint16_t* x, const pi_ffn_desc& f, float* h, float* part) {
     const bool glu = f.act == PI_ACT_REGLU;
     const dim3 gb(pl.ntile);
+    const size_t lds = pl.lds_b + (FUSED ? 0 : hot_lds_bytes(f, pl.ntile));
     if (f.wfmt == PI_W_F16)
-        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
-                   : dispatch_b<0, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
-    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
-               : dispatch_b<1, false, FUSED>(pl.q, gb, pl.lds_b, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+        return glu ? dispatch_b<0, true, FUSED>(pl.q, gb, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
+                   : dispatch_b<0, false, FUSED>(pl.q, gb, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
+    return glu ? dispatch_b<1, true, FUSED>(pl.q, gb, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)
+               : dispatch_b<1, false, FUSED>(pl.q, gb, lds, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
 }
 
 }  // namespace
+
+// The plan's nsplit ranges (about one down block per CU) are shared between the hot and the cold
+// words in proportion to their expected active neurons, a hot word taken as DOWN_HOT_DENSITY
+// times as dense as a cold one (profiled hot blocks fire on 70-99% of tokens, the cold rest on
+// 3-7%: ratios of 14 to 30 on the workloads here).
+constexpr int DOWN_HOT_DENSITY = 16;
+
+DownRanges down_ranges(const DecPlan& pl, int nhot, int F) {
+    DownRanges r{};
+    const int W = (F + 31) / 32;
+    r.Wh = nhot > 0 ? std::min(W, (nhot + 31) / 32) : 0;
+    if (r.Wh == 0) {
+        r.wps_hot = 1;
+        r.Rh = 0;
+        r.P = pl.nsplit;
+        r.wps_cold = pl.wps;
+        return r;
+    }
+    const double wh = (double)DOWN_HOT_DENSITY * r.Wh, wc = (double)(W - r.Wh);
+    int rh = (int)std::lround(pl.nsplit * wh / (wh + wc));
+    rh = std::max(1, std::min(rh, std::min(r.Wh, pl.nsplit - (W > r.Wh ? 1 : 0))));
+    r.wps_hot = (r.Wh + rh - 1) / rh;
+    r.Rh = (r.Wh + r.wps_hot - 1) / r.wps_hot;
+    const int rc = std::max(1, pl.nsplit - r.Rh);
+    const int wps_c = std::max(pl.wps, (W - r.Wh + rc - 1) / rc);   // never more words than fit in LDS
+    r.P = r.Rh + (W - r.Wh + wps_c - 1) / wps_c;
+    r.wps_cold = wps_c;
+    return r;
+}
+
+size_t hot_lds_bytes(const pi_ffn_desc& f, int ntile) {
+    if (f.nhot <= 0) return 0;
+    const size_t rb = f.wfmt == PI_W_F16 ? (size_t)f.d * 2 : (size_t)f.d / 2;
+    const size_t hslot = (rb + 1023) & ~(size_t)1023;
+    const int hpb = (f.nhot + ntile - 1) / ntile;               // hot neurons (waves) per tile block
+    return (size_t)hpb * (f.act == PI_ACT_REGLU ? 2 : 1) * hslot;
+}
+
+// the most ranges any hot block (nhot <= 8 ceil(F / 64)) can give the split down projection
+static int max_down_ranges(const DecPlan& p, int F) {
+    return down_ranges(p, std::min(F, 8 * p.ntile), F).P;
+}
 
 DecPlan plan_decode(int d, int r, int F, int wfmt) {
     DecPlan p{};
@@ -515,8 +638,8 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     off = align_up(off + (size_t)r * sizeof(float), 256);
     p.off_h = off;
     off = align_up(off + (size_t)F * sizeof(float), 256);
-    p.off_part = off;          // partial rows of either schedule
-    off = align_up(off + (size_t)std::max(p.ntile, p.nsplit) * d * sizeof(float), 256);
+    p.off_part = off;          // partial rows of either schedule (a hot block adds ranges)
+    off = align_up(off + (size_t)std::max(p.ntile, max_down_ranges(p, F)) * d * sizeof(float), 256);
     p.bytes = off;
     return p;
 }
@@ -530,27 +653,28 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     // the previous step (same schedule) left its partial rows: stage 1 sums them into y
     hipError_t e = launch_pred_stage1(p, pl.pred, x, 1, z, s, convert_prev ? part : nullptr, y,
-                                      fused ? pl.ntile : pl.nsplit);
+                                      fused ? pl.ntile : down_ranges(pl, f.nhot, f.F).P);
     if (e != hipSuccess) return e;
     if (fused) return dispatch_b_fmt<true>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, part);
     if ((e = dispatch_b_fmt<false>(pl, s, e0, e1, z, p, theta, logits, mask, x, f, h, part)) != hipSuccess)
         return e;
-    const dim3 gc(pl.nsplit, pl.nslices);     // range fastest: one range's blocks on one XCD
+    const DownRanges dr = down_ranges(pl, f.nhot, f.F);
+    const dim3 gc(dr.P, pl.nslices);          // range fastest: one range's blocks on one XCD
     if (f.wfmt == PI_W_F16)
         hipLaunchKernelGGL((k_dec_down<0, 8>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, part);
+                           f.s_down, f.d, dr.wps_cold, part, dr.Wh, dr.wps_hot, dr.Rh);
     else
         hipLaunchKernelGGL((k_dec_down<1, 12>), gc, dim3(DN_NW * 64), 0, s, mask, f.F, h, f.w_down,
-                           f.s_down, f.d, pl.wps, part);
+                           f.s_down, f.d, dr.wps_cold, part, dr.Wh, dr.wps_hot, dr.Rh);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int d, int F, const uint32_t* mask,
+hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int nhot, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s) {
     const float* part = reinterpret_cast<const float*>(ws + pl.off_part);
     const int nq = d / 4;                         // one 4-column quad per wave
     hipLaunchKernelGGL(k_dec_finish, dim3((nq + 3) / 4), dim3(256), 0, s, part,
-                       fused ? pl.ntile : pl.nsplit, y, d, mask, F, idx, count);
+                       fused ? pl.ntile : down_ranges(pl, nhot, F).P, y, d, mask, F, idx, count);
     return hipGetLastError();
 }
 

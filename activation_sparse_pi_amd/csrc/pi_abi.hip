@@ -88,6 +88,8 @@ int check_ffn(const pi_ffn_desc* f, int B) {
         if (q && !aligned16(q)) return fail(PI_ERR_ALIGN, "ffn weights must be 16-byte aligned");
     if (B > 1 && f->wfmt != PI_W_F16)
         return fail(PI_ERR_UNSUPPORTED, "batch > 1 union path is fp16 only");
+    if (f->nhot < 0 || f->nhot > f->F || f->nhot > 8 * ((f->F + 63) / 64))
+        return fail(PI_ERR_SHAPE, "nhot=%d outside 0..min(F, 8 ceil(F/64)) (F=%d)", f->nhot, f->F);
     return PI_OK;
 }
 
@@ -344,11 +346,19 @@ int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep
                         "(d=%d r=%d F=%d, %d co-resident blocks)", d, r, F, G);
     }
     const DecPlan pl = plan_decode(d, r, F, wfmt);
-    const bool fused = mode == PI_RUN_FUSED || (mode != PI_RUN_SPLIT && pl.fused_default);
+    // a hot block runs in the split schedule (the fused one computes every neuron from the
+    // predicted set, hot or not)
+    const bool fused = mode == PI_RUN_FUSED || (mode != PI_RUN_SPLIT && ffns[0].nhot == 0 && pl.fused_default);
+    for (int i = 0; i < nrep; ++i)
+        if (ffns[i].nhot != ffns[0].nhot) return fail(PI_ERR_SHAPE, "replica %d has another hot block", i);
+    if (!persistent && !fused && pl.lds_b + hot_lds_bytes(ffns[0], pl.ntile) > (size_t)DEC_LDS_MAX)
+        return fail(PI_ERR_UNSUPPORTED, "the hot block needs %zu bytes of LDS per tile block, more than %d",
+                    pl.lds_b + hot_lds_bytes(ffns[0], pl.ntile), DEC_LDS_MAX);
     // the kernel schedules use the partial rows of the schedule they run (the workspace from
     // pi_workspace_bytes holds those of either)
     const size_t need = persistent ? rp.bytes
-                                   : pl.off_part + (size_t)(fused ? pl.ntile : pl.nsplit) * d * sizeof(float);
+                                   : pl.off_part + (size_t)(fused ? pl.ntile : down_ranges(pl, ffns[0].nhot, F).P) *
+                                                       d * sizeof(float);
     if (noalloc) {
         if (need > (size_t)PI_NOALLOC_SCRATCH_BYTES)
             return fail(PI_ERR_WORKSPACE, "this layer's decode scratch is %zu bytes, more than the %u "
@@ -430,7 +440,7 @@ int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep
                                    y, i > 0, w, s, k0, k1);
             if (e != hipSuccess) return hip_fail(e, "pi_decode_run launch");
         }
-        if ((e = launch_decode_finish(pl, fused, d, F, mask, idx, count, y, w, s)) != hipSuccess)
+        if ((e = launch_decode_finish(pl, fused, ffns[0].nhot, d, F, mask, idx, count, y, w, s)) != hipSuccess)
             return hip_fail(e, "pi_decode_run final y");
     }
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
@@ -548,6 +558,46 @@ int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size
     if (n <= 0 || row_bytes == 0) return fail(PI_ERR_SHAPE, "need n > 0 and row_bytes > 0 (n=%d)", n);
     const hipError_t e = launch_permute_rows(src, dst, perm, n, row_bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "pi_permute_rows");
+}
+
+int pi_place_neurons_hot(const int32_t* counts, int F, int ntok, float hot_rate, int32_t* perm,
+                         int32_t* nhot) {
+    if (!counts || !perm || !nhot) return fail(PI_ERR_NULL, "counts / perm / nhot NULL");
+    if (F <= 0 || ntok <= 0) return fail(PI_ERR_SHAPE, "need F > 0 and ntok > 0 (F=%d ntok=%d)", F, ntok);
+    if (!(hot_rate > 0.f && hot_rate <= 1.f)) return fail(PI_ERR_SHAPE, "hot_rate %g outside (0, 1]", (double)hot_rate);
+    for (int i = 0; i < F; ++i)
+        if (counts[i] < 0 || counts[i] > ntok) return fail(PI_ERR_SHAPE, "count %d at neuron %d outside 0..ntok", counts[i], i);
+    std::vector<int32_t> order(F);
+    for (int i = 0; i < F; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+    const int T = (F + 63) / 64;
+    int H = 0;
+    while (H < F && H < 8 * T && (double)counts[order[H]] >= (double)hot_rate * ntok) ++H;
+    for (int k = 0; k < H; ++k) perm[k] = order[k];           // the hot block, hottest first
+    // the cold neurons, by descending count, dealt in serpentine order over the tiles' free
+    // positions (those from H on), so every cold tile expects about the same number active
+    std::vector<int> next(T), end(T);
+    std::vector<int> tiles;
+    for (int t = 0; t < T; ++t) {
+        next[t] = std::max(64 * t, H);
+        end[t] = std::min(64 * t + 64, F);
+        if (next[t] < end[t]) tiles.push_back(t);
+    }
+    const int nt = (int)tiles.size();
+    int j = 0, dir = 1;
+    for (int k = H; k < F; ++k) {
+        while (next[tiles[j]] == end[tiles[j]]) {
+            j += dir;
+            if (j == nt) { j = nt - 1; dir = -1; }
+            if (j < 0) { j = 0; dir = 1; }
+        }
+        perm[next[tiles[j]]++] = order[k];
+        j += dir;
+        if (j == nt) { j = nt - 1; dir = -1; }
+        if (j < 0) { j = 0; dir = 1; }
+    }
+    *nhot = H;
+    return ok();
 }
 
 int pi_count_active(const uint32_t* mask, int B, int F, int32_t* counts, void* stream) {

@@ -20,10 +20,13 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 class DeviceLayer:
     def __init__(self, inputs: dict, replicas: int = 1, B_max: int = 1, device="cuda",
-                 threshold: float = 0.5, perm: np.ndarray | None = None, pred_format: str = "f16"):
+                 threshold: float = 0.5, perm: np.ndarray | None = None, pred_format: str = "f16",
+                 nhot: int = 0):
         """perm: optional neuron placement (int32 [F], placed position p holds original
-        neuron perm[p], from ``pi_place_neurons``): every per-neuron array is permuted on the
-        device with ``pi_permute_rows``; ``map_ids`` turns placed ids back into original ones.
+        neuron perm[p], from ``pi_place_neurons`` or ``pi_place_neurons_hot``): every per-neuron
+        array is permuted on the device with ``pi_permute_rows``; ``map_ids`` turns placed ids
+        back into original ones.  nhot: the hot block's size (placed positions [0, nhot)), from
+        ``pi_place_neurons_hot``; it goes into every FFN descriptor.
         pred_format: "f16", or "i8g128" for the int8 group-128 predictor, whose factors come in
         ``inputs`` as q_p1t, s_p1t, q_p2t, s_p2t (one row per predictor output)."""
         cfg = inputs["cfg"]
@@ -45,6 +48,9 @@ class DeviceLayer:
             host["w_p2"] = np.ascontiguousarray(inputs["w_p2"].T)    # [F, r]
         base = {k: _dev(v, self.device) for k, v in host.items()}
         self.perm = None
+        self.nhot = nhot
+        if nhot and perm is None:
+            raise ValueError("a hot block needs the placement that laid it out (perm)")
         if perm is not None:
             perm = np.ascontiguousarray(perm, dtype=np.int32)
             if perm.shape != (cfg.F,):
@@ -71,13 +77,13 @@ class DeviceLayer:
             if cfg.wfmt == "f16":
                 g = t["w_gate"].data_ptr() if "w_gate" in t else None
                 self.ffn.append(L.FfnDesc(g, t["w_up"].data_ptr(), t["w_down"].data_ptr(), None, None,
-                                          None, cfg.d, cfg.F, self.act, self.wfmt))
+                                          None, cfg.d, cfg.F, self.act, self.wfmt, nhot))
             else:
                 g = t["q_gate"].data_ptr() if "q_gate" in t else None
                 sg = t["s_gate"].data_ptr() if "s_gate" in t else None
                 self.ffn.append(L.FfnDesc(g, t["q_up"].data_ptr(), t["q_down"].data_ptr(), sg,
                                           t["s_up"].data_ptr(), t["s_down"].data_ptr(), cfg.d, cfg.F,
-                                          self.act, self.wfmt))
+                                          self.act, self.wfmt, nhot))
         self.ws_bytes = L.pi_workspace_bytes(self.pred[0], self.ffn[0], B_max)
         if self.ws_bytes == 0:
             raise L.PiError(L.PI_ERR_SHAPE, "pi_workspace_bytes rejected the layer: " + L.pi_last_error())

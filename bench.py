@@ -63,9 +63,12 @@ def parse():
                          "persistent: one pi_decode_run call, one cooperative launch; "
                          "eager: one Python call per ABI function")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget, 0 = skip")
-    ap.add_argument("--placement", choices=("none", "dealt"), default="none",
+    ap.add_argument("--placement", choices=("none", "dealt", "hot"), default="none",
                     help="dealt: neurons dealt over the 64-neuron tiles by their activation counts "
-                         "on calibration tokens (pi_place_neurons), batch 1 only")
+                         "on calibration tokens (pi_place_neurons); hot: the neurons firing on at "
+                         "least --hot-rate of them form a hot block computed without waiting for "
+                         "the predictor, the rest dealt (pi_place_neurons_hot); batch 1 only")
+    ap.add_argument("--hot-rate", type=float, default=0.7, help="profiled rate of the hot block")
     ap.add_argument("--calib-tokens", type=int, default=256, help="calibration tokens for --placement")
     ap.add_argument("--pred-format", choices=("f16", "i8g128"), default="f16",
                     help="i8g128: the predictor factors in int8 with one fp16 scale per 128 (batch 1)")
@@ -103,9 +106,10 @@ def bytes_model(cfg, n, pb=2.0):
     return dict(pred=pred, ffn=ffn, up=up, stage2=stage2, tile_fused=tile_fused, total=total)
 
 
-def kernel_schedule(cfg) -> str:
-    """The schedule PI_RUN_KERNELS takes for this shape (documented in include/pi.h)."""
-    return "fused" if ((cfg.F + 63) // 64) * cfg.d <= (1 << 20) else "split"
+def kernel_schedule(cfg, nhot=0) -> str:
+    """The schedule PI_RUN_KERNELS takes for this shape (documented in include/pi.h): split for a
+    layer with a hot block."""
+    return "fused" if nhot == 0 and ((cfg.F + 63) // 64) * cfg.d <= (1 << 20) else "split"
 
 
 def bytes_model_batch(cfg, n_tok, U):
@@ -465,8 +469,8 @@ def main():
         inputs.update(gen.predictor_int8(inputs))
     probe = bytes_model(cfg, cfg.mean_rate * cfg.F, pb)
     R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
-    perm = None
-    if a.placement == "dealt":
+    perm, nhot = None, 0
+    if a.placement in ("dealt", "hot"):
         # profiling run on calibration tokens of their own (none of the timed stream), then
         # the placement; the timed layer holds the placed weights
         prof = DeviceLayer(inputs, replicas=1, B_max=1 if p8 else L.PI_MAX_BATCH, device=dev,
@@ -476,8 +480,15 @@ def main():
         del prof, cal
         torch.cuda.empty_cache()
         perm = np.empty(cfg.F, dtype=np.int32)
-        L.check(L.pi_place_neurons(cal_counts.ctypes.data, cfg.F, perm.ctypes.data))
-    layer = DeviceLayer(inputs, replicas=R, device=dev, perm=perm, pred_format=a.pred_format)
+        if a.placement == "dealt":
+            L.check(L.pi_place_neurons(cal_counts.ctypes.data, cfg.F, perm.ctypes.data))
+        else:
+            import ctypes
+            nh = ctypes.c_int32(0)
+            L.check(L.pi_place_neurons_hot(cal_counts.ctypes.data, cfg.F, a.calib_tokens, a.hot_rate,
+                                           perm.ctypes.data, nh))
+            nhot = nh.value
+    layer = DeviceLayer(inputs, replicas=R, device=dev, perm=perm, pred_format=a.pred_format, nhot=nhot)
     T = cfg.T
     xd = torch.from_numpy(inputs["x"][:, 0, :].copy()).to(dev)     # [T, d] resident in HBM
     bufs = layer.buffers(1)
@@ -503,7 +514,7 @@ def main():
     K, Wm = a.steps, a.warmup
     up_ms = []
     passes_ms = []
-    sched = a.mode if a.mode in ("fused", "split") else kernel_schedule(cfg)
+    sched = a.mode if a.mode in ("fused", "split") else kernel_schedule(cfg, nhot)
     sched_desc = ("two kernels per step (fused down)" if sched == "fused"
                   else "three kernels per step (split down)")
     if a.mode in ("persistent", "kernels", "fused", "split"):
@@ -568,7 +579,7 @@ def main():
         kernel_key = f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}"
         launch_bytes, launch_ms = float(np.mean(bm["up"])), float(np.mean(up_ms))
     else:
-        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act},{sched}{',p8' if p8 else ''}] {cfg.name}"
+        kernel_key = f"k_dec_stage2_up[{cfg.wfmt},{cfg.act},{sched}{',p8' if p8 else ''}{',hot' if nhot else ''}] {cfg.name}"
         bm_r = bytes_model(cfg, counts[roof_steps].astype(np.float64), pb)
         launch_bytes = float(np.mean(bm_r["tile_fused" if sched == "fused" else "stage2"]))
         launch_ms = float(np.mean(up_ms))
@@ -605,7 +616,10 @@ def main():
             "predictor": "int8 group-128, fp16 scales" if p8 else "fp16",
             "placement": ("none" if perm is None else
                           f"neurons dealt over the 64-neuron tiles by their activation counts on "
-                          f"{a.calib_tokens} calibration tokens (pi_place_neurons)"),
+                          f"{a.calib_tokens} calibration tokens (pi_place_neurons)" if nhot == 0 else
+                          f"hot block of {nhot} neurons (profiled rate >= {a.hot_rate} on "
+                          f"{a.calib_tokens} calibration tokens) computed before the predictor's "
+                          f"decision, the rest dealt over the tiles (pi_place_neurons_hot)"),
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_step": round(path_bytes),

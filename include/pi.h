@@ -106,6 +106,16 @@ typedef struct pi_ffn_desc {
     int32_t F;
     int32_t act;            /* PI_ACT_*                                                */
     int32_t wfmt;           /* PI_W_*                                                  */
+    int32_t nhot;           /* neurons [0, nhot) form the layer's hot block (0: none; a
+                               zero-filled descriptor has none).  PowerInfer, "Neuron Placement
+                               and Management" and its hot/cold split: the neurons that fire on
+                               most tokens are laid out together (pi_place_neurons_hot) and, in
+                               pi_decode_run's split schedule, computed densely -- their up/gate
+                               rows read alongside the predictor, without waiting for it -- while
+                               the cold rest is gathered from the predicted set.  Only the
+                               results of predicted-active neurons reach y, so the output is
+                               that of the same layer without a hot block.  Other calls ignore
+                               it.  0 <= nhot <= 8 * ceil(F / 64).                          */
 } pi_ffn_desc;
 
 /* ---- status / info ------------------------------------------------------------------ */
@@ -308,6 +318,19 @@ int pi_place_neurons(const int32_t* counts, int F, int32_t* perm);
  * PI_ERR_HIP.                                                                                */
 int pi_permute_rows(const void* src, void* dst, const int32_t* perm, int n, size_t row_bytes,
                     void* stream);
+
+/* The hot/cold layout (PowerInfer: power-law activation locality; "Neuron Placement and
+ * Management"): the neurons that fire on at least hot_rate of the ntok profiled tokens (counts
+ * as pi_count_active accumulates them, 0 <= counts[i] <= ntok) form the hot block at placed
+ * positions [0, *nhot), hottest first (ties by ascending original index), at most
+ * 8 * ceil(F / 64) of them; the cold rest, by descending count, is dealt in serpentine order
+ * over the tiles' remaining positions.  Set the layer's pi_ffn_desc.nhot to *nhot and apply
+ * perm with pi_permute_rows; pi_map_ids names original neurons as for pi_place_neurons.
+ * Host only, no HIP call.  perm int32 [F] and nhot are host pointers, written on success.
+ * Errors: PI_ERR_NULL, PI_ERR_SHAPE (F or ntok <= 0, a count outside 0..ntok, hot_rate outside
+ * (0, 1]).                                                                                   */
+int pi_place_neurons_hot(const int32_t* counts, int F, int ntok, float hot_rate, int32_t* perm,
+                         int32_t* nhot);
 
 /* PowerInfer, offline phase ("LLM Profiler"): the profiler runs requests through the model and
  * records which neurons fire in every layer; the placement above ranks neurons by those counts.

@@ -42,10 +42,10 @@ def pred(**kw):
 
 def ffn(**kw):
     a = dict(w_gate=None, w_up=A, w_down=A + 0x1000000, s_gate=None, s_up=None, s_down=None,
-             d=1024, F=4096, act=L.PI_ACT_RELU, wfmt=L.PI_W_F16)
+             d=1024, F=4096, act=L.PI_ACT_RELU, wfmt=L.PI_W_F16, nhot=0)
     a.update(kw)
     return L.FfnDesc(a["w_gate"], a["w_up"], a["w_down"], a["s_gate"], a["s_up"], a["s_down"],
-                     a["d"], a["F"], a["act"], a["wfmt"])
+                     a["d"], a["F"], a["act"], a["wfmt"], a["nhot"])
 
 
 def test_status_strings_and_version():
@@ -112,6 +112,8 @@ def test_predict_validation(kw, code):
     (dict(desc=ffn(F=4095)), L.PI_ERR_SHAPE),
     (dict(desc=ffn(d=8200)), L.PI_ERR_UNSUPPORTED),
     (dict(desc=ffn(w_down=A + 4)), L.PI_ERR_ALIGN),
+    (dict(desc=ffn(nhot=-1)), L.PI_ERR_SHAPE),
+    (dict(desc=ffn(nhot=4097)), L.PI_ERR_SHAPE),
     (dict(B=2, token_mask=None), L.PI_ERR_NULL),
     (dict(B=2, token_mask=A, desc=ffn(wfmt=L.PI_W_I4G128, s_up=A, s_down=A)), L.PI_ERR_UNSUPPORTED),
     (dict(B=32, token_mask=A, wsb="batch1"), L.PI_ERR_WORKSPACE),

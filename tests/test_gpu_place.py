@@ -257,3 +257,80 @@ def test_placed_union_tiny():
         ref_L = O.predictor_logits(X, inp["w_p1"], inp["w_p2"], inp["bias"])
         for b in range(cfg.B):
             _check_placed(layer, perm, bufs, b, ref_L[b], W, X[b], cfg.F, f"union t={t} b={b}")
+
+
+# ----------------------------------------------------------------------------- hot block
+def _placement_hot(inp, ncal=64, rate=0.5):
+    """pi_place_neurons_hot from a profiling run of the unplaced layer on calibration tokens."""
+    import ctypes
+    L = _L()
+    cfg = inp["cfg"]
+    prof = _layer(inp, B_max=L.PI_MAX_BATCH)
+    cal = torch.from_numpy(gen.calibration_x(cfg, ncal)).cuda()
+    counts = prof.activation_counts(cal)
+    perm = np.empty(cfg.F, np.int32)
+    nh = ctypes.c_int32(0)
+    L.check(L.pi_place_neurons_hot(counts.ctypes.data, cfg.F, ncal, rate, perm.ctypes.data, nh))
+    return perm, nh.value, counts
+
+
+HOT_TINY = [
+    configs.tiny("relu", "f16", d=384, F=1000, r=40, seed=61, mean_rate=0.25),
+    configs.tiny("reglu", "i4g128", d=384, F=1000, r=40, seed=62, mean_rate=0.25),
+    configs.tiny("reglu", "f16", d=1032, F=2000, r=48, seed=63, mean_rate=0.25),
+    configs.tiny("reglu", "i4g128", d=2176, F=1000, r=40, seed=64, mean_rate=0.3),
+]
+
+
+@pytest.mark.parametrize("mode", ["split", "kernels", "fused"])
+@pytest.mark.parametrize("cfg", HOT_TINY, ids=lambda c: c.name)
+def test_hot_block_decode_tiny(cfg, mode):
+    """A layer with a hot block (its hot neurons computed densely, before the predictor's
+    decision, in the split schedule): every token as a one-step run against the oracle of the
+    original layer through the neuron table, then a 40-step run that must end bit-identical to
+    a one-step run of its last token.  The fused schedule ignores the hot block."""
+    L = _L()
+    inp = gen.make(cfg)
+    W = O.Weights.from_inputs(inp)
+    perm, nhot, counts = _placement_hot(inp)
+    say(f"[gpu] hot block decode {mode} {cfg.name}: nhot={nhot}")
+    assert 0 < nhot < cfg.F
+    layer = _layer(inp, replicas=2, perm=perm, nhot=nhot)
+    X = inp["x"][:, 0, :]
+    xd = torch.from_numpy(X.copy()).cuda()
+    ref_L = O.predictor_logits(X, inp["w_p1"], inp["w_p2"], inp["bias"])
+    m = {"split": L.PI_RUN_SPLIT, "kernels": L.PI_RUN_KERNELS, "fused": L.PI_RUN_FUSED}[mode]
+    bufs = layer.buffers(1)
+    for t in range(cfg.T):
+        layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs, mode=m)
+        torch.cuda.synchronize()
+        _check_placed(layer, perm, bufs, 0, ref_L[t], W, X[t], cfg.F, f"{cfg.name} hot {mode} t={t}")
+    ref = layer.buffers(1)
+    layer.decode_run(xd.data_ptr(), cfg.T, 1, 40, bufs, mode=m)
+    layer.decode_run(xd.data_ptr(), cfg.T, 40, 1, ref, mode=m)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs["y"], ref["y"]) and torch.equal(bufs["mask"], ref["mask"])
+
+
+@pytest.mark.parametrize("name,rate", [("c2", 0.85), ("c5", 0.7)])
+def test_hot_block_decode_full(name, rate):
+    """The LLaMA-7B- and LLaMA-70B-shaped layers with a hot block from 256 calibration tokens,
+    in the default kernel schedule (split, since the layer has a hot block), on sampled
+    tokens; the hot block holds the neurons the profile saw firing on >= rate of the tokens."""
+    L = _L()
+    cfg = configs.get(name)
+    inp = gen.make(cfg)
+    W = O.Weights.from_inputs(inp)
+    perm, nhot, counts = _placement_hot(inp, ncal=256, rate=rate)
+    say(f"[gpu] hot block decode {cfg.name}: nhot={nhot}")
+    assert nhot > 300
+    layer = _layer(inp, replicas=2, perm=perm, nhot=nhot)
+    X = inp["x"][:, 0, :]
+    xd = torch.from_numpy(X.copy()).cuda()
+    tokens = [0, cfg.T // 2, cfg.T - 1]
+    ref_L = O.predictor_logits(X[tokens], inp["w_p1"], inp["w_p2"], inp["bias"])
+    bufs = layer.buffers(1)
+    for i, t in enumerate(tokens):
+        layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs, mode=L.PI_RUN_KERNELS)
+        torch.cuda.synchronize()
+        _check_placed(layer, perm, bufs, 0, ref_L[i], W, X[t], cfg.F, f"{name} hot t={t}")
