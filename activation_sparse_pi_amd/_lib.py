@@ -21,13 +21,14 @@ PI_P_F16, PI_P_I8G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
 PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 1, 2, 3, 4
 PI_MAX_BATCH = 32
-PI_BATCH_TOKENS, PI_BATCH_UNION = 0, 1
+PI_BATCH_TOKENS, PI_BATCH_UNION, PI_BATCH_AUTO = 0, 1, 2
+PI_MAX_BATCH_RUN = 64
 
 EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_bytes",
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
            "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan",
-           "pi_count_active", "pi_decode_run_noalloc", "pi_place_neurons_hot")
+           "pi_count_active", "pi_decode_run_noalloc", "pi_place_neurons_hot", "pi_batch_run")
 PI_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -114,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.pi_decode_run_noalloc.restype = c_int
         L.pi_place_neurons_hot.argtypes = [c_void_p, c_int, c_int, c_float, c_void_p, c_void_p]
         L.pi_place_neurons_hot.restype = c_int
+        L.pi_batch_run.argtypes = [P(PredDesc), P(FfnDesc), c_int, c_void_p, c_int, c_int,
+                                   ctypes.c_longlong, c_int, c_int, c_void_p, ctypes.c_double,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.pi_batch_run.restype = c_int
         L.pi_count_active.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p]
         L.pi_count_active.restype = c_int
         L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
@@ -218,3 +223,11 @@ def pi_decode_run_noalloc(preds, ffns, nrep, x, T, s0, nsteps, mode, mask, idx, 
 def pi_place_neurons_hot(counts: int, F: int, ntok: int, hot_rate: float, perm: int, nhot) -> int:
     """counts / perm host addresses (int32 [F]); nhot a ctypes.c_int32, set on success."""
     return lib().pi_place_neurons_hot(counts, F, ntok, hot_rate, perm, ctypes.byref(nhot))
+
+
+def pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs, mask, y, events,
+                 ws, ws_bytes, stream) -> int:
+    """preds / ffns: ctypes arrays; rate: host address (float32 [F]) or None; events: ctypes array
+    of two hipEvent_t handles or None."""
+    return lib().pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs, mask,
+                              y, events, ws, ws_bytes, stream)

@@ -141,10 +141,11 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
                           float theta, float* logits, uint32_t* mask, int32_t* idx, int32_t* count,
                           char* ws, hipStream_t s);
 
-// 1 < B <= 32: stage 1 and stage 2 with threshold and mask words (no neuron tables)
+// 1 < B <= 32: stage 1 and stage 2 with threshold and mask words (no neuron tables); umask
+// (optional, ceil(F/32) words): the OR of the B tokens' masks
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
-                                hipStream_t s);
+                                hipStream_t s, uint32_t* umask = nullptr);
 
 // part / y (batch-1 decode executor only): also sum the previous step's P partial rows of d
 // floats into y (reduce_partials)

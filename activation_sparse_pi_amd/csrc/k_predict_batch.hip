@@ -128,8 +128,10 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
                                                     const uint16_t* __restrict__ W2t,
                                                     const float* __restrict__ bias, int r, int F,
                                                     float theta, float* __restrict__ logits,
-                                                    uint32_t* __restrict__ mask) {
+                                                    uint32_t* __restrict__ mask,
+                                                    uint32_t* __restrict__ umask) {
     __shared__ uint4 s_z[2][32][ZC / 8];     // z_hi, z_lo: [token][chunk of 8, swizzled]
+    __shared__ unsigned long long s_u[PB_NW][2];   // per wave: OR of its tokens' ballots
     __shared__ uint4 s_w[PB_NW][32][8];      // per wave: W2t staging, then its accumulator
     __shared__ int s_e[32];                  // per-token exponent e
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -140,6 +142,9 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     // rows past F read row F - 1, rank positions past r read its last 8, tokens past B token
     // 0.  z past r is zeroed before it is staged, so those W2t values meet zeros; rows past F
     // and tokens past B only reach outputs that are never written.
+    // the bias of this lane's two neurons in the epilogue (n0 + lane and n0 + 64 + lane), loaded
+    // now so that the epilogue's ballots do not each wait for a load
+    const float bias0 = bias[min(n0 + lane, F - 1)], bias1 = bias[min(n0 + 64 + lane, F - 1)];
     const uint16_t* wrow[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -243,6 +248,7 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     for (int q = 0; q < 16; ++q) red[q * 64 + lane] = acc[q];
     __syncthreads();
     const int W = (F + 31) >> 5;
+    unsigned long long uor[2] = {0ull, 0ull};
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int tb = wave * 4 + (it >> 1), nh = it & 1;
@@ -253,16 +259,32 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
         const int o = d_reg(nl) * 64 + d_lane(nl, tb);
         bool act = false;
         if (tb < B && i < F) {
-            const float l = ldexpf(r0[o] + r1[o], -s_e[tb]) + bias[i];
+            const float l = ldexpf(r0[o] + r1[o], -s_e[tb]) + (nh ? bias1 : bias0);
             act = l > theta;
             if (logits) logits[(size_t)tb * F + i] = l;
         }
         const unsigned long long bal = __ballot(act);
+        uor[nh] |= bal;
         const int w0 = (n0 + nh * 64) >> 5;
         if (lane == 0 && tb < B) {
             if (w0 < W) mask[(size_t)tb * W + w0] = (uint32_t)bal;
             if (w0 + 1 < W) mask[(size_t)tb * W + w0 + 1] = (uint32_t)(bal >> 32);
         }
+    }
+    if (umask == nullptr) return;
+    // the union over the B tokens of this block's 128 neurons: the OR of every wave's ballots
+    if (lane == 0) {
+        s_u[wave][0] = uor[0];
+        s_u[wave][1] = uor[1];
+    }
+    __syncthreads();
+    if (tid < 4) {                                   // mask word n0 / 32 + tid
+        const int nh = tid >> 1;
+        unsigned long long u = 0ull;
+#pragma unroll
+        for (int w = 0; w < PB_NW; ++w) u |= s_u[w][nh];
+        const int wd = (n0 >> 5) + tid;
+        if (wd < W) umask[wd] = (tid & 1) ? (uint32_t)(u >> 32) : (uint32_t)u;
     }
 }
 
@@ -283,7 +305,7 @@ void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
 
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
-                                hipStream_t s) {
+                                hipStream_t s, uint32_t* umask) {
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_PRED1;
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
@@ -295,7 +317,7 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
     hipLaunchKernelGGL(p.r <= ZC ? k_pb2<true> : k_pb2<false>, dim3((p.F + 127) / 128),
                        dim3(PB_NW * 64), 0, s, z, B,
                        static_cast<const uint16_t*>(p.w_p2t),
-                       p.bias, p.r, p.F, theta, logits, mask);
+                       p.bias, p.r, p.F, theta, logits, mask, umask);
     return hipGetLastError();
 }
 

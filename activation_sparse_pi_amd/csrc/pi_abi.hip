@@ -110,6 +110,95 @@ size_t ffn_bytes(const pi_ffn_desc& f, int B) {
     return p.bytes;
 }
 
+// The region every call shares (each plan starts its own layout at COUNTER_BYTES; the calls run
+// one after another on a stream), for batches of 1 .. B_max tokens.  0 on invalid descriptors.
+size_t ws_base(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
+    size_t need = COUNTER_BYTES;
+    if (pred) {
+        if (check_pred(pred) != PI_OK) return 0;
+        for (int B = 1; B <= B_max; ++B) {
+            const size_t b = plan_pred(pred->d, pred->r, pred->F, B).bytes;
+            if (b > need) need = b;
+        }
+    }
+    if (ffn) {
+        if (check_ffn(ffn, 1) != PI_OK) return 0;
+        for (int B = 1; B <= B_max; ++B) {
+            const size_t b = ffn_bytes(*ffn, B);
+            if (b > need) need = b;
+        }
+    }
+    if (pred && ffn && pred->d == ffn->d && pred->F == ffn->F) {
+        size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
+        if (b > need) need = b;
+        b = plan_run(pred->d, pred->r, pred->F, ffn->wfmt, 512).bytes;   // independent of the grid
+        if (b > need) need = b;
+    }
+    return need;
+}
+
+// pi_batch_run's union path keeps the batch's union mask, list and count past the shared region
+// (they live from the predictor's launch to the union FFN's, which uses that region)
+struct BatchWs {
+    size_t off_umask, off_uidx, off_ucount, bytes;
+};
+BatchWs batch_ws(size_t base, int F) {
+    BatchWs w{};
+    w.off_umask = align_up(base, 256);
+    w.off_uidx = align_up(w.off_umask + (size_t)((F + 31) / 32) * 4, 256);
+    w.off_ucount = align_up(w.off_uidx + (size_t)F * 4, 256);
+    w.bytes = w.off_ucount + 256;
+    return w;
+}
+
+// The batch-size dispatch estimate (pi_batch_plan).  The fixed costs and bandwidth fractions are
+// fitted to this library's own measurements on MI355X (one FFN layer of d = 8192, F = 32768, fp16,
+// ReLU, 8% of the neurons per token, B = 1 .. 32): the batch-1 operators move a token's rows at
+// ~40% of peak after ~4 us of launches and ramps; the union path (compaction + two MFMA kernels)
+// moves the union's rows at ~63% after ~15 us.  B > 32 runs as union passes of at most 32 tokens.
+constexpr double BATCH_TOK_FIXED_US = 4.0, BATCH_TOK_EFF = 0.40;
+constexpr double BATCH_UNION_FIXED_US = 15.0, BATCH_UNION_EFF = 0.63;
+
+int batch_groups(int B) { return (B + PI_MAX_BATCH - 1) / PI_MAX_BATCH; }
+// size of group g of B tokens split into batch_groups(B) near-equal groups
+int group_size(int B, int g) {
+    const int G = batch_groups(B);
+    return B / G + (g < B % G ? 1 : 0);
+}
+
+int batch_plan_impl(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_gbs,
+                    pi_batch_plan_t* plan) {
+    int st;
+    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
+    if (!rate || !plan) return fail(PI_ERR_NULL, "rate / plan NULL");
+    if (B < 1 || B > PI_MAX_BATCH_RUN) return fail(PI_ERR_SHAPE, "batch %d outside 1..%d", B, PI_MAX_BATCH_RUN);
+    if (!(hbm_gbs > 0.0)) return fail(PI_ERR_SHAPE, "hbm_gbs must be positive, got %g", hbm_gbs);
+    const int G = batch_groups(B);
+    double n = 0.0, ug[2] = {0.0, 0.0};
+    const int b0 = group_size(B, 0), b1 = G > 1 ? group_size(B, 1) : 0;
+    for (int i = 0; i < ffn->F; ++i) {
+        const double p = rate[i];
+        if (!(p >= 0.0 && p <= 1.0)) return fail(PI_ERR_SHAPE, "rate[%d] = %g outside [0, 1]", i, p);
+        n += p;
+        ug[0] += 1.0 - std::pow(1.0 - p, (double)b0);
+        if (G > 1) ug[1] += 1.0 - std::pow(1.0 - p, (double)b1);
+    }
+    const int m = ffn->act == PI_ACT_REGLU ? 3 : 2;
+    const double w = ffn->wfmt == PI_W_F16 ? 2.0 : 0.5 + 2.0 / 128.0;
+    const double row = (double)m * ffn->d * w;                    // bytes per listed neuron
+    const double bw = hbm_gbs * 1e3;                               // bytes per us
+    plan->n_mean = n;
+    plan->u_mean = G > 1 ? (ug[0] + ug[1]) * 0.5 : ug[0];
+    plan->t_tokens_us = B * (BATCH_TOK_FIXED_US + n * row / (BATCH_TOK_EFF * bw));
+    const bool union_ok = B > 1 && ffn->wfmt == PI_W_F16;
+    double tu = 0.0;
+    for (int g = 0; g < G; ++g)
+        tu += BATCH_UNION_FIXED_US + ug[g == 0 ? 0 : 1] * row / (BATCH_UNION_EFF * bw);
+    plan->t_union_us = union_ok ? tu : HUGE_VAL;
+    plan->choice = plan->t_union_us < plan->t_tokens_us ? PI_BATCH_UNION : PI_BATCH_TOKENS;
+    return ok();
+}
+
 // ---- scratch of pi_decode_run_noalloc -------------------------------------------------------
 // The one entry point that allocates nothing keeps its scratch (z, h, the partial rows) in this
 // file-scope device array: PI_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held until
@@ -170,28 +259,11 @@ int pi_version(void) { return 100; }
 
 size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
     if (B_max < 1 || B_max > PI_MAX_BATCH) return 0;
-    size_t need = COUNTER_BYTES;
-    if (pred) {
-        if (check_pred(pred) != PI_OK) return 0;
-        for (int B = 1; B <= B_max; ++B) {
-            const size_t b = plan_pred(pred->d, pred->r, pred->F, B).bytes;
-            if (b > need) need = b;
-        }
-    }
-    if (ffn) {
-        if (check_ffn(ffn, 1) != PI_OK) return 0;
-        for (int B = 1; B <= B_max; ++B) {
-            const size_t b = ffn_bytes(*ffn, B);
-            if (b > need) need = b;
-        }
-    }
-    if (pred && ffn && pred->d == ffn->d && pred->F == ffn->F) {
-        size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
-        if (b > need) need = b;
-        b = plan_run(pred->d, pred->r, pred->F, ffn->wfmt, 512).bytes;   // independent of the grid
-        if (b > need) need = b;
-    }
-    return need;
+    const size_t base = ws_base(pred, ffn, B_max);
+    if (base == 0) return 0;
+    // with both descriptors and B_max > 1: also pi_batch_run's union mask, list and count
+    if (pred && ffn && B_max > 1 && pred->F == ffn->F) return batch_ws(base, ffn->F).bytes;
+    return base;
 }
 
 int pi_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -515,40 +587,107 @@ int pi_place_neurons(const int32_t* counts, int F, int32_t* perm) {
     return ok();
 }
 
-// Batch-size dispatch.  The fixed costs and bandwidth fractions are fitted to this library's
-// own measurements on MI355X (one FFN layer of d = 8192, F = 32768, fp16, ReLU, 8% of the
-// neurons per token, B = 1 .. 32): the batch-1 operators move a token's rows at ~40% of peak
-// after ~4 us of launches and ramps; the union path (compaction + two MFMA kernels) moves
-// the union's rows at ~63% after ~15 us.
-namespace {
-constexpr double BATCH_TOK_FIXED_US = 4.0, BATCH_TOK_EFF = 0.40;
-constexpr double BATCH_UNION_FIXED_US = 15.0, BATCH_UNION_EFF = 0.63;
-}  // namespace
-
 int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_gbs,
                   pi_batch_plan_t* plan) {
+    return batch_plan_impl(ffn, B, rate, hbm_gbs, plan);
+}
+
+int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                 int T, int B, long long s0, int nsteps, int schedule, const float* rate,
+                 double hbm_gbs, uint32_t* mask, float* y, void* const* events, void* ws,
+                 size_t ws_bytes, void* stream) {
     int st;
-    if ((st = check_ffn(ffn, 1)) != PI_OK) return st;
-    if (!rate || !plan) return fail(PI_ERR_NULL, "rate / plan NULL");
-    if ((st = check_batch(B)) != PI_OK) return st;
-    if (!(hbm_gbs > 0.0)) return fail(PI_ERR_SHAPE, "hbm_gbs must be positive, got %g", hbm_gbs);
-    double n = 0.0, u = 0.0;
-    for (int i = 0; i < ffn->F; ++i) {
-        const double p = rate[i];
-        if (!(p >= 0.0 && p <= 1.0)) return fail(PI_ERR_SHAPE, "rate[%d] = %g outside [0, 1]", i, p);
-        n += p;
-        u += 1.0 - std::pow(1.0 - p, (double)B);
+    if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
+    if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
+    if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
+    if (B < 1 || B > PI_MAX_BATCH_RUN) return fail(PI_ERR_SHAPE, "batch %d outside 1..%d", B, PI_MAX_BATCH_RUN);
+    if (schedule != PI_BATCH_TOKENS && schedule != PI_BATCH_UNION && schedule != PI_BATCH_AUTO)
+        return fail(PI_ERR_DTYPE, "unknown batch schedule %d", schedule);
+    if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
+    if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
+    for (int i = 0; i < nrep; ++i) {
+        if ((st = check_pred(&preds[i])) != PI_OK) return st;
+        if ((st = check_ffn(&ffns[i], 1)) != PI_OK) return st;
+        if (preds[i].d != ffns[i].d || preds[i].F != ffns[i].F || preds[i].d != preds[0].d ||
+            preds[i].F != preds[0].F || preds[i].r != preds[0].r || ffns[i].act != ffns[0].act ||
+            ffns[i].wfmt != ffns[0].wfmt || preds[i].threshold != preds[0].threshold ||
+            preds[i].pfmt != preds[0].pfmt || ffns[i].nhot != ffns[0].nhot)
+            return fail(PI_ERR_SHAPE, "replica %d does not match replica 0 / its ffn", i);
     }
-    const int m = ffn->act == PI_ACT_REGLU ? 3 : 2;
-    const double w = ffn->wfmt == PI_W_F16 ? 2.0 : 0.5 + 2.0 / 128.0;
-    const double row = (double)m * ffn->d * w;                    // bytes per listed neuron
-    const double bw = hbm_gbs * 1e3;                               // bytes per us
-    plan->n_mean = n;
-    plan->u_mean = u;
-    plan->t_tokens_us = B * (BATCH_TOK_FIXED_US + n * row / (BATCH_TOK_EFF * bw));
-    const bool union_ok = B > 1 && ffn->wfmt == PI_W_F16;
-    plan->t_union_us = union_ok ? BATCH_UNION_FIXED_US + u * row / (BATCH_UNION_EFF * bw) : HUGE_VAL;
-    plan->choice = plan->t_union_us < plan->t_tokens_us ? PI_BATCH_UNION : PI_BATCH_TOKENS;
+    if (events && (!events[0] || !events[1])) return fail(PI_ERR_NULL, "events must hold two events");
+    const int d = preds[0].d, r = preds[0].r, F = preds[0].F, W = (F + 31) / 32;
+    int sched = schedule;
+    if (sched == PI_BATCH_AUTO) {
+        if (!rate) return fail(PI_ERR_NULL, "PI_BATCH_AUTO needs the activation rates");
+        pi_batch_plan_t pl{};
+        if ((st = batch_plan_impl(&ffns[0], B, rate, hbm_gbs, &pl)) != PI_OK) return st;
+        // the token schedule also runs the predictor once per token, the union schedule once per
+        // pass: its bytes (2 d r + 2 r F, fp16) at each schedule's bandwidth fraction
+        const double pb = 2.0 * d * r + 2.0 * r * F, bw = hbm_gbs * 1e3;
+        const double tt = pl.t_tokens_us + B * pb / (BATCH_TOK_EFF * bw);
+        const double tu = pl.t_union_us + batch_groups(B) * pb / (BATCH_UNION_EFF * bw);
+        sched = tu < tt ? PI_BATCH_UNION : PI_BATCH_TOKENS;
+    }
+    if (sched == PI_BATCH_UNION && B == 1) sched = PI_BATCH_TOKENS;     // nothing to unite
+    if (sched == PI_BATCH_UNION) {
+        if (ffns[0].wfmt != PI_W_F16 || preds[0].pfmt != PI_P_F16)
+            return fail(PI_ERR_UNSUPPORTED, "the union schedule takes fp16 weights and an fp16 predictor");
+        if ((size_t)r * d * 2 > (size_t)INT_MAX)
+            return fail(PI_ERR_UNSUPPORTED, "the batch predictor needs r * d * 2 < 2^31 bytes");
+    }
+    const int Gmax = sched == PI_BATCH_UNION ? group_size(B, 0) : 1;   // the largest group
+    const size_t base = ws_base(&preds[0], &ffns[0], Gmax);
+    const BatchWs bw = batch_ws(base, F);
+    const size_t need = sched == PI_BATCH_UNION ? bw.bytes : base;
+    if ((st = check_ws(ws, ws_bytes, need)) != PI_OK) return st;
+    const DecPlan dpl = plan_decode(d, r, F, ffns[0].wfmt);
+    const bool fused = ffns[0].nhot == 0 && dpl.fused_default;
+    const double tau = preds[0].threshold;
+    const float theta = (float)std::log(tau / (1.0 - tau));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    uint32_t* umask = reinterpret_cast<uint32_t*>(w + bw.off_umask);
+    int32_t* uidx = reinterpret_cast<int32_t*>(w + bw.off_uidx);
+    int32_t* ucount = reinterpret_cast<int32_t*>(w + bw.off_ucount);
+    hipError_t e;
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+        return hip_fail(e, "pi_batch_run start event");
+    for (int i = 0; i < nsteps; ++i) {
+        const long long g = s0 + i;
+        const int rep = (int)(g % nrep);
+        const uint16_t* xs = x + (size_t)(g % T) * B * d;
+        const pi_pred_desc& P = preds[rep];
+        const pi_ffn_desc& Fd = ffns[rep];
+        if (sched == PI_BATCH_TOKENS) {
+            // every token through the batch-1 kernel schedule; a token's first kernel sums the
+            // previous token's partial rows into that token's row of y
+            for (int b = 0; b < B; ++b) {
+                const bool first = i == 0 && b == 0;
+                float* yprev = y + (size_t)(b == 0 ? B - 1 : b - 1) * d;
+                e = launch_decode_step(P, Fd, dpl, fused, xs + (size_t)b * d, theta, nullptr,
+                                       mask + (size_t)b * W, yprev, !first, w, s, nullptr, nullptr);
+                if (e != hipSuccess) return hip_fail(e, "pi_batch_run token step");
+            }
+        } else {
+            for (int gi = 0, b0 = 0; gi < batch_groups(B); b0 += group_size(B, gi), ++gi) {
+                const int Bg = group_size(B, gi);
+                const PredPlan ppl = plan_pred(d, r, F, Bg);
+                const FfnPlan fpl = plan_ffn(d, F, Fd.wfmt, Bg);
+                if ((e = launch_predict_batch(P, ppl, xs + (size_t)b0 * d, Bg, theta, nullptr,
+                                              mask + (size_t)b0 * W, w, s, umask)) != hipSuccess ||
+                    (e = launch_compact(umask, 1, F, PI_PER_TOKEN, uidx, ucount, s)) != hipSuccess ||
+                    (e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, uidx, ucount,
+                                          mask + (size_t)b0 * W, y + (size_t)b0 * d, w, s)) != hipSuccess)
+                    return hip_fail(e, "pi_batch_run union pass");
+            }
+        }
+    }
+    if (sched == PI_BATCH_TOKENS && nsteps > 0 &&
+        (e = launch_decode_finish(dpl, fused, ffns[0].nhot, d, F, mask + (size_t)(B - 1) * W, nullptr,
+                                  nullptr, y + (size_t)(B - 1) * d, w, s)) != hipSuccess)
+        return hip_fail(e, "pi_batch_run final y");
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
+        return hip_fail(e, "pi_batch_run end event");
     return ok();
 }
 

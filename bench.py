@@ -253,8 +253,11 @@ def cpu_baseline_batch(inputs, budget_s):
 
 
 def bench_batch(a, cfg):
-    """Small-batch decode: one step = pi_predict(B, masks only) -> pi_compact(UNION) ->
-    pi_sparse_ffn(B) over one batch of B independent tokens (the union FFN runs on MFMA)."""
+    """Small-batch decode: one step = the B independent tokens of one batch through the union
+    schedule of pi_batch_run (batch predictor with per-token masks and their union, the union's
+    neuron table, the union FFN on MFMA where every token gets only its own neurons).  The K
+    timed steps are one pi_batch_run call.  The roofline pass times the union FFN pair alone,
+    through the operators (pi_predict, pi_compact, pi_sparse_ffn), events around pi_sparse_ffn."""
     import torch
 
     from activation_sparse_pi_amd.layer import DeviceLayer
@@ -290,21 +293,33 @@ def bench_batch(a, cfg):
         if ev is not None:
             ev[1].record()
 
-    for s in range(Wm):
+    from activation_sparse_pi_amd import _lib as L
+    mask_r = torch.empty((B, (cfg.F + 31) // 32), dtype=torch.int32, device=dev)
+    y_r = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+    layer.batch_run(xd.data_ptr(), T, B, 0, Wm, mask_r.data_ptr(), y_r.data_ptr(),
+                    schedule=L.PI_BATCH_UNION)                                   # untimed warmup
+    t01 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in t01:
+        e.record()
+    torch.cuda.synchronize()
+    layer.batch_run(xd.data_ptr(), T, B, Wm, K, mask_r.data_ptr(), y_r.data_ptr(),
+                    schedule=L.PI_BATCH_UNION, events=t01)                       # timed: K steps
+    torch.cuda.synchronize()
+    total_ms = t01[0].elapsed_time(t01[1])
+    # roofline pass: the union FFN pair alone, events around pi_sparse_ffn
+    Kr = min(K, 128)
+    for s in range(8):
         step(s)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+          for _ in range(Kr)]
     torch.cuda.synchronize()
-    t0.record()
-    for s in range(K):
-        step(Wm + s, ev[s])
-    t1.record()
+    for s in range(Kr):
+        step(Wm + K + s, ev[s])
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
     ffn_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
     steps = (Wm + np.arange(K)) % T
-    ffn_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["ffn"] for t in steps]))
+    rsteps = (Wm + K + np.arange(Kr)) % T
+    ffn_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["ffn"] for t in rsteps]))
     path_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["total"] for t in steps]))
     ms_per_step = total_ms / K
     achieved = ffn_bytes / (float(ffn_ms.mean()) * 1e-3) / 1e9
@@ -326,7 +341,8 @@ def bench_batch(a, cfg):
             "batch": B, "d": cfg.d, "ffn": cfg.F, "rank": cfg.r, "replicas": R,
             "mean_active_per_token": round(float(n_tok.mean()), 1),
             "mean_union": round(float(U.mean()), 1),
-            "launch": "three ABI calls per step from Python (pi_predict, pi_compact, pi_sparse_ffn)",
+            "launch": "one pi_batch_run call, union schedule: per step the batch predictor (per-token "
+                      "masks and their union), the union's neuron table and the union FFN on MFMA",
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_step": round(path_bytes)},
@@ -337,7 +353,7 @@ def bench_batch(a, cfg):
             "traffic": traffic_from_profiles(kernel_key),
             "avg_us": round(float(ffn_ms.mean()) * 1e3, 3),
             "bytes_per_launch": round(ffn_bytes),
-            "mfma_tflops": round((3 if cfg.act == "reglu" else 2) * 2 * B * U[steps].mean() * cfg.d
+            "mfma_tflops": round((3 if cfg.act == "reglu" else 2) * 2 * B * U[rsteps].mean() * cfg.d
                                  / (float(ffn_ms.mean()) * 1e-3) / 1e12, 1),
         },
     }

@@ -59,7 +59,8 @@ extern "C" {
 #define PI_PER_TOKEN  0   /* pi_compact: one index list per token                     */
 #define PI_UNION      1   /* pi_compact: one list of the OR of the B token masks      */
 
-#define PI_MAX_BATCH  32
+#define PI_MAX_BATCH  32        /* tokens of one union pass (pi_predict / pi_sparse_ffn at B > 1) */
+#define PI_MAX_BATCH_RUN 64     /* tokens per step of pi_batch_run and pi_batch_plan            */
 #define PI_MAX_D_F16  8192    /* largest d of the fp16 batch-1 kernels                */
 #define PI_MAX_D_I4   16384   /* largest d of the int4 batch-1 kernels                */
 
@@ -363,12 +364,15 @@ int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int
  *   n = sum_i rate[i],   U = sum_i (1 - (1 - rate[i])^B).
  * Each schedule's time is a fixed cost per step or per token (its kernel launches) plus its
  * bytes over its measured fraction of hbm_gbs (figures measured on MI355X, stated with the
- * implementation).  B = 1 and int4 weights (no union path) give PI_BATCH_TOKENS.
+ * implementation).  B = 1 and int4 weights (no union path) give PI_BATCH_TOKENS.  More than
+ * PI_MAX_BATCH tokens run as ceil(B / 32) union passes of near-equal size (e.g. 64 = 32 + 32,
+ * 33 = 17 + 16), each priced on its own group's union; u_mean is then the mean union of a pass.
  * Host only, no HIP call.  rate: host float [F], each in [0, 1].  Errors: PI_ERR_NULL,
- * PI_ERR_SHAPE (B outside 1..PI_MAX_BATCH, a rate outside [0, 1], hbm_gbs <= 0), and the
+ * PI_ERR_SHAPE (B outside 1..PI_MAX_BATCH_RUN, a rate outside [0, 1], hbm_gbs <= 0), and the
  * descriptor checks of pi_sparse_ffn; *plan untouched on error.                             */
 #define PI_BATCH_TOKENS 0
 #define PI_BATCH_UNION  1
+#define PI_BATCH_AUTO   2   /* pi_batch_run: the cheaper of the two, estimated as below      */
 typedef struct {
     double n_mean;       /* expected active neurons per token                    */
     double u_mean;       /* expected size of the union of B tokens' lists        */
@@ -378,6 +382,32 @@ typedef struct {
 } pi_batch_plan_t;
 int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_gbs,
                   pi_batch_plan_t* plan);
+
+/* ---- pi_batch_run: native small-batch decode executor ----------------------------------------
+ * The client-inference page's planning step (a schedule per number of tokens, chosen by a roofline
+ * estimate) executed inside the library, around PowerInfer's online engine.  Enqueues nsteps
+ * steps on `stream`; step i decodes the B tokens x[(s0 + i) % T] (x fp16 [T, B, d]) through the
+ * layer of replica (s0 + i) % nrep (as pi_decode_run), every token with its own predicted
+ * neurons, in one of two schedules:
+ *   PI_BATCH_TOKENS: every token through pi_decode_run's kernel schedule, one after another;
+ *   PI_BATCH_UNION:  ceil(B / 32) passes of near-equal groups, each the batch predictor (per-token
+ *                    masks, and their union), the union's neuron table, and the union FFN on MFMA
+ *                    where each token only receives the neurons of its own mask (fp16 weights and
+ *                    predictor; B = 1 runs PI_BATCH_TOKENS);
+ *   PI_BATCH_AUTO:   the cheaper of the two by pi_batch_plan's estimate from rate (host float [F],
+ *                    activation rates of a profile) and hbm_gbs, with the predictor's bytes
+ *                    (2 d r + 2 r F) added once per token to the first and once per pass to the
+ *                    second.
+ * 1 <= B <= PI_MAX_BATCH_RUN.  mask u32 [B, ceil(F/32)] and y fp32 [B, d] hold the last step's
+ * per-token masks and outputs.  events: NULL or 2 hipEvent_t recorded around the enqueued work.
+ * Workspace: pi_workspace_bytes(pred, ffn, min(B, 32)) with both descriptors given (B_max > 1
+ * includes the union list), zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN,
+ * PI_ERR_DTYPE (schedule), PI_ERR_UNSUPPORTED (the union schedule on int4 weights or an int8
+ * predictor), PI_ERR_WORKSPACE, PI_ERR_HIP; all but the last before any HIP call.           */
+int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
+                 int T, int B, long long s0, int nsteps, int schedule, const float* rate,
+                 double hbm_gbs, uint32_t* mask, float* y, void* const* events, void* ws,
+                 size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -178,3 +178,35 @@ def test_decode_run_noalloc_validation():
     assert _run_noalloc(pred(), ffn(), L.PI_RUN_PERSISTENT) == L.PI_ERR_UNSUPPORTED
     assert _run_noalloc(pred(d=1001), ffn(), L.PI_RUN_KERNELS) == L.PI_ERR_SHAPE
     assert _run_noalloc(pred(), ffn(), 17) == L.PI_ERR_DTYPE
+
+
+
+def _batch_run(p, f, B=4, schedule=L.PI_BATCH_UNION, ws=WS, wsb=WSB, rate=None, **kw):
+    preds = (L.PredDesc * 1)(p)
+    ffns = (L.FfnDesc * 1)(f)
+    a = dict(x=A + 0x3000000, mask=A + 0x4000000, y=A + 0x7000000)
+    a.update(kw)
+    return L.pi_batch_run(preds, ffns, 1, a["x"], 4, B, 0, 2, schedule, rate, 8000.0, a["mask"],
+                          a["y"], None, ws, wsb, None)
+
+
+def test_batch_run_validation():
+    """pi_batch_run rejects bad arguments before any HIP call: batch range, schedule enum,
+    missing rates for the automatic choice, int4 weights on the union schedule, alignment and
+    the workspace."""
+    import numpy as np
+    assert _batch_run(pred(), ffn(), B=0) == L.PI_ERR_SHAPE
+    assert _batch_run(pred(), ffn(), B=65) == L.PI_ERR_SHAPE
+    assert _batch_run(pred(), ffn(), schedule=9) == L.PI_ERR_DTYPE
+    assert _batch_run(pred(), ffn(), schedule=L.PI_BATCH_AUTO) == L.PI_ERR_NULL
+    i4 = ffn(wfmt=L.PI_W_I4G128, s_up=A, s_down=A)
+    assert _batch_run(pred(), i4, schedule=L.PI_BATCH_UNION) == L.PI_ERR_UNSUPPORTED
+    assert _batch_run(pred(), ffn(), x=A + 2) == L.PI_ERR_ALIGN
+    assert _batch_run(pred(), ffn(), mask=None) == L.PI_ERR_NULL
+    assert _batch_run(pred(), ffn(), ws=None) == L.PI_ERR_WORKSPACE
+    need = L.pi_workspace_bytes(pred(), ffn(), 32)
+    assert need > L.pi_workspace_bytes(pred(), None, 32)
+    assert _batch_run(pred(), ffn(), B=64, wsb=need - 256) == L.PI_ERR_WORKSPACE
+    rate = np.full(4096, 0.1, np.float32)
+    assert _batch_run(pred(), ffn(), schedule=L.PI_BATCH_AUTO, rate=rate.ctypes.data, ws=None) == \
+        L.PI_ERR_WORKSPACE

@@ -87,7 +87,7 @@ def test_token_time_is_linear_in_batch():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), L.PI_ERR_SHAPE),
-    (dict(B=33), L.PI_ERR_SHAPE),
+    (dict(B=65), L.PI_ERR_SHAPE),
     (dict(hbm=0.0), L.PI_ERR_SHAPE),
     (dict(bad=1.5), L.PI_ERR_SHAPE),
     (dict(bad=float("nan")), L.PI_ERR_SHAPE),
@@ -123,3 +123,20 @@ def test_bytes_per_row_follow_matrices_and_format():
     assert tok(glu) / tok(base) == pytest.approx(1.5, rel=1e-6)
     assert uni(glu) / uni(base) == pytest.approx(1.5, rel=1e-6)
     assert tok(i4) / tok(base) == pytest.approx((0.5 + 2 / 128) / 2, rel=1e-6)
+
+
+def test_more_than_32_tokens_run_as_union_passes():
+    """B > 32 is priced as ceil(B / 32) union passes of near-equal groups: 64 tokens as two
+    passes of 32 (twice the 32-token union estimate), 33 as 17 + 16 (u_mean the mean of the two
+    groups' expected unions); the token path stays linear in B."""
+    F = 4096
+    rate = np.clip(np.random.default_rng(5).gamma(0.5, 0.1, F), 0, 1).astype(np.float32)
+    r64 = rate.astype(np.float64)
+    eu = lambda b: float(np.sum(1.0 - (1.0 - r64) ** b))          # noqa: E731
+    p32, p64 = plan(rate, 32), plan(rate, 64)
+    assert p64.u_mean == pytest.approx(eu(32), rel=1e-9)
+    assert p64.t_union_us == pytest.approx(2 * p32.t_union_us, rel=1e-9)
+    assert p64.t_tokens_us == pytest.approx(2 * p32.t_tokens_us, rel=1e-9)
+    p33, p17, p16 = plan(rate, 33), plan(rate, 17), plan(rate, 16)
+    assert p33.u_mean == pytest.approx(0.5 * (eu(17) + eu(16)), rel=1e-9)
+    assert p33.t_union_us == pytest.approx(p17.t_union_us + p16.t_union_us, rel=1e-9)
