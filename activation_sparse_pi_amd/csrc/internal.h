@@ -145,7 +145,8 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
 // (optional, ceil(F/32) words): the OR of the B tokens' masks
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
-                                hipStream_t s, uint32_t* umask = nullptr);
+                                hipStream_t s, uint32_t* umask = nullptr,
+                                uint32_t* tokbits = nullptr);
 
 // part / y (batch-1 decode executor only): also sum the previous step's P partial rows of d
 // floats into y (reduce_partials)
@@ -169,10 +170,13 @@ hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t
                           const int32_t* count, int dense_F, const float* h, float* y, char* ws,
                           hipStream_t s);
 
-// 1 < B <= 32 union-mask path on MFMA
+// 1 < B <= 32 union-mask path on MFMA.  With umask == nullptr the union list idx[0 .. *count)
+// is read; otherwise the list is built from the union mask umask and written to idx / count,
+// and tokbits[F] (per neuron, bit b: in token b's mask) stands in for the token masks.
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
-                            const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
-                            float* y, char* ws, hipStream_t s);
+                            const uint32_t* umask, const uint32_t* tokbits, int32_t* idx,
+                            int32_t* count, const uint32_t* token_mask, float* y, char* ws,
+                            hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* perm, int n,

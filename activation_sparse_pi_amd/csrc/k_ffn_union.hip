@@ -12,11 +12,15 @@
 // that neither the staging writes nor the operand reads conflict).  No block barrier
 // sits in either streaming loop: each wave stages and consumes its own data.
 //
-//   up    one block per 32-neuron tile of the union list; its 8 waves split d in runs
-//         of 64 elements.  Per run a wave stages the tile's 32 rows x 128 bytes of
-//         W_up (and W_gate) and the 32 tokens' x, then issues 4 (8) MFMAs.  The waves
-//         meet in LDS; h = act(.) * [neuron in token b's mask] is rounded to fp16 and
-//         written in the down kernel's A-operand order ("H fragments": for each group
+//   up    one block per 32-neuron tile of the union list; its 8 waves split d in runs of 64
+//         elements.  The tile's ids come from the union list, or straight from the union mask
+//         (a block-wide scan of its words' popcounts locates the tile's 32 positions, which
+//         the block writes to the list for the down kernel).  Per token a keep word (bit n:
+//         position n of the tile is in that token's mask) comes from the per-neuron token
+//         words (loaded with the first rows, transposed after streaming) or, for a given list,
+//         from the token masks before streaming.  Per run a wave stages the tile's 32 rows x
+//         128 bytes of W_up (and W_gate) and the 32 tokens' x, then issues 4 (8) MFMAs.  The
+//         waves meet in LDS; h = act(.) * keep is rounded to fp16 and written in the down kernel's A-operand order ("H fragments": for each group
 //         of 16 union positions, 64 lanes x 16 bytes, lane l holding positions
 //         8 (l / 32) .. + 7 of token l % 32), so that operand is one 1 KB load.
 //   down  y[b, :] = sum_k H[b, k] W_down[u_k, :].  Block = 256 columns (512 contiguous
@@ -38,12 +42,54 @@ namespace pi {
 namespace {
 
 constexpr int UP_NW = 8;      // waves per up block
+constexpr int UP_NT = UP_NW * 64;
 constexpr int DN_NWU = 4;     // waves per down block (one per SIMD)
 constexpr int DN_COLS = 256;  // columns per down block
 constexpr int DN_TILES = DN_COLS / 32;   // 32-column MFMA tiles per down block
 
-PI_DEV bool bit_of(const uint32_t* __restrict__ mask, int W, int b, int i) {
-    return (mask[(size_t)b * W + (i >> 5)] >> (i & 31)) & 1u;
+// The ids at union positions lo .. lo + 31 from the union mask, whose set bits among the first
+// F are the union in ascending order: every thread takes runs of 4 consecutive words and an
+// exclusive scan of the runs' popcounts gives each run its first position; then each wave walks
+// its runs that hold positions of the tile (usually a handful), one word at a time with one
+// lane per bit, and writes those ids to s_ids.  Returns the union's size U (block-uniform).
+// s_tmp: UP_NW + 1 ints.
+PI_DEV int tile_ids_from_mask(const uint32_t* __restrict__ umask, int F, int lo, int* s_ids,
+                              int* s_tmp) {
+    const int W = (F + 31) >> 5, hi = lo + 32, lane = threadIdx.x & 63;
+    int base = 0;
+    for (int c0 = 0; c0 < W; c0 += 4 * UP_NT) {
+        const int w0 = c0 + 4 * (int)threadIdx.x;
+        uint32_t v[4];
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int w = w0 + k;
+            uint32_t m = w < W ? umask[w] : 0u;
+            if (w == W - 1 && (F & 31)) m &= (1u << (F & 31)) - 1u;       // bits past F
+            v[k] = m;
+            cnt += __popc(m);
+        }
+        int total;
+        const int pos = base + block_exclusive_scan(cnt, s_tmp, &total);
+        unsigned long long hit = __ballot(pos < hi && pos + cnt > lo);
+        while (hit) {                                 // wave-uniform
+            const int j = __builtin_ctzll(hit);
+            hit &= hit - 1ull;
+            int r = __builtin_amdgcn_readlane(pos, j);
+            const int wj = __builtin_amdgcn_readlane(w0, j);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t vk = (uint32_t)__builtin_amdgcn_readlane((int)v[k], j);
+                if (lane < 32 && ((vk >> lane) & 1u)) {
+                    const int rank = r + __popc(vk & ((1u << lane) - 1u));
+                    if (rank >= lo && rank < hi) s_ids[rank - lo] = ((wj + k) << 5) + lane;
+                }
+                r += __popc(vk);
+            }
+        }
+        base += total;
+    }
+    return base;
 }
 
 PI_DEV uint32_t pack_h2(float lo, float hi) {
@@ -52,28 +98,70 @@ PI_DEV uint32_t pack_h2(float lo, float hi) {
 }
 
 // ------------------------------------------------------------------------------------ up
-// ReLU with 32-bit offsets fits 128 registers: two blocks per CU
-template <bool GLU, bool OFF32>
-__global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
+// ReLU with 32-bit offsets fits 128 registers: two blocks per CU (ReGLU: one).
+// FROM_MASK: the tile's ids come from the union mask umask and are written to uidx[32 tile ..]
+// (block 0 writes U to *ucount), the keep words from the token words tokbits[F]; otherwise the
+// ids are read from the union list uidx[0 .. *ucount) and the keep words from the token masks
+// tmask [B, ceil(F / 32)].
+template <bool GLU, bool OFF32, bool FROM_MASK>
+__global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
     const uint16_t* __restrict__ x, int B, const uint16_t* __restrict__ Wg,
-    const uint16_t* __restrict__ Wu, int d, int F, const int32_t* __restrict__ uidx,
-    const int32_t* __restrict__ ucount, const uint32_t* __restrict__ tmask,
-    uint4* __restrict__ Hf) {
+    const uint16_t* __restrict__ Wu, int d, int F, const uint32_t* __restrict__ umask,
+    const uint32_t* __restrict__ tokbits, int32_t* __restrict__ uidx, int32_t* __restrict__ ucount,
+    const uint32_t* __restrict__ tmask, uint4* __restrict__ Hf) {
     constexpr int NM = GLU ? 2 : 1;                   // weight matrices: up [, gate]
     __shared__ uint4 s_st[UP_NW][NM + 1][32][8];      // per wave: x, up [, gate] staging
+    __shared__ int s_ids[32];                         // the tile's neuron ids, -1 past the union
+    __shared__ uint32_t s_keep[32];                   // per token: bit n = position n in its mask
+    __shared__ int s_tmp[UP_NW + 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int U = min(*ucount, F);
-    const int tile = blockIdx.x;
-    if (tile * 32 >= U) return;                       // whole block: past the union
+    const int tile = blockIdx.x, lo = tile * 32;
+    if (tid < 32) s_ids[tid] = -1;
+    uint32_t tok = 0u;             // FROM_MASK, wave 0 lane n < 32: token word of position n
+    if constexpr (FROM_MASK) {
+        const int U = tile_ids_from_mask(umask, F, lo, s_ids, s_tmp);   // its barriers order the -1s
+        if (tile == 0 && tid == 0) *ucount = U;       // also when the union is empty
+        if (lo >= U) return;                          // whole block: past the union
+        __syncthreads();
+        if (tid < 32) {
+            const int id = s_ids[tid];
+            if (lo + tid < U) uidx[lo + tid] = id;
+            tok = (unsigned)id < (unsigned)F ? tokbits[id] : 0u;        // used after streaming
+        }
+    } else {
+        const int U = min(*ucount, F);
+        if (lo >= U) return;
+        if (tid < 32 && lo + tid < U) s_ids[tid] = uidx[lo + tid];
+        __syncthreads();
+        // keep words from the token masks: pair p = (token p / 32, position p % 32), a wave's
+        // ballot covers two tokens; every load of a thread is issued before the first ballot
+        const int W = (F + 31) >> 5;
+        constexpr int NP = 1024 / UP_NT;
+        uint32_t wv[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int p = tid + k * UP_NT, b = p >> 5, id = s_ids[p & 31];
+            wv[k] = tmask[(size_t)min(b, B - 1) * W + ((unsigned)id < (unsigned)F ? id >> 5 : 0)];
+        }
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int p = tid + k * UP_NT, b = p >> 5, id = s_ids[p & 31];
+            const bool kb = b < B && (unsigned)id < (unsigned)F && ((wv[k] >> (id & 31)) & 1u);
+            const unsigned long long bal = __ballot(kb);
+            if (lane == 0) {
+                s_keep[b] = (uint32_t)bal;
+                s_keep[b + 1] = (uint32_t)(bal >> 32);
+            }
+        }
+    }
 
     // loader slot q (0..3) of a run brings row 8q + lane/8 of the tile and of x
     const int lrow = lane >> 3;
     long long offw[4], offx[4];                       // element offsets, -1 = zero row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int kp = tile * 32 + 8 * q + lrow;
-        const int row = kp < U ? uidx[kp] : -1;
+        const int row = s_ids[8 * q + lrow];
         offw[q] = (unsigned)row < (unsigned)F ? (long long)row * d : -1;
         const int tok = 8 * q + lrow;
         offx[q] = tok < B ? (long long)tok * d : -1;
@@ -111,6 +199,16 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
         runs_mfma<NM>(x, offx, Wm, offw, d, r0, r1, s_st[wave], acc);
     }
 
+    if constexpr (FROM_MASK) {
+        // keep word of token b = bit b of the 32 positions' token words (lanes 32.. hold 0)
+        if (wave == 0) {
+#pragma unroll
+            for (int b = 0; b < 32; ++b) {
+                const unsigned long long bal = __ballot((tok >> b) & 1u);
+                if (lane == 0) s_keep[b] = b < B ? (uint32_t)bal : 0u;
+            }
+        }
+    }
     // the waves meet in LDS (each wave's staging area holds its own accumulators)
     float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
 #pragma unroll
@@ -124,7 +222,7 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
         // 16 gg + 8 (fl / 32) + j.  D[n][b] sits in register (n/8)*4 + n%4 of lane
         // b + 32 ((n/4) % 2).
         const int fl = tid & 63, gg = tid >> 6, h = fl >> 5, b = fl & 31;
-        const int W = (F + 31) >> 5;
+        const uint32_t keep = s_keep[b];              // 0 for tokens past B
         float hv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -137,14 +235,8 @@ __global__ __launch_bounds__(UP_NW * 64, GLU || !OFF32 ? 2 : 4) void k_union_up(
                 a += rw[rg * 64 + ln];
                 if constexpr (GLU) g += rw[1024 + rg * 64 + ln];
             }
-            const int k = tile * 32 + gg * 16 + 8 * h + j;
-            float v = 0.f;                     // positions past U and tokens past B give 0
-            if (k < U && b < B) {
-                const int i = uidx[k];
-                if ((unsigned)i < (unsigned)F && bit_of(tmask, W, b, i))
-                    v = GLU ? fmaxf(g, 0.f) * a : fmaxf(a, 0.f);
-            }
-            hv[j] = v;
+            // positions past U, invalid ids and tokens past B have no keep bit: h = 0
+            hv[j] = (keep >> n) & 1u ? (GLU ? fmaxf(g, 0.f) * a : fmaxf(a, 0.f)) : 0.f;
         }
         Hf[(size_t)(tile * 2 + gg) * 64 + fl] =
             make_uint4(pack_h2(hv[0], hv[1]), pack_h2(hv[2], hv[3]), pack_h2(hv[4], hv[5]),
@@ -394,8 +486,9 @@ size_t plan_union(FfnPlan& p, int d, int F, size_t off) {
 }
 
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
-                            const int32_t* idx, const int32_t* count, const uint32_t* token_mask,
-                            float* y, char* ws, hipStream_t s) {
+                            const uint32_t* umask, const uint32_t* tokbits, int32_t* idx,
+                            int32_t* count, const uint32_t* token_mask, float* y, char* ws,
+                            hipStream_t s) {
     uint4* Hf = reinterpret_cast<uint4*>(ws + pl.off_H);
     const int tiles = (f.F + 31) / 32;
     const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
@@ -403,13 +496,17 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
     // 32-bit buffer offsets when every byte of a weight matrix is within 2^31
     const bool off32 = (size_t)f.F * f.d * 2 <= (size_t)INT_MAX;
     auto up = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(tiles), dim3(UP_NW * 64), 0, s, x, B, Wg, Wu, f.d, f.F, idx,
-                           count, token_mask, Hf);
+        hipLaunchKernelGGL(kern, dim3(tiles), dim3(UP_NT), 0, s, x, B, Wg, Wu, f.d, f.F, umask,
+                           tokbits, idx, count, token_mask, Hf);
     };
-    if (f.act == PI_ACT_REGLU)
-        off32 ? up(k_union_up<true, true>) : up(k_union_up<true, false>);
-    else
-        off32 ? up(k_union_up<false, true>) : up(k_union_up<false, false>);
+    const bool glu = f.act == PI_ACT_REGLU;
+    if (umask) {
+        if (glu) off32 ? up(k_union_up<true, true, true>) : up(k_union_up<true, false, true>);
+        else off32 ? up(k_union_up<false, true, true>) : up(k_union_up<false, false, true>);
+    } else {
+        if (glu) off32 ? up(k_union_up<true, true, false>) : up(k_union_up<true, false, false>);
+        else off32 ? up(k_union_up<false, true, false>) : up(k_union_up<false, false, false>);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_UNION;

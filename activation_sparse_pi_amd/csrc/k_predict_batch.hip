@@ -18,7 +18,9 @@
 //   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  The
 //            block's z loads, then all of its W2t loads are issued first; z is scaled, split
 //            and staged in LDS while the W2t rows are in flight; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
-//            and one wave ballot per 64 neurons of a token gives two mask words.
+//            and one wave ballot per 64 neurons of a token gives two mask words.  Optionally
+//            the block also writes the union of the tokens' masks over its 128 neurons (4
+//            words) and each neuron's token word (bit b: the neuron is in token b's mask).
 #include "internal.h"
 #include "mfma_tile.h"
 
@@ -129,9 +131,11 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
                                                     const float* __restrict__ bias, int r, int F,
                                                     float theta, float* __restrict__ logits,
                                                     uint32_t* __restrict__ mask,
-                                                    uint32_t* __restrict__ umask) {
+                                                    uint32_t* __restrict__ umask,
+                                                    uint32_t* __restrict__ tokbits) {
     __shared__ uint4 s_z[2][32][ZC / 8];     // z_hi, z_lo: [token][chunk of 8, swizzled]
     __shared__ unsigned long long s_u[PB_NW][2];   // per wave: OR of its tokens' ballots
+    __shared__ unsigned long long s_bal[32][2];    // per token: its ballots of the 2 x 64 neurons
     __shared__ uint4 s_w[PB_NW][32][8];      // per wave: W2t staging, then its accumulator
     __shared__ int s_e[32];                  // per-token exponent e
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -265,20 +269,28 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
         }
         const unsigned long long bal = __ballot(act);
         uor[nh] |= bal;
+        if (lane == 0) s_bal[tb][nh] = bal;           // tb < 32; 0 for tokens past B
         const int w0 = (n0 + nh * 64) >> 5;
         if (lane == 0 && tb < B) {
             if (w0 < W) mask[(size_t)tb * W + w0] = (uint32_t)bal;
             if (w0 + 1 < W) mask[(size_t)tb * W + w0 + 1] = (uint32_t)(bal >> 32);
         }
     }
-    if (umask == nullptr) return;
+    if (umask == nullptr && tokbits == nullptr) return;
     // the union over the B tokens of this block's 128 neurons: the OR of every wave's ballots
     if (lane == 0) {
         s_u[wave][0] = uor[0];
         s_u[wave][1] = uor[1];
     }
     __syncthreads();
-    if (tid < 4) {                                   // mask word n0 / 32 + tid
+    // token word of neuron n0 + tid: bit b = neuron in token b's mask (the ballots transposed)
+    if (tokbits && tid < 128 && n0 + tid < F) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int b = 0; b < 32; ++b) t |= (uint32_t)((s_bal[b][tid >> 6] >> (tid & 63)) & 1ull) << b;
+        tokbits[n0 + tid] = t;
+    }
+    if (umask && tid < 4) {                          // mask word n0 / 32 + tid
         const int nh = tid >> 1;
         unsigned long long u = 0ull;
 #pragma unroll
@@ -305,7 +317,7 @@ void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
 
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
-                                hipStream_t s, uint32_t* umask) {
+                                hipStream_t s, uint32_t* umask, uint32_t* tokbits) {
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_PRED1;
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
@@ -317,7 +329,7 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
     hipLaunchKernelGGL(p.r <= ZC ? k_pb2<true> : k_pb2<false>, dim3((p.F + 127) / 128),
                        dim3(PB_NW * 64), 0, s, z, B,
                        static_cast<const uint16_t*>(p.w_p2t),
-                       p.bias, p.r, p.F, theta, logits, mask, umask);
+                       p.bias, p.r, p.F, theta, logits, mask, umask, tokbits);
     return hipGetLastError();
 }
 

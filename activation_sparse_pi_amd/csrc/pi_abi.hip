@@ -137,15 +137,16 @@ size_t ws_base(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
     return need;
 }
 
-// pi_batch_run's union path keeps the batch's union mask, list and count past the shared region
+// pi_batch_run's union path keeps the batch's union mask, token words, list and count past the shared region
 // (they live from the predictor's launch to the union FFN's, which uses that region)
 struct BatchWs {
-    size_t off_umask, off_uidx, off_ucount, bytes;
+    size_t off_umask, off_tokbits, off_uidx, off_ucount, bytes;
 };
 BatchWs batch_ws(size_t base, int F) {
     BatchWs w{};
     w.off_umask = align_up(base, 256);
-    w.off_uidx = align_up(w.off_umask + (size_t)((F + 31) / 32) * 4, 256);
+    w.off_tokbits = align_up(w.off_umask + (size_t)((F + 31) / 32) * 4, 256);
+    w.off_uidx = align_up(w.off_tokbits + (size_t)F * 4, 256);
     w.off_ucount = align_up(w.off_uidx + (size_t)F * 4, 256);
     w.bytes = w.off_ucount + 256;
     return w;
@@ -329,7 +330,9 @@ int pi_sparse_ffn(const pi_ffn_desc* ffn, const uint16_t* x, int B, const int32_
     if (B == 1) {
         e = launch_ffn_b1(*ffn, pl, x, idx, count, 0, y, static_cast<char*>(ws), s);
     } else {
-        e = launch_ffn_union(*ffn, pl, x, B, idx, count, token_mask, y, static_cast<char*>(ws), s);
+        // the list is only read (umask == nullptr)
+        e = launch_ffn_union(*ffn, pl, x, B, nullptr, nullptr, const_cast<int32_t*>(idx),
+                             const_cast<int32_t*>(count), token_mask, y, static_cast<char*>(ws), s);
     }
     if (e != hipSuccess) return hip_fail(e, "pi_sparse_ffn launch");
     return ok();
@@ -647,6 +650,7 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
     uint32_t* umask = reinterpret_cast<uint32_t*>(w + bw.off_umask);
+    uint32_t* tokbits = reinterpret_cast<uint32_t*>(w + bw.off_tokbits);
     int32_t* uidx = reinterpret_cast<int32_t*>(w + bw.off_uidx);
     int32_t* ucount = reinterpret_cast<int32_t*>(w + bw.off_ucount);
     hipError_t e;
@@ -673,10 +677,10 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
                 const int Bg = group_size(B, gi);
                 const PredPlan ppl = plan_pred(d, r, F, Bg);
                 const FfnPlan fpl = plan_ffn(d, F, Fd.wfmt, Bg);
+                // the union FFN builds the union's list from the union mask itself
                 if ((e = launch_predict_batch(P, ppl, xs + (size_t)b0 * d, Bg, theta, nullptr,
-                                              mask + (size_t)b0 * W, w, s, umask)) != hipSuccess ||
-                    (e = launch_compact(umask, 1, F, PI_PER_TOKEN, uidx, ucount, s)) != hipSuccess ||
-                    (e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, uidx, ucount,
+                                              mask + (size_t)b0 * W, w, s, umask, tokbits)) != hipSuccess ||
+                    (e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, umask, tokbits, uidx, ucount,
                                           mask + (size_t)b0 * W, y + (size_t)b0 * d, w, s)) != hipSuccess)
                     return hip_fail(e, "pi_batch_run union pass");
             }

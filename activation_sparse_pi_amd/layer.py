@@ -18,6 +18,13 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def _event_handle(e):
+    """The hipEvent_t of a torch event (torch creates it lazily, at the first record)."""
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
+
+
 class DeviceLayer:
     def __init__(self, inputs: dict, replicas: int = 1, B_max: int = 1, device="cuda",
                  threshold: float = 0.5, perm: np.ndarray | None = None, pred_format: str = "f16",
@@ -159,7 +166,7 @@ class DeviceLayer:
             self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
 
         def handles(evs):
-            return None if evs is None else (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+            return None if evs is None else (ctypes.c_void_p * len(evs))(*[_event_handle(e) for e in evs])
 
         L.check(L.pi_decode_run(self._pred_arr, self._ffn_arr, self.replicas, x, T, s0, nsteps,
                                 mode, bufs["mask"].data_ptr(), bufs["idx"].data_ptr(),
@@ -177,7 +184,7 @@ class DeviceLayer:
         if not hasattr(self, "_pred_arr"):
             self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
             self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
-        ev = None if events is None else (ctypes.c_void_p * 2)(*[e.cuda_event for e in events])
+        ev = None if events is None else (ctypes.c_void_p * 2)(*[_event_handle(e) for e in events])
         rp = None if rate is None else np.ascontiguousarray(rate, dtype=np.float32)
         L.check(L.pi_batch_run(self._pred_arr, self._ffn_arr, self.replicas, x, T, B, s0, nsteps,
                                schedule, None if rp is None else rp.ctypes.data, hbm_gbs, mask, y, ev,

@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--pred-format", choices=("f16", "i8g128"), default="f16",
                     help="i8g128: the predictor factors in int8 with one fp16 scale per 128 (batch 1)")
     ap.add_argument("--batch-sweep", action="store_true",
-                    help="batch workload: token-by-token vs union sparse FFN for B = 1, 2, 4, ...")
+                    help="pi_batch_run per schedule for B = 1, 2, 4, ... up to --batch-max")
+    ap.add_argument("--batch-max", type=int, default=0, help="--batch-sweep: largest B (0 = max(batch, 64))")
     ap.add_argument("--passes", type=int, default=5,
                     help="also time this many whole passes over the T-token stream and report "
                          "their median (0 = skip)")
@@ -363,11 +364,13 @@ def bench_batch(a, cfg):
 
 
 def bench_batch_sweep(a, cfg):
-    """Batch-size dispatch on the batch workload's layer: for B = 1, 2, 4, ... up to the
-    workload's batch, the sparse FFN of B tokens run (i) token by token through the batch-1
-    operators, each with its own list, and (ii) as one union pass on MFMA (compaction
-    included), next to pi_batch_plan's estimates from the tokens' activation rates.  The
-    predictor is common to both and left out of the timed region."""
+    """Batch-size dispatch on a layer of the workload's shape: for B = 1, 2, 4, ... up to
+    --batch-max, one decode step of B tokens (predictor, tables, FFN) through pi_batch_run with
+    each schedule -- token by token on the batch-1 kernel schedule, union passes of at most 32
+    tokens on MFMA, and the automatic choice -- next to pi_batch_plan's FFN estimates.  The
+    schedule the automatic choice ran is read off its y, which equals bit for bit the y of the
+    schedule it took (each schedule sums in a fixed order).  The activation rates it decides on
+    are the predicted masks' rates over the sampled steps."""
     import torch
 
     from activation_sparse_pi_amd import _lib as L
@@ -375,79 +378,72 @@ def bench_batch_sweep(a, cfg):
     from synth import gen
 
     dev = torch.device("cuda:0")
+    Bmax = a.batch_max or max(cfg.B, 64)
+    S = 16                                                # distinct steps cycled through
+    cfg = cfg.with_(B=Bmax, T=S)
     inputs = gen.make(cfg)
-    Bmax, F = cfg.B, cfg.F
-    S = min(cfg.T, 16)                                   # distinct steps cycled through
-    xd = torch.from_numpy(inputs["x"][:S].copy()).to(dev)                 # [S, Bmax, d]
+    F, W = cfg.F, (cfg.F + 31) // 32
     R = a.replicas or 2
-    layer = DeviceLayer(inputs, replicas=R, B_max=Bmax, device=dev)
-    W = (F + 31) // 32
-    mask = torch.empty((S, Bmax, W), dtype=torch.int32, device=dev)
-    idx = torch.empty((S, Bmax, F), dtype=torch.int32, device=dev)
-    cnt = torch.empty((S, Bmax), dtype=torch.int32, device=dev)
+    layer = DeviceLayer(inputs, replicas=R, B_max=min(Bmax, 32), device=dev)
+    xall = torch.from_numpy(inputs["x"].copy()).to(dev)                  # [S, Bmax, d]
+    # activation rates from the predicted masks (batches of at most 32 tokens)
+    m = torch.empty((32, W), dtype=torch.int32, device=dev)
+    hits = np.zeros(F)
+    ntok = 0
     for t in range(S):
-        layer.predict(xd[t].data_ptr(), Bmax, None, mask[t].data_ptr(), idx[t].data_ptr(),
-                      cnt[t].data_ptr())
-    torch.cuda.synchronize()
-    bits = np.unpackbits(mask.cpu().numpy().view(np.uint8), axis=-1, bitorder="little")[..., :F]
-    rate = np.ascontiguousarray(bits.reshape(-1, F).mean(axis=0), dtype=np.float32)
-    uidx = torch.empty((F,), dtype=torch.int32, device=dev)
-    ucnt = torch.empty((1,), dtype=torch.int32, device=dev)
+        for b0 in range(0, Bmax, 32):
+            nb = min(32, Bmax - b0)
+            layer.predict(xall[t, b0].data_ptr(), nb, None, m.data_ptr(), None, None)
+            bits = np.unpackbits(m[:nb].cpu().numpy().view(np.uint8), axis=-1, bitorder="little")[:, :F]
+            hits += bits.sum(axis=0)
+            ntok += nb
+    rate = np.ascontiguousarray(hits / ntok, dtype=np.float32)
+    mask = torch.empty((Bmax, W), dtype=torch.int32, device=dev)
     y = torch.empty((Bmax, cfg.d), dtype=torch.float32, device=dev)
-    K, Wm = 32, 4
+    K, Wm = 16, 4
+    names = {L.PI_BATCH_TOKENS: "tokens", L.PI_BATCH_UNION: "union", L.PI_BATCH_AUTO: "auto"}
 
-    def timed(run):
-        for s in range(Wm):
-            run(s)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed(x, B, sched):
+        layer.batch_run(x.data_ptr(), S, B, 0, Wm, mask.data_ptr(), y.data_ptr(), schedule=sched, rate=rate)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in ev:
+            e.record()                                    # creates the underlying events
         torch.cuda.synchronize()
-        e0.record()
-        for s in range(K):
-            run(Wm + s)
-        e1.record()
+        layer.batch_run(x.data_ptr(), S, B, Wm, K, mask.data_ptr(), y.data_ptr(), schedule=sched,
+                        rate=rate, events=ev)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K * 1e3          # us per step
+        return ev[0].elapsed_time(ev[1]) / K * 1e3, y[:B].clone()      # us per step, last y
 
     rows = []
     B = 1
     while B <= Bmax:
-        def tokens(s, B=B):
-            t, rep = s % S, s % R
-            for b in range(B):
-                layer.sparse_ffn(xd[t, b].data_ptr(), 1, idx[t, b].data_ptr(), cnt[t, b:].data_ptr(),
-                                 None, y[b].data_ptr(), rep)
-
-        def union(s, B=B):
-            t, rep = s % S, s % R
-            layer.compact(mask[t].data_ptr(), B, L.PI_UNION, uidx.data_ptr(), ucnt.data_ptr())
-            layer.sparse_ffn(xd[t].data_ptr(), B, uidx.data_ptr(), ucnt.data_ptr(), mask[t].data_ptr(),
-                             y.data_ptr(), rep)
-
-        t_tok = timed(tokens)
-        t_uni = timed(union) if B > 1 else None
-        u_meas = float(np.mean([bits[t, :B].any(axis=0).sum() for t in range(S)]))
+        x = xall[:, :B].contiguous()                                   # [S, B, d]
+        t_tok, y_tok = timed(x, B, L.PI_BATCH_TOKENS)
+        t_uni, y_uni = timed(x, B, L.PI_BATCH_UNION) if B > 1 and cfg.wfmt == "f16" else (None, None)
+        t_auto, y_auto = timed(x, B, L.PI_BATCH_AUTO)
+        ran = ("tokens" if torch.equal(y_auto, y_tok) else
+               "union" if y_uni is not None and torch.equal(y_auto, y_uni) else "neither")
+        best = "tokens" if t_uni is None or t_tok <= t_uni else "union"
         p = L.BatchPlan()
         L.check(L.pi_batch_plan(layer.ffn[0], B, rate.ctypes.data, HBM_PEAK_GBS, p))
-        best = "tokens" if t_uni is None or t_tok <= t_uni else "union"
         rows.append({
             "B": B, "tokens_us": round(t_tok, 2), "union_us": None if t_uni is None else round(t_uni, 2),
-            "best": best, "mean_union": round(u_meas, 1),
-            "plan": {"choice": "union" if p.choice == L.PI_BATCH_UNION else "tokens",
-                     "tokens_us": round(p.t_tokens_us, 2),
-                     "union_us": None if math.isinf(p.t_union_us) else round(p.t_union_us, 2),
-                     "n_mean": round(p.n_mean, 1), "u_mean": round(p.u_mean, 1)},
+            "auto_us": round(t_auto, 2), "auto_ran": ran, "best": best,
+            "ffn_plan": {"tokens_us": round(p.t_tokens_us, 2),
+                         "union_us": None if math.isinf(p.t_union_us) else round(p.t_union_us, 2),
+                         "n_mean": round(p.n_mean, 1), "u_mean": round(p.u_mean, 1)},
         })
-        print(f"# B={B}: tokens {t_tok:.1f} us, union {t_uni} us, plan {rows[-1]['plan']}", file=sys.stderr,
-              flush=True)
-        B *= 2
+        print(f"# B={B}: tokens {t_tok:.1f} us, union {t_uni} us, auto {t_auto:.1f} us ran {ran}, "
+              f"best {best}", file=sys.stderr, flush=True)
+        B = B * 2 if B * 2 <= Bmax or B == Bmax else Bmax
     out = {
-        "metric": "batch-size dispatch: sparse FFN of B tokens, token by token vs one union pass (us per step)",
+        "metric": "batch-size dispatch: one decode step of B tokens through pi_batch_run per schedule (us per step)",
         "unit": "us", "n_gpus": 1, "data": "synthetic", "dtype": "f16",
-        "config": {"workload": f"{cfg.name}: one FFN layer, d={cfg.d}, ffn={F}, {cfg.act}, fp16 weights; "
-                               f"the first B of each step's {Bmax} tokens, {S} steps cycled, {R} replicas",
-                   "steps": K, "warmup": Wm},
+        "config": {"workload": f"{cfg.name}: one layer, d={cfg.d}, ffn={F}, rank {cfg.r}, {cfg.act}, "
+                               f"{cfg.wfmt} weights; the first B of each step's {Bmax} tokens, {S} steps "
+                               f"cycled, {R} replicas", "steps": K, "warmup": Wm},
         "rows": rows,
-        "plan_agrees": sum(r["plan"]["choice"] == r["best"] for r in rows),
+        "auto_took_best": sum(r["auto_ran"] == r["best"] for r in rows),
     }
     print(json.dumps(out), flush=True)
 
@@ -471,9 +467,6 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = configs.get(a.config)
     if a.batch_sweep:
-        if cfg.B == 1:
-            print("--batch-sweep needs a batch workload (c4)", file=sys.stderr)
-            sys.exit(2)
         return bench_batch_sweep(a, cfg)
     if cfg.B != 1:
         return bench_batch(a, cfg)

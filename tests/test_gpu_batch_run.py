@@ -120,3 +120,29 @@ def test_batch_run_c4_shape(B):
     mu, yu = _run(layer, cfg, xd, B, 1, 1, L.PI_BATCH_UNION)
     assert np.array_equal(mu, mask) and np.array_equal(yu, y), "AUTO must have taken the union schedule"
     say(f"  worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("sched", ["union", "tokens"])
+def test_batch_run_empty_union(sched):
+    """A step where no token has an active neuron (x = 0 and every bias below the threshold):
+    masks and y are all zero, also right after a step with a non-empty union on the same
+    workspace, and the next non-empty step is unaffected."""
+    L = _L()
+    cfg = configs.tiny("relu", "f16", d=384, F=1000, r=40, B=8, T=2, seed=74)
+    inp = gen.make(cfg)
+    inp["bias"] = np.minimum(inp["bias"], np.float32(-1e-3))      # x = 0 gives l = bias < 0
+    W = O.Weights.from_inputs(inp)
+    assert not np.any(O.predicted_active(inp["bias"])), "x = 0 must predict no neuron"
+    layer = _layer(inp, replicas=1, B_max=8)
+    s = {"union": L.PI_BATCH_UNION, "tokens": L.PI_BATCH_TOKENS}[sched]
+    X = np.ascontiguousarray(inp["x"][:1])                           # [1, B, d]
+    xd = torch.from_numpy(X).cuda()
+    zd = torch.zeros_like(xd)
+    m1, y1 = _run(layer, cfg, xd, cfg.B, 0, 1, s)
+    _check_step(inp, W, X[0], m1, y1, f"empty-union {sched}: before")
+    assert m1.any(), "the regular step should have active neurons"
+    m0, y0 = _run(layer, cfg, zd, cfg.B, 0, 1, s)
+    assert not m0.any(), f"{sched}: masks of x = 0 must be empty"
+    assert np.array_equal(y0, np.zeros_like(y0)), f"{sched}: y of an empty union must be 0"
+    m2, y2 = _run(layer, cfg, xd, cfg.B, 0, 1, s)
+    assert np.array_equal(m1, m2) and np.array_equal(y1, y2), f"{sched}: step after the empty one"
