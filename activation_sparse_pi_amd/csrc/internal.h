@@ -10,10 +10,10 @@
 namespace pi {
 
 // ---- arrival-counter slots inside the workspace (unsigned ints) ------------------------------
-constexpr int CNT_PRED1 = 0;      // one per predictor column group (r / 64 <= 256)
+constexpr int CNT_PRED1 = 0;      // (free: 256 slots)
 constexpr int CNT_PRED2 = 256;    // one for stage 2's compaction
 constexpr int CNT_DOWN = 512;     // one per down-projection column slice (<= 512)
-constexpr int CNT_UNION = 1024;   // union path (<= 512)
+constexpr int CNT_UNION = 1024;   // union path, down-product column groups (<= 512)
 constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
@@ -46,7 +46,7 @@ struct FfnPlan {
     // union (B > 1) path: H fragments, down-product column groups and list shares,
     // the shares' partial sums (all 0 when B == 1)
     int u_ncg, u_ks;
-    size_t off_H, off_upart;
+    size_t off_H, off_upart, off_upcnt, off_uppart;
 };
 FfnPlan plan_ffn(int d, int F, int wfmt, int B);
 // appends the union path's workspace to p from offset off; returns the new end

@@ -33,7 +33,11 @@
 //         fewer columns.  The waves meet in LDS; with KS > 1 the shares meet in the
 //         workspace and the last-arriving block of the column group adds them in a fixed
 //         order (bitwise reproducible).
+#include <algorithm>
 #include <climits>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "internal.h"
 #include "mfma_tile.h"
@@ -98,17 +102,35 @@ PI_DEV uint32_t pack_h2(float lo, float hi) {
 }
 
 // ------------------------------------------------------------------------------------ up
+// Block roles.  The first S blocks (S: as many as are resident at once) take whole tiles
+// 0 .. S - 1.  The tiles past them would run as a second round behind the first, one block each;
+// instead each is split over d into sp parts (sp = 2 when the layer has more than S tiles),
+// block S + (t - S) sp + p taking part p of tile t, so the second round has twice the blocks in
+// flight at half the length.  A part stores its 32 x 32 pre-activation sums; the last part of
+// the tile to arrive adds the sp partials in part order and finishes the tile.
+constexpr int UP_SP = 2;
+struct UpRole {
+    int tile, part, sp;
+};
+PI_DEV UpRole up_role(int b, int S, int sp) {
+    if (b < S || sp == 1) return {b, 0, 1};
+    const int bb = b - S;
+    return {S + bb / sp, bb % sp, sp};
+}
+
 // ReLU with 32-bit offsets fits 128 registers: two blocks per CU (ReGLU: one).
 // FROM_MASK: the tile's ids come from the union mask umask and are written to uidx[32 tile ..]
 // (block 0 writes U to *ucount), the keep words from the token words tokbits[F]; otherwise the
 // ids are read from the union list uidx[0 .. *ucount) and the keep words from the token masks
-// tmask [B, ceil(F / 32)].
+// tmask [B, ceil(F / 32)].  S, sp: the block roles above; upart / ucnt: the split tiles'
+// partials and arrival counters.
 template <bool GLU, bool OFF32, bool FROM_MASK>
 __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
     const uint16_t* __restrict__ x, int B, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ Wu, int d, int F, const uint32_t* __restrict__ umask,
     const uint32_t* __restrict__ tokbits, int32_t* __restrict__ uidx, int32_t* __restrict__ ucount,
-    const uint32_t* __restrict__ tmask, uint4* __restrict__ Hf) {
+    const uint32_t* __restrict__ tmask, int S, int sp, float* __restrict__ upart,
+    unsigned* __restrict__ ucnt, uint4* __restrict__ Hf) {
     constexpr int NM = GLU ? 2 : 1;                   // weight matrices: up [, gate]
     __shared__ uint4 s_st[UP_NW][NM + 1][32][8];      // per wave: x, up [, gate] staging
     __shared__ int s_ids[32];                         // the tile's neuron ids, -1 past the union
@@ -116,17 +138,18 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
     __shared__ int s_tmp[UP_NW + 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = blockIdx.x, lo = tile * 32;
     if (tid < 32) s_ids[tid] = -1;
+    const UpRole ro = up_role(blockIdx.x, S, sp);
+    const int tile = ro.tile, lo = tile * 32;
     uint32_t tok = 0u;             // FROM_MASK, wave 0 lane n < 32: token word of position n
     if constexpr (FROM_MASK) {
-        const int U = tile_ids_from_mask(umask, F, lo, s_ids, s_tmp);   // its barriers order the -1s
-        if (tile == 0 && tid == 0) *ucount = U;       // also when the union is empty
+        const int U = __builtin_amdgcn_readfirstlane(tile_ids_from_mask(umask, F, lo, s_ids, s_tmp));   // its barriers order the -1s
+        if (blockIdx.x == 0 && tid == 0) *ucount = U; // also when the union is empty
         if (lo >= U) return;                          // whole block: past the union
         __syncthreads();
         if (tid < 32) {
             const int id = s_ids[tid];
-            if (lo + tid < U) uidx[lo + tid] = id;
+            if (ro.part == 0 && lo + tid < U) uidx[lo + tid] = id;
             tok = (unsigned)id < (unsigned)F ? tokbits[id] : 0u;        // used after streaming
         }
     } else {
@@ -156,18 +179,24 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
         }
     }
 
-    // loader slot q (0..3) of a run brings row 8q + lane/8 of the tile and of x
+    // loader slot q (0..3) of a run brings row 8q + lane/8 of the tile and of x (element
+    // offsets, -1 = zero row; recomputed where needed rather than kept across the stream)
     const int lrow = lane >> 3;
-    long long offw[4], offx[4];                       // element offsets, -1 = zero row
+    auto offsets = [&](long long(&offw)[4], long long(&offx)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int row = s_ids[8 * q + lrow];
-        offw[q] = (unsigned)row < (unsigned)F ? (long long)row * d : -1;
-        const int tok = 8 * q + lrow;
-        offx[q] = tok < B ? (long long)tok * d : -1;
-    }
+        for (int q = 0; q < 4; ++q) {
+            const int row = s_ids[8 * q + lrow];
+            offw[q] = (unsigned)row < (unsigned)F ? (long long)row * d : -1;
+            const int tk = 8 * q + lrow;
+            offx[q] = tk < B ? (long long)tk * d : -1;
+        }
+    };
+    // this part's runs of 64 (the partial run, if any, belongs to the last part), then this
+    // wave's share of them
     f32x16_t acc[NM] = {};
     if constexpr (OFF32) {
+        long long offw[4], offx[4];
+        offsets(offw, offx);
         // full runs through buffer resources (byte offsets of F rows fit 31 bits): zero rows
         // read row 0 of W and x instead, their h is zeroed below; the partial run, if any,
         // goes the general way
@@ -181,18 +210,26 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
             ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
             ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
         }
-        const int nfull = d >> 6, per = (nfull + UP_NW - 1) / UP_NW;
-        const int r0 = min(nfull, wave * per), r1 = min(nfull, r0 + per);
+        const int nfull = d >> 6;
+        const int p0 = ro.part * nfull / ro.sp, p1 = (ro.part + 1) * nfull / ro.sp;
+        const int per = (p1 - p0 + UP_NW - 1) / UP_NW;
+        const int r0 = min(p1, p0 + wave * per), r1 = min(p1, r0 + per);
         runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
-        if ((d & 63) && wave == UP_NW - 1) {
+        if ((d & 63) && wave == UP_NW - 1 && ro.part == ro.sp - 1) {
             const uint16_t* Wm[NM];
             Wm[0] = Wu;
             if constexpr (GLU) Wm[1] = Wg;
-            runs_mfma<NM>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);
+            long long offw2[4], offx2[4];
+            offsets(offw2, offx2);
+            runs_mfma<NM>(x, offx2, Wm, offw2, d, nfull, nfull + 1, s_st[wave], acc);
         }
     } else {
-        const int nrun = (d + 63) / 64, per = (nrun + UP_NW - 1) / UP_NW;
-        const int r0 = min(nrun, wave * per), r1 = min(nrun, r0 + per);
+        long long offw[4], offx[4];
+        offsets(offw, offx);
+        const int nrun = (d + 63) / 64;
+        const int p0 = ro.part * nrun / ro.sp, p1 = (ro.part + 1) * nrun / ro.sp;
+        const int per = (p1 - p0 + UP_NW - 1) / UP_NW;
+        const int r0 = min(p1, p0 + wave * per), r1 = min(p1, r0 + per);
         const uint16_t* Wm[NM];
         Wm[0] = Wu;
         if constexpr (GLU) Wm[1] = Wg;
@@ -217,13 +254,11 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
         if constexpr (GLU) red[1024 + r * 64 + lane] = acc[1][r];
     }
     __syncthreads();
+    // H-fragment lane fl of group 2 tile + gg: token b = fl % 32, positions 16 gg + 8 (fl / 32)
+    // + j.  D[n][b] sits in register (n/8)*4 + n%4 of lane b + 32 ((n/4) % 2).
+    const int fl = tid & 63, gg = (tid >> 6) & 1, h = fl >> 5, b = fl & 31;
+    float av[8], gv[8];
     if (tid < 128) {
-        // H-fragment lane fl of group 2 tile + gg: token b = fl % 32, positions
-        // 16 gg + 8 (fl / 32) + j.  D[n][b] sits in register (n/8)*4 + n%4 of lane
-        // b + 32 ((n/4) % 2).
-        const int fl = tid & 63, gg = tid >> 6, h = fl >> 5, b = fl & 31;
-        const uint32_t keep = s_keep[b];              // 0 for tokens past B
-        float hv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int n = gg * 16 + 8 * h + j;
@@ -235,8 +270,57 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
                 a += rw[rg * 64 + ln];
                 if constexpr (GLU) g += rw[1024 + rg * 64 + ln];
             }
+            av[j] = a;
+            gv[j] = g;
+        }
+    }
+    if (ro.sp > 1) {
+        // split tile: this part's sums to the workspace; the last part to arrive adds all of
+        // them in part order (its own from registers)
+        const size_t slot = (size_t)(tile - S) * ro.sp;
+        auto at = [&](int p) { return upart + ((slot + p) * 128 + tid) * (8 * NM); };
+        if (tid < 128) {
+            float* my = at(ro.part);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                st_agent(my + j, av[j]);
+                if constexpr (GLU) st_agent(my + 8 + j, gv[j]);
+            }
+        }
+        if (!last_block_arrive(&ucnt[tile - S], ro.sp)) return;
+        if (tid < 128) {
+            float pa[UP_SP][8], pg[UP_SP][8];
+#pragma unroll
+            for (int p = 0; p < UP_SP; ++p) {
+                const float* src = at(p < ro.sp ? p : 0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pa[p][j] = p < ro.sp && p != ro.part ? ld_agent(src + j) : 0.f;
+                    pg[p][j] = GLU && p < ro.sp && p != ro.part ? ld_agent(src + 8 + j) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float a = 0.f, g = 0.f;
+#pragma unroll
+                for (int p = 0; p < UP_SP; ++p) {
+                    if (p >= ro.sp) continue;
+                    a += p == ro.part ? av[j] : pa[p][j];
+                    g += p == ro.part ? gv[j] : pg[p][j];
+                }
+                av[j] = a;
+                gv[j] = g;
+            }
+        }
+    }
+    if (tid < 128) {
+        const uint32_t keep = s_keep[b];              // 0 for tokens past B
+        float hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = gg * 16 + 8 * h + j;
             // positions past U, invalid ids and tokens past B have no keep bit: h = 0
-            hv[j] = (keep >> n) & 1u ? (GLU ? fmaxf(g, 0.f) * a : fmaxf(a, 0.f)) : 0.f;
+            hv[j] = (keep >> n) & 1u ? (GLU ? fmaxf(gv[j], 0.f) * av[j] : fmaxf(av[j], 0.f)) : 0.f;
         }
         Hf[(size_t)(tile * 2 + gg) * 64 + fl] =
             make_uint4(pack_h2(hv[0], hv[1]), pack_h2(hv[2], hv[3]), pack_h2(hv[4], hv[5]),
@@ -482,7 +566,35 @@ size_t plan_union(FfnPlan& p, int d, int F, size_t off) {
     p.u_ks = ks < 1 ? 1 : (ks > 16 ? 16 : ks);
     p.off_upart = off;
     if (p.u_ks > 1) off = align_up(off + (size_t)p.u_ks * 32 * d * sizeof(float), 256);
+    // split up tiles: an arrival counter and UP_SP x 8 KB of partials (ReGLU: 16 KB) per tile
+    const size_t tiles = (size_t)(F + 31) / 32;
+    p.off_upcnt = off;
+    off = align_up(off + tiles * sizeof(unsigned), 256);
+    p.off_uppart = off;
+    off = align_up(off + tiles * UP_SP * 128 * 8 * 2 * sizeof(float), 256);
     return off;
+}
+
+// blocks of one up-kernel variant resident on the whole device at once (queried once per
+// device and variant)
+template <typename K>
+int up_slots(K kern) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, reinterpret_cast<const void*>(kern));
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int per_cu = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), UP_NT, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int S = std::max(1, per_cu * ncu);
+    cache[key] = S;
+    return S;
 }
 
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
@@ -490,16 +602,29 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
                             int32_t* count, const uint32_t* token_mask, float* y, char* ws,
                             hipStream_t s) {
     uint4* Hf = reinterpret_cast<uint4*>(ws + pl.off_H);
+    float* upart = reinterpret_cast<float*>(ws + pl.off_uppart);
+    unsigned* ucnt = reinterpret_cast<unsigned*>(ws + pl.off_upcnt);
     const int tiles = (f.F + 31) / 32;
     const uint16_t* Wg = static_cast<const uint16_t*>(f.w_gate);
     const uint16_t* Wu = static_cast<const uint16_t*>(f.w_up);
     // 32-bit buffer offsets when every byte of a weight matrix is within 2^31
     const bool off32 = (size_t)f.F * f.d * 2 <= (size_t)INT_MAX;
-    auto up = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(tiles), dim3(UP_NT), 0, s, x, B, Wg, Wu, f.d, f.F, umask,
-                           tokbits, idx, count, token_mask, Hf);
-    };
     const bool glu = f.act == PI_ACT_REGLU;
+    hipError_t e = hipSuccess;
+    auto up = [&](auto kern) {
+        const int S = up_slots(kern);
+        if (S <= 0) {
+            e = hipErrorInvalidValue;
+            return;
+        }
+        // blocks for every tile the union could have (its size is known on the device only);
+        // those past the union return at once
+        const int sp = tiles > S ? UP_SP : 1;
+        const int grid = tiles > S ? S + (tiles - S) * sp : tiles;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(UP_NT), 0, s, x, B, Wg, Wu, f.d, f.F, umask,
+                           tokbits, idx, count, token_mask, S, sp, upart, ucnt, Hf);
+        e = hipGetLastError();
+    };
     if (umask) {
         if (glu) off32 ? up(k_union_up<true, true, true>) : up(k_union_up<true, false, true>);
         else off32 ? up(k_union_up<false, true, true>) : up(k_union_up<false, false, true>);
@@ -507,7 +632,6 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
         if (glu) off32 ? up(k_union_up<true, true, false>) : up(k_union_up<true, false, false>);
         else off32 ? up(k_union_up<false, true, false>) : up(k_union_up<false, false, false>);
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_UNION;
     float* part = reinterpret_cast<float*>(ws + pl.off_upart);

@@ -13,8 +13,9 @@
 //
 //   stage 1  block = 32 rows of W1t x one of KS shares of d; 8 waves split the share in
 //            runs of 64 and stream rows and x through the staged 32 x 32 MFMA tile; the
-//            waves meet in LDS; the shares meet in the workspace, added in a fixed order
-//            by the last-arriving block of the row tile.
+//            waves meet in LDS; the shares' partial z land in the workspace and a small
+//            kernel adds them in share order (a kernel boundary instead of a cross-block
+//            hand-off, which costs several round trips to the memory-side cache).
 //   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  The
 //            block's z loads, then all of its W2t loads are issued first; z is scaled, split
 //            and staged in LDS while the W2t rows are in flight; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
@@ -29,12 +30,12 @@ namespace {
 
 constexpr int PB_NW = 8;      // waves per block (both stages)
 constexpr int ZC = 512;       // rank values of z staged per pass in stage 2
+constexpr int PB_KS = 32;     // most stage-1 shares of d
 
 // ------------------------------------------------------------------------------------ stage 1
 __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__ x, int B,
                                                     const uint16_t* __restrict__ W1t, int d, int r,
                                                     int ntile, int nks, float* __restrict__ part,
-                                                    unsigned* __restrict__ counter,
                                                     float* __restrict__ z) {
     __shared__ uint4 s_st[PB_NW][2][32][8];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -98,25 +99,23 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-        if (ob[q] < B && oj[q] < r) st_agent(&part[((size_t)ks * 32 + ob[q]) * r + oj[q]], v[q]);
-    if (!last_block_arrive(&counter[tile], nks)) return;
-    // every share's partials in flight at once (nks <= 16), added in share order
-    float pv[2][16];
+        if (ob[q] < B && oj[q] < r) part[((size_t)ks * 32 + ob[q]) * r + oj[q]] = v[q];
+}
+
+// z[b, j] = the nks shares' partials of (b, j) added in share order; all loads in flight at once
+__global__ __launch_bounds__(256) void k_pbz(const float* __restrict__ part, int B, int r, int nks,
+                                             float* __restrict__ z) {
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= B * r) return;
+    const int b = o / r, j = o - b * r;
+    float pv[PB_KS];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int k = 0; k < PB_KS; ++k) pv[k] = k < nks ? part[((size_t)k * 32 + b) * r + j] : 0.f;
+    float t = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2)
-            pv[q][k2] = (k2 < nks && k2 != ks && ob[q] < B && oj[q] < r)
-                            ? ld_agent(&part[((size_t)k2 * 32 + ob[q]) * r + oj[q]]) : 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        if (ob[q] >= B || oj[q] >= r) continue;
-        float t = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2)
-            if (k2 < nks) t += k2 == ks ? v[q] : pv[q][k2];
-        z[(size_t)ob[q] * r + oj[q]] = t;
-    }
+    for (int k = 0; k < PB_KS; ++k)
+        if (k < nks) t += pv[k];
+    z[o] = t;
 }
 
 // ------------------------------------------------------------------------------------ stage 2
@@ -307,9 +306,9 @@ void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
     const int nrun = (d + 63) / 64;
     p.b_ntile = (r + 31) / 32;
     int ks = (128 + p.b_ntile - 1) / p.b_ntile;        // >= 128 stage-1 blocks
-    if (ks > 16) ks = 16;
+    if (ks > PB_KS) ks = PB_KS;
     if (ks > nrun) ks = nrun;
-    if (ks < 1 || p.b_ntile > 256) ks = 1;              // one arrival counter per row tile
+    if (ks < 1) ks = 1;
     p.b_nks = ks;
     p.off_zpart = off;
     if (ks > 1) off = align_up(off + (size_t)ks * 32 * r * sizeof(float), 256);
@@ -318,14 +317,18 @@ void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
                                 hipStream_t s, uint32_t* umask, uint32_t* tokbits) {
-    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_PRED1;
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
     hipLaunchKernelGGL(k_pb1, dim3(pl.b_ntile * pl.b_nks), dim3(PB_NW * 64), 0, s, x, B,
                        static_cast<const uint16_t*>(p.w_p1t),
-                       p.d, p.r, pl.b_ntile, pl.b_nks, part, cnt, z);
+                       p.d, p.r, pl.b_ntile, pl.b_nks, part, z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (pl.b_nks > 1) {
+        hipLaunchKernelGGL(k_pbz, dim3((B * p.r + 255) / 256), dim3(256), 0, s, part, B, p.r,
+                           pl.b_nks, z);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(p.r <= ZC ? k_pb2<true> : k_pb2<false>, dim3((p.F + 127) / 128),
                        dim3(PB_NW * 64), 0, s, z, B,
                        static_cast<const uint16_t*>(p.w_p2t),
