@@ -17,7 +17,7 @@
 //            kernel adds them in share order (a kernel boundary instead of a cross-block
 //            hand-off, which costs several round trips to the memory-side cache).
 //   stage 2  block = 128 neurons; waves (tile m = w % 4, half of the rank w / 4).  The
-//            block's z loads, then all of its W2t loads are issued first; z is scaled, split
+//            block's z arrives first, then all of its W2t loads are issued; z is scaled, split
 //            and staged in LDS while the W2t rows are in flight; 8 MFMAs per run of 64.  The two halves meet in LDS, the bias is added,
 //            and one wave ballot per 64 neurons of a token gives two mask words.  Optionally
 //            the block also writes the union of the tokens' masks over its 128 neurons (4
@@ -177,8 +177,9 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
             zr[2 * i + 1] = *reinterpret_cast<const float4*>(p + 4);
         }
     };
-    // z first: it is small and in L2, and a load waits for every load issued before it,
-    // so issued behind the W2t rows it would only arrive with them
+    // z first, and waited for before the W2t rows are issued: every block reads the same 64 KB
+    // of z, and issued together with the rows of all blocks it would arrive behind most of them
+    // (a load also waits for every load issued before it)
     // 1. per-token exponent e: the largest |z| of the token brought into [2^14, 2^15)
     float m = 0.f;
     auto zmax = [&]() {
@@ -187,10 +188,10 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     };
     if constexpr (ONE) {                        // the pass's z stays in zr
         load_z(0);
+        zmax();
         __builtin_amdgcn_sched_barrier(0);
         load_w(0);
         __builtin_amdgcn_sched_barrier(0);
-        zmax();
     } else {
         load_w(0);
         for (int c0 = 0; c0 < r; c0 += ZC) {
