@@ -28,7 +28,9 @@ EXPORTS = ("pi_status_string", "pi_last_error", "pi_version", "pi_workspace_byte
            "pi_workspace_init", "pi_predict", "pi_compact", "pi_sparse_ffn",
            "pi_ffn_up", "pi_ffn_down", "pi_decode_run", "pi_ffn_dense_ref_gpu",
            "pi_place_neurons", "pi_permute_rows", "pi_map_ids", "pi_batch_plan",
-           "pi_count_active", "pi_decode_run_noalloc", "pi_place_neurons_hot", "pi_batch_run")
+           "pi_count_active", "pi_decode_run_noalloc", "pi_place_neurons_hot", "pi_batch_run",
+           "pi_attn_workspace_bytes", "pi_attn_qkv", "pi_attn_out", "pi_attn_run")
+PI_ATTN_MAX_HEADS, PI_ATTN_MAX_D = 1024, 16384
 PI_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -43,6 +45,11 @@ class FfnDesc(ctypes.Structure):
                 ("s_gate", c_void_p), ("s_up", c_void_p), ("s_down", c_void_p),
                 ("d", c_int32), ("F", c_int32), ("act", c_int32), ("wfmt", c_int32),
                 ("nhot", c_int32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("d", c_int32), ("H", c_int32),
+                ("dh", c_int32)]
 
 
 class BatchPlan(ctypes.Structure):
@@ -124,6 +131,17 @@ def lib() -> ctypes.CDLL:
         L.pi_batch_plan.argtypes = [ctypes.POINTER(FfnDesc), c_int, c_void_p, ctypes.c_double,
                                     ctypes.POINTER(BatchPlan)]
         L.pi_batch_plan.restype = c_int
+        L.pi_attn_workspace_bytes.argtypes = [P(AttnDesc)]
+        L.pi_attn_workspace_bytes.restype = c_size_t
+        L.pi_attn_qkv.argtypes = [P(AttnDesc), c_void_p, c_void_p, c_void_p, c_void_p]
+        L.pi_attn_qkv.restype = c_int
+        L.pi_attn_out.argtypes = [P(AttnDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_size_t, c_void_p]
+        L.pi_attn_out.restype = c_int
+        L.pi_attn_run.argtypes = [P(PredDesc), P(AttnDesc), c_int, c_void_p, c_void_p, c_int,
+                                  ctypes.c_longlong, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.pi_attn_run.restype = c_int
         _LIB = L
     return _LIB
 
@@ -231,3 +249,21 @@ def pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs
     of two hipEvent_t handles or None."""
     return lib().pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs, mask,
                               y, events, ws, ws_bytes, stream)
+
+
+def pi_attn_workspace_bytes(a) -> int:
+    return lib().pi_attn_workspace_bytes(_p(a))
+
+
+def pi_attn_qkv(a, x, head_mask, qkv, stream) -> int:
+    return lib().pi_attn_qkv(_p(a), x, head_mask, qkv, stream)
+
+
+def pi_attn_out(a, o, heads, count, y, ws, ws_bytes, stream) -> int:
+    return lib().pi_attn_out(_p(a), o, heads, count, y, ws, ws_bytes, stream)
+
+
+def pi_attn_run(preds, attns, nrep, x, o, T, s0, nsteps, mask, idx, count, qkv, y, events,
+                kernel_events, ws, ws_bytes, stream) -> int:
+    return lib().pi_attn_run(preds, attns, nrep, x, o, T, s0, nsteps, mask, idx, count, qkv, y, events,
+                             kernel_events, ws, ws_bytes, stream)

@@ -166,9 +166,10 @@ hipError_t launch_ffn_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t
 hipError_t launch_up_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x,
                         const int32_t* idx, const int32_t* count, int dense_F, float* h,
                         hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// group > 0 (fp16 weights): idx lists groups of `group` consecutive rows and h is indexed by row
 hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t* idx,
                           const int32_t* count, int dense_F, const float* h, float* y, char* ws,
-                          hipStream_t s);
+                          hipStream_t s, int group = 0);
 
 // 1 < B <= 32 union-mask path on MFMA.  With umask == nullptr the union list idx[0 .. *count)
 // is read; otherwise the list is built from the union mask umask and written to idx / count,
@@ -177,6 +178,18 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
                             const uint32_t* umask, const uint32_t* tokbits, int32_t* idx,
                             int32_t* count, const uint32_t* token_mask, float* y, char* ws,
                             hipStream_t s);
+
+// ---- attention side ----------------------------------------------------------------------
+struct AttnPlan {
+    FfnPlan ffn;              // the down projection over the H d_head rows of W_o^T
+    size_t bytes;
+};
+AttnPlan plan_attn(int d, int H, int dh);
+hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint32_t* hmask,
+                           float* qkv, hipStream_t s);
+hipError_t launch_attn_out(const pi_attn_desc& a, const AttnPlan& pl, const float* o,
+                           const int32_t* heads, const int32_t* count, float* y, char* ws,
+                           hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* perm, int n,

@@ -150,11 +150,13 @@ __global__ __launch_bounds__(256) void k_up_i4(const uint16_t* __restrict__ x,
 constexpr int DOWN_WAVES_F16 = 16;
 constexpr int DOWN_WAVES_I4 = 8;
 
+// G > 0: idx lists groups of G consecutive rows (list entry j stands for rows idx[j] G ..
+// idx[j] G + G - 1, *count entries) and h is indexed by row; otherwise h[k] goes with idx[k].
 template <int U>
 __global__ __launch_bounds__(1024) void k_down_f16(const uint16_t* __restrict__ Wd, int d, int F,
                                                    const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ count, int dense_F,
-                                                   const float* __restrict__ h,
+                                                   int G, const float* __restrict__ h,
                                                    float* __restrict__ part, float* __restrict__ y,
                                                    unsigned* __restrict__ counters) {
     constexpr int NW = DOWN_WAVES_F16;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(1024) void k_down_f16(const uint16_t* __restrict__ 
     const int nc = d >> 3;
     const int c = slice * 64 + lane;
     const bool cok = c < nc;
-    const int n = dense_F > 0 ? dense_F : min(*count, F);
+    const int n = dense_F > 0 ? dense_F : G > 0 ? min(*count, F / G) * G : min(*count, F);
     const int stride = nsplit * NW;
     float acc[8];
 #pragma unroll
@@ -176,9 +178,19 @@ __global__ __launch_bounds__(1024) void k_down_f16(const uint16_t* __restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kk = k0 + u * stride;
-            const int irow = kk < n ? (dense_F > 0 ? kk : idx[kk]) : -1;
+            int irow = -1;
+            if (kk < n) {
+                if (dense_F > 0) {
+                    irow = kk;
+                } else if (G > 0) {
+                    const int j = kk / G, g = idx[j];
+                    irow = (unsigned)g < (unsigned)(F / G) ? g * G + (kk - j * G) : -1;
+                } else {
+                    irow = idx[kk];
+                }
+            }
             if ((unsigned)irow < (unsigned)F) {
-                hv[u] = h[kk];
+                hv[u] = h[G > 0 ? irow : kk];
                 w[u] = cok ? ld16(Wd + (size_t)irow * d + 8 * c) : zero4();
             } else {
                 hv[u] = 0.f;
@@ -402,14 +414,14 @@ hipError_t launch_up_b1(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t*
 
 hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t* idx,
                           const int32_t* count, int dense_F, const float* h, float* y, char* ws,
-                          hipStream_t s) {
+                          hipStream_t s, int group) {
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     const dim3 gd(pl.nslices, pl.nsplit);
     if (f.wfmt == PI_W_F16) {
         hipLaunchKernelGGL((k_down_f16<4>), gd, dim3(64 * DOWN_WAVES_F16), 0, s,
-                           static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, dense_F, h,
-                           part, y, cnt);
+                           static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, dense_F,
+                           group, h, part, y, cnt);
     } else {
         hipLaunchKernelGGL((k_down_i4<4>), gd, dim3(64 * DOWN_WAVES_I4), 0, s,
                            static_cast<const uint8_t*>(f.w_down), f.s_down, f.d, f.F, idx, count,

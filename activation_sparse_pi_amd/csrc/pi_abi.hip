@@ -761,3 +761,110 @@ int pi_map_ids(const int32_t* idx, const int32_t* count, int B, int F, const int
 }
 
 }  // extern "C"
+
+namespace {
+
+int check_attn(const pi_attn_desc* a) {
+    if (!a) return fail(PI_ERR_NULL, "attention descriptor is NULL");
+    if (!a->w_qkv || !a->w_o) return fail(PI_ERR_NULL, "w_qkv and w_o are required");
+    if (!aligned16(a->w_qkv) || !aligned16(a->w_o)) return fail(PI_ERR_ALIGN, "attention weights must be 16-byte aligned");
+    if (a->d < 8 || a->d % 8 || a->d > PI_ATTN_MAX_D)
+        return fail(PI_ERR_SHAPE, "attention needs 8 <= d <= %d with d %% 8 == 0 (d=%d)", PI_ATTN_MAX_D, a->d);
+    if (a->H < 1 || a->H > PI_ATTN_MAX_HEADS)
+        return fail(PI_ERR_SHAPE, "attention needs 1 <= H <= %d (H=%d)", PI_ATTN_MAX_HEADS, a->H);
+    if (a->dh < 1 || (long long)a->H * a->dh * 3 > INT_MAX / a->d)
+        return fail(PI_ERR_SHAPE, "attention needs d_head >= 1 and 3 H d_head d < 2^31 (H=%d d_head=%d d=%d)",
+                    a->H, a->dh, a->d);
+    return PI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pi_attn_workspace_bytes(const pi_attn_desc* a) {
+    if (check_attn(a) != PI_OK) return 0;
+    return plan_attn(a->d, a->H, a->dh).bytes;
+}
+
+int pi_attn_qkv(const pi_attn_desc* a, const uint16_t* x, const uint32_t* head_mask, float* qkv,
+                void* stream) {
+    int st;
+    if ((st = check_attn(a)) != PI_OK) return st;
+    if (!x || !head_mask || !qkv) return fail(PI_ERR_NULL, "x, head_mask and qkv are required");
+    if (!aligned16(x)) return fail(PI_ERR_ALIGN, "x must be 16-byte aligned");
+    const hipError_t e = launch_attn_qkv(*a, x, head_mask, qkv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pi_attn_qkv launch");
+}
+
+int pi_attn_out(const pi_attn_desc* a, const float* o, const int32_t* heads, const int32_t* count,
+                float* y, void* ws, size_t ws_bytes, void* stream) {
+    int st;
+    if ((st = check_attn(a)) != PI_OK) return st;
+    if (!o || !heads || !count || !y) return fail(PI_ERR_NULL, "o, heads, count and y are required");
+    if (!aligned16(y)) return fail(PI_ERR_ALIGN, "y must be 16-byte aligned");
+    const AttnPlan pl = plan_attn(a->d, a->H, a->dh);
+    if ((st = check_ws(ws, ws_bytes, pl.bytes)) != PI_OK) return st;
+    const hipError_t e = launch_attn_out(*a, pl, o, heads, count, y, static_cast<char*>(ws),
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "pi_attn_out launch");
+}
+
+int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, const uint16_t* x,
+                const float* o, int T, long long s0, int nsteps, uint32_t* mask, int32_t* idx,
+                int32_t* count, float* qkv, float* y, void* const* events,
+                void* const* kernel_events, void* ws, size_t ws_bytes, void* stream) {
+    int st;
+    if (!preds || !attns) return fail(PI_ERR_NULL, "descriptor arrays are required");
+    if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
+    if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
+    if (!x || !o || !mask || !idx || !count || !qkv || !y)
+        return fail(PI_ERR_NULL, "x, o, mask, idx, count, qkv and y are required");
+    if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
+    for (int i = 0; i < nrep; ++i) {
+        if ((st = check_pred(&preds[i])) != PI_OK) return st;
+        if ((st = check_attn(&attns[i])) != PI_OK) return st;
+        if (preds[i].pfmt != PI_P_F16) return fail(PI_ERR_UNSUPPORTED, "the head predictor takes fp16 factors");
+        if (preds[i].F != attns[i].H || preds[i].d != attns[i].d)
+            return fail(PI_ERR_SHAPE, "replica %d: the head predictor needs F = H and the same d", i);
+        if (preds[i].d != preds[0].d || preds[i].r != preds[0].r || attns[i].H != attns[0].H ||
+            attns[i].dh != attns[0].dh || preds[i].threshold != preds[0].threshold)
+            return fail(PI_ERR_SHAPE, "replica %d does not match replica 0", i);
+    }
+    if (events && (!events[0] || !events[1])) return fail(PI_ERR_NULL, "events must hold two events");
+    if (kernel_events)
+        for (int i = 0; i < 2 * nsteps; ++i)
+            if (!kernel_events[i]) return fail(PI_ERR_NULL, "kernel_events[%d] is NULL", i);
+    const int d = attns[0].d, H = attns[0].H, dh = attns[0].dh;
+    const PredPlan ppl = plan_pred(d, preds[0].r, H, 1);
+    const AttnPlan apl = plan_attn(d, H, dh);
+    if ((st = check_ws(ws, ws_bytes, std::max(ppl.bytes, apl.bytes))) != PI_OK) return st;
+    const double tau = preds[0].threshold;
+    const float theta = (float)std::log(tau / (1.0 - tau));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    hipError_t e;
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
+        return hip_fail(e, "pi_attn_run start event");
+    for (int i = 0; i < nsteps; ++i) {
+        const long long g = s0 + i;
+        const int rep = (int)(g % nrep), t = (int)(g % T);
+        const uint16_t* xs = x + (size_t)t * d;
+        const float* os = o + (size_t)t * H * dh;
+        if ((e = launch_predict(preds[rep], ppl, xs, 1, theta, nullptr, mask, idx, count, w, s)) != hipSuccess)
+            return hip_fail(e, "pi_attn_run head predictor");
+        if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i]), s)) != hipSuccess)
+            return hip_fail(e, "pi_attn_run kernel event");
+        if ((e = launch_attn_qkv(attns[rep], xs, mask, qkv, s)) != hipSuccess)
+            return hip_fail(e, "pi_attn_run q/k/v");
+        if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i + 1]), s)) != hipSuccess)
+            return hip_fail(e, "pi_attn_run kernel event");
+        if ((e = launch_attn_out(attns[rep], apl, os, idx, count, y, w, s)) != hipSuccess)
+            return hip_fail(e, "pi_attn_run output projection");
+    }
+    if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
+        return hip_fail(e, "pi_attn_run end event");
+    return ok();
+}
+
+}  // extern "C"

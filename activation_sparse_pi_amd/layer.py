@@ -237,3 +237,77 @@ class DeviceLayer:
             y=torch.empty((B, self.d), dtype=torch.float32, device=dev),
             h=torch.empty((self.F,), dtype=torch.float32, device=dev),
         )
+
+
+class DeviceAttn:
+    """The attention side of one layer on the device: the head predictor (pi_predict with one
+    output per head) and the head-major projections for pi_attn_qkv / pi_attn_out.
+
+    ``inputs``: w_a1 fp16 [d, r], w_a2 fp16 [r, H], bias_a fp32 [H], w_qkv fp16 [H, 3, dh, d],
+    w_o fp16 [H, dh, d] and ``cfg`` (d, H, dh, r).  Replicas are independent copies (the bench
+    cycles through them so each step streams its weights from HBM)."""
+
+    def __init__(self, inputs: dict, replicas: int = 1, device: str = "cuda:0", threshold: float = 0.5):
+        cfg = inputs["cfg"]
+        self.cfg, self.d, self.H, self.dh, self.r = cfg, cfg.d, cfg.H, cfg.dh, cfg.r
+        self.device = torch.device(device)
+        self.replicas = replicas
+        host = {"w_a1": np.ascontiguousarray(inputs["w_a1"].T),      # [r, d]
+                "w_a2": np.ascontiguousarray(inputs["w_a2"].T),      # [H, r]
+                "bias_a": inputs["bias_a"], "w_qkv": inputs["w_qkv"], "w_o": inputs["w_o"]}
+        base = {k: _dev(v, self.device) for k, v in host.items()}
+        self.tensors = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(replicas - 1)]
+        self.pred = [L.PredDesc(t["w_a1"].data_ptr(), t["w_a2"].data_ptr(), t["bias_a"].data_ptr(),
+                                cfg.d, cfg.r, cfg.H, threshold) for t in self.tensors]
+        self.attn = [L.AttnDesc(t["w_qkv"].data_ptr(), t["w_o"].data_ptr(), cfg.d, cfg.H, cfg.dh)
+                     for t in self.tensors]
+        pb = L.pi_workspace_bytes(self.pred[0], None, 1)
+        ab = L.pi_attn_workspace_bytes(self.attn[0])
+        if pb == 0 or ab == 0:
+            raise L.PiError(L.PI_ERR_SHAPE, "the library rejected the attention layer: " + L.pi_last_error())
+        self.ws_bytes = max(pb, ab)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        L.check(L.pi_workspace_init(self.ws.data_ptr(), self.ws_bytes, self.stream()))
+
+    def stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def buffers(self) -> dict:
+        W = (self.H + 31) // 32
+        z = dict(dtype=torch.float32, device=self.device)
+        return {"logits": torch.empty(self.H, **z), "mask": torch.zeros(W, dtype=torch.int32, device=self.device),
+                "idx": torch.empty(self.H, dtype=torch.int32, device=self.device),
+                "count": torch.empty(1, dtype=torch.int32, device=self.device),
+                "qkv": torch.empty((self.H, 3, self.dh), **z), "y": torch.empty(self.d, **z)}
+
+    def predict(self, x, bufs: dict, rep: int = 0, logits: bool = True) -> None:
+        """pi_predict with the head predictor: head mask, head table (ascending) and count."""
+        L.check(L.pi_predict(self.pred[rep], x, 1, bufs["logits"].data_ptr() if logits else None,
+                             bufs["mask"].data_ptr(), bufs["idx"].data_ptr(), bufs["count"].data_ptr(),
+                             self.ws.data_ptr(), self.ws_bytes, self.stream()))
+
+    def qkv(self, x, bufs: dict, rep: int = 0) -> None:
+        L.check(L.pi_attn_qkv(self.attn[rep], x, bufs["mask"].data_ptr(), bufs["qkv"].data_ptr(), self.stream()))
+
+    def out(self, o, bufs: dict, rep: int = 0) -> None:
+        """o: device address of fp32 [H, dh] (the attention core's per-head output); the head
+        table is the one ``predict`` wrote into bufs."""
+        L.check(L.pi_attn_out(self.attn[rep], o, bufs["idx"].data_ptr(), bufs["count"].data_ptr(),
+                              bufs["y"].data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.stream()))
+
+    def run(self, x, o, T: int, s0: int, nsteps: int, bufs: dict, events=None, kernel_events=None) -> None:
+        """pi_attn_run: nsteps steps over tokens x (device fp16 [T, d]) and attention outputs o
+        (device fp32 [T, H, dh]), replicas rotating; events: None or two torch events;
+        kernel_events: None or 2 nsteps torch events around each step's q/k/v kernel."""
+        import ctypes
+        if not hasattr(self, "_pred_arr"):
+            self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
+            self._attn_arr = (L.AttnDesc * self.replicas)(*self.attn)
+
+        def handles(evs):
+            return None if evs is None else (ctypes.c_void_p * len(evs))(*[_event_handle(e) for e in evs])
+
+        L.check(L.pi_attn_run(self._pred_arr, self._attn_arr, self.replicas, x, o, T, s0, nsteps,
+                              bufs["mask"].data_ptr(), bufs["idx"].data_ptr(), bufs["count"].data_ptr(),
+                              bufs["qkv"].data_ptr(), bufs["y"].data_ptr(), handles(events),
+                              handles(kernel_events), self.ws.data_ptr(), self.ws_bytes, self.stream()))

@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5440)
     ap.add_argument("--warmup", type=int, default=1088)
-    ap.add_argument("--config", default="c5")
+    ap.add_argument("--config", default="c5", help="c1..c5 (FFN), a2 / a3 (attention side)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to bust the caches")
     ap.add_argument("--mode", choices=("kernels", "fused", "split", "persistent", "eager"), default="kernels",
                     help="kernels: one pi_decode_run call, three kernels per step (default); "
@@ -448,6 +448,124 @@ def bench_batch_sweep(a, cfg):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------------------- attention side
+def bytes_model_attn(cfg, n):
+    """Algorithmic bytes of one attention-side step with n predicted heads.
+    Head predictor: 2dr + 2rH (fp16 factors) + 4H (bias) + 2d (x) + the mask and the head table.
+    q/k/v: the n heads' 3 d_head rows of d fp16 (n 3 dh d 2), x 2d, the mask, qkv written for every
+    head (4 H 3 dh: zeros for the others).  Output: the n heads' d_head rows of W_o^T (n dh d 2),
+    their o values (4 n dh), the head table (4 n + 4), y 4d."""
+    d, H, dh, r = cfg.d, cfg.H, cfg.dh, cfg.r
+    mw = 4 * ((H + 31) // 32)
+    pred = 2 * d * r + 2 * r * H + 4 * H + 2 * d + mw + 4 * H
+    qkv = n * 3 * dh * d * 2 + 2 * d + mw + 4 * H * 3 * dh
+    out = n * dh * d * 2 + 4 * n * dh + 4 * n + 4 + 4 * d
+    return dict(pred=pred, qkv=qkv, out=out, total=pred + qkv + out)
+
+
+def cpu_baseline_attn(inputs, budget_s):
+    import oracle.attn_oracle as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    X, Ob = inputs["x"], inputs["o"]
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s and n < 4 * X.shape[0]:
+        A.attn_step(inputs, X[n % X.shape[0]], Ob[n % X.shape[0]])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} tokens of the same stream (wrapping), one at a time through the "
+                      f"attention-side oracle (head predictor, q/k/v and output projection of the "
+                      f"predicted heads), numpy float64, {dt:.1f} s",
+            "cpu_model": cpu_model(), **host_cpus()}
+
+
+def bench_attn(a, cfg):
+    """The attention side at batch 1: one step = the head predictor (pi_predict, one output per
+    head), the q/k/v projections of the predicted heads (pi_attn_qkv) and the output projection
+    over them (pi_attn_out) of one token, the attention core's output standing in as a seeded
+    input; K steps through one pi_attn_run call.  The roofline is the q/k/v kernel's, from
+    events around it in every step of a second pi_attn_run."""
+    import numpy as np
+    import torch
+
+    from activation_sparse_pi_amd.layer import DeviceAttn
+    from synth import attn as SA
+
+    dev = torch.device("cuda:0")
+    inputs = SA.make(cfg)
+    T = cfg.T
+    probe = bytes_model_attn(cfg, cfg.mean_rate * cfg.H)
+    R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
+    att = DeviceAttn(inputs, replicas=R, device=dev)
+    bufs = att.buffers()
+    xd = torch.from_numpy(inputs["x"].copy()).to(dev)                 # [T, d] in HBM
+    od = torch.from_numpy(inputs["o"].copy()).to(dev)                 # [T, H, dh]
+    heads = np.zeros(T)
+    for t in range(T):
+        att.predict(xd[t].data_ptr(), bufs, logits=False)
+        heads[t] = int(bufs["count"][0].item())
+    K = a.steps if a.steps != parse_defaults["steps"] else 2048
+    Wm = a.warmup if a.warmup != parse_defaults["warmup"] else 256
+    att.run(xd.data_ptr(), od.data_ptr(), T, 0, Wm, bufs)             # untimed warmup
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    att.run(xd.data_ptr(), od.data_ptr(), T, Wm, K, bufs, events=ev)  # timed: K steps
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[1])
+    Kr = min(K, 512)
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
+    torch.cuda.synchronize()
+    att.run(xd.data_ptr(), od.data_ptr(), T, Wm + K, Kr, bufs, kernel_events=kev)
+    torch.cuda.synchronize()
+    qkv_ms = np.array([kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(Kr)])
+    steps = (Wm + np.arange(K)) % T
+    rsteps = (Wm + K + np.arange(Kr)) % T
+    path_bytes = float(np.mean([bytes_model_attn(cfg, heads[t])["total"] for t in steps]))
+    qkv_bytes = float(np.mean([bytes_model_attn(cfg, heads[t])["qkv"] for t in rsteps]))
+    ms_per_step = total_ms / K
+    path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = qkv_bytes / (float(qkv_ms.mean()) * 1e-3) / 1e9
+    kernel_key = f"k_attn_qkv {cfg.name}"
+    copy_probe(a.copy_probe_mb, dev)
+    out = {
+        "metric": "attention-side decode tokens/sec at batch 1 (predicted heads only) + effective HBM GB/s (% of peak)",
+        "value": round(K / (total_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one attention block's predictor and projections, d={cfg.d}, "
+                        f"{cfg.H} heads of {cfg.dh}, fp16 weights, fp32 accumulate, head predictor "
+                        f"rank {cfg.r}, batch 1, {T}-token stream; the attention core's output is a "
+                        f"seeded input",
+            "d": cfg.d, "heads": cfg.H, "d_head": cfg.dh, "rank": cfg.r, "replicas": R,
+            "mean_predicted_heads": round(float(heads.mean()), 2),
+            "launch": "one pi_attn_run call: per step the head predictor (two kernels), q/k/v of the "
+                      "predicted heads (one kernel), the output projection over the head table (one kernel)",
+        },
+        "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": round(path_bytes)},
+        "roofline": {
+            "bound": "hbm", "kernel": kernel_key,
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(kernel_key),
+            "avg_us": round(float(qkv_ms.mean()) * 1e3, 3),
+            "bytes_per_launch": round(qkv_bytes),
+        },
+    }
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline_attn(inputs, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------------------- main
 def main():
     a = parse()
@@ -465,6 +583,9 @@ def main():
     from synth import configs, gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from synth import attn as SA
+    if a.config in SA.SHORT or a.config in SA.CONFIGS:
+        return bench_attn(a, SA.get(a.config))
     cfg = configs.get(a.config)
     if a.batch_sweep:
         return bench_batch_sweep(a, cfg)

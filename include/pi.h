@@ -409,6 +409,69 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
                  double hbm_gbs, uint32_t* mask, float* y, void* const* events, void* ws,
                  size_t ws_bytes, void* stream);
 
+/* ---- the attention side: head-sparse q/k/v and output projections ------------------------
+ * PowerInfer, "Adaptive Sparsity Predictors": every layer has a second predictor, for the
+ * self-attention block, and only the neurons it predicts are computed; "Neuron-aware Operator":
+ * their rows and columns are read in place.  The attention block's neurons are its heads (head h
+ * owns d_head rows each of W_q, W_k, W_v and d_head rows of W_o^T).  The head predictor is
+ * pi_predict with a pi_pred_desc of F = H (its factors W_a1 [d, r] and W_a2 [r, H] passed
+ * transposed as for the MLP predictor, H % 8 == 0); its mask (one bit per head, strict
+ * l > theta) drives the two calls below, and its index list is the head table.  The attention
+ * core over the KV cache is not part of this library: its per-head output o is an input here.
+ *
+ * Weights (fp16, head-major, caller-owned device memory):
+ *   w_qkv [H, 3, d_head, d]: head h's q rows, then its k rows, then its v rows, each row of d;
+ *   w_o   [H, d_head, d]:    head h's rows of W_o^T (y = sum_h sum_c o[h, c] w_o[h, c, :]).
+ * 8 <= d <= PI_ATTN_MAX_D with d % 8 == 0; 1 <= H <= PI_ATTN_MAX_HEADS; 1 <= d_head.        */
+#define PI_ATTN_MAX_HEADS 1024
+#define PI_ATTN_MAX_D 16384
+typedef struct pi_attn_desc {
+    const void* w_qkv;
+    const void* w_o;
+    int32_t d;
+    int32_t H;
+    int32_t dh;             /* d_head */
+} pi_attn_desc;
+
+/* Bytes of device workspace pi_attn_out needs (reusable across calls on one stream; zero-fill
+ * it once with pi_workspace_init: its arrival counters start at zero and are left at zero).
+ * 0 on an invalid descriptor.                                                                */
+size_t pi_attn_workspace_bytes(const pi_attn_desc* a);
+
+/* q, k and v of the predicted heads: qkv fp32 [H, 3, d_head] (device) gets, for every head h
+ * whose bit is set in head_mask (u32 [ceil(H/32)], device, as pi_predict writes it),
+ * qkv[h, m, c] = w_qkv[h, m, c, :] . x (fp32 accumulation), and 0 for every other head.
+ * x: fp16 [d], device, 16-byte aligned.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN before
+ * any HIP call; PI_ERR_HIP.                                                                  */
+int pi_attn_qkv(const pi_attn_desc* a, const uint16_t* x, const uint32_t* head_mask, float* qkv,
+                void* stream);
+
+/* The output projection over the predicted heads: y fp32 [d] (device) =
+ * sum over the heads h of the head table, c < d_head, of o[h, c] w_o[h, c, :], summed in a
+ * fixed order (bitwise reproducible).  heads int32 [*count] and count (device) are the table
+ * pi_predict writes (ascending head ids; ids outside [0, H) contribute nothing, a count above
+ * H is taken as H).  o: fp32 [H, d_head], device; only the listed heads' values are read.  An
+ * empty table gives y = 0.  ws: pi_attn_workspace_bytes(a) bytes, 256-byte aligned.
+ * Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_WORKSPACE before any HIP call;
+ * PI_ERR_HIP.                                                                                */
+int pi_attn_out(const pi_attn_desc* a, const float* o, const int32_t* heads, const int32_t* count,
+                float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* nsteps attention-side decode steps enqueued on `stream`: step i takes token t = (s0 + i) % T
+ * (x fp16 [T, d], device) through the replica (s0 + i) % nrep: the head predictor (pi_predict
+ * of preds[rep], F = H, fp16 factors) writes mask u32 [ceil(H/32)], the ascending head table idx
+ * int32 [H] and count [1]; pi_attn_qkv writes qkv fp32 [H, 3, d_head]; pi_attn_out projects
+ * o[t] (o fp32 [T, H, d_head], the attention core's output for token t) over those heads into
+ * y fp32 [d].  The outputs hold the last step's.  events: NULL or 2 hipEvent_t recorded around
+ * the enqueued work; kernel_events: NULL or 2 nsteps hipEvent_t recorded around each step's
+ * q/k/v kernel.  Workspace: max(pi_workspace_bytes(pred, NULL, 1), pi_attn_workspace_bytes(a)),
+ * zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_UNSUPPORTED (an
+ * int8 head predictor), PI_ERR_WORKSPACE before any HIP call; PI_ERR_HIP.                  */
+int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, const uint16_t* x,
+                const float* o, int T, long long s0, int nsteps, uint32_t* mask, int32_t* idx,
+                int32_t* count, float* qkv, float* y, void* const* events,
+                void* const* kernel_events, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

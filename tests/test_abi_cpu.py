@@ -210,3 +210,87 @@ def test_batch_run_validation():
     rate = np.full(4096, 0.1, np.float32)
     assert _batch_run(pred(), ffn(), schedule=L.PI_BATCH_AUTO, rate=rate.ctypes.data, ws=None) == \
         L.PI_ERR_WORKSPACE
+
+
+def attn(**kw):
+    a = dict(w_qkv=A, w_o=A + 0x1000000, d=4096, H=32, dh=128)
+    a.update(kw)
+    return L.AttnDesc(a["w_qkv"], a["w_o"], a["d"], a["H"], a["dh"])
+
+
+def test_attn_workspace_bytes():
+    n = L.pi_attn_workspace_bytes(attn())
+    # the down projection's counters and partial rows (and its unused up-output area)
+    assert n > 32 * 128 * 4 and n % 256 == 0
+    assert L.pi_attn_workspace_bytes(attn(H=8, dh=24, d=200)) > 0
+    for bad in (dict(d=12), dict(d=0), dict(d=L.PI_ATTN_MAX_D + 8), dict(H=0),
+                dict(H=L.PI_ATTN_MAX_HEADS + 1), dict(dh=0), dict(w_qkv=None), dict(w_o=A + 8)):
+        assert L.pi_attn_workspace_bytes(attn(**bad)) == 0, bad
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(desc=None), L.PI_ERR_NULL),
+    (dict(x=None), L.PI_ERR_NULL),
+    (dict(mask=None), L.PI_ERR_NULL),
+    (dict(qkv=None), L.PI_ERR_NULL),
+    (dict(x=A + 8), L.PI_ERR_ALIGN),
+    (dict(desc=attn(w_qkv=A + 4)), L.PI_ERR_ALIGN),
+    (dict(desc=attn(d=100)), L.PI_ERR_SHAPE),
+    (dict(desc=attn(H=2000)), L.PI_ERR_SHAPE),
+    (dict(desc=attn(dh=0)), L.PI_ERR_SHAPE),
+    (dict(desc=attn(d=16384, H=1024, dh=1024)), L.PI_ERR_SHAPE),
+])
+def test_attn_qkv_validation(kw, code):
+    a = dict(desc=attn(), x=A, mask=A + 0x100, qkv=A + 0x200)
+    a.update(kw)
+    assert L.pi_attn_qkv(a["desc"], a["x"], a["mask"], a["qkv"], None) == code, L.pi_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), L.PI_ERR_NULL),
+    (dict(heads=None), L.PI_ERR_NULL),
+    (dict(count=None), L.PI_ERR_NULL),
+    (dict(y=None), L.PI_ERR_NULL),
+    (dict(y=A + 4), L.PI_ERR_ALIGN),
+    (dict(ws=None), L.PI_ERR_WORKSPACE),
+    (dict(ws=A + 64), L.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), L.PI_ERR_WORKSPACE),
+    (dict(desc=attn(d=4100)), L.PI_ERR_SHAPE),
+])
+def test_attn_out_validation(kw, code):
+    d = attn()
+    a = dict(desc=d, o=A, heads=A + 0x100, count=A + 0x180, y=A + 0x200, ws=A + 0x10000,
+             ws_bytes=L.pi_attn_workspace_bytes(d))
+    a.update(kw)
+    assert L.pi_attn_out(a["desc"], a["o"], a["heads"], a["count"], a["y"], a["ws"], a["ws_bytes"],
+                         None) == code, L.pi_last_error()
+
+
+def test_attn_run_validation():
+    import ctypes
+    d = attn(d=4096, H=32, dh=128)
+    p = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 32, 0.5)
+    preds, attns = (L.PredDesc * 1)(p), (L.AttnDesc * 1)(d)
+    ws_need = max(L.pi_workspace_bytes(p, None, 1), L.pi_attn_workspace_bytes(d))
+    base = dict(preds=preds, attns=attns, nrep=1, x=A, o=A + 0x10000, T=4, s0=0, n=2, mask=A + 0x20000,
+                idx=A + 0x20100, count=A + 0x20200, qkv=A + 0x30000, y=A + 0x40000, ev=None, kev=None,
+                ws=A + 0x100000, ws_bytes=ws_need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.pi_attn_run(a["preds"], a["attns"], a["nrep"], a["x"], a["o"], a["T"], a["s0"], a["n"],
+                             a["mask"], a["idx"], a["count"], a["qkv"], a["y"], a["ev"], a["kev"],
+                             a["ws"], a["ws_bytes"], None)
+    assert call(preds=None) == L.PI_ERR_NULL
+    assert call(nrep=0) == L.PI_ERR_SHAPE
+    assert call(T=0) == L.PI_ERR_SHAPE
+    assert call(o=None) == L.PI_ERR_NULL
+    assert call(x=A + 8) == L.PI_ERR_ALIGN
+    assert call(ws_bytes=ws_need - 256) == L.PI_ERR_WORKSPACE
+    bad = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 40, 0.5)   # F != H
+    assert call(preds=(L.PredDesc * 1)(bad)) == L.PI_ERR_SHAPE, L.pi_last_error()
+    i8 = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 32, 0.5, L.PI_P_I8G128,
+                    A + 0x6000000, A + 0x7000000)
+    assert call(preds=(L.PredDesc * 1)(i8)) == L.PI_ERR_UNSUPPORTED, L.pi_last_error()
+    assert call(ev=(ctypes.c_void_p * 2)(None, None)) == L.PI_ERR_NULL
+    assert call(kev=(ctypes.c_void_p * 4)(A, A, None, A)) == L.PI_ERR_NULL
