@@ -124,7 +124,7 @@ def lib() -> ctypes.CDLL:
         L.pi_place_neurons_hot.restype = c_int
         L.pi_batch_run.argtypes = [P(PredDesc), P(FfnDesc), c_int, c_void_p, c_int, c_int,
                                    ctypes.c_longlong, c_int, c_int, c_void_p, ctypes.c_double,
-                                   c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.pi_batch_run.restype = c_int
         L.pi_count_active.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p]
         L.pi_count_active.restype = c_int
@@ -244,11 +244,11 @@ def pi_place_neurons_hot(counts: int, F: int, ntok: int, hot_rate: float, perm: 
 
 
 def pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs, mask, y, events,
-                 ws, ws_bytes, stream) -> int:
+                 kernel_events, ws, ws_bytes, stream) -> int:
     """preds / ffns: ctypes arrays; rate: host address (float32 [F]) or None; events: ctypes array
-    of two hipEvent_t handles or None."""
+    of two hipEvent_t handles or None; kernel_events: ctypes array of 2 nsteps handles or None."""
     return lib().pi_batch_run(preds, ffns, nrep, x, T, B, s0, nsteps, schedule, rate, hbm_gbs, mask,
-                              y, events, ws, ws_bytes, stream)
+                              y, events, kernel_events, ws, ws_bytes, stream)
 
 
 def pi_attn_workspace_bytes(a) -> int:

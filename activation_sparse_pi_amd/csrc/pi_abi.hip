@@ -597,8 +597,8 @@ int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_g
 
 int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
                  int T, int B, long long s0, int nsteps, int schedule, const float* rate,
-                 double hbm_gbs, uint32_t* mask, float* y, void* const* events, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 double hbm_gbs, uint32_t* mask, float* y, void* const* events,
+                 void* const* kernel_events, void* ws, size_t ws_bytes, void* stream) {
     int st;
     if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
     if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
@@ -632,6 +632,13 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
         sched = tu < tt ? PI_BATCH_UNION : PI_BATCH_TOKENS;
     }
     if (sched == PI_BATCH_UNION && B == 1) sched = PI_BATCH_TOKENS;     // nothing to unite
+    if (kernel_events) {
+        if (sched != PI_BATCH_UNION || batch_groups(B) != 1)
+            return fail(PI_ERR_SHAPE, "kernel_events need the union schedule in one pass (2 <= B <= %d)",
+                        PI_MAX_BATCH);
+        for (int i = 0; i < 2 * nsteps; ++i)
+            if (!kernel_events[i]) return fail(PI_ERR_NULL, "kernel_events[%d] is NULL", i);
+    }
     if (sched == PI_BATCH_UNION) {
         if (ffns[0].wfmt != PI_W_F16 || preds[0].pfmt != PI_P_F16)
             return fail(PI_ERR_UNSUPPORTED, "the union schedule takes fp16 weights and an fp16 predictor");
@@ -679,10 +686,17 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
                 const FfnPlan fpl = plan_ffn(d, F, Fd.wfmt, Bg);
                 // the union FFN builds the union's list from the union mask itself
                 if ((e = launch_predict_batch(P, ppl, xs + (size_t)b0 * d, Bg, theta, nullptr,
-                                              mask + (size_t)b0 * W, w, s, umask, tokbits)) != hipSuccess ||
-                    (e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, umask, tokbits, uidx, ucount,
+                                              mask + (size_t)b0 * W, w, s, umask, tokbits)) != hipSuccess)
+                    return hip_fail(e, "pi_batch_run union pass");
+                if (kernel_events &&
+                    (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i]), s)) != hipSuccess)
+                    return hip_fail(e, "pi_batch_run kernel event");
+                if ((e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, umask, tokbits, uidx, ucount,
                                           mask + (size_t)b0 * W, y + (size_t)b0 * d, w, s)) != hipSuccess)
                     return hip_fail(e, "pi_batch_run union pass");
+                if (kernel_events &&
+                    (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i + 1]), s)) != hipSuccess)
+                    return hip_fail(e, "pi_batch_run kernel event");
             }
         }
     }

@@ -176,19 +176,22 @@ class DeviceLayer:
 
     def batch_run(self, x, T: int, B: int, s0: int, nsteps: int, mask, y,
                   schedule: int = L.PI_BATCH_AUTO, rate=None, hbm_gbs: float = 8000.0,
-                  events=None) -> None:
+                  events=None, kernel_events=None) -> None:
         """pi_batch_run: nsteps steps of B tokens (x: device address of fp16 [T, B, d]); mask /
         y: device addresses of [B, ceil(F/32)] u32 and [B, d] fp32 (the last step's); rate: host
-        float32 ndarray [F] (for PI_BATCH_AUTO) or None; events: None or two torch events."""
+        float32 ndarray [F] (for PI_BATCH_AUTO) or None; events: None or two torch events;
+        kernel_events: None or 2 nsteps torch events around each step's union FFN."""
         import ctypes
         if not hasattr(self, "_pred_arr"):
             self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)
             self._ffn_arr = (L.FfnDesc * self.replicas)(*self.ffn)
         ev = None if events is None else (ctypes.c_void_p * 2)(*[_event_handle(e) for e in events])
+        kev = None if kernel_events is None else \
+            (ctypes.c_void_p * len(kernel_events))(*[_event_handle(e) for e in kernel_events])
         rp = None if rate is None else np.ascontiguousarray(rate, dtype=np.float32)
         L.check(L.pi_batch_run(self._pred_arr, self._ffn_arr, self.replicas, x, T, B, s0, nsteps,
                                schedule, None if rp is None else rp.ctypes.data, hbm_gbs, mask, y, ev,
-                               self.ws.data_ptr(), self.ws_bytes, self.stream()))
+                               kev, self.ws.data_ptr(), self.ws_bytes, self.stream()))
 
     def decode_run_noalloc(self, x, T: int, s0: int, nsteps: int, bufs: dict,
                            mode: int = L.PI_RUN_AUTO) -> None:

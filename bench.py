@@ -257,8 +257,8 @@ def bench_batch(a, cfg):
     """Small-batch decode: one step = the B independent tokens of one batch through the union
     schedule of pi_batch_run (batch predictor with per-token masks and their union, the union's
     neuron table, the union FFN on MFMA where every token gets only its own neurons).  The K
-    timed steps are one pi_batch_run call.  The roofline pass times the union FFN pair alone,
-    through the operators (pi_predict, pi_compact, pi_sparse_ffn), events around pi_sparse_ffn."""
+    timed steps are one pi_batch_run call; the roofline comes from a second call with events
+    around every step's union FFN (its two kernels)."""
     import torch
 
     from activation_sparse_pi_amd.layer import DeviceLayer
@@ -281,43 +281,25 @@ def bench_batch(a, cfg):
         n_tok[t] = bufs["count"][:B].cpu().numpy()
         U[t] = int(bufs["ucount"][0].item())
 
-    def step(s, ev=None):
-        t, rep = s % T, s % R
-        xp = xd[t].data_ptr()
-        # masks only: the union FFN needs the per-token masks and their union list
-        layer.predict(xp, B, None, bufs["mask"].data_ptr(), None, None, rep)
-        layer.compact(bufs["mask"].data_ptr(), B, 1, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr())
-        if ev is not None:
-            ev[0].record()
-        layer.sparse_ffn(xp, B, bufs["uidx"].data_ptr(), bufs["ucount"].data_ptr(),
-                         bufs["mask"].data_ptr(), bufs["y"].data_ptr(), rep)
-        if ev is not None:
-            ev[1].record()
-
     from activation_sparse_pi_amd import _lib as L
     mask_r = torch.empty((B, (cfg.F + 31) // 32), dtype=torch.int32, device=dev)
     y_r = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
     layer.batch_run(xd.data_ptr(), T, B, 0, Wm, mask_r.data_ptr(), y_r.data_ptr(),
                     schedule=L.PI_BATCH_UNION)                                   # untimed warmup
     t01 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for e in t01:
-        e.record()
     torch.cuda.synchronize()
     layer.batch_run(xd.data_ptr(), T, B, Wm, K, mask_r.data_ptr(), y_r.data_ptr(),
                     schedule=L.PI_BATCH_UNION, events=t01)                       # timed: K steps
     torch.cuda.synchronize()
     total_ms = t01[0].elapsed_time(t01[1])
-    # roofline pass: the union FFN pair alone, events around pi_sparse_ffn
+    # roofline pass: the same call with events around every step's union FFN
     Kr = min(K, 128)
-    for s in range(8):
-        step(s)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(Kr)]
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
     torch.cuda.synchronize()
-    for s in range(Kr):
-        step(Wm + K + s, ev[s])
+    layer.batch_run(xd.data_ptr(), T, B, Wm + K, Kr, mask_r.data_ptr(), y_r.data_ptr(),
+                    schedule=L.PI_BATCH_UNION, kernel_events=kev)
     torch.cuda.synchronize()
-    ffn_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    ffn_ms = np.array([kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(Kr)])
     steps = (Wm + np.arange(K)) % T
     rsteps = (Wm + K + np.arange(Kr)) % T
     ffn_bytes = float(np.mean([bytes_model_batch(cfg, n_tok[t], U[t])["ffn"] for t in rsteps]))

@@ -399,15 +399,17 @@ int pi_batch_plan(const pi_ffn_desc* ffn, int B, const float* rate, double hbm_g
  *                    (2 d r + 2 r F) added once per token to the first and once per pass to the
  *                    second.
  * 1 <= B <= PI_MAX_BATCH_RUN.  mask u32 [B, ceil(F/32)] and y fp32 [B, d] hold the last step's
- * per-token masks and outputs.  events: NULL or 2 hipEvent_t recorded around the enqueued work.
+ * per-token masks and outputs.  events: NULL or 2 hipEvent_t recorded around the enqueued work;
+ * kernel_events: NULL or 2 nsteps hipEvent_t recorded around each step's union FFN (the union
+ * schedule in one pass only, 2 <= B <= PI_MAX_BATCH; PI_ERR_SHAPE otherwise).
  * Workspace: pi_workspace_bytes(pred, ffn, min(B, 32)) with both descriptors given (B_max > 1
  * includes the union list), zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN,
  * PI_ERR_DTYPE (schedule), PI_ERR_UNSUPPORTED (the union schedule on int4 weights or an int8
  * predictor), PI_ERR_WORKSPACE, PI_ERR_HIP; all but the last before any HIP call.           */
 int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, const uint16_t* x,
                  int T, int B, long long s0, int nsteps, int schedule, const float* rate,
-                 double hbm_gbs, uint32_t* mask, float* y, void* const* events, void* ws,
-                 size_t ws_bytes, void* stream);
+                 double hbm_gbs, uint32_t* mask, float* y, void* const* events,
+                 void* const* kernel_events, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- the attention side: head-sparse q/k/v and output projections ------------------------
  * PowerInfer, "Adaptive Sparsity Predictors": every layer has a second predictor, for the

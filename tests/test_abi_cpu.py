@@ -187,7 +187,7 @@ def _batch_run(p, f, B=4, schedule=L.PI_BATCH_UNION, ws=WS, wsb=WSB, rate=None, 
     a = dict(x=A + 0x3000000, mask=A + 0x4000000, y=A + 0x7000000)
     a.update(kw)
     return L.pi_batch_run(preds, ffns, 1, a["x"], 4, B, 0, 2, schedule, rate, 8000.0, a["mask"],
-                          a["y"], None, ws, wsb, None)
+                          a["y"], None, a.get("kev"), ws, wsb, None)
 
 
 def test_batch_run_validation():
@@ -210,6 +210,11 @@ def test_batch_run_validation():
     rate = np.full(4096, 0.1, np.float32)
     assert _batch_run(pred(), ffn(), schedule=L.PI_BATCH_AUTO, rate=rate.ctypes.data, ws=None) == \
         L.PI_ERR_WORKSPACE
+    import ctypes
+    kev = (ctypes.c_void_p * 4)(A, A, A, A)
+    assert _batch_run(pred(), ffn(), B=40, kev=kev) == L.PI_ERR_SHAPE                  # two passes
+    assert _batch_run(pred(), ffn(), schedule=L.PI_BATCH_TOKENS, kev=kev) == L.PI_ERR_SHAPE
+    assert _batch_run(pred(), ffn(), kev=(ctypes.c_void_p * 4)(A, None, A, A)) == L.PI_ERR_NULL
 
 
 def attn(**kw):

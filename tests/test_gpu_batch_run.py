@@ -119,6 +119,18 @@ def test_batch_run_c4_shape(B):
     worst = _check_step(inp, W, inp["x"][1], mask, y, f"c4 B={B}")
     mu, yu = _run(layer, cfg, xd, B, 1, 1, L.PI_BATCH_UNION)
     assert np.array_equal(mu, mask) and np.array_equal(yu, y), "AUTO must have taken the union schedule"
+    if B <= L.PI_MAX_BATCH:
+        # events around each step's union FFN change nothing in the results and all complete
+        W = (cfg.F + 31) // 32
+        mk = torch.full((B, W), -1, dtype=torch.int32, device="cuda")
+        yk = torch.full((B, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+        kev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        layer.batch_run(xd.data_ptr(), cfg.T, B, 0, 2, mk.data_ptr(), yk.data_ptr(),
+                        schedule=L.PI_BATCH_UNION, kernel_events=kev)
+        torch.cuda.synchronize()
+        assert np.array_equal(mk.cpu().numpy().view(np.uint32), mask) and \
+            np.array_equal(yk.cpu().numpy().astype(np.float64), y), "kernel events changed the results"
+        assert all(kev[2 * i].elapsed_time(kev[2 * i + 1]) > 0 for i in range(2))
     say(f"  worst rel-L2 {worst:.2e}")
 
 
