@@ -152,13 +152,16 @@ BatchWs batch_ws(size_t base, int F) {
     return w;
 }
 
-// The batch-size dispatch estimate (pi_batch_plan).  The fixed costs and bandwidth fractions are
-// fitted to this library's own measurements on MI355X (one FFN layer of d = 8192, F = 32768, fp16,
-// ReLU, 8% of the neurons per token, B = 1 .. 32): the batch-1 operators move a token's rows at
-// ~40% of peak after ~4 us of launches and ramps; the union path (compaction + two MFMA kernels)
-// moves the union's rows at ~63% after ~15 us.  B > 32 runs as union passes of at most 32 tokens.
-constexpr double BATCH_TOK_FIXED_US = 4.0, BATCH_TOK_EFF = 0.40;
-constexpr double BATCH_UNION_FIXED_US = 15.0, BATCH_UNION_EFF = 0.63;
+// The batch-size dispatch estimate (pi_batch_plan, pi_batch_run's automatic choice).  The fixed
+// costs and bandwidth fractions are fitted (least squares on relative error) to pi_batch_run's
+// own step times on MI355X over three layers -- d 4096 / F 11008 ReGLU, d 7168 / F 28672 ReLU,
+// d 8192 / F 32768 ReLU, fp16, B = 1 .. 64, predictor included: a token through the batch-1
+// kernel schedule costs ~9 us plus its rows and predictor at ~69% of peak; a union pass ~52 us
+// (five dependent kernels) plus the union's rows and one predictor pass at ~84%.  The fit is
+// within 17% of every measured step and picks the faster schedule at every point but one, where
+// the two differ by 1%.  B > 32 runs as union passes of at most 32 tokens.
+constexpr double BATCH_TOK_FIXED_US = 9.0, BATCH_TOK_EFF = 0.69;
+constexpr double BATCH_UNION_FIXED_US = 51.8, BATCH_UNION_EFF = 0.845;
 
 int batch_groups(int B) { return (B + PI_MAX_BATCH - 1) / PI_MAX_BATCH; }
 // size of group g of B tokens split into batch_groups(B) near-equal groups

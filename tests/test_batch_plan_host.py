@@ -67,13 +67,21 @@ def test_one_token_and_int4_take_the_token_path():
 
 
 def test_overlap_decides():
-    """Identical lists (rates 0 or 1): the union costs one token's rows, so it wins at any
-    B > 1; disjoint-looking sparse rates at small B keep the token path's lower fixed cost."""
+    """Identical lists (rates 0 or 1): the union pass reads one token's rows for all B tokens,
+    so once B tokens' rows outweigh the union pass's larger fixed cost it wins, and it keeps
+    winning as B grows; sparse, barely overlapping lists stay on the token path."""
     F = 32768
     rate = np.zeros(F, np.float32)
     rate[:2600] = 1.0
-    p = plan(rate, 2, ffn(F=F))
-    assert p.u_mean == pytest.approx(2600) and p.choice == L.PI_BATCH_UNION
+    picks = []
+    for B in (2, 4, 8, 16, 32):
+        p = plan(rate, B, ffn(F=F))
+        assert p.u_mean == pytest.approx(2600)
+        # the union's estimate does not grow with B (one pass), the tokens' grows linearly
+        picks.append(p.choice)
+    assert picks[-1] == L.PI_BATCH_UNION
+    first = picks.index(L.PI_BATCH_UNION)
+    assert all(c == L.PI_BATCH_UNION for c in picks[first:]), picks
     sparse = np.full(F, 4.0 / F, np.float32)            # ~4 neurons per token
     q = plan(sparse, 2, ffn(F=F))
     assert q.choice == L.PI_BATCH_TOKENS
