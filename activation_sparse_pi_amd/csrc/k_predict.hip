@@ -15,7 +15,8 @@
 //   stage 1  one wave per row j; x slice in registers; 64-lane reduction.
 //   stage 2  one block per 64-neuron tile, 8 waves x 8 rows; z staged in LDS;
 //            one wave ballot turns the tile's 64 decisions into two mask words;
-//            the last-arriving block compacts the mask into the ascending table.
+//            the last-arriving block compacts the mask into the ascending table; with one
+//            tile (F <= 64, one token) the single block writes the table from its ballot.
 #include "device_common.h"
 #include "internal.h"
 
@@ -212,6 +213,50 @@ __global__ __launch_bounds__(P2_WAVES * 64) void k_p2(const float* __restrict__ 
     }
 }
 
+// One token and at most 64 neurons (one tile, so one block: the attention side's head
+// predictor has one output per head).  The W2t rows and the bias go out before z is staged,
+// and the block writes the mask words and the ascending table straight from its ballot -- no
+// arrival counter and no second pass over the mask.
+template <bool P8>
+__global__ __launch_bounds__(P2_WAVES * 64) void k_p2_one(const float* __restrict__ z,
+                                                 const void* __restrict__ W2t,
+                                                 const uint16_t* __restrict__ S2,
+                                                 const float* __restrict__ bias, int r, int F,
+                                                 float theta, float* __restrict__ logits,
+                                                 uint32_t* __restrict__ mask,
+                                                 int32_t* __restrict__ idx,
+                                                 int32_t* __restrict__ count) {
+    extern __shared__ __align__(16) float s_z[];   // [r]
+    __shared__ float s_l[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    TileRows<P2_WAVES, P8> tr;
+    tile_rows_load<P2_WAVES, P8>(tr, W2t, S2, r, F, 0, 0);
+    const float bv = bias[lane < F ? lane : 0];
+    for (int i = tid; i < r; i += P2_WAVES * 64) s_z[i] = z[i];
+    __syncthreads();
+    float acc[TileRows<P2_WAVES, P8>::RPW] = {};
+    tile_rows_fma<P2_WAVES, P8>(tr, s_z, r, 0, acc);
+    for (int c0 = TILE_SEG<P8>; c0 < tile_chunks<P8>(r); c0 += TILE_SEG<P8>) {
+        tile_rows_load<P2_WAVES, P8>(tr, W2t, S2, r, F, 0, c0);
+        tile_rows_fma<P2_WAVES, P8>(tr, s_z, r, c0, acc);
+    }
+    tile_rows_store<P2_WAVES>(acc, s_l);
+    __syncthreads();
+    if (wave != 0) return;
+    const float l = s_l[lane] + bv;
+    const bool act = lane < F && l > theta;
+    if (logits != nullptr && lane < F) logits[lane] = l;
+    const unsigned long long bal = __ballot(act);
+    if (lane == 0) {
+        mask[0] = (uint32_t)bal;
+        if (F > 32) mask[1] = (uint32_t)(bal >> 32);
+    }
+    if (idx != nullptr) {
+        if (act) idx[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = lane;
+        if (lane == 0) *count = __popcll(bal);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,
@@ -283,6 +328,15 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     hipError_t e = launch_pred_stage1(p, pl, x, B, z, s);
     if (e != hipSuccess) return e;
+    if (p.F <= 64 && p.r <= 8192) {      // z (r floats) in LDS next to the static arrays
+        if (p.pfmt == PI_P_I8G128)
+            hipLaunchKernelGGL(k_p2_one<true>, dim3(1), dim3(P2_WAVES * 64), (size_t)p.r * sizeof(float), s, z,
+                               p.w_p2t, p.s_p2t, p.bias, p.r, p.F, theta, logits, mask, idx, count);
+        else
+            hipLaunchKernelGGL(k_p2_one<false>, dim3(1), dim3(P2_WAVES * 64), (size_t)p.r * sizeof(float), s, z,
+                               p.w_p2t, nullptr, p.bias, p.r, p.F, theta, logits, mask, idx, count);
+        return hipGetLastError();
+    }
     if (p.pfmt == PI_P_I8G128)
         hipLaunchKernelGGL(k_p2<true>, dim3(pl.nblk2), dim3(P2_WAVES * 64), pl.lds2, s, z, B, p.w_p2t, p.s_p2t,
                            p.bias, p.r, p.F, theta, pl.nbz, logits, mask, idx, count, cnt + CNT_PRED2);

@@ -160,3 +160,41 @@ def test_attn_run(cfg):
              y=b1["y"].cpu().numpy().astype(np.float64))
     eq, ey, nh = _check(inp, g, inp["x"][t], inp["o"][t], f"{cfg.name} run")
     say(f"[gpu] {cfg.name} pi_attn_run: {nh} heads, qkv {eq:.2e}, y {ey:.2e}")
+
+
+ONE_TILE = [
+    SA.tiny(d=16384, H=64, dh=1, r=1000, T=3, seed=45, mean_rate=0.4),   # two row segments, 250 blocks
+    SA.tiny(d=4104, H=40, dh=2, r=8, T=3, seed=46),                      # two blocks, F past one word
+    SA.tiny(d=264, H=64, dh=1, r=64, T=3, seed=47, mean_rate=0.9),
+]
+
+
+@pytest.mark.parametrize("cfg", ONE_TILE, ids=lambda c: c.name)
+def test_head_predictor_one_tile(cfg):
+    """pi_predict at one token and F <= 64 (one launch, logits summed from per-block partial rows
+    by the last block): logits within 5e-5 of the oracle's fp64 logits, the head set equal to the
+    oracle's outside the band, the mask the bitmask of the table; every call of a token gives the
+    same bits (the arrival counter resets itself), with or without the logits output."""
+    say(f"[gpu] one-tile predictor {cfg.name}")
+    inp = SA.make(cfg)
+    att = _dev_attn(inp)
+    xd = torch.from_numpy(inp["x"].copy()).to(att.device)
+    first = None
+    for rnd in range(2):
+        for t in range(cfg.T):
+            bufs = att.buffers()
+            att.predict(xd[t].data_ptr(), bufs, logits=(rnd == 0))
+            torch.cuda.synchronize()
+            n = int(bufs["count"][0].item())
+            heads = bufs["idx"][:n].cpu().numpy().astype(np.int64)
+            mask = bufs["mask"].cpu().numpy().view(np.uint32).copy()
+            ref_L = A.head_logits(inp["x"][t], inp["w_a1"], inp["w_a2"], inp["bias_a"])
+            if rnd == 0:
+                lg = bufs["logits"].cpu().numpy().astype(np.float64)
+                assert np.max(np.abs(lg - ref_L)) < 5e-5, f"{cfg.name} t={t}: logits"
+                P.check_index_set(heads, mask, ref_L, cfg.H, ctx=f"{cfg.name} t={t}")
+                first = first or {}
+                first[t] = (heads, mask)
+            else:
+                assert np.array_equal(heads, first[t][0]) and np.array_equal(mask, first[t][1]), \
+                    f"{cfg.name} t={t}: a second call differs"

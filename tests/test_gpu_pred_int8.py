@@ -52,6 +52,7 @@ TINY8 = [
     configs.tiny("reglu", "f16", d=1024, F=2000, r=256, seed=52),
     configs.tiny("reglu", "i4g128", d=384, F=1000, r=128, seed=53),
     configs.tiny("relu", "f16", d=128, F=8, r=128, seed=54, mean_rate=0.5),
+    configs.tiny("reglu", "f16", d=256, F=64, r=256, seed=56, mean_rate=0.4),   # one full tile
     # d >= 3200: stage 1 takes one row per block with four waves (208 chunks of 16 weights,
     # split raggedly: the fourth wave holds 16), also in the multi-step conversion variant
     configs.tiny("reglu", "f16", d=3328, F=1000, r=256, seed=55),
