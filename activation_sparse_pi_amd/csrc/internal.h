@@ -181,7 +181,8 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
 
 // ---- attention side ----------------------------------------------------------------------
 struct AttnPlan {
-    FfnPlan ffn;              // the down projection over the H d_head rows of W_o^T
+    int nslices;              // 512-column slices of the output projection
+    size_t off_part;          // its partial rows: H x d floats (one per head-table entry)
     size_t bytes;
 };
 AttnPlan plan_attn(int d, int H, int dh);

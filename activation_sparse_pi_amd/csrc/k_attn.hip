@@ -12,10 +12,14 @@
 //        registers and has both rows' 16-byte loads (every chunk of the row) in flight at once.
 //        A head's 3 d_head rows are contiguous, so the stream over an active head is one
 //        sequential read of 6 d_head d bytes.
-//   out  y = sum over predicted heads h, c < d_head of o[h, c] W_o[h, c, :]: the column-sparse
-//        axpy of the FFN's down projection over the rows of the predicted heads, run by the
-//        batch-1 down kernel with the head table as its list (an entry stands for its head's
-//        d_head consecutive rows; o read by row).
+//   out  y = sum over predicted heads h, c < d_head of o[h, c] W_o[h, c, :].  Block (s, j) takes
+//        entry j of the head table over the 512-column slice s: its head's d_head rows (one
+//        contiguous d_head d block of W_o) are all in flight at once, 8 per wave, 1 KB per row.
+//        The block's column sums go to partial row j with agent-scope stores, and the last of
+//        the slice's H blocks to arrive (entries past the count arrive without work) sums rows
+//        j < count in a fixed order into y.  The grid's slice dimension is padded to a multiple
+//        of 8, so block s + 8k j of the dispatch order -- and with it every block of slice s --
+//        lands on XCD s mod 8, and the hand-off stays inside one L2.
 #include "device_common.h"
 #include "internal.h"
 
@@ -75,6 +79,94 @@ hipError_t qkv_launch(const pi_attn_desc& a, const uint16_t* x, const uint32_t* 
     return hipGetLastError();
 }
 
+constexpr int AO_WAVES = 16;                         // 1024 threads over a 512-column slice
+constexpr int AO_COLS = 512;
+constexpr int AO_U = 8;                              // rows in flight per wave
+
+__global__ __launch_bounds__(64 * AO_WAVES) void k_attn_out(const uint16_t* __restrict__ Wo,
+                                                          const float* __restrict__ o,
+                                                          const int32_t* __restrict__ heads,
+                                                          const int32_t* __restrict__ count, int d,
+                                                          int H, int dh, int nslices,
+                                                          float* __restrict__ part,
+                                                          float* __restrict__ y,
+                                                          unsigned* __restrict__ counters) {
+    __shared__ float4 s_red[AO_WAVES][AO_COLS / 4];
+    __shared__ float s_half[AO_COLS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slice = blockIdx.x, j = blockIdx.y;
+    if (slice >= nslices) return;                    // padding of the slice dimension
+    const int nc = d >> 3;
+    const int c = slice * 64 + lane;                 // this lane's 16-byte chunk (8 columns)
+    const bool cok = c < nc;
+    const int cc = cok ? c : 0;
+    const int n = min(*count, H);
+    const int col = tid & (AO_COLS - 1), hf = tid >> 9;
+    const int gcol = slice * AO_COLS + col;
+    if (j < n) {
+        const int hd = heads[j];
+        const bool hok = (unsigned)hd < (unsigned)H;
+        const size_t hrow = (size_t)(hok ? hd : 0) * dh;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int i0 = wave; i0 < dh; i0 += AO_WAVES * AO_U) {
+            uint4 w[AO_U];
+            float ov[AO_U];
+            // unconditional clamped loads, discarded at use (a lane-guarded load is waited for
+            // on the spot)
+#pragma unroll
+            for (int u = 0; u < AO_U; ++u) {
+                const int i = i0 + AO_WAVES * u;
+                const size_t rw = hrow + (i < dh ? i : 0);
+                w[u] = ld16(Wo + rw * d + 8 * (size_t)cc);
+                ov[u] = o[rw];
+            }
+#pragma unroll
+            for (int u = 0; u < AO_U; ++u) {
+                const float hv = (hok && cok && i0 + AO_WAVES * u < dh) ? ov[u] : 0.f;
+                const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = fmaf(hv, lo_f(ww[e]), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(hv, hi_f(ww[e]), acc[2 * e + 1]);
+                }
+            }
+        }
+        s_red[wave][2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        s_red[wave][2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        __syncthreads();
+        // 1024 threads over 512 columns: half hf sums waves [8 hf, 8 hf + 8) in order
+        const float* sr = reinterpret_cast<const float*>(s_red);
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < AO_WAVES / 2; ++w) t += sr[(hf * (AO_WAVES / 2) + w) * AO_COLS + col];
+        if (hf == 1) s_half[col] = t;
+        __syncthreads();
+        if (hf == 0 && gcol < d) st_agent(&part[(size_t)j * d + gcol], t + s_half[col]);
+    }
+    if (!last_block_arrive(&counters[slice], (unsigned)H)) return;
+    // rows j < n: half hf takes j = hf, hf + 2, ... (16 loads in flight), then the halves meet
+    float t = 0.f;
+    if (gcol < d) {
+        for (int b0 = hf; b0 < n; b0 += 32) {
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int jj = b0 + 2 * k;
+                v[k] = ld_agent(&part[(size_t)(jj < n ? jj : 0) * d + gcol]);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (b0 + 2 * k < n) t += v[k];
+        }
+    }
+    __syncthreads();
+    if (hf == 1) s_half[col] = t;
+    __syncthreads();
+    if (hf == 0 && gcol < d) y[gcol] = t + s_half[col];
+}
+
 }  // namespace
 
 hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint32_t* hmask,
@@ -88,23 +180,23 @@ hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint3
 }
 
 AttnPlan plan_attn(int d, int H, int dh) {
+    (void)dh;
     AttnPlan p{};
-    p.ffn = plan_ffn(d, H * dh, PI_W_F16, 1);
-    p.bytes = p.ffn.bytes;
+    p.nslices = (d + AO_COLS - 1) / AO_COLS;          // <= 32 (d <= PI_ATTN_MAX_D)
+    p.off_part = align_up(COUNTER_BYTES, 256);
+    p.bytes = align_up(p.off_part + (size_t)H * d * sizeof(float), 256);
     return p;
 }
 
 hipError_t launch_attn_out(const pi_attn_desc& a, const AttnPlan& pl, const float* o,
                            const int32_t* heads, const int32_t* count, float* y, char* ws,
                            hipStream_t s) {
-    // the down projection over rows of W_o^T, its list the head table with d_head rows per entry
-    pi_ffn_desc f{};
-    f.w_down = a.w_o;
-    f.d = a.d;
-    f.F = a.H * a.dh;
-    f.act = PI_ACT_RELU;                              // not read by the down projection
-    f.wfmt = PI_W_F16;
-    return launch_down_b1(f, pl.ffn, heads, count, 0, o, y, ws, s, a.dh);
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
+    float* part = reinterpret_cast<float*>(ws + pl.off_part);
+    const dim3 g((pl.nslices + 7) & ~7, a.H);
+    hipLaunchKernelGGL(k_attn_out, g, dim3(64 * AO_WAVES), 0, s, static_cast<const uint16_t*>(a.w_o), o,
+                       heads, count, a.d, a.H, a.dh, pl.nslices, part, y, cnt);
+    return hipGetLastError();
 }
 
 }  // namespace pi
