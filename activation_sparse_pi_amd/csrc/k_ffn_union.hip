@@ -104,18 +104,22 @@ PI_DEV uint32_t pack_h2(float lo, float hi) {
 // ------------------------------------------------------------------------------------ up
 // Block roles.  The first S blocks (S: as many as are resident at once) take whole tiles
 // 0 .. S - 1.  The tiles past them would run as a second round behind the first, one block each;
-// instead each is split over d into sp parts (sp = 2 when the layer has more than S tiles),
-// block S + (t - S) sp + p taking part p of tile t, so the second round has twice the blocks in
-// flight at half the length.  A part stores its 32 x 32 pre-activation sums; the last part of
-// the tile to arrive adds the sp partials in part order and finishes the tile.
+// instead each is split over d into sp parts (sp = 2 when the layer has more than S tiles), so
+// the second round has twice the blocks in flight at half the length.  A part stores its
+// 32 x 32 pre-activation sums; the last part of the tile to arrive adds the sp partials in part
+// order and finishes the tile.  The split blocks go in groups of 8 sp: block r of group g takes
+// part r / 8 of tile S + 8 g + r % 8, so the parts of a tile are 8 blocks apart in the dispatch
+// order -- on one XCD (S is a multiple of 8), their hand-off inside one L2.  A last group of
+// m < 8 tiles pairs block r with tile S + 8 g + r % m, part r / m.
 constexpr int UP_SP = 2;
 struct UpRole {
     int tile, part, sp;
 };
-PI_DEV UpRole up_role(int b, int S, int sp) {
+PI_DEV UpRole up_role(int b, int S, int sp, int tiles) {
     if (b < S || sp == 1) return {b, 0, 1};
-    const int bb = b - S;
-    return {S + bb / sp, bb % sp, sp};
+    const int bb = b - S, g = bb / (8 * sp), r = bb - g * 8 * sp;
+    const int m = min(8, tiles - S - 8 * g);
+    return {S + 8 * g + r % m, r / m, sp};
 }
 
 // ReLU with 32-bit offsets fits 128 registers: two blocks per CU (ReGLU: one).
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < 32) s_ids[tid] = -1;
-    const UpRole ro = up_role(blockIdx.x, S, sp);
+    const UpRole ro = up_role(blockIdx.x, S, sp, (F + 31) >> 5);
     const int tile = ro.tile, lo = tile * 32;
     uint32_t tok = 0u;             // FROM_MASK, wave 0 lane n < 32: token word of position n
     if constexpr (FROM_MASK) {
