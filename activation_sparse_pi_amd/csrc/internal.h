@@ -186,6 +186,11 @@ struct AttnPlan {
     size_t bytes;
 };
 AttnPlan plan_attn(int d, int H, int dh);
+// the executor's step for H <= 64: head predictor stage 2 folded into the q/k/v kernel (z from
+// launch_pred_stage1); writes mask, heads, count (and logits when not null) as pi_predict does
+hipError_t launch_attn_pqkv(const pi_attn_desc& a, const pi_pred_desc& p, const uint16_t* x,
+                            const float* z, float theta, float* logits, uint32_t* mask,
+                            int32_t* heads, int32_t* count, float* qkv, hipStream_t s);
 hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint32_t* hmask,
                            float* qkv, hipStream_t s);
 hipError_t launch_attn_out(const pi_attn_desc& a, const AttnPlan& pl, const float* o,

@@ -70,6 +70,111 @@ __global__ __launch_bounds__(64 * QKV_WAVES) void k_attn_qkv(const uint16_t* __r
     }
 }
 
+// l_h = W2t[h, :] . z + bias[h] (fp16 weights, fp32 z): lane i takes elements i, i + 64, ... (four
+// in flight), the lanes meet in wave_sum.  Every wave that evaluates head h gets the same bits.
+PI_DEV float head_logit(const uint16_t* __restrict__ W2t, const float* __restrict__ z,
+                        const float* __restrict__ bias, int r, int h) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* w = W2t + (size_t)h * r;
+    float acc = 0.f;
+    for (int i0 = 0; i0 < r; i0 += 256) {
+        uint16_t wv[4];
+        float zv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + lane + 64 * u;
+            wv[u] = w[i < r ? i : 0];
+            zv[u] = z[i < r ? i : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + lane + 64 * u < r) acc = fmaf(h2f(wv[u]), zv[u], acc);
+    }
+    return wave_sum(acc) + bias[h];
+}
+
+// The executor's q/k/v step with the head predictor's second stage folded in (one token,
+// H <= 64): every wave computes its head's logit from z and the head's W2t row (an L2 round
+// trip) and goes on to the head's rows or its zeros, so no kernel and no mask stand between
+// stage 1 and the q/k/v rows.  Block 0 also computes every head's logit (head_logit again, so
+// its bits are the ones the blocks acted on) and writes the logits, the mask words, the
+// ascending head table and its count.  Rows as in k_attn_qkv.
+template <int Q, int RPW>
+__global__ __launch_bounds__(64 * QKV_WAVES) void k_attn_pqkv(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, int d, int dh, int bph,
+    float* __restrict__ qkv, const float* __restrict__ z, const uint16_t* __restrict__ W2t,
+    const float* __restrict__ bias, int r, int H, float theta, float* __restrict__ logits,
+    uint32_t* __restrict__ mask, int32_t* __restrict__ heads, int32_t* __restrict__ count) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = blockIdx.x / bph;
+    const int nrow = 3 * dh;
+    const int r0 = (blockIdx.x - h * bph) * (QKV_WAVES * RPW) + wave * RPW;
+    float* out = qkv + (size_t)h * nrow;
+    const float lh = head_logit(W2t, z, bias, r, h);
+    if (blockIdx.x == 0) {
+        __shared__ float s_l[64];
+        for (int hh = wave; hh < H; hh += QKV_WAVES) {
+            const float l = head_logit(W2t, z, bias, r, hh);
+            if (lane == 0) s_l[hh] = l;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const float l = lane < H ? s_l[lane] : 0.f;
+            const bool act = lane < H && l > theta;
+            if (logits != nullptr && lane < H) logits[lane] = l;
+            const unsigned long long bal = __ballot(act);
+            if (lane == 0) {
+                mask[0] = (uint32_t)bal;
+                if (H > 32) mask[1] = (uint32_t)(bal >> 32);
+                *count = __popcll(bal);
+            }
+            if (act) heads[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = lane;
+        }
+    }
+    if (!(lh > theta)) {                              // a head predicted inactive: zeros
+        if (lane < RPW && r0 + lane < nrow) out[r0 + lane] = 0.f;
+        return;
+    }
+    if (r0 >= nrow) return;
+    const int nc = d >> 3;
+    uint4 xr[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int c = lane + 64 * q;
+        xr[q] = c < nc ? ld16(x + 8 * c) : zero4();
+    }
+    uint4 w[RPW][Q];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const uint16_t* p = W + ((size_t)h * nrow + min(r0 + j, nrow - 1)) * d;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = lane + 64 * q;
+            w[j][q] = c < nc ? ld16_nt(p + 8 * c) : zero4();
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) acc = dot8(w[j][q], xr[q], acc);
+        acc = wave_sum(acc);
+        if (lane == 0 && r0 + j < nrow) out[r0 + j] = acc;
+    }
+}
+
+template <int Q, int RPW>
+hipError_t pqkv_launch(const pi_attn_desc& a, const pi_pred_desc& p, const uint16_t* x, const float* z,
+                       float theta, float* logits, uint32_t* mask, int32_t* heads, int32_t* count,
+                       float* qkv, hipStream_t s) {
+    const int bph = (3 * a.dh + QKV_WAVES * RPW - 1) / (QKV_WAVES * RPW);
+    hipLaunchKernelGGL((k_attn_pqkv<Q, RPW>), dim3(a.H * bph), dim3(64 * QKV_WAVES), 0, s, x,
+                       static_cast<const uint16_t*>(a.w_qkv), a.d, a.dh, bph, qkv, z,
+                       static_cast<const uint16_t*>(p.w_p2t), p.bias, p.r, a.H, theta, logits, mask,
+                       heads, count);
+    return hipGetLastError();
+}
+
 template <int Q, int RPW>
 hipError_t qkv_launch(const pi_attn_desc& a, const uint16_t* x, const uint32_t* hmask, float* qkv,
                       hipStream_t s) {
@@ -177,6 +282,18 @@ hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint3
     if (q <= 8) return qkv_launch<8, 2>(a, x, hmask, qkv, s);
     if (q <= 16) return qkv_launch<16, 2>(a, x, hmask, qkv, s);
     return qkv_launch<32, 1>(a, x, hmask, qkv, s);    // d <= PI_ATTN_MAX_D
+}
+
+hipError_t launch_attn_pqkv(const pi_attn_desc& a, const pi_pred_desc& p, const uint16_t* x,
+                            const float* z, float theta, float* logits, uint32_t* mask,
+                            int32_t* heads, int32_t* count, float* qkv, hipStream_t s) {
+    if (a.H > 64 || p.F != a.H || p.pfmt != PI_P_F16) return hipErrorInvalidValue;
+    const int q = (a.d + 511) / 512;
+    if (q <= 2) return pqkv_launch<2, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
+    if (q <= 4) return pqkv_launch<4, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
+    if (q <= 8) return pqkv_launch<8, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
+    if (q <= 16) return pqkv_launch<16, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
+    return pqkv_launch<32, 1>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
 }
 
 AttnPlan plan_attn(int d, int H, int dh) {

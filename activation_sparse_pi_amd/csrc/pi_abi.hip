@@ -868,11 +868,16 @@ int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, 
         const int rep = (int)(g % nrep), t = (int)(g % T);
         const uint16_t* xs = x + (size_t)t * d;
         const float* os = o + (size_t)t * H * dh;
-        if ((e = launch_predict(preds[rep], ppl, xs, 1, theta, nullptr, mask, idx, count, w, s)) != hipSuccess)
+        // H <= 64: stage 1, then one kernel for the heads' logits, mask, table and q/k/v
+        const bool fold = H <= 64;
+        if ((e = fold ? launch_pred_stage1(preds[rep], ppl, xs, 1, reinterpret_cast<float*>(w + ppl.off_z), s)
+                      : launch_predict(preds[rep], ppl, xs, 1, theta, nullptr, mask, idx, count, w, s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run head predictor");
         if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i]), s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run kernel event");
-        if ((e = launch_attn_qkv(attns[rep], xs, mask, qkv, s)) != hipSuccess)
+        if ((e = fold ? launch_attn_pqkv(attns[rep], preds[rep], xs, reinterpret_cast<const float*>(w + ppl.off_z),
+                                         theta, nullptr, mask, idx, count, qkv, s)
+                      : launch_attn_qkv(attns[rep], xs, mask, qkv, s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run q/k/v");
         if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i + 1]), s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run kernel event");

@@ -432,15 +432,22 @@ def bench_batch_sweep(a, cfg):
 
 # ------------------------------------------------------------------------------- attention side
 def bytes_model_attn(cfg, n):
-    """Algorithmic bytes of one attention-side step with n predicted heads.
-    Head predictor: 2dr + 2rH (fp16 factors) + 4H (bias) + 2d (x) + the mask and the head table.
-    q/k/v: the n heads' 3 d_head rows of d fp16 (n 3 dh d 2), x 2d, the mask, qkv written for every
-    head (4 H 3 dh: zeros for the others).  Output: the n heads' d_head rows of W_o^T (n dh d 2),
-    their o values (4 n dh), the head table (4 n + 4), y 4d."""
+    """Algorithmic bytes of one attention-side step with n predicted heads, by kernel.
+    Predictor stage 1: W_p1 2dr, x 2d, z written 4r.  Stage 2: W_p2 2rH, bias 4H, z read 4r, the
+    mask words and the head table with its count written (4 ceil(H/32) + 4H + 4).  q/k/v: the n
+    heads' 3 d_head rows of d fp16 (n 3 dh d 2), x 2d, qkv written for every head (4 H 3 dh: zeros
+    for the others), and the mask read -- or, with H <= 64, stage 2 itself, which the step runs
+    inside its q/k/v kernel.  Output: the n heads' d_head rows of W_o^T (n dh d 2), their o values
+    (4 n dh), the head table (4 n + 4), y 4d."""
     d, H, dh, r = cfg.d, cfg.H, cfg.dh, cfg.r
     mw = 4 * ((H + 31) // 32)
-    pred = 2 * d * r + 2 * r * H + 4 * H + 2 * d + mw + 4 * H
-    qkv = n * 3 * dh * d * 2 + 2 * d + mw + 4 * H * 3 * dh
+    stage1 = 2 * d * r + 2 * d + 4 * r
+    stage2 = 2 * r * H + 4 * H + 4 * r + mw + 4 * H + 4
+    rows = n * 3 * dh * d * 2 + 2 * d + 4 * H * 3 * dh
+    if H <= 64:
+        pred, qkv = stage1, rows + stage2
+    else:
+        pred, qkv = stage1 + stage2, rows + mw
     out = n * dh * d * 2 + 4 * n * dh + 4 * n + 4 + 4 * d
     return dict(pred=pred, qkv=qkv, out=out, total=pred + qkv + out)
 
@@ -512,7 +519,7 @@ def bench_attn(a, cfg):
     ms_per_step = total_ms / K
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = qkv_bytes / (float(qkv_ms.mean()) * 1e-3) / 1e9
-    kernel_key = f"k_attn_qkv {cfg.name}"
+    kernel_key = f"{'k_attn_pqkv' if cfg.H <= 64 else 'k_attn_qkv'} {cfg.name}"
     copy_probe(a.copy_probe_mb, dev)
     out = {
         "metric": "attention-side decode tokens/sec at batch 1 (predicted heads only) + effective HBM GB/s (% of peak)",
@@ -529,8 +536,11 @@ def bench_attn(a, cfg):
                         f"seeded input",
             "d": cfg.d, "heads": cfg.H, "d_head": cfg.dh, "rank": cfg.r, "replicas": R,
             "mean_predicted_heads": round(float(heads.mean()), 2),
-            "launch": "one pi_attn_run call: per step the head predictor (two kernels), q/k/v of the "
-                      "predicted heads (one kernel), the output projection over the head table (one kernel)",
+            "launch": ("one pi_attn_run call: per step the head predictor's stage 1 (one kernel), its "
+                       "stage 2 folded into the q/k/v kernel of the predicted heads (one kernel), the output "
+                       "projection over the head table (one kernel)") if cfg.H <= 64 else
+                      ("one pi_attn_run call: per step the head predictor (two kernels), q/k/v of the "
+                       "predicted heads (one kernel), the output projection over the head table (one kernel)"),
         },
         "effective_hbm": {"GB/s": round(path_gbs, 1), "frac": round(path_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_step": round(path_bytes)},

@@ -466,7 +466,10 @@ int pi_attn_out(const pi_attn_desc* a, const float* o, const int32_t* heads, con
  * o[t] (o fp32 [T, H, d_head], the attention core's output for token t) over those heads into
  * y fp32 [d].  The outputs hold the last step's.  events: NULL or 2 hipEvent_t recorded around
  * the enqueued work; kernel_events: NULL or 2 nsteps hipEvent_t recorded around each step's
- * q/k/v kernel.  Workspace: max(pi_workspace_bytes(pred, NULL, 1), pi_attn_workspace_bytes(a)),
+ * q/k/v kernel.  With H <= 64 the heads' logits are computed inside the q/k/v kernel (from the
+ * same z and factors; the fp32 sum runs in another order than pi_predict's, so a head within
+ * rounding of the threshold can be decided the other way); the outputs are the same arrays.
+ * Workspace: max(pi_workspace_bytes(pred, NULL, 1), pi_attn_workspace_bytes(a)),
  * zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_UNSUPPORTED (an
  * int8 head predictor), PI_ERR_WORKSPACE before any HIP call; PI_ERR_HIP.                  */
 int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, const uint16_t* x,

@@ -133,10 +133,20 @@ def test_attn_model_shapes(name, steps):
         say(f"[gpu] {cfg.name} t={t}: {n}/{cfg.H} heads, qkv {eq:.2e}, y {ey:.2e}")
 
 
-@pytest.mark.parametrize("cfg", [TINY[1], SA.get("a2").with_(T=6)], ids=lambda c: c.name)
+RUN = [
+    TINY[1],
+    SA.tiny(d=264, H=40, dh=8, r=16, T=4, seed=48),    # two mask words, logits folded into q/k/v
+    SA.tiny(d=200, H=72, dh=4, r=16, T=3, seed=49),    # H > 64: pi_predict, then the q/k/v kernel
+    SA.get("a2").with_(T=6),
+    SA.get("a3").with_(T=4),
+]
+
+
+@pytest.mark.parametrize("cfg", RUN, ids=lambda c: c.name)
 def test_attn_run(cfg):
     """pi_attn_run over several tokens and two replicas: the last step's outputs equal a one-step
-    run of that token bit for bit, and the oracle's."""
+    run of that token bit for bit, and the oracle's (up to H = 64 the step computes the heads'
+    logits inside its q/k/v kernel, above that through pi_predict)."""
     inp = SA.make(cfg)
     att = _dev_attn(inp, replicas=2)
     xd = torch.from_numpy(inp["x"].copy()).cuda()
