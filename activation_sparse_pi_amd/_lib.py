@@ -19,7 +19,7 @@ PI_ACT_RELU, PI_ACT_REGLU = 0, 1
 PI_W_F16, PI_W_I4G128 = 0, 1
 PI_P_F16, PI_P_I8G128 = 0, 1
 PI_PER_TOKEN, PI_UNION = 0, 1
-PI_RUN_AUTO, PI_RUN_PERSISTENT, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 1, 2, 3, 4
+PI_RUN_AUTO, PI_RUN_KERNELS, PI_RUN_FUSED, PI_RUN_SPLIT = 0, 2, 3, 4
 PI_MAX_BATCH = 32
 PI_BATCH_TOKENS, PI_BATCH_UNION, PI_BATCH_AUTO = 0, 1, 2
 PI_MAX_BATCH_RUN = 64

@@ -14,7 +14,6 @@ constexpr int CNT_PRED1 = 0;      // (free: 256 slots)
 constexpr int CNT_PRED2 = 256;    // one for stage 2's compaction
 constexpr int CNT_DOWN = 512;     // one per down-projection column slice (<= 512)
 constexpr int CNT_UNION = 1024;   // union path, down-product column groups (<= 512)
-constexpr int CNT_RUN = 2048;     // persistent decode launch: hand-off flags (RUN_FLAG_BYTES)
 constexpr int CNT_TOTAL = 4096;
 constexpr size_t COUNTER_BYTES = CNT_TOTAL * sizeof(unsigned);
 
@@ -84,57 +83,6 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
 // table (idx, count; skipped when idx is NULL) from its mask.
 hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int nhot, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s);
-
-// ---- persistent batch-1 decode (a run of steps in one cooperative launch) -----------------
-constexpr int RUN_NTAB = 32;          // replicas one launch can address
-constexpr int RUN_WPS_MAX = 128;      // mask words per down split (4096 neuron ids in LDS)
-constexpr int RUN_FLAG_BYTES = 4112;  // hand-off flags and counters of one launch
-constexpr int RUN_MAX_STEPS = 65536;  // steps per launch
-
-// one layer's device pointers (a replica of the layer, or another layer of the same shape)
-struct RunRep {
-    const uint16_t* w1t;   // fp16 [r, d]
-    const uint16_t* w2t;   // fp16 [F, r]
-    const float* bias;     // fp32 [F]
-    const void* wg;        // [F, d] fp16 or int4 (NULL for ReLU)
-    const void* wu;
-    const void* wd;
-    const uint16_t* sg;    // int4 scales [F, d/128] (NULL for fp16)
-    const uint16_t* su;
-    const uint16_t* sd;
-};
-
-struct RunPlan {
-    int G;                 // blocks, all co-resident (cooperative launch)
-    int W;                 // mask words
-    int qa;                // stage-1 16-byte chunks per thread per predictor row
-    int nrb;               // stage-1 rows per block, at most
-    int tpb;               // 64-neuron tiles per block, at most (the kernel takes 1)
-    int q;                 // 16-byte chunks per lane of an up/gate row (template bucket)
-    int nslices, nsplit;   // down: column slices x neuron-word splits
-    size_t lds;            // dynamic LDS
-    size_t off_flags, off_z, off_h, off_part, bytes;
-};
-
-struct RunArgs {
-    RunRep rep[RUN_NTAB];
-    const uint16_t* x;     // fp16 [T, d]
-    long long g0;          // global step of local step 0: token (g0 + k) % T
-    int T, e0, tabn, L;    // local step k uses rep[(e0 + k) % tabn]; L steps
-    int d, r, F, act, wfmt;
-    float theta;
-    uint32_t* mask;
-    int32_t* idx;
-    int32_t* count;
-    float* y;
-    char* ws;
-    RunPlan pl;
-};
-
-RunPlan plan_run(int d, int r, int F, int wfmt, int G);
-bool run_fits(const RunPlan& p, int d, int r, int F, int wfmt);
-int run_grid(int wfmt, int act, int q, size_t lds);   // co-resident blocks (0 on failure)
-hipError_t launch_run(const RunArgs& ra, hipStream_t s);
 
 // ---- launchers (return hipError_t of the launch) ---------------------------------------------------
 hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x, int B,

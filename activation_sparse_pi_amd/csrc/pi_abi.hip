@@ -129,9 +129,7 @@ size_t ws_base(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
         }
     }
     if (pred && ffn && pred->d == ffn->d && pred->F == ffn->F) {
-        size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
-        if (b > need) need = b;
-        b = plan_run(pred->d, pred->r, pred->F, ffn->wfmt, 512).bytes;   // independent of the grid
+        const size_t b = plan_decode(pred->d, pred->r, pred->F, ffn->wfmt).bytes;
         if (b > need) need = b;
     }
     return need;
@@ -379,11 +377,8 @@ int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep
     if (!preds || !ffns) return fail(PI_ERR_NULL, "descriptor arrays are required");
     if (nrep < 1) return fail(PI_ERR_SHAPE, "nrep must be >= 1 (nrep=%d)", nrep);
     if (T < 1 || nsteps < 0 || s0 < 0) return fail(PI_ERR_SHAPE, "need T >= 1, nsteps >= 0, s0 >= 0");
-    if (mode != PI_RUN_AUTO && mode != PI_RUN_PERSISTENT && mode != PI_RUN_KERNELS &&
-        mode != PI_RUN_FUSED && mode != PI_RUN_SPLIT)
+    if (mode != PI_RUN_AUTO && mode != PI_RUN_KERNELS && mode != PI_RUN_FUSED && mode != PI_RUN_SPLIT)
         return fail(PI_ERR_DTYPE, "unknown run mode %d", mode);
-    if (noalloc && mode == PI_RUN_PERSISTENT)
-        return fail(PI_ERR_UNSUPPORTED, "pi_decode_run_noalloc runs the kernel schedules only");
     if (!x || !mask || !y) return fail(PI_ERR_NULL, "x, mask and y are required");
     if ((idx == nullptr) != (count == nullptr)) return fail(PI_ERR_NULL, "idx and count go together");
     if (!aligned16(x) || !aligned16(y)) return fail(PI_ERR_ALIGN, "x and y must be 16-byte aligned");
@@ -398,45 +393,25 @@ int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep
     }
     if (preds[0].F > 131072) return fail(PI_ERR_UNSUPPORTED, "pi_decode_run supports F <= 131072");
     if (events && (!events[0] || !events[1])) return fail(PI_ERR_NULL, "events must hold two events");
-    if (kernel_events) {
-        if (mode == PI_RUN_PERSISTENT) return fail(PI_ERR_SHAPE, "kernel_events need a kernel-per-phase schedule");
+    if (kernel_events)
         for (int i = 0; i < 2 * nsteps; ++i)
             if (!kernel_events[i]) return fail(PI_ERR_NULL, "kernel_events[%d] is NULL", i);
-    }
     const int d = preds[0].d, r = preds[0].r, F = preds[0].F;
-    const int act = ffns[0].act, wfmt = ffns[0].wfmt;
-    // PI_RUN_AUTO and PI_RUN_KERNELS take the fused or the split kernel schedule by shape: on
-    // MI355X every hand-off inside the persistent launch costs more than a kernel boundary
-    // (measured on all five workloads)
-    bool persistent = false;
-    RunPlan rp{};
-    if (mode == PI_RUN_PERSISTENT && preds[0].pfmt != PI_P_F16)
-        return fail(PI_ERR_UNSUPPORTED, "the persistent decode launch takes an fp16 predictor");
-    if (mode == PI_RUN_PERSISTENT) {
-        const RunPlan probe = plan_run(d, r, F, wfmt, 512);
-        const int G = run_grid(wfmt, act, probe.q, probe.lds);
-        if (G > 0) {
-            rp = plan_run(d, r, F, wfmt, G);
-            persistent = run_fits(rp, d, r, F, wfmt);
-        }
-        if (!persistent)
-            return fail(PI_ERR_UNSUPPORTED, "this layer shape does not fit the persistent decode launch "
-                        "(d=%d r=%d F=%d, %d co-resident blocks)", d, r, F, G);
-    }
+    const int wfmt = ffns[0].wfmt;
+    // PI_RUN_AUTO and PI_RUN_KERNELS take the fused or the split kernel schedule by shape
     const DecPlan pl = plan_decode(d, r, F, wfmt);
     // a hot block runs in the split schedule (the fused one computes every neuron from the
     // predicted set, hot or not)
     const bool fused = mode == PI_RUN_FUSED || (mode != PI_RUN_SPLIT && ffns[0].nhot == 0 && pl.fused_default);
     for (int i = 0; i < nrep; ++i)
         if (ffns[i].nhot != ffns[0].nhot) return fail(PI_ERR_SHAPE, "replica %d has another hot block", i);
-    if (!persistent && !fused && pl.lds_b + hot_lds_bytes(ffns[0], pl.ntile) > (size_t)DEC_LDS_MAX)
+    if (!fused && pl.lds_b + hot_lds_bytes(ffns[0], pl.ntile) > (size_t)DEC_LDS_MAX)
         return fail(PI_ERR_UNSUPPORTED, "the hot block needs %zu bytes of LDS per tile block, more than %d",
                     pl.lds_b + hot_lds_bytes(ffns[0], pl.ntile), DEC_LDS_MAX);
     // the kernel schedules use the partial rows of the schedule they run (the workspace from
     // pi_workspace_bytes holds those of either)
-    const size_t need = persistent ? rp.bytes
-                                   : pl.off_part + (size_t)(fused ? pl.ntile : down_ranges(pl, ffns[0].nhot, F).P) *
-                                                       d * sizeof(float);
+    const size_t need = pl.off_part + (size_t)(fused ? pl.ntile : down_ranges(pl, ffns[0].nhot, F).P) *
+                                          d * sizeof(float);
     if (noalloc) {
         if (need > (size_t)PI_NOALLOC_SCRATCH_BYTES)
             return fail(PI_ERR_WORKSPACE, "this layer's decode scratch is %zu bytes, more than the %u "
@@ -456,57 +431,7 @@ int decode_run_impl(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep
     hipError_t e;
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
         return hip_fail(e, "pi_decode_run start event");
-    if (persistent) {
-        RunArgs ra{};
-        ra.x = x;
-        ra.T = T;
-        ra.d = d;
-        ra.r = r;
-        ra.F = F;
-        ra.act = act;
-        ra.wfmt = wfmt;
-        ra.theta = theta;
-        ra.mask = mask;
-        ra.idx = idx;
-        ra.count = count;
-        ra.y = y;
-        ra.ws = w;
-        ra.pl = rp;
-        auto fill = [&](int slot, int rep) {
-            RunRep& R = ra.rep[slot];
-            R.w1t = static_cast<const uint16_t*>(preds[rep].w_p1t);
-            R.w2t = static_cast<const uint16_t*>(preds[rep].w_p2t);
-            R.bias = preds[rep].bias;
-            R.wg = ffns[rep].w_gate;
-            R.wu = ffns[rep].w_up;
-            R.wd = ffns[rep].w_down;
-            R.sg = ffns[rep].s_gate;
-            R.su = ffns[rep].s_up;
-            R.sd = ffns[rep].s_down;
-        };
-        // up to RUN_NTAB replicas fit one launch's table; more are walked in launches of
-        // RUN_NTAB steps whose table lists the replicas of exactly those steps
-        const bool whole = nrep <= RUN_NTAB;
-        if (whole) {
-            for (int i = 0; i < nrep; ++i) fill(i, i);
-            ra.tabn = nrep;
-        }
-        const int chunk = whole ? RUN_MAX_STEPS : RUN_NTAB;
-        for (long long i = 0; i < nsteps; i += chunk) {
-            const long long g0 = s0 + i;
-            const int L = (int)std::min<long long>(chunk, nsteps - i);
-            ra.g0 = g0;
-            ra.L = L;
-            if (whole) {
-                ra.e0 = (int)(g0 % nrep);
-            } else {
-                for (int j = 0; j < L; ++j) fill(j, (int)((g0 + j) % nrep));
-                ra.e0 = 0;
-                ra.tabn = L;
-            }
-            if ((e = launch_run(ra, s)) != hipSuccess) return hip_fail(e, "pi_decode_run persistent launch");
-        }
-    } else if (nsteps > 0) {
+    if (nsteps > 0) {
         // every step leaves its down projection as fp32 partial rows; the next step's first
         // kernel sums them into y in a fixed order, and a small kernel does so after the last
         for (int i = 0; i < nsteps; ++i) {

@@ -157,9 +157,9 @@ class DeviceLayer:
         """Enqueue nsteps batch-1 steps from native code (token (s0+i) % T, replica
         (s0+i) % R).  events: None or two torch.cuda.Event objects recorded around the
         enqueued work; kernel_events: None or 2*nsteps events attached to the tile kernel
-        of every step (not with the persistent launch).  Events must have been recorded
+        of every step.  Events must have been recorded
         once already (torch creates the HIP event on first record).
-        mode: PI_RUN_AUTO / PI_RUN_KERNELS / PI_RUN_FUSED / PI_RUN_SPLIT / PI_RUN_PERSISTENT."""
+        mode: PI_RUN_AUTO / PI_RUN_KERNELS / PI_RUN_FUSED / PI_RUN_SPLIT."""
         import ctypes
         if not hasattr(self, "_pred_arr"):
             self._pred_arr = (L.PredDesc * self.replicas)(*self.pred)

@@ -19,16 +19,14 @@ Modes (--mode): "kernels" (default) enqueues the K timed steps with one
 pi_decode_run call in the kernel schedule the library picks for the shape: "fused"
 (two kernels per step, the tile kernel also does the down rows) where
 ceil(F/64) * d <= 2^20, else "split" (three kernels per step, the down projection
-its own kernel); "fused" and "split" force one of them; "persistent" runs the same
-call as one cooperative launch (slower on MI355X: its in-launch hand-offs cost more
-than kernel boundaries); "eager" makes one Python call per ABI function.  Inputs are
+its own kernel); "fused" and "split" force one of them; "eager" makes one Python call
+per ABI function.  Inputs are
 resident in HBM before the timed region starts; two events recorded on the library's
 stream around the enqueued steps time them.  The roofline figure is the tile kernel
 (the one that moves the most bytes): its algorithmic bytes over its average duration,
 taken in a second pass over the same stream in which that kernel of every step
 carries its own start/end events (those events slow the step down, so the headline
-value comes from the first pass, which has none).  In persistent mode the launch is
-the only kernel and its bytes over its duration are the roofline figure.
+value comes from the first pass, which has none).
 
 Prints one JSON line.  --gpus N with N > 1 exits: the layer runs on one GPU.
 """
@@ -58,9 +56,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1088)
     ap.add_argument("--config", default="c5", help="c1..c5 (FFN), a2 / a3 (attention side)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to bust the caches")
-    ap.add_argument("--mode", choices=("kernels", "fused", "split", "persistent", "eager"), default="kernels",
-                    help="kernels: one pi_decode_run call, three kernels per step (default); "
-                         "persistent: one pi_decode_run call, one cooperative launch; "
+    ap.add_argument("--mode", choices=("kernels", "fused", "split", "eager"), default="kernels",
+                    help="kernels: one pi_decode_run call, the schedule the library picks (default); "
+                         "fused / split: one pi_decode_run call in that schedule; "
                          "eager: one Python call per ABI function")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget, 0 = skip")
     ap.add_argument("--placement", choices=("none", "dealt", "hot"), default="none",
@@ -639,9 +637,8 @@ def main():
     sched = a.mode if a.mode in ("fused", "split") else kernel_schedule(cfg, nhot)
     sched_desc = ("two kernels per step (fused down)" if sched == "fused"
                   else "three kernels per step (split down)")
-    if a.mode in ("persistent", "kernels", "fused", "split"):
-        mode = {"persistent": L.PI_RUN_PERSISTENT, "kernels": L.PI_RUN_KERNELS,
-                "fused": L.PI_RUN_FUSED, "split": L.PI_RUN_SPLIT}[a.mode]
+    if a.mode in ("kernels", "fused", "split"):
+        mode = {"kernels": L.PI_RUN_KERNELS, "fused": L.PI_RUN_FUSED, "split": L.PI_RUN_SPLIT}[a.mode]
         layer.decode_run(xd.data_ptr(), T, 0, Wm, bufs, mode=mode)            # untimed warmup
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in ev:                 # torch creates the HIP event on first record
@@ -660,17 +657,16 @@ def main():
             layer.decode_run(xd.data_ptr(), T, 0, T, bufs, events=pe, mode=mode)
             torch.cuda.synchronize()
             passes_ms.append(pe[0].elapsed_time(pe[1]))
-        if a.mode != "persistent":
-            # roofline pass: the tile kernel of every step carries its own start/end events
-            Kr = min(K, 1088)
-            kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
-            for e in kev:
-                e.record()
-            torch.cuda.synchronize()
-            layer.decode_run(xd.data_ptr(), T, Wm + K, Kr, bufs, mode=mode, kernel_events=kev)
-            torch.cuda.synchronize()
-            up_ms = [kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(Kr)]
-            roof_steps = (Wm + K + np.arange(Kr)) % T
+        # roofline pass: the tile kernel of every step carries its own start/end events
+        Kr = min(K, 1088)
+        kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * Kr)]
+        for e in kev:
+            e.record()
+        torch.cuda.synchronize()
+        layer.decode_run(xd.data_ptr(), T, Wm + K, Kr, bufs, mode=mode, kernel_events=kev)
+        torch.cuda.synchronize()
+        up_ms = [kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(Kr)]
+        roof_steps = (Wm + K + np.arange(Kr)) % T
     else:
         for s in range(Wm):
             step(s)
@@ -693,11 +689,7 @@ def main():
     path_bytes = float(np.mean(bm["total"]))
     path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbs = float(np.mean(bm["ffn"])) / (ms_per_step * 1e-3) / 1e9
-    if a.mode == "persistent":
-        # the launch is the whole path: its bytes (K steps) over its duration
-        kernel_key = f"k_run[{cfg.wfmt},{cfg.act}] {cfg.name}"
-        launch_bytes, launch_ms = path_bytes * K, total_ms
-    elif a.mode == "eager":
+    if a.mode == "eager":
         kernel_key = f"k_up_{cfg.wfmt}[{cfg.act}] {cfg.name}"
         launch_bytes, launch_ms = float(np.mean(bm["up"])), float(np.mean(up_ms))
     else:
@@ -729,9 +721,7 @@ def main():
                         f"{T}-token stream",
             "batch": 1, "d": cfg.d, "ffn": cfg.F, "rank": cfg.r, "replicas": R,
             "mean_active": round(float(counts.mean()), 1),
-            "launch": {"persistent": "one pi_decode_run call: one cooperative launch per run "
-                                     "(per 32 steps when there are more than 32 replicas)",
-                       "kernels": f"one pi_decode_run call: {sched_desc}",
+            "launch": {"kernels": f"one pi_decode_run call: {sched_desc}",
                        "fused": f"one pi_decode_run call: {sched_desc}",
                        "split": f"one pi_decode_run call: {sched_desc}",
                        "eager": "one Python call per ABI function"}[a.mode],

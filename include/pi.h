@@ -213,22 +213,15 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  * up/gate rows and the column operator on their down rows.  Steps run strictly one
  * after another: a step starts only when the previous step's y is complete.
  *   mode PI_RUN_FUSED: two kernels per step (predictor stage 1; then one block per
- *        64-neuron tile: its logits, mask words, up/gate rows and down rows, whose partial
- *        sums are added to y).  Issues ceil(F/64) * d atomic adds per step.
+ *        64-neuron tile: its logits, mask words, up/gate rows and down rows, whose column
+ *        sums are the tile's partial row: ceil(F/64) partial rows of d per step).
  *   mode PI_RUN_SPLIT: three kernels per step (predictor stage 1; logits + mask + up/gate
- *        rows per tile; down projection from the mask over ranges of neurons).  Issues
- *        about 256 * 512 atomic adds per step, whatever the shape.
- *   mode PI_RUN_KERNELS: PI_RUN_FUSED where ceil(F/64) * d <= 2^20, else PI_RUN_SPLIT.
- *   mode PI_RUN_PERSISTENT: the whole run is one cooperative launch (a launch per
- *        32 steps when nrep > 32); inside it, the phases of a step and the steps
- *        themselves hand over through flags in the workspace, with no kernel boundary.
- *        Needs r <= 1024, d <= 8192 (fp16) and at most 64 neurons per block of the
- *        co-resident grid (F <= 32768 on a 256-CU device); PI_ERR_UNSUPPORTED otherwise.
- *        A hand-off that never completes (only possible if co-residency were broken)
- *        ends the launch after a spin limit and leaves y all NaN and *count = -1.
- *        On MI355X each of its hand-offs costs more than a kernel boundary, so it is
- *        the slower schedule on every workload measured; it is kept as an alternative.
+ *        rows per tile; down projection from the mask over ranges of neurons: at most 32
+ *        partial rows of d per step, whatever the shape).
+ *   mode PI_RUN_KERNELS: PI_RUN_FUSED where ceil(F/64) * d <= 2^20, else PI_RUN_SPLIT
+ *        (a layer with a hot block always runs split).
  *   mode PI_RUN_AUTO: as PI_RUN_KERNELS.
+ *   (Mode 1 is not assigned.)
  * y of the kernel schedules: every block that owns a share of the step's neurons stores its
  * d column sums as one fp32 partial row in the workspace (no atomics); a later kernel sums
  * the rows into y in an order fixed by the number of rows and d alone.  So y is fp32 with
@@ -237,19 +230,18 @@ int pi_ffn_down(const pi_ffn_desc* ffn, const int32_t* idx, const int32_t* count
  * in any fp32 sum (a non-finite h or weight of a listed neuron makes the affected columns of
  * y non-finite); a run is bit-identical to itself, and a step's y does not depend on the
  * steps before it.  The fused and split schedules group the sums differently and agree to
- * fp32 rounding.  The persistent launch sums in fp32 in a fixed order of its own.
+ * fp32 rounding.
  * mask u32 [ceil(F/32)], idx int32 [F] + count int32 [1] (both NULL or both set)
  * and y fp32 [d] hold the LAST step's results.  The summation order of z differs
  * from pi_predict's, so logits agree to fp32 rounding, not bit for bit.
  * events: NULL, or 2 hipEvent_t: events[0] is recorded on the stream before the
  * first launch and events[1] after the last, so their elapsed time is the run's.
- * kernel_events: NULL, or 2*nsteps hipEvent_t (not with PI_RUN_PERSISTENT): kernel 2
+ * kernel_events: NULL, or 2*nsteps hipEvent_t: kernel 2
  * of step i (the tile kernel, the one that moves the most bytes) is launched with
  * kernel_events[2i] / [2i+1] attached to its own start / end, so their elapsed time is
  * that kernel's execution time.  Attaching them slows the run down; time a run without
  * them.                                                                               */
 #define PI_RUN_AUTO        0
-#define PI_RUN_PERSISTENT  1
 #define PI_RUN_KERNELS     2
 #define PI_RUN_FUSED       3
 #define PI_RUN_SPLIT       4
@@ -272,7 +264,7 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
  * Scratch a layer needs: 256-aligned (16384 + 4 r) + 256-aligned (4 F) + 4 d P bytes, with
  * P = ceil(F/64) for the fused schedule and the split schedule's range count (at most 32)
  * otherwise; a layer that needs more than PI_NOALLOC_SCRATCH_BYTES is rejected with
- * PI_ERR_WORKSPACE, and PI_RUN_PERSISTENT with PI_ERR_UNSUPPORTED, both before any HIP call.
+ * PI_ERR_WORKSPACE before any HIP call.
  * Every other argument, output, check and error is that of pi_decode_run.                  */
 #define PI_NOALLOC_SCRATCH_BYTES (4u << 20)
 int pi_decode_run_noalloc(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,

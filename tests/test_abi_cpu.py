@@ -171,11 +171,11 @@ def _run_noalloc(p, f, mode):
 def test_decode_run_noalloc_validation():
     """The static-scratch decode entry point rejects, before any HIP call, a layer whose scratch
     exceeds PI_NOALLOC_SCRATCH_BYTES (here a fused step of 2048 tiles x 8192 columns of partial
-    rows: 64 MiB) and the persistent schedule, besides pi_decode_run's own argument checks."""
+    rows: 64 MiB), besides pi_decode_run's own argument checks (mode 1 is not assigned)."""
     big_p, big_f = pred(d=8192, r=512, F=131072), ffn(d=8192, F=131072)
     assert _run_noalloc(big_p, big_f, L.PI_RUN_FUSED) == L.PI_ERR_WORKSPACE, L.pi_last_error()
     assert "static scratch" in L.pi_last_error()
-    assert _run_noalloc(pred(), ffn(), L.PI_RUN_PERSISTENT) == L.PI_ERR_UNSUPPORTED
+    assert _run_noalloc(pred(), ffn(), 1) == L.PI_ERR_DTYPE
     assert _run_noalloc(pred(d=1001), ffn(), L.PI_RUN_KERNELS) == L.PI_ERR_SHAPE
     assert _run_noalloc(pred(), ffn(), 17) == L.PI_ERR_DTYPE
 

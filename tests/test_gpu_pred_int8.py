@@ -193,6 +193,3 @@ def test_int8_unsupported_paths_raise():
     with pytest.raises(L.PiError) as e:
         layer.predict(xd.data_ptr(), 2, None, bufs["mask"].data_ptr(), None, None)
     assert e.value.status == L.PI_ERR_UNSUPPORTED
-    with pytest.raises(L.PiError) as e:
-        layer.decode_run(xd.data_ptr(), cfg.T, 0, 1, layer.buffers(1), mode=L.PI_RUN_PERSISTENT)
-    assert e.value.status == L.PI_ERR_UNSUPPORTED

@@ -30,15 +30,3 @@ WS, WSB = A + 0x10000000, 1 << 30
 def test_predict_int8_validation(kw, B, code):
     st = L.pi_predict(pred8(**kw), A + 0x3000000, B, None, A + 0x4000000, None, None, WS, WSB, None)
     assert st == code, L.pi_last_error()
-
-
-def test_decode_run_int8_persistent_unsupported():
-    import ctypes
-    preds = (L.PredDesc * 1)(pred8())
-    ffns = (L.FfnDesc * 1)(L.FfnDesc(None, A + 0x1000000, A + 0x2000000, None, None, None, 1024, 4096,
-                                     L.PI_ACT_RELU, L.PI_W_F16))
-    st = L.pi_decode_run(preds, ffns, 1, A + 0x3000000, 4, 0, 1, L.PI_RUN_PERSISTENT, A + 0x4000000,
-                         None, None, A + 0x5000000, None, None, WS, WSB, None)
-    assert st == L.PI_ERR_UNSUPPORTED, L.pi_last_error()
-    assert "fp16 predictor" in L.pi_last_error()
-    del ctypes
