@@ -247,8 +247,9 @@ def cpu_baseline_batch(inputs, budget_s):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} tokens of step 0 onwards, each through its own predicted "
-                      f"neuron list (what the union path computes per token), numpy float64, "
-                      f"{dt:.1f} s"}
+                      f"neuron list (what the union path computes per token), numpy float64 with "
+                      f"its BLAS pool of {threads} threads, {dt:.1f} s",
+            "cpu_model": cpu_model(), **host_cpus()}
 
 
 def bench_batch(a, cfg):
