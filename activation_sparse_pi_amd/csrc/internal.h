@@ -102,6 +102,12 @@ hipError_t launch_pred_stage1(const pi_pred_desc& p, const PredPlan& pl, const u
                               float* z, hipStream_t s, const float* part = nullptr,
                               float* y = nullptr, int P = 0);
 
+// stage 2 of one token from the z that stage 1 left at pl.off_z: logits, mask, table
+hipError_t launch_pred_stage2_b1(const pi_pred_desc& p, const PredPlan& pl, float theta, float* logits,
+                                 uint32_t* mask, int32_t* idx, int32_t* count, char* ws, hipStream_t s);
+// y = the fixed-order sum of P partial rows of d floats (reduce_partials)
+hipError_t launch_reduce_rows(const float* part, int P, int d, float* y, hipStream_t s);
+
 hipError_t launch_compact(const uint32_t* mask, int B, int F, int mode, int32_t* idx,
                           int32_t* count, hipStream_t s);
 
@@ -130,7 +136,7 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
 // ---- attention side ----------------------------------------------------------------------
 struct AttnPlan {
     int nslices;              // 512-column slices of the output projection
-    size_t off_part;          // its partial rows: H x d floats (one per head-table entry)
+    size_t off_part;          // pi_attn_out's partial rows: H x d floats
     size_t bytes;
 };
 AttnPlan plan_attn(int d, int H, int dh);
@@ -139,6 +145,10 @@ AttnPlan plan_attn(int d, int H, int dh);
 hipError_t launch_attn_pqkv(const pi_attn_desc& a, const pi_pred_desc& p, const uint16_t* x,
                             const float* z, float theta, float* logits, uint32_t* mask,
                             int32_t* heads, int32_t* count, float* qkv, hipStream_t s);
+// the executor's output projection: H partial rows of d floats at part (rows of entries past
+// the count are zeros), summed into y by the next step's stage 1 or launch_reduce_rows
+hipError_t launch_attn_out_rows(const pi_attn_desc& a, const AttnPlan& pl, const float* o,
+                                const int32_t* heads, const int32_t* count, float* part, hipStream_t s);
 hipError_t launch_attn_qkv(const pi_attn_desc& a, const uint16_t* x, const uint32_t* hmask,
                            float* qkv, hipStream_t s);
 hipError_t launch_attn_out(const pi_attn_desc& a, const AttnPlan& pl, const float* o,

@@ -14,10 +14,13 @@
 //        sequential read of 6 d_head d bytes.
 //   out  y = sum over predicted heads h, c < d_head of o[h, c] W_o[h, c, :].  Block (s, j) takes
 //        entry j of the head table over the 512-column slice s: its head's d_head rows (one
-//        contiguous d_head d block of W_o) are all in flight at once, 8 per wave, 1 KB per row.
-//        The block's column sums go to partial row j with agent-scope stores, and the last of
-//        the slice's H blocks to arrive (entries past the count arrive without work) sums rows
-//        j < count in a fixed order into y.  The grid's slice dimension is padded to a multiple
+//        contiguous block of W_o), all in flight at once, 8 per wave, 1 KB per row, and stores
+//        its column sums as partial row j.  pi_attn_out: agent-scope stores, and the last of the
+//        slice's H blocks to arrive (entries past the count arrive without work) sums rows
+//        j < count in a fixed order into y.  The executor: plain stores, zero rows for the
+//        entries past the count, and the next step's stage-1 kernel -- or, after the last step,
+//        a small kernel -- sums the H rows into y, as the FFN decode schedules do: no hand-off
+//        between blocks.  The grid's slice dimension is padded to a multiple
 //        of 8, so block s + 8k j of the dispatch order -- and with it every block of slice s --
 //        lands on XCD s mod 8, and the hand-off stays inside one L2.
 #include "device_common.h"
@@ -188,6 +191,7 @@ constexpr int AO_WAVES = 16;                         // 1024 threads over a 512-
 constexpr int AO_COLS = 512;
 constexpr int AO_U = 8;                              // rows in flight per wave
 
+template <bool DEFER>
 __global__ __launch_bounds__(64 * AO_WAVES) void k_attn_out(const uint16_t* __restrict__ Wo,
                                                           const float* __restrict__ o,
                                                           const int32_t* __restrict__ heads,
@@ -208,6 +212,10 @@ __global__ __launch_bounds__(64 * AO_WAVES) void k_attn_out(const uint16_t* __re
     const int n = min(*count, H);
     const int col = tid & (AO_COLS - 1), hf = tid >> 9;
     const int gcol = slice * AO_COLS + col;
+    if (DEFER && j >= n) {                           // an entry past the count: a zero row
+        if (hf == 0 && gcol < d) part[(size_t)j * d + gcol] = 0.f;
+        return;
+    }
     if (j < n) {
         const int hd = heads[j];
         const bool hok = (unsigned)hd < (unsigned)H;
@@ -248,7 +256,11 @@ __global__ __launch_bounds__(64 * AO_WAVES) void k_attn_out(const uint16_t* __re
         for (int w = 0; w < AO_WAVES / 2; ++w) t += sr[(hf * (AO_WAVES / 2) + w) * AO_COLS + col];
         if (hf == 1) s_half[col] = t;
         __syncthreads();
-        if (hf == 0 && gcol < d) st_agent(&part[(size_t)j * d + gcol], t + s_half[col]);
+        if (hf == 0 && gcol < d) {
+            if (DEFER) part[(size_t)j * d + gcol] = t + s_half[col];
+            else st_agent(&part[(size_t)j * d + gcol], t + s_half[col]);
+        }
+        if (DEFER) return;
     }
     if (!last_block_arrive(&counters[slice], (unsigned)H)) return;
     // rows j < n: half hf takes j = hf, hf + 2, ... (16 loads in flight), then the halves meet
@@ -301,7 +313,7 @@ AttnPlan plan_attn(int d, int H, int dh) {
     AttnPlan p{};
     p.nslices = (d + AO_COLS - 1) / AO_COLS;          // <= 32 (d <= PI_ATTN_MAX_D)
     p.off_part = align_up(COUNTER_BYTES, 256);
-    p.bytes = align_up(p.off_part + (size_t)H * d * sizeof(float), 256);
+    p.bytes = align_up(p.off_part + (size_t)H * d * sizeof(float), 256);   // H partial rows
     return p;
 }
 
@@ -311,8 +323,16 @@ hipError_t launch_attn_out(const pi_attn_desc& a, const AttnPlan& pl, const floa
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_DOWN;
     float* part = reinterpret_cast<float*>(ws + pl.off_part);
     const dim3 g((pl.nslices + 7) & ~7, a.H);
-    hipLaunchKernelGGL(k_attn_out, g, dim3(64 * AO_WAVES), 0, s, static_cast<const uint16_t*>(a.w_o), o,
+    hipLaunchKernelGGL(k_attn_out<false>, g, dim3(64 * AO_WAVES), 0, s, static_cast<const uint16_t*>(a.w_o), o,
                        heads, count, a.d, a.H, a.dh, pl.nslices, part, y, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_out_rows(const pi_attn_desc& a, const AttnPlan& pl, const float* o,
+                                const int32_t* heads, const int32_t* count, float* part, hipStream_t s) {
+    const dim3 g((pl.nslices + 7) & ~7, a.H);
+    hipLaunchKernelGGL(k_attn_out<true>, g, dim3(64 * AO_WAVES), 0, s, static_cast<const uint16_t*>(a.w_o), o,
+                       heads, count, a.d, a.H, a.dh, pl.nslices, part, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -669,6 +669,13 @@ hipError_t launch_decode_step(const pi_pred_desc& p, const pi_ffn_desc& f, const
     return hipGetLastError();
 }
 
+hipError_t launch_reduce_rows(const float* part, int P, int d, float* y, hipStream_t s) {
+    const int nq = d / 4;                         // one 4-column quad per wave
+    hipLaunchKernelGGL(k_dec_finish, dim3((nq + 3) / 4), dim3(256), 0, s, part, P, y, d, nullptr, 0,
+                       nullptr, nullptr);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_finish(const DecPlan& pl, bool fused, int nhot, int d, int F, const uint32_t* mask,
                                 int32_t* idx, int32_t* count, float* y, char* ws, hipStream_t s) {
     const float* part = reinterpret_cast<const float*>(ws + pl.off_part);

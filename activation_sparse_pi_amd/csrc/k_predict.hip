@@ -324,10 +324,16 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
         if (e != hipSuccess || idx == nullptr) return e;
         return launch_compact(mask, B, p.F, PI_PER_TOKEN, idx, count, s);
     }
-    unsigned* cnt = reinterpret_cast<unsigned*>(ws);
-    float* z = reinterpret_cast<float*>(ws + pl.off_z);
-    hipError_t e = launch_pred_stage1(p, pl, x, B, z, s);
+    hipError_t e = launch_pred_stage1(p, pl, x, B, reinterpret_cast<float*>(ws + pl.off_z), s);
     if (e != hipSuccess) return e;
+    return launch_pred_stage2_b1(p, pl, theta, logits, mask, idx, count, ws, s);
+}
+
+hipError_t launch_pred_stage2_b1(const pi_pred_desc& p, const PredPlan& pl, float theta, float* logits,
+                                 uint32_t* mask, int32_t* idx, int32_t* count, char* ws, hipStream_t s) {
+    const int B = 1;
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws);
+    const float* z = reinterpret_cast<const float*>(ws + pl.off_z);
     if (p.F <= 64 && p.r <= 8192) {      // z (r floats) in LDS next to the static arrays
         if (p.pfmt == PI_P_I8G128)
             hipLaunchKernelGGL(k_p2_one<true>, dim3(1), dim3(P2_WAVES * 64), (size_t)p.r * sizeof(float), s, z,

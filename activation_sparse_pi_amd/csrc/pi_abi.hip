@@ -780,7 +780,11 @@ int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, 
     const int d = attns[0].d, H = attns[0].H, dh = attns[0].dh;
     const PredPlan ppl = plan_pred(d, preds[0].r, H, 1);
     const AttnPlan apl = plan_attn(d, H, dh);
-    if ((st = check_ws(ws, ws_bytes, std::max(ppl.bytes, apl.bytes))) != PI_OK) return st;
+    // the output projection's partial rows sit past the predictor's area (the next step's stage 1
+    // reads them while it writes z)
+    const size_t off_rows = align_up(ppl.bytes, 256);
+    const int P = H;                             // one partial row per head-table entry
+    if ((st = check_ws(ws, ws_bytes, off_rows + (size_t)P * d * sizeof(float))) != PI_OK) return st;
     const double tau = preds[0].threshold;
     const float theta = (float)std::log(tau / (1.0 - tau));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -788,15 +792,18 @@ int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, 
     hipError_t e;
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
         return hip_fail(e, "pi_attn_run start event");
+    float* rows = reinterpret_cast<float*>(w + off_rows);
     for (int i = 0; i < nsteps; ++i) {
         const long long g = s0 + i;
         const int rep = (int)(g % nrep), t = (int)(g % T);
         const uint16_t* xs = x + (size_t)t * d;
         const float* os = o + (size_t)t * H * dh;
-        // H <= 64: stage 1, then one kernel for the heads' logits, mask, table and q/k/v
+        // stage 1 (which also sums the previous step's partial rows into y); with H <= 64 one
+        // kernel then takes the heads' logits, mask, table and q/k/v, else stage 2 runs first
         const bool fold = H <= 64;
-        if ((e = fold ? launch_pred_stage1(preds[rep], ppl, xs, 1, reinterpret_cast<float*>(w + ppl.off_z), s)
-                      : launch_predict(preds[rep], ppl, xs, 1, theta, nullptr, mask, idx, count, w, s)) != hipSuccess)
+        if ((e = launch_pred_stage1(preds[rep], ppl, xs, 1, reinterpret_cast<float*>(w + ppl.off_z), s,
+                                    i > 0 ? rows : nullptr, y, P)) != hipSuccess ||
+            (!fold && (e = launch_pred_stage2_b1(preds[rep], ppl, theta, nullptr, mask, idx, count, w, s)) != hipSuccess))
             return hip_fail(e, "pi_attn_run head predictor");
         if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i]), s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run kernel event");
@@ -806,9 +813,11 @@ int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, 
             return hip_fail(e, "pi_attn_run q/k/v");
         if (kernel_events && (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i + 1]), s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run kernel event");
-        if ((e = launch_attn_out(attns[rep], apl, os, idx, count, y, w, s)) != hipSuccess)
+        if ((e = launch_attn_out_rows(attns[rep], apl, os, idx, count, rows, s)) != hipSuccess)
             return hip_fail(e, "pi_attn_run output projection");
     }
+    if (nsteps > 0 && (e = launch_reduce_rows(rows, P, d, y, s)) != hipSuccess)
+        return hip_fail(e, "pi_attn_run final y");
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[1]), s)) != hipSuccess)
         return hip_fail(e, "pi_attn_run end event");
     return ok();

@@ -268,7 +268,7 @@ class DeviceAttn:
         ab = L.pi_attn_workspace_bytes(self.attn[0])
         if pb == 0 or ab == 0:
             raise L.PiError(L.PI_ERR_SHAPE, "the library rejected the attention layer: " + L.pi_last_error())
-        self.ws_bytes = max(pb, ab)
+        self.ws_bytes = pb + ab            # pi_attn_run: the predictor's area, then the partial rows
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         L.check(L.pi_workspace_init(self.ws.data_ptr(), self.ws_bytes, self.stream()))
 

@@ -461,8 +461,10 @@ int pi_attn_out(const pi_attn_desc* a, const float* o, const int32_t* heads, con
  * q/k/v kernel.  With H <= 64 the heads' logits are computed inside the q/k/v kernel (from the
  * same z and factors; the fp32 sum runs in another order than pi_predict's, so a head within
  * rounding of the threshold can be decided the other way); the outputs are the same arrays.
- * Workspace: max(pi_workspace_bytes(pred, NULL, 1), pi_attn_workspace_bytes(a)),
- * zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_UNSUPPORTED (an
+ * The output projection of a step stores fp32 partial rows that the next step's first kernel
+ * (after the last step, a small kernel) sums into y in a fixed order, so y is bitwise that of
+ * a one-step run of the last token.  Workspace: pi_workspace_bytes(pred, NULL, 1) +
+ * pi_attn_workspace_bytes(a) bytes, zero-filled once.  Errors: PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_ALIGN, PI_ERR_UNSUPPORTED (an
  * int8 head predictor), PI_ERR_WORKSPACE before any HIP call; PI_ERR_HIP.                  */
 int pi_attn_run(const pi_pred_desc* preds, const pi_attn_desc* attns, int nrep, const uint16_t* x,
                 const float* o, int T, long long s0, int nsteps, uint32_t* mask, int32_t* idx,

@@ -276,7 +276,7 @@ def test_attn_run_validation():
     d = attn(d=4096, H=32, dh=128)
     p = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 32, 0.5)
     preds, attns = (L.PredDesc * 1)(p), (L.AttnDesc * 1)(d)
-    ws_need = max(L.pi_workspace_bytes(p, None, 1), L.pi_attn_workspace_bytes(d))
+    ws_need = L.pi_workspace_bytes(p, None, 1) + L.pi_attn_workspace_bytes(d)
     base = dict(preds=preds, attns=attns, nrep=1, x=A, o=A + 0x10000, T=4, s0=0, n=2, mask=A + 0x20000,
                 idx=A + 0x20100, count=A + 0x20200, qkv=A + 0x30000, y=A + 0x40000, ev=None, kev=None,
                 ws=A + 0x100000, ws_bytes=ws_need)
@@ -291,7 +291,8 @@ def test_attn_run_validation():
     assert call(T=0) == L.PI_ERR_SHAPE
     assert call(o=None) == L.PI_ERR_NULL
     assert call(x=A + 8) == L.PI_ERR_ALIGN
-    assert call(ws_bytes=ws_need - 256) == L.PI_ERR_WORKSPACE
+    # the predictor's area alone leaves no room for the output projection's partial rows
+    assert call(ws_bytes=L.pi_workspace_bytes(p, None, 1)) == L.PI_ERR_WORKSPACE
     bad = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 40, 0.5)   # F != H
     assert call(preds=(L.PredDesc * 1)(bad)) == L.PI_ERR_SHAPE, L.pi_last_error()
     i8 = L.PredDesc(A + 0x3000000, A + 0x4000000, A + 0x5000000, 4096, 128, 32, 0.5, L.PI_P_I8G128,
