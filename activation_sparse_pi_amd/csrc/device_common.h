@@ -289,6 +289,33 @@ PI_DEV void reduce_partials(const float* __restrict__ part, int P, int d, float*
     }
 }
 
+// Batch rows: y[b, c] = the nks shares' partials part[(k * 32 + b) * d + c] added in share order,
+// from 0, in groups of 8 with zeros for the shares past nks -- bit for bit the sum the union down
+// kernel's last block forms.  Unit q (one 4-column quad of one token, q < B d / 4) per thread;
+// its nks loads are in flight together, 8 at a time.  d % 4 == 0, part and y 16-byte aligned.
+PI_DEV void reduce_share_rows(const float* __restrict__ part, int nks, int B, int d,
+                              float* __restrict__ y, int q) {
+    const int nq = d >> 2;
+    if (q >= B * nq) return;
+    const int b = q / nq, c = 4 * (q - b * nq);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < nks; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = *reinterpret_cast<const float4*>(part + ((size_t)(k0 + k < nks ? k0 + k : 0) * 32 + b) * d + c);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool ok = k0 + k < nks;
+            t.x += ok ? v[k].x : 0.f;
+            t.y += ok ? v[k].y : 0.f;
+            t.z += ok ? v[k].z : 0.f;
+            t.w += ok ? v[k].w : 0.f;
+        }
+    }
+    *reinterpret_cast<float4*>(y + (size_t)b * d + c) = t;
+}
+
 // Every block calls this once, after all its threads issued their st_agent
 // partials.  The barrier drains the stores (vmcnt(0)) before thread 0 bumps the
 // arrival counter, so the block that sees the final count reads complete

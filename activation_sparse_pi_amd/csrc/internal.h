@@ -91,10 +91,14 @@ hipError_t launch_predict(const pi_pred_desc& p, const PredPlan& pl, const uint1
 
 // 1 < B <= 32: stage 1 and stage 2 with threshold and mask words (no neuron tables); umask
 // (optional, ceil(F/32) words): the OR of the B tokens' masks
+// yprev (optional): the previous union pass's deferred down shares -- ynks shares of 32 rows of d
+// floats at ypart -- are summed into yprev [yB, d] by this pass's predictor (its share-summing
+// kernel, or a kernel of its own where stage 1 has no shares)
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
                                 hipStream_t s, uint32_t* umask = nullptr,
-                                uint32_t* tokbits = nullptr);
+                                uint32_t* tokbits = nullptr, const float* ypart = nullptr,
+                                int ynks = 0, int yB = 0, float* yprev = nullptr);
 
 // part / y (batch-1 decode executor only): also sum the previous step's P partial rows of d
 // floats into y (reduce_partials)
@@ -128,10 +132,14 @@ hipError_t launch_down_b1(const pi_ffn_desc& f, const FfnPlan& pl, const int32_t
 // 1 < B <= 32 union-mask path on MFMA.  With umask == nullptr the union list idx[0 .. *count)
 // is read; otherwise the list is built from the union mask umask and written to idx / count,
 // and tokbits[F] (per neuron, bit b: in token b's mask) stands in for the token masks.
+// defer_part (optional, with pl.u_ks > 1): the down shares' partials go there (pl.u_ks shares
+// of 32 rows of d floats) and y is left to a later reduce_share_rows (launch_union_yred or the
+// next pass's predictor) instead of the down kernel's last blocks.
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
                             const uint32_t* umask, const uint32_t* tokbits, int32_t* idx,
                             int32_t* count, const uint32_t* token_mask, float* y, char* ws,
-                            hipStream_t s);
+                            hipStream_t s, float* defer_part = nullptr);
+hipError_t launch_union_yred(const float* part, int nks, int B, int d, float* y, hipStream_t s);
 
 // ---- attention side ----------------------------------------------------------------------
 struct AttnPlan {

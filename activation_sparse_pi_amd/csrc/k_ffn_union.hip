@@ -358,7 +358,7 @@ PI_DEV int dn_z(int i) { return 4 * (i & 3) + (i >> 2); }
 __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
     const uint4* __restrict__ Hf, int B, const uint16_t* __restrict__ Wd, int d, int F,
     const int32_t* __restrict__ uidx, const int32_t* __restrict__ ucount, int ncg, int nks,
-    float* __restrict__ part, unsigned* __restrict__ counter, float* __restrict__ y) {
+    float* __restrict__ part, unsigned* __restrict__ counter, float* __restrict__ y, int defer) {
     constexpr int NB = DN_NB;
     __shared__ uint4 s_t[DN_NWU][2 * DN_HS];         // per wave: two k-halves x 256 column units
     const int tid = threadIdx.x, lane = tid & 63;
@@ -516,6 +516,8 @@ __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
 #pragma unroll
     for (int i = 0; i < NV; ++i)
         if (row_of(i) < B && col(i) < d) st_agent(&part[((size_t)ks * 32 + row_of(i)) * d + col(i)], v[i]);
+    // deferred: a later kernel sums the shares into y (reduce_share_rows), no hand-off here
+    if (defer) return;
     if (!last_block_arrive(&counter[cgi], nks)) return;
     // The last block of the column group adds every share's partial (its own included) in
     // share order.  Chunk q = tid + 256 m (m < 8) is token q / 64 (wave-uniform), columns
@@ -560,7 +562,18 @@ __global__ __launch_bounds__(DN_NWU * 64) void k_union_down(
     }
 }
 
+__global__ __launch_bounds__(256) void k_union_yred(const float* __restrict__ part, int nks, int B, int d,
+                                                    float* __restrict__ y) {
+    reduce_share_rows(part, nks, B, d, y, blockIdx.x * 256 + threadIdx.x);
+}
+
 }  // namespace
+
+hipError_t launch_union_yred(const float* part, int nks, int B, int d, float* y, hipStream_t s) {
+    const int nq = B * (d / 4);
+    hipLaunchKernelGGL(k_union_yred, dim3((nq + 255) / 256), dim3(256), 0, s, part, nks, B, d, y);
+    return hipGetLastError();
+}
 
 size_t plan_union(FfnPlan& p, int d, int F, size_t off) {
     p.off_H = off;
@@ -604,7 +617,7 @@ int up_slots(K kern) {
 hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint16_t* x, int B,
                             const uint32_t* umask, const uint32_t* tokbits, int32_t* idx,
                             int32_t* count, const uint32_t* token_mask, float* y, char* ws,
-                            hipStream_t s) {
+                            hipStream_t s, float* defer_part) {
     uint4* Hf = reinterpret_cast<uint4*>(ws + pl.off_H);
     float* upart = reinterpret_cast<float*>(ws + pl.off_uppart);
     unsigned* ucnt = reinterpret_cast<unsigned*>(ws + pl.off_upcnt);
@@ -638,10 +651,11 @@ hipError_t launch_ffn_union(const pi_ffn_desc& f, const FfnPlan& pl, const uint1
     }
     if (e != hipSuccess) return e;
     unsigned* cnt = reinterpret_cast<unsigned*>(ws) + CNT_UNION;
-    float* part = reinterpret_cast<float*>(ws + pl.off_upart);
+    const bool defer = defer_part != nullptr && pl.u_ks > 1;
+    float* part = defer ? defer_part : reinterpret_cast<float*>(ws + pl.off_upart);
     hipLaunchKernelGGL(k_union_down, dim3(pl.u_ncg * pl.u_ks), dim3(DN_NWU * 64), 0, s, Hf, B,
                        static_cast<const uint16_t*>(f.w_down), f.d, f.F, idx, count, pl.u_ncg,
-                       pl.u_ks, part, cnt, y);
+                       pl.u_ks, part, cnt, y, defer ? 1 : 0);
     return hipGetLastError();
 }
 

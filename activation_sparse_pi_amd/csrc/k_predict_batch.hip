@@ -102,9 +102,16 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
         if (ob[q] < B && oj[q] < r) part[((size_t)ks * 32 + ob[q]) * r + oj[q]] = v[q];
 }
 
-// z[b, j] = the nks shares' partials of (b, j) added in share order; all loads in flight at once
+// z[b, j] = the nks shares' partials of (b, j) added in share order; all loads in flight at once.
+// Blocks past zblocks sum the previous union pass's deferred down shares into its y instead.
 __global__ __launch_bounds__(256) void k_pbz(const float* __restrict__ part, int B, int r, int nks,
-                                             float* __restrict__ z) {
+                                             float* __restrict__ z, int zblocks,
+                                             const float* __restrict__ ypart, int ynks, int yB, int d,
+                                             float* __restrict__ y) {
+    if ((int)blockIdx.x >= zblocks) {
+        reduce_share_rows(ypart, ynks, yB, d, y, (blockIdx.x - zblocks) * 256 + threadIdx.x);
+        return;
+    }
     const int o = blockIdx.x * 256 + threadIdx.x;
     if (o >= B * r) return;
     const int b = o / r, j = o - b * r;
@@ -317,7 +324,8 @@ void plan_pred_batch(PredPlan& p, int d, int r, int F, size_t& off) {
 
 hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const uint16_t* x,
                                 int B, float theta, float* logits, uint32_t* mask, char* ws,
-                                hipStream_t s, uint32_t* umask, uint32_t* tokbits) {
+                                hipStream_t s, uint32_t* umask, uint32_t* tokbits, const float* ypart,
+                                int ynks, int yB, float* yprev) {
     float* z = reinterpret_cast<float*>(ws + pl.off_z);
     float* part = reinterpret_cast<float*>(ws + pl.off_zpart);
     hipLaunchKernelGGL(k_pb1, dim3(pl.b_ntile * pl.b_nks), dim3(PB_NW * 64), 0, s, x, B,
@@ -325,10 +333,14 @@ hipError_t launch_predict_batch(const pi_pred_desc& p, const PredPlan& pl, const
                        p.d, p.r, pl.b_ntile, pl.b_nks, part, z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int yblocks = ypart ? (yB * (p.d / 4) + 255) / 256 : 0;
     if (pl.b_nks > 1) {
-        hipLaunchKernelGGL(k_pbz, dim3((B * p.r + 255) / 256), dim3(256), 0, s, part, B, p.r,
-                           pl.b_nks, z);
+        const int zblocks = (B * p.r + 255) / 256;
+        hipLaunchKernelGGL(k_pbz, dim3(zblocks + yblocks), dim3(256), 0, s, part, B, p.r, pl.b_nks, z,
+                           zblocks, ypart, ynks, yB, p.d, yprev);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (ypart && (e = launch_union_yred(ypart, ynks, yB, p.d, yprev, s)) != hipSuccess) {
+        return e;
     }
     hipLaunchKernelGGL(p.r <= ZC ? k_pb2<true> : k_pb2<false>, dim3((p.F + 127) / 128),
                        dim3(PB_NW * 64), 0, s, z, B,

@@ -138,15 +138,19 @@ size_t ws_base(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int B_max) {
 // pi_batch_run's union path keeps the batch's union mask, token words, list and count past the shared region
 // (they live from the predictor's launch to the union FFN's, which uses that region)
 struct BatchWs {
-    size_t off_umask, off_tokbits, off_uidx, off_ucount, bytes;
+    size_t off_umask, off_tokbits, off_uidx, off_ucount, off_ypart, bytes;
+    int yks;    // union down shares whose partials a pass leaves for the next pass to sum (0: none)
 };
-BatchWs batch_ws(size_t base, int F) {
+BatchWs batch_ws(size_t base, int F, int d) {
     BatchWs w{};
     w.off_umask = align_up(base, 256);
     w.off_tokbits = align_up(w.off_umask + (size_t)((F + 31) / 32) * 4, 256);
     w.off_uidx = align_up(w.off_tokbits + (size_t)F * 4, 256);
     w.off_ucount = align_up(w.off_uidx + (size_t)F * 4, 256);
-    w.bytes = w.off_ucount + 256;
+    w.off_ypart = w.off_ucount + 256;
+    const int ks = plan_ffn(d, F, PI_W_F16, 2).u_ks;
+    w.yks = ks > 1 ? ks : 0;
+    w.bytes = align_up(w.off_ypart + (size_t)w.yks * 32 * d * sizeof(float), 256);
     return w;
 }
 
@@ -264,7 +268,7 @@ size_t pi_workspace_bytes(const pi_pred_desc* pred, const pi_ffn_desc* ffn, int 
     const size_t base = ws_base(pred, ffn, B_max);
     if (base == 0) return 0;
     // with both descriptors and B_max > 1: also pi_batch_run's union mask, list and count
-    if (pred && ffn && B_max > 1 && pred->F == ffn->F) return batch_ws(base, ffn->F).bytes;
+    if (pred && ffn && B_max > 1 && pred->F == ffn->F) return batch_ws(base, ffn->F, ffn->d).bytes;
     return base;
 }
 
@@ -575,7 +579,7 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
     }
     const int Gmax = sched == PI_BATCH_UNION ? group_size(B, 0) : 1;   // the largest group
     const size_t base = ws_base(&preds[0], &ffns[0], Gmax);
-    const BatchWs bw = batch_ws(base, F);
+    const BatchWs bw = batch_ws(base, F, d);
     const size_t need = sched == PI_BATCH_UNION ? bw.bytes : base;
     if ((st = check_ws(ws, ws_bytes, need)) != PI_OK) return st;
     const DecPlan dpl = plan_decode(d, r, F, ffns[0].wfmt);
@@ -588,6 +592,11 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
     uint32_t* tokbits = reinterpret_cast<uint32_t*>(w + bw.off_tokbits);
     int32_t* uidx = reinterpret_cast<int32_t*>(w + bw.off_uidx);
     int32_t* ucount = reinterpret_cast<int32_t*>(w + bw.off_ucount);
+    // one union pass per step with its down projection in shares: the pass leaves the shares'
+    // partials and the next pass's predictor (after the last step, a small kernel) sums them
+    // into y -- bit for bit the down kernel's own sum, without its cross-block hand-off
+    const bool defer = sched == PI_BATCH_UNION && batch_groups(B) == 1 && bw.yks > 0;
+    float* ypart = reinterpret_cast<float*>(w + bw.off_ypart);
     hipError_t e;
     if (events && (e = hipEventRecord(static_cast<hipEvent_t>(events[0]), s)) != hipSuccess)
         return hip_fail(e, "pi_batch_run start event");
@@ -613,14 +622,17 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
                 const PredPlan ppl = plan_pred(d, r, F, Bg);
                 const FfnPlan fpl = plan_ffn(d, F, Fd.wfmt, Bg);
                 // the union FFN builds the union's list from the union mask itself
+                const bool yprev = defer && i > 0;
                 if ((e = launch_predict_batch(P, ppl, xs + (size_t)b0 * d, Bg, theta, nullptr,
-                                              mask + (size_t)b0 * W, w, s, umask, tokbits)) != hipSuccess)
+                                              mask + (size_t)b0 * W, w, s, umask, tokbits,
+                                              yprev ? ypart : nullptr, bw.yks, B, y)) != hipSuccess)
                     return hip_fail(e, "pi_batch_run union pass");
                 if (kernel_events &&
                     (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i]), s)) != hipSuccess)
                     return hip_fail(e, "pi_batch_run kernel event");
                 if ((e = launch_ffn_union(Fd, fpl, xs + (size_t)b0 * d, Bg, umask, tokbits, uidx, ucount,
-                                          mask + (size_t)b0 * W, y + (size_t)b0 * d, w, s)) != hipSuccess)
+                                          mask + (size_t)b0 * W, y + (size_t)b0 * d, w, s,
+                                          defer ? ypart : nullptr)) != hipSuccess)
                     return hip_fail(e, "pi_batch_run union pass");
                 if (kernel_events &&
                     (e = hipEventRecord(static_cast<hipEvent_t>(kernel_events[2 * i + 1]), s)) != hipSuccess)
@@ -628,6 +640,8 @@ int pi_batch_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep, c
             }
         }
     }
+    if (defer && nsteps > 0 && (e = launch_union_yred(ypart, bw.yks, B, d, y, s)) != hipSuccess)
+        return hip_fail(e, "pi_batch_run final y");
     if (sched == PI_BATCH_TOKENS && nsteps > 0 &&
         (e = launch_decode_finish(dpl, fused, ffns[0].nhot, d, F, mask + (size_t)(B - 1) * W, nullptr,
                                   nullptr, y + (size_t)(B - 1) * d, w, s)) != hipSuccess)
