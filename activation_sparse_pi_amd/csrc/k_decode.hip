@@ -110,21 +110,38 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         }
     }
 
-    // --- logits of the tile: the first segment of its W2t rows (and the tile's bias) goes
-    // out before z is staged
+    // --- logits of the tile: the first segment of its W2t rows (and the tile's bias) goes out
+    // first, then z and x.  fp16 rows, r <= 1024 and d <= 8192: two values of each per thread,
+    // all in flight together and staged after one wait (staged in a loop, each iteration waits
+    // for everything issued before it); the stores go to clamped addresses (a thread past r or
+    // d rewrites the last value), so no branch takes the loads with it.  (Measured: OPT-30B
+    // layer -0.55 us per step, LLaMA-7B -0.1; the int4 LLaMA-70B layer +1.3 us, so int4 rows
+    // keep the loop.)
     TileRows<B_WAVES, P8> tr;
     tile_rows_load<B_WAVES, P8>(tr, W2t, S2, r, F, tile, 0);
     const float bv = (wave == 0 && tile * 64 + lane < F) ? bias[tile * 64 + lane] : 0.f;
-    for (int j = tid; j < r; j += NT) s_z[j] = z[j];
     const int nc8 = d >> 3;
-    for (int c = tid; c < nc8; c += NT) {
-        const uint4 a = ld16(x + 8 * c);
-        if (WF == 0) {
-            s_x[c] = a;
-        } else {
-            s_x[c] = make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
-                                (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
+    auto regroup = [](uint4 a) {
+        return WF == 0 ? a
+                       : make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
+                                    (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
+    };
+    if (WF == 0 && r <= 2 * NT && nc8 <= 2 * NT) {   // block-uniform
+        float zr[2];
+        uint4 xq[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            zr[k] = z[min(tid + NT * k, r - 1)];
+            xq[k] = ld16(x + 8 * min(tid + NT * k, nc8 - 1));
         }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            s_z[min(tid + NT * k, r - 1)] = zr[k];
+            s_x[min(tid + NT * k, nc8 - 1)] = regroup(xq[k]);
+        }
+    } else {
+        for (int j = tid; j < r; j += NT) s_z[j] = z[j];
+        for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
     }
     __syncthreads();
     float acc[TileRows<B_WAVES, P8>::RPW] = {};
