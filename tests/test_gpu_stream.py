@@ -1,14 +1,20 @@
 """The benchmarked paths over whole token streams, as bench.py runs them (needs an MI355X).
 
-* c2 and c5 through pi_decode_run in its kernel schedule (two kernels per step on c2, three on
-  c5) with the bench's replica count (17 and 6): every token of the stream as a one-step run
+* c2, c3 and c5 through pi_decode_run in its kernel schedule (two kernels per step on c2, three
+  on c3 and c5) with the bench's replica count: every token of the stream as a one-step run
   (token t on replica t mod R) -- its index set against the oracle outside the 1e-4 band, its
   mask equal to the bitmask of its table, its y against the oracle's FFN over its own table
-  (every token on c2, every sixteenth on c5, whose int4 oracle takes seconds a token) -- and then one run over
-  the whole stream that must end bit-identical to the one-step run of its last token.
+  (every token on c2, every fourth on c3, every sixteenth on c5, whose int4 oracle takes
+  seconds a token) -- and then one run over the whole stream that must end bit-identical to the
+  one-step run of its last token.
 * c4 through pi_batch_run's union schedule at B = 32: every step of the 64-step stream as a
   one-step run, all 32 tokens' index sets against the oracle, y for one token every other step
   (a different slot b each time).
+* a2 and a3 (the attention side) through pi_attn_run with the bench's replica count: every
+  token of the stream as a one-step run -- its head set against the oracle outside the band,
+  the mask equal to the table's bitmask, q/k/v of the listed heads and y against the oracle
+  over the GPU's own head table -- and a run over the stream that must end bit-identical to
+  the one-step run of its last token.
 """
 import math
 import sys
@@ -36,7 +42,7 @@ def _replicas(cfg):
     return max(2, math.ceil(bench.CACHE_BUST_BYTES / bench.bytes_model(cfg, cfg.mean_rate * cfg.F)["total"]))
 
 
-@pytest.mark.parametrize("name,y_every", [("c2", 1), ("c5", 16)])
+@pytest.mark.parametrize("name,y_every", [("c2", 1), ("c3", 4), ("c5", 16)])
 def test_decode_stream(name, y_every):
     from activation_sparse_pi_amd import _lib as L
     from activation_sparse_pi_amd.layer import DeviceLayer
@@ -100,3 +106,48 @@ def test_batch_stream_c4():
             if t % 2 == 0 and b == (t // 2 * 7) % B:
                 worst = max(worst, P.check_ffn(yh[b], W, X[b], idx, ctx=f"c4 t={t} b={b}"))
     say(f"  all {T * B} tokens' sets checked: band differences {band}, worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", ["a2", "a3"])
+def test_attn_stream(name):
+    import bench
+    from synth import attn as SA
+    import oracle.attn_oracle as A
+    from activation_sparse_pi_amd.layer import DeviceAttn
+    cfg = SA.get(name)
+    R = max(2, math.ceil(bench.CACHE_BUST_BYTES / bench.bytes_model_attn(cfg, cfg.mean_rate * cfg.H)["total"]))
+    say(f"[gpu] attention stream {cfg.name}: {cfg.T} tokens, {R} replicas")
+    inp = SA.make(cfg)
+    att = DeviceAttn(inp, replicas=R)
+    xd = torch.from_numpy(inp["x"].copy()).to(att.device)
+    od = torch.from_numpy(inp["o"].copy()).to(att.device)
+    ref_L = A.head_logits(inp["x"], inp["w_a1"], inp["w_a2"], inp["bias_a"])
+    bufs = att.buffers()
+    worst = 0.0
+    for t in range(cfg.T):
+        att.run(xd.data_ptr(), od.data_ptr(), cfg.T, t, 1, bufs)
+        torch.cuda.synchronize()
+        n = int(bufs["count"][0].item())
+        heads = bufs["idx"][:n].cpu().numpy().astype(np.int64)
+        ctx = f"{name} t={t} replica {t % R}"
+        P.check_index_set(heads, bufs["mask"].cpu().numpy().view(np.uint32), ref_L[t], cfg.H, ctx=ctx)
+        qkv = bufs["qkv"].cpu().numpy().astype(np.float64)
+        off = np.setdiff1d(np.arange(cfg.H), heads)
+        assert not np.any(qkv[off]), f"{ctx}: unlisted heads not 0"
+        if heads.size:
+            ref_qkv = A.qkv_heads(inp["w_qkv"], inp["x"][t], heads)
+            worst = max(worst, P.rel_l2(qkv[heads], ref_qkv[heads]))
+            worst = max(worst, P.rel_l2(bufs["y"].cpu().numpy().astype(np.float64),
+                                        A.out_heads(inp["w_o"], inp["o"][t], heads)))
+        else:
+            assert not np.any(bufs["y"].cpu().numpy()), f"{ctx}: y of no head must be 0"
+        assert worst <= P.REL_TOL, f"{ctx}: rel-L2 {worst:.3e}"
+    say(f"  every token checked: worst rel-L2 {worst:.2e}")
+    long, one = att.buffers(), att.buffers()
+    att.run(xd.data_ptr(), od.data_ptr(), cfg.T, 0, 2 * cfg.T + 3, long)
+    att.run(xd.data_ptr(), od.data_ptr(), cfg.T, 2 * cfg.T + 2, 1, one)
+    torch.cuda.synchronize()
+    for k in ("mask", "count", "qkv", "y"):
+        assert torch.equal(long[k], one[k]), f"{name}: {k} of a long run differs from its last one-step run"
+    c = int(one["count"][0].item())
+    assert torch.equal(long["idx"][:c], one["idx"][:c])
