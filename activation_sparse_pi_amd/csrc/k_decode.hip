@@ -126,6 +126,9 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
                        : make_uint4((a.x & 0xFFFFu) | (a.z << 16), (a.x >> 16) | (a.z & 0xFFFF0000u),
                                     (a.y & 0xFFFFu) | (a.w << 16), (a.y >> 16) | (a.w & 0xFFFF0000u));
     };
+    // int4 rows without a hot block stage x after the ballot, where only the dot products need
+    // it, instead of behind the W2t rows (the hot block dots its rows with x before the ballot)
+    const bool late_x = WF == 1 && nhot == 0;          // block-uniform
     if (WF == 0 && r <= 2 * NT && nc8 <= 2 * NT) {   // block-uniform
         float zr[2];
         uint4 xq[2];
@@ -141,7 +144,8 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         }
     } else {
         for (int j = tid; j < r; j += NT) s_z[j] = z[j];
-        for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
+        if (!late_x)
+            for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
     }
     __syncthreads();
     float acc[TileRows<B_WAVES, P8>::RPW] = {};
@@ -211,6 +215,10 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     // --- rows of the active neurons: (neuron, matrix) items, IPW per wave in flight
     const int na = s_n;
     const int items = na * M;
+    if (late_x) {                                     // x for the dot products (block-uniform)
+        for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
+        __syncthreads();
+    }
     for (int it0 = wave * IPW; it0 < items; it0 += B_WAVES * IPW) {
         uint4 wr[IPW][Q];
         uint32_t sr[IPW][Q];   // raw fp16 scales, one per register
