@@ -142,6 +142,14 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
             s_z[min(tid + NT * k, r - 1)] = zr[k];
             s_x[min(tid + NT * k, nc8 - 1)] = regroup(xq[k]);
         }
+    } else if (late_x && r <= 2 * NT) {
+        // z in one round (two values per thread, clamped as above); x comes after the ballot
+        // (measured: the LLaMA-70B-shaped layer 33.57 -> 33.40 us per step)
+        float zr[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) zr[k] = z[min(tid + NT * k, r - 1)];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) s_z[min(tid + NT * k, r - 1)] = zr[k];
     } else {
         for (int j = tid; j < r; j += NT) s_z[j] = z[j];
         if (!late_x)
