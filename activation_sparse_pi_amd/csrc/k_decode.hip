@@ -386,6 +386,26 @@ PI_DEV int range_compact(const uint32_t* __restrict__ mask, int w0, int w1, int 
                          int* s_tmp) {
     const int W = (F + 31) >> 5;
     const int t = threadIdx.x;
+    if (w1 - w0 <= 64) {                             // block-uniform: wave 0 alone, one barrier
+        if (t < 64) {
+            uint32_t v = 0;
+            if (w0 + t < w1) {
+                v = mask[w0 + t];
+                if (w0 + t == W - 1 && (F & 31)) v &= (1u << (F & 31)) - 1u;
+            }
+            const int c = __popc(v);
+            const int inc = wave_inclusive_scan(c);
+            int pos = inc - c;
+            while (v) {
+                const int b = __ffs(v) - 1;
+                s_ids[pos++] = ((w0 + t) << 5) + b;
+                v &= v - 1u;
+            }
+            if (t == 63) s_tmp[0] = inc;
+        }
+        __syncthreads();
+        return s_tmp[0];
+    }
     uint32_t v = 0;
     if (w0 + t < w1) {
         v = mask[w0 + t];
