@@ -213,6 +213,25 @@ PI_DEV float wave_sum(float v) {
     return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
+// Position of the k-th (from 0) set bit of m (k < popcount(m)): a binary search on popcounts,
+// scalar when m and k are wave-uniform.
+PI_DEV int kth_set_bit(unsigned long long m, int k) {
+    int pos = 0;
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) {
+        const unsigned long long low = m & ((1ull << s) - 1ull);
+        const int c = __popcll(low);
+        if (k >= c) {
+            k -= c;
+            m >>= s;
+            pos += s;
+        } else {
+            m = low;
+        }
+    }
+    return pos;
+}
+
 // Inclusive prefix sum over the 64 lanes (integers): row_shr 1, 2, 4, 8 inside each row of
 // 16, then row_bcast 15 / 31 carry row totals into the rows above.
 PI_DEV int wave_inclusive_scan(int v) {

@@ -73,8 +73,8 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     __shared__ float s_red[64];
     __shared__ float s_dot[2][64];
     __shared__ int s_list[64];
-    __shared__ int s_n;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: item indices stay scalar
     const int tile = blockIdx.x;
     const int W = (F + 31) >> 5;
 
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     // keep the loop.)
     TileRows<B_WAVES, P8> tr;
     tile_rows_load<B_WAVES, P8>(tr, W2t, S2, r, F, tile, 0);
-    const float bv = (wave == 0 && tile * 64 + lane < F) ? bias[tile * 64 + lane] : 0.f;
+    const float bv = tile * 64 + lane < F ? bias[tile * 64 + lane] : 0.f;   // every wave thresholds
     const int nc8 = d >> 3;
     auto regroup = [](uint4 a) {
         return WF == 0 ? a
@@ -197,31 +197,33 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         if (lane == 0) h[hn] = GLU ? fmaxf(hd[0], 0.f) * hd[M - 1] : fmaxf(hd[0], 0.f);
     }
 
-    // --- threshold, mask words, the tile's active list (wave 0: lane = neuron of the tile)
+    // --- threshold: every wave forms the tile's ballot from the logits in LDS (lane = neuron
+    // of the tile) and finds its own items' neurons in it (kth_set_bit), with no barrier before
+    // the gather; wave 0 also writes the mask words, the logits and the list the phases after
+    // the gather read
+    const int n = tile * 64 + lane;
+    bool act = false;
+    float lg = 0.f;
+    if (n < F) {
+        lg = s_red[lane] + bv;
+        act = lg > theta;
+    }
+    const unsigned long long bal = __ballot(act);
+    // the row list holds the active neurons outside the hot block (all of them when fused)
+    const bool listed = act && (FUSED || n >= nhot);
+    const unsigned long long bl = __ballot(listed);
     if (wave == 0) {
-        const int n = tile * 64 + lane;
-        bool act = false;
-        if (n < F) {
-            const float l = s_red[lane] + bv;
-            act = l > theta;
-            if (logits) logits[n] = l;
-        }
-        const unsigned long long bal = __ballot(act);
+        if (logits && n < F) logits[n] = lg;
         if (lane == 0) {
             mask[2 * tile] = (uint32_t)bal;
             if (2 * tile + 1 < W) mask[2 * tile + 1] = (uint32_t)(bal >> 32);
         }
-        // the row list holds the active neurons outside the hot block (all of them when fused)
-        const bool listed = act && (FUSED || n >= nhot);
-        const unsigned long long bl = __ballot(listed);
         const uint32_t lo = (uint32_t)bl, hi = (uint32_t)(bl >> 32);
-        if (lane == 0) s_n = __popcll(bl);
         if (listed) s_list[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = lane;
     }
-    __syncthreads();
 
     // --- rows of the active neurons: (neuron, matrix) items, IPW per wave in flight
-    const int na = s_n;
+    const int na = __popcll(bl);
     const int items = na * M;
     if (late_x) {                                     // x for the dot products (block-uniform)
         for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
             const bool valid = it < items;
             const int k = GLU ? (it >> 1) : it;
             const int mat = GLU ? (it & 1) : 1;        // 0 = gate, 1 = up
-            const size_t row = valid ? (size_t)(tile * 64 + s_list[k < 64 ? k : 63]) : 0;
+            const size_t row = valid ? (size_t)(tile * 64 + kth_set_bit(bl, k)) : 0;
             const uint8_t* base = static_cast<const uint8_t*>(mat ? Wu : Wg) + row * rb;
             const uint16_t* sbase = WF == 1 ? (mat ? Su : Sg) + row * G : nullptr;
 #pragma unroll
