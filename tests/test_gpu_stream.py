@@ -6,7 +6,9 @@
   mask equal to the bitmask of its table, its y against the oracle's FFN over its own table
   (every token on c2, every fourth on c3, every sixteenth on c5, whose int4 oracle takes
   seconds a token) -- and then one run over the whole stream that must end bit-identical to the
-  one-step run of its last token.
+  one-step run of its last token.  c3 and c5 also as the bench times them, with the neurons
+  dealt over the tiles (placed): every token's set mapped back to original ids against the
+  oracle, and y with the table from pi_map_ids on every 8th / 32nd token.
 * c4 through pi_batch_run's union schedule at B = 32: every step of the 64-step stream as a
   one-step run, all 32 tokens' index sets against the oracle, y for one token every other step
   (a different slot b each time).
@@ -42,16 +44,22 @@ def _replicas(cfg):
     return max(2, math.ceil(bench.CACHE_BUST_BYTES / bench.bytes_model(cfg, cfg.mean_rate * cfg.F)["total"]))
 
 
-@pytest.mark.parametrize("name,y_every", [("c2", 1), ("c3", 4), ("c5", 16)])
-def test_decode_stream(name, y_every):
+@pytest.mark.parametrize("name,y_every,placed", [("c2", 1, False), ("c3", 4, False), ("c5", 16, False),
+                                                  ("c3", 8, True), ("c5", 32, True)])
+def test_decode_stream(name, y_every, placed):
+    """placed: the layer as the bench times the split-schedule layers -- neurons dealt over the
+    tiles from 256 calibration tokens -- checked through its neuron table against the oracle of
+    the original layer."""
     from activation_sparse_pi_amd import _lib as L
     from activation_sparse_pi_amd.layer import DeviceLayer
+    from .test_gpu_place import _check_placed, _placement
     cfg = configs.get(name)
     R = _replicas(cfg)
-    say(f"[gpu] stream {cfg.name}: {cfg.T} tokens, {R} replicas")
+    say(f"[gpu] stream {cfg.name}: {cfg.T} tokens, {R} replicas{', dealt placement' if placed else ''}")
     inp = gen.make(cfg)
     W = O.Weights.from_inputs(inp)
-    layer = DeviceLayer(inp, replicas=R)
+    perm = _placement(inp, ncal=256)[0] if placed else None
+    layer = DeviceLayer(inp, replicas=R, perm=perm)
     X = inp["x"][:, 0, :]
     xd = torch.from_numpy(X.copy()).to(layer.device)
     ref_L = O.predictor_logits(X, inp["w_p1"], inp["w_p2"], inp["bias"])
@@ -60,9 +68,19 @@ def test_decode_stream(name, y_every):
     for t in range(cfg.T):
         layer.decode_run(xd.data_ptr(), cfg.T, t, 1, bufs, mode=L.PI_RUN_KERNELS)
         torch.cuda.synchronize()
+        ctx = f"{name} t={t} replica {t % R}"
+        if placed:
+            if t % y_every == 0:
+                worst = max(worst, _check_placed(layer, perm, bufs, 0, ref_L[t], W, X[t], cfg.F, ctx))
+            else:                                     # the index set, mapped back on the host
+                n = int(bufs["count"][0].item())
+                orig = np.sort(perm[bufs["idx"][0, :n].cpu().numpy()].astype(np.int64))
+                act = np.zeros(cfg.F, bool)
+                act[orig] = True
+                band += P.check_index_set(orig, O.mask_words(act), ref_L[t], cfg.F, ctx=ctx)
+            continue
         n = int(bufs["count"][0].item())
         idx = bufs["idx"][0, :n].cpu().numpy().astype(np.int64)
-        ctx = f"{name} t={t} replica {t % R}"
         band += P.check_index_set(idx, bufs["mask"][0].cpu().numpy().view(np.uint32), ref_L[t], cfg.F, ctx=ctx)
         if t % y_every == 0:
             worst = max(worst, P.check_ffn(bufs["y"][0].cpu().numpy().astype(np.float64), W, X[t], idx, ctx=ctx))
