@@ -66,9 +66,7 @@ def parse():
                          "on calibration tokens (pi_place_neurons); hot: the neurons firing on at "
                          "least --hot-rate of them form a hot block computed without waiting for "
                          "the predictor, the rest dealt (pi_place_neurons_hot); auto (default): "
-                         "dealt for the layers the split schedule runs, none for the fused ones "
-                         "(measured: the deal balances the split tile kernel's tiles and costs the "
-                         "fused one a little); batch 1 only")
+                         "dealt (it balances the tile kernel's tiles); batch 1 only")
     ap.add_argument("--hot-rate", type=float, default=0.7, help="profiled rate of the hot block")
     ap.add_argument("--calib-tokens", type=int, default=256, help="calibration tokens for --placement")
     ap.add_argument("--pred-format", choices=("f16", "i8g128"), default="f16",
@@ -595,7 +593,7 @@ def main():
     R = a.replicas or max(2, math.ceil(CACHE_BUST_BYTES / probe["total"]))
     perm, nhot = None, 0
     if a.placement == "auto":
-        a.placement = "dealt" if kernel_schedule(cfg) == "split" else "none"
+        a.placement = "dealt"
     if a.placement in ("dealt", "hot"):
         # profiling run on calibration tokens of their own (none of the timed stream), then
         # the placement; the timed layer holds the placed weights

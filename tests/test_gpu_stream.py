@@ -6,9 +6,9 @@
   mask equal to the bitmask of its table, its y against the oracle's FFN over its own table
   (every token on c2, every fourth on c3, every sixteenth on c5, whose int4 oracle takes
   seconds a token) -- and then one run over the whole stream that must end bit-identical to the
-  one-step run of its last token.  c3 and c5 also as the bench times them, with the neurons
+  one-step run of its last token.  Every layer also as the bench times it, with the neurons
   dealt over the tiles (placed): every token's set mapped back to original ids against the
-  oracle, and y with the table from pi_map_ids on every 8th / 32nd token.
+  oracle, and y with the table from pi_map_ids on sampled tokens.
 * c4 through pi_batch_run's union schedule at B = 32: every step of the 64-step stream as a
   one-step run, all 32 tokens' index sets against the oracle, y for one token every other step
   (a different slot b each time).
@@ -45,11 +45,12 @@ def _replicas(cfg):
 
 
 @pytest.mark.parametrize("name,y_every,placed", [("c2", 1, False), ("c3", 4, False), ("c5", 16, False),
-                                                  ("c3", 8, True), ("c5", 32, True)])
+                                                  ("c1", 1, True), ("c2", 4, True), ("c3", 8, True),
+                                                  ("c5", 32, True)])
 def test_decode_stream(name, y_every, placed):
-    """placed: the layer as the bench times the split-schedule layers -- neurons dealt over the
-    tiles from 256 calibration tokens -- checked through its neuron table against the oracle of
-    the original layer."""
+    """placed: the layer as the bench times it -- neurons dealt over the tiles from 256
+    calibration tokens -- checked through its neuron table against the oracle of the original
+    layer."""
     from activation_sparse_pi_amd import _lib as L
     from activation_sparse_pi_amd.layer import DeviceLayer
     from .test_gpu_place import _check_placed, _placement
