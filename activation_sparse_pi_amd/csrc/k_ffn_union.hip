@@ -216,9 +216,10 @@ __global__ __launch_bounds__(UP_NT, GLU || !OFF32 ? 2 : 4) void k_union_up(
         }
         const int nfull = d >> 6;
         const int p0 = ro.part * nfull / ro.sp, p1 = (ro.part + 1) * nfull / ro.sp;
-        const int per = (p1 - p0 + UP_NW - 1) / UP_NW;
-        const int r0 = min(p1, p0 + wave * per), r1 = min(p1, r0 + per);
-        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+        // the waves take the part's runs in turn (wave w: runs p0 + w, p0 + w + 8, ..), so the
+        // block reads neighbouring 128-byte pieces of its 32 rows together
+        const int r0 = p0 + wave, nr = r0 < p1 ? (p1 - r0 + UP_NW - 1) / UP_NW : 0;
+        runs_mfma_full<NM, 2>(rx, ox, rw, ow, r0, nr, UP_NW, s_st[wave], acc);
         if ((d & 63) && wave == UP_NW - 1 && ro.part == ro.sp - 1) {
             const uint16_t* Wm[NM];
             Wm[0] = Wu;

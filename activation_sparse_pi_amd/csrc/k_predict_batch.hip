@@ -31,6 +31,10 @@ namespace {
 constexpr int PB_NW = 8;      // waves per block (both stages)
 constexpr int ZC = 512;       // rank values of z staged per pass in stage 2
 constexpr int PB_KS = 32;     // most stage-1 shares of d
+// Row pitch (floats) of a wave's 32 x 32 accumulator tile in LDS: lane l of register q at
+// q RP + l.  The reads take one token's 32 rows across the lanes, i.e. 16 registers at one lane
+// offset; with a pitch of 64 they would all fall in one bank, with 65 they spread over 16.
+constexpr int RP = 65;
 
 // ------------------------------------------------------------------------------------ stage 1
 __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__ x, int B,
@@ -67,15 +71,15 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
         ox[q] = 2u * (uint32_t)(offx[q] < 0 ? 0 : offx[q]) + 16u * (lane & 7);
         ow[q] = 2u * (uint32_t)(offw[q] < 0 ? 0 : offw[q]) + 16u * (lane & 7);
     }
-    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, r1, s_st[wave], acc);
+    runs_mfma_full<1, 2>(rx, ox, rw, ow, r0, r1 - r0, 1, s_st[wave], acc);
     if ((d & 63) && ks == nks - 1 && wave == PB_NW - 1) {
         const uint16_t* const Wm[1] = {W1t};
         runs_mfma<1>(x, offx, Wm, offw, d, nfull, nfull + 1, s_st[wave], acc);
     }
 
-    float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);
+    float* red = reinterpret_cast<float*>(&s_st[wave][0][0][0]);   // 16 RP of its 2048 floats
 #pragma unroll
-    for (int q = 0; q < 16; ++q) red[q * 64 + lane] = acc[0][q];
+    for (int q = 0; q < 16; ++q) red[q * RP + lane] = acc[0][q];
     __syncthreads();
     // outputs (row n of the tile, token b), two per thread, 32 consecutive rows per token
     float v[2];
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb1(const uint16_t* __restrict__
         float t = 0.f;
 #pragma unroll
         for (int w = 0; w < PB_NW; ++w)
-            t += reinterpret_cast<const float*>(&s_st[w][0][0][0])[d_reg(n) * 64 + d_lane(n, b)];
+            t += reinterpret_cast<const float*>(&s_st[w][0][0][0])[d_reg(n) * RP + d_lane(n, b)];
         v[q] = t;
         ob[q] = b;
         oj[q] = tile * 32 + n;
@@ -142,7 +146,8 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     __shared__ uint4 s_z[2][32][ZC / 8];     // z_hi, z_lo: [token][chunk of 8, swizzled]
     __shared__ unsigned long long s_u[PB_NW][2];   // per wave: OR of its tokens' ballots
     __shared__ unsigned long long s_bal[32][2];    // per token: its ballots of the 2 x 64 neurons
-    __shared__ uint4 s_w[PB_NW][32][8];      // per wave: W2t staging, then its accumulator
+    __shared__ uint4 s_w[PB_NW][33][8];      // per wave: W2t staging (32 rows), then its
+                                             // accumulator tile (16 RP floats)
     __shared__ int s_e[32];                  // per-token exponent e
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 128;
@@ -256,21 +261,32 @@ __global__ __launch_bounds__(PB_NW * 64) void k_pb2(const float* __restrict__ z,
     // 4. the two halves of the rank meet in LDS
     float* red = reinterpret_cast<float*>(&s_w[wave][0][0]);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) red[q * 64 + lane] = acc[q];
+    for (int q = 0; q < 16; ++q) red[q * RP + lane] = acc[q];
     __syncthreads();
     const int W = (F + 31) >> 5;
     unsigned long long uor[2] = {0ull, 0ull};
+    // every LDS read of the 8 (token, half) items first (unconditional: all addresses lie in
+    // the block's tiles), so that their latencies overlap instead of adding up item by item
+    float sum[8];
+    int es[4];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int tb = wave * 4 + (it >> 1), nh = it & 1;
-        const int n = nh * 64 + lane, i = n0 + n;
+        const int n = nh * 64 + lane;
         const int m = n >> 5, nl = n & 31;
         const float* r0 = reinterpret_cast<const float*>(&s_w[m][0][0]);
         const float* r1 = reinterpret_cast<const float*>(&s_w[m + 4][0][0]);
-        const int o = d_reg(nl) * 64 + d_lane(nl, tb);
+        const int o = d_reg(nl) * RP + d_lane(nl, tb);
+        sum[it] = r0[o] + r1[o];
+        if (nh == 0) es[it >> 1] = s_e[tb];
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int tb = wave * 4 + (it >> 1), nh = it & 1;
+        const int i = n0 + nh * 64 + lane;
         bool act = false;
         if (tb < B && i < F) {
-            const float l = ldexpf(r0[o] + r1[o], -s_e[tb]) + (nh ? bias1 : bias0);
+            const float l = ldexpf(sum[it], -es[it >> 1]) + (nh ? bias1 : bias0);
             act = l > theta;
             if (logits) logits[(size_t)tb * F + i] = l;
         }

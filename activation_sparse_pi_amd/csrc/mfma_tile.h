@@ -80,8 +80,8 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
     }
 }
 
-// runs_mfma over the full runs [r0, r1) (every one inside the rows), rows read
-// through buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and
+// runs_mfma over the full runs r0, r0 + rs, .. (n of them, every one inside the rows), rows
+// read through buffer resources: loader slot q takes byte offset ox[q] into x (resource rx) and
 // ow[q] into every W_m (resource rw[m], non-temporal), plus 128 bytes per run.  NB runs are
 // in flight per wave: a run's registers are refilled with the run NB ahead as soon as they
 // are staged.  The steady loop issues every load unconditionally and is unrolled NB times so
@@ -91,14 +91,14 @@ PI_DEV void runs_mfma(const uint16_t* __restrict__ x, const long long (&offx)[4]
 template <int NM, int NB>
 PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
                            const __amdgpu_buffer_rsrc_t (&rw)[NM], const uint32_t (&ow)[4],
-                           int r0, int r1, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
+                           int r0, int n, int rs, uint4 (*st)[32][8], f32x16_t (&acc)[NM]) {
     constexpr int NP = NM + 1;
     const int lane = threadIdx.x & 63;
     const int lrow = lane >> 3, lch = lane & 7;
     const int mi = lane & 31, half = lane >> 5;
     uint4 v[NB][NP][4];
-    auto load = [&](int rr, uint4(&b)[NP][4]) {
-        const int so = rr * 128;
+    auto load = [&](int j, uint4(&b)[NP][4]) {
+        const int so = (r0 + j * rs) * 128;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             b[0][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[q], so, 0));
@@ -124,8 +124,9 @@ PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
             for (int m = 0; m < NM; ++m) acc[m] = mfma16(st[m + 1][mi][slot], bx, acc[m]);
         }
     };
-    if (r1 - r0 < NB) {
-        for (int rr = r0; rr < r1; ++rr) {
+    const int r1 = n;               // runs are counted from 0 below
+    if (r1 < NB) {
+        for (int rr = 0; rr < r1; ++rr) {
             load(rr, v[0]);
             stage(v[0]);
             compute();
@@ -133,8 +134,8 @@ PI_DEV void runs_mfma_full(__amdgpu_buffer_rsrc_t rx, const uint32_t (&ox)[4],
         return;
     }
 #pragma unroll
-    for (int k = 0; k < NB; ++k) load(r0 + k, v[k]);
-    int rr = r0;
+    for (int k = 0; k < NB; ++k) load(k, v[k]);
+    int rr = 0;
     for (; rr + 2 * NB - 1 < r1; rr += NB) {
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
