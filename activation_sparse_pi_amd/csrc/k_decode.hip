@@ -63,10 +63,13 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     const uint16_t* __restrict__ Su, int d, float* __restrict__ h, const void* __restrict__ Wd,
     const uint16_t* __restrict__ Sd, float* __restrict__ part, int nhot) {
     constexpr int NT = B_WAVES * 64;
-    // row items per wave in flight: as many as the register budget of two blocks per CU
-    // allows, so that a tile with up to 3 (fp16, d <= 4096) or 4 (int4, d <= 8192) times 8
-    // items needs one memory round trip
-    constexpr int IPW = Q <= 4 ? 4 : Q <= 8 ? (WF == 0 ? 3 : 2) : 1;
+    // row items per wave in flight, so that a tile with up to 3 (fp16, d <= 4096; int4,
+    // d <= 8192) times 8 items needs one memory round trip.  The items are dealt round-robin
+    // (wave w: items w, w + 8, ..), so the dot products of a round are spread over all the
+    // waves; a slot past the tile's items still loads (a row already in L2), so int4 rows take
+    // 3 slots rather than the 4 the registers would allow (LLaMA-70B-shaped layer: 4 slots in
+    // blocks of 4 items per wave 32.47, round-robin 32.22, with 3 slots 31.70 us per step)
+    constexpr int IPW = Q <= 4 ? (WF == 1 ? 3 : 4) : Q <= 8 ? (WF == 0 ? 3 : 2) : 1;
     extern __shared__ __align__(16) char smem[];
     float* s_z = reinterpret_cast<float*>(smem);
     uint4* s_x = reinterpret_cast<uint4*>(smem + align16i(r * 4));
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         for (int c = tid; c < nc8; c += NT) s_x[c] = regroup(ld16(x + 8 * c));
         __syncthreads();
     }
-    for (int it0 = wave * IPW; it0 < items; it0 += B_WAVES * IPW) {
+    for (int it0 = wave; it0 < items; it0 += B_WAVES * IPW) {
         uint4 wr[IPW][Q];
         uint32_t sr[IPW][Q];   // raw fp16 scales, one per register
         // Every load is issued unconditionally, from chunk 0 of the row (row 0 for an empty
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         // round's loads into one memory round trip each.
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int it = it0 + i;
+            const int it = it0 + i * B_WAVES;
             const bool valid = it < items;
             const int k = GLU ? (it >> 1) : it;
             const int mat = GLU ? (it & 1) : 1;        // 0 = gate, 1 = up
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         }
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int it = it0 + i;
+            const int it = it0 + i * B_WAVES;
             if (it >= items) break;
             float dot = 0.f;
 #pragma unroll
