@@ -533,6 +533,37 @@ PI_DEV void tile_rows_store(const float* acc, float* s_l) {
     }
 }
 
+// The same 64 row sums through a transposed butterfly (8 rows per wave): a lane swaps half of
+// what it holds with the lane 1, 2 and then 4 apart, keeping (and adding) the other half --
+// one add per kept row instead of a whole-wave reduction per row -- and then adds the value of
+// the lane 8 apart.  Lane l of each row of 16 then holds the 16-lane sum of the wave's row
+// 4 b0 + 2 b1 + b2 (b: bits of l); the lanes with b3 = 0 store it as s4[4 k + l / 16] for tile
+// row k.  tile_row_sum(s4, k) adds the four in a fixed order.  Caller syncs between the two.
+template <int NW>
+PI_DEV void tile_rows_store4(const float* acc, float* s4) {
+    static_assert(TileRows<NW>::RPW == 8, "8 rows per wave");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
+    float a4[4], a2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                       // keep rows 4 b0 + i
+        const float keep = b0 ? acc[i + 4] : acc[i], send = b0 ? acc[i] : acc[i + 4];
+        a4[i] = keep + dpp_f<0xB1>(send);               // quad_perm [1,0,3,2]: lane ^ 1
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {                       // keep rows 4 b0 + 2 b1 + j
+        const float keep = b1 ? a4[j + 2] : a4[j], send = b1 ? a4[j] : a4[j + 2];
+        a2[j] = keep + dpp_f<0x4E>(send);               // quad_perm [2,3,0,1]: lane ^ 2
+    }
+    float v = (b2 ? a2[1] : a2[0]) + __shfl_xor(b2 ? a2[0] : a2[1], 4);
+    v += dpp_f<0x128>(v);                               // row_ror:8: lane ^ 8 within 16
+    if ((lane & 8) == 0) s4[(wave * 8 + 4 * b0 + 2 * b1 + b2) * 4 + (lane >> 4)] = v;
+}
+PI_DEV float tile_row_sum(const float* s4, int k) {
+    const float4 q = reinterpret_cast<const float4*>(s4)[k];
+    return (q.x + q.y) + (q.z + q.w);
+}
+
 // s_l[k] = W2t[tile*64 + k, :] . z for k < 64 (before the bias); z in LDS.  Caller syncs after.
 template <int NW, bool P8 = false>
 PI_DEV void tile_logits(const void* __restrict__ W2t, const uint16_t* __restrict__ S2, const float* s_z,

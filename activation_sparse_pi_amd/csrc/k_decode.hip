@@ -73,7 +73,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     extern __shared__ __align__(16) char smem[];
     float* s_z = reinterpret_cast<float*>(smem);
     uint4* s_x = reinterpret_cast<uint4*>(smem + align16i(r * 4));
-    __shared__ float s_red[64];
+    __shared__ __align__(16) float s_red[256];   // per tile row, four 16-lane partial sums
     __shared__ float s_dot[2][64];
     __shared__ int s_list[64];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
         tile_rows_load<B_WAVES, P8>(tr, W2t, S2, r, F, tile, c0);
         tile_rows_fma<B_WAVES, P8>(tr, s_z, r, c0, acc);
     }
-    tile_rows_store<B_WAVES>(acc, s_red);
+    tile_rows_store4<B_WAVES>(acc, s_red);
     __syncthreads();
 
     // --- the wave's hot neuron: its rows are in LDS by now (issued before the W2t rows, whose
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(B_WAVES * 64) void k_dec_stage2_up(
     bool act = false;
     float lg = 0.f;
     if (n < F) {
-        lg = s_red[lane] + bv;
+        lg = tile_row_sum(s_red, lane) + bv;
         act = lg > theta;
     }
     const unsigned long long bal = __ballot(act);
