@@ -303,7 +303,10 @@ hipError_t launch_attn_pqkv(const pi_attn_desc& a, const pi_pred_desc& p, const 
     const int q = (a.d + 511) / 512;
     if (q <= 2) return pqkv_launch<2, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
     if (q <= 4) return pqkv_launch<4, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
-    if (q <= 8) return pqkv_launch<8, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
+    // 3 rows a wave for d <= 4096: a LLaMA-7B-shaped layer (32 heads x 384 rows) fits one round
+    // of waves on the chip (2 rows: 22.2 us per step, 3: 21.8; OPT-30B-shaped d = 7168 keeps 2,
+    // 1 row there: 42.8 -> 43.6)
+    if (q <= 8) return pqkv_launch<8, 3>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
     if (q <= 16) return pqkv_launch<16, 2>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
     return pqkv_launch<32, 1>(a, p, x, z, theta, logits, mask, heads, count, qkv, s);
 }
