@@ -682,10 +682,14 @@ DecPlan plan_decode(int d, int r, int F, int wfmt) {
     const int sc = f16 ? DnGeom<0>::SC : DnGeom<1>::SC;
     p.nslices = (d + sc - 1) / sc;
     const int W = (F + 31) / 32;
-    // about 256 down blocks (one per CU); every range adds one partial row of d floats
-    int ns = (256 + p.nslices - 1) / p.nslices;
+    // down blocks: every range adds one partial row of d floats.  int4 rows: about 256, one per
+    // CU (the block's LDS leaves room for one; 512 would run as two rounds: LLaMA-70B-shaped
+    // layer 31.6 -> 36.1 us per step); fp16 rows: about 512, two per CU at once (OPT-30B-shaped
+    // layer 24.28 -> 23.62; 768: 26.2)
+    const int nblk = f16 ? 512 : 256, ns_max = f16 ? 64 : 32;
+    int ns = (nblk + p.nslices - 1) / p.nslices;
     const int ns_min = (W + (DEC_IDCAP / 32) - 1) / (DEC_IDCAP / 32);
-    if (ns > 32) ns = 32;
+    if (ns > ns_max) ns = ns_max;
     if (ns > W) ns = W;
     if (ns < ns_min) ns = ns_min;
     if (ns < 1) ns = 1;

@@ -262,8 +262,9 @@ int pi_decode_run(const pi_pred_desc* preds, const pi_ffn_desc* ffns, int nrep,
  * the last call's contents (nothing in it needs to start at zero): calls that overlap on one
  * GPU -- different streams or threads -- race, so the caller orders them.
  * Scratch a layer needs: 256-aligned (16384 + 4 r) + 256-aligned (4 F) + 4 d P bytes, with
- * P = ceil(F/64) for the fused schedule and the split schedule's range count (at most 32)
- * otherwise; a layer that needs more than PI_NOALLOC_SCRATCH_BYTES is rejected with
+ * P = ceil(F/64) for the fused schedule and the split schedule's range count (at most 32 for
+ * int4 rows, 64 for fp16 rows) otherwise; a layer that needs more than PI_NOALLOC_SCRATCH_BYTES
+ * is rejected with
  * PI_ERR_WORKSPACE before any HIP call.
  * Every other argument, output, check and error is that of pi_decode_run.                  */
 #define PI_NOALLOC_SCRATCH_BYTES (4u << 20)
